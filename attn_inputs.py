@@ -1,0 +1,111 @@
+"""Seeded synthetic inputs shared by the oracle side and the GPU side.
+
+This module holds no attention arithmetic: it only draws random numbers and
+names the workloads.  Both the parity tests and bench.py build Q/K/V here, so
+the two sides always see the same bf16 bits.
+
+Recipe: a CPU ``torch.Generator`` seeded with the workload's seed draws
+standard normals in float32 in the order Q, K, V (shape [B,S,H,D], or
+[T,H,D] for packed variable-length batches); each tensor is multiplied by
+its standard deviation and rounded to bfloat16 with round-to-nearest-even.
+Variable-length batches draw their lengths first from
+``numpy.random.default_rng(seed).integers(lo, hi, n, endpoint=True)``.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic attention-forward problem."""
+    name: str
+    B: int                      # batch size, or number of packed sequences
+    S: int                      # sequence length (varlen: the maximum length)
+    H: int
+    D: int
+    causal: bool
+    seed: int
+    q_std: float = 1.0
+    kv_std: float = 1.0
+    varlen: Optional[tuple] = None   # (n_seqs, lo, hi) drawn uniformly, inclusive
+    lengths: tuple = field(default=())
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+
+def varlen_lengths(n: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Sequence lengths uniform on [lo, hi] (inclusive), seeded."""
+    return np.random.default_rng(seed).integers(lo, hi, n, endpoint=True).astype(np.int64)
+
+
+def cu_seqlens_of(lengths) -> np.ndarray:
+    """int32 prefix sums [0, L0, L0+L1, ...]."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, np.int64))]).astype(np.int32)
+
+
+def draw_qkv(shape, seed: int, q_std: float = 1.0, kv_std: float = 1.0):
+    """Q, K, V as CPU bf16 tensors of the given shape (drawn in that order)."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    out = []
+    for std in (q_std, kv_std, kv_std):
+        x = torch.randn(*shape, generator=g, dtype=torch.float32)
+        if std != 1.0:
+            x = x * std
+        out.append(x.to(torch.bfloat16))
+    return tuple(out)
+
+
+def make(w: Workload):
+    """(q, k, v, cu_seqlens or None, S) for a workload; tensors are CPU bf16."""
+    if w.varlen is not None:
+        n, lo, hi = w.varlen
+        lens = varlen_lengths(n, lo, hi, w.seed)
+        cu = cu_seqlens_of(lens)
+        q, k, v = draw_qkv((int(cu[-1]), w.H, w.D), w.seed, w.q_std, w.kv_std)
+        return q, k, v, cu, int(lens.max())
+    if w.lengths:
+        cu = cu_seqlens_of(w.lengths)
+        q, k, v = draw_qkv((int(cu[-1]), w.H, w.D), w.seed, w.q_std, w.kv_std)
+        return q, k, v, cu, int(max(w.lengths))
+    q, k, v = draw_qkv((w.B, w.S, w.H, w.D), w.seed, w.q_std, w.kv_std)
+    return q, k, v, None, w.S
+
+
+def flops(w: Workload, cu=None) -> float:
+    """Algorithmic flops: 4*B*H*S^2*D, halved for causal (varlen: sum over sequences)."""
+    if cu is not None:
+        lens = np.diff(np.asarray(cu, np.int64))
+        tot = float(np.sum(lens.astype(np.float64) ** 2)) * 4.0 * w.H * w.D
+    else:
+        tot = 4.0 * w.B * w.H * float(w.S) ** 2 * w.D
+    return tot / 2.0 if w.causal else tot
+
+
+# The workloads: a tiny non-causal case the oracle finishes instantly; dense
+# 2k heads (both masks); 32k causal long context; a packed variable-length
+# causal batch; wide heads with high-spread logits; 8k causal (the other
+# sequence length the throughput metric names); and the install-check shape
+# (1, 8, 512, 64) causal from the FlashAttention-4 usage guide.
+WORKLOADS = {
+    "tiny_b1h2s128d64": Workload("tiny_b1h2s128d64", 1, 128, 2, 64, False, seed=1),
+    "dense_b2h16s2048d128": Workload("dense_b2h16s2048d128", 2, 2048, 16, 128, False, seed=2),
+    "dense_b2h16s2048d128_causal": Workload("dense_b2h16s2048d128_causal", 2, 2048, 16, 128,
+                                            True, seed=2),
+    "long_b1h16s32768d128_causal": Workload("long_b1h16s32768d128_causal", 1, 32768, 16, 128,
+                                            True, seed=3),
+    "varlen_16x512to8192_h32d128_causal": Workload("varlen_16x512to8192_h32d128_causal", 16,
+                                                   8192, 32, 128, True, seed=4,
+                                                   varlen=(16, 512, 8192)),
+    "wide_b2h16s8192d256_spread3": Workload("wide_b2h16s8192d256_spread3", 2, 8192, 16, 256,
+                                            False, seed=5, q_std=3.0),
+    "causal_b2h16s8192d128": Workload("causal_b2h16s8192d128", 2, 8192, 16, 128, True, seed=6),
+    "smoke_b1h8s512d64_causal": Workload("smoke_b1h8s512d64_causal", 1, 512, 8, 64, True, seed=7),
+}

@@ -1,0 +1,203 @@
+"""Test infrastructure only: the fp64 CPU oracle for exact attention forward.
+
+The oracle is a plain, slow, double-precision C implementation of
+O = softmax(scale * Q K^T + causal mask) V and the row logsumexp
+(``attn_oracle.c``), plus a 50-digit brute-force evaluator for tiny inputs
+(``brute.py``).  It shares no code with the HIP library and never imports it.
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may use it; the product path must never route through it.
+
+Every method below is a thin ctypes wrapper; the arithmetic lives in C.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "attn_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force: bool = False, src: str = SOURCE, out: str = LIB_PATH) -> str:
+    """Compile an oracle C source into a shared library with gcc + OpenMP."""
+    stale = not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src)
+    if force or stale:
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC",
+               "-std=c11", "-o", tmp, src, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _as_bits(t) -> np.ndarray:
+    """bf16 data as a contiguous uint16 numpy array of its bit patterns.
+
+    Accepts a numpy uint16 array or a CPU torch bfloat16 tensor.
+    """
+    if isinstance(t, np.ndarray):
+        assert t.dtype == np.uint16
+        return np.ascontiguousarray(t)
+    import torch  # local: torch is only needed when handed a tensor
+    assert t.dtype == torch.bfloat16 and t.device.type == "cpu"
+    return np.ascontiguousarray(t.contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def _cu(cu_seqlens):
+    if cu_seqlens is None:
+        return None
+    return np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+
+
+def _dims(q_shape, cu):
+    """(B, S, H, D) from a dense [B,S,H,D] shape, or varlen [T,H,D] + cu_seqlens."""
+    if cu is None:
+        B, S, H, D = q_shape
+        return B, S, H, D
+    _, H, D = q_shape
+    B = len(cu) - 1
+    S = int(np.max(np.diff(cu))) if B > 0 else 0
+    return B, S, H, D
+
+
+def _shapes(B, S, H, D, cu):
+    if cu is None:
+        return (B, S, H, D), (B, H, S)
+    T = int(cu[-1])
+    return (T, H, D), (H, T)
+
+
+class OracleLib:
+    """ctypes view of one compiled oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_attn_fwd_f64.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, P]
+        lib.oracle_attn_fwd_bf16.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, P]
+        lib.oracle_attn_rows_bf16.argtypes = [P, P, P, P, i64, P, P, i32, i32, i32, i32,
+                                              f64, i32, P]
+        for fn in (lib.oracle_attn_fwd_f64, lib.oracle_attn_fwd_bf16, lib.oracle_attn_rows_bf16):
+            fn.restype = i32
+        lib.oracle_exp2.argtypes = [P, P, i64]
+        lib.oracle_exp2.restype = None
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = i32
+        lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_f64.restype = f64
+        self.lib = lib
+        self.path = path
+
+    def attention_f64(self, q, k, v, scale, causal, cu_seqlens=None):
+        """Attention on float64 inputs; q, k, v are [B,S,H,D] (or [T,H,D] varlen).
+
+        Returns (o float64 like q, lse float64 [B,H,S] or [H,T]).
+        """
+        q = np.ascontiguousarray(q, dtype=np.float64)
+        k = np.ascontiguousarray(k, dtype=np.float64)
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        cu = _cu(cu_seqlens)
+        B, S, H, D = _dims(q.shape, cu)
+        o_shape, l_shape = _shapes(B, S, H, D, cu)
+        o = np.empty(o_shape, np.float64)
+        lse = np.empty(l_shape, np.float64)
+        rc = self.lib.oracle_attn_fwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                          B, H, S, D, float(scale), int(bool(causal)), _ptr(cu))
+        if rc != 0:
+            raise ValueError("oracle_attn_fwd_f64 rejected its arguments")
+        return o, lse
+
+    def attention_bf16(self, q, k, v, scale, causal, cu_seqlens=None):
+        """Attention on bf16 inputs (torch bf16 CPU tensors or uint16 bit arrays).
+
+        Shapes as in attention_f64; the result is float64.
+        """
+        qb, kb, vb = _as_bits(q), _as_bits(k), _as_bits(v)
+        cu = _cu(cu_seqlens)
+        B, S, H, D = _dims(qb.shape, cu)
+        o_shape, l_shape = _shapes(B, S, H, D, cu)
+        o = np.empty(o_shape, np.float64)
+        lse = np.empty(l_shape, np.float64)
+        rc = self.lib.oracle_attn_fwd_bf16(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(o), _ptr(lse),
+                                           B, H, S, D, float(scale), int(bool(causal)), _ptr(cu))
+        if rc != 0:
+            raise ValueError("oracle_attn_fwd_bf16 rejected its arguments")
+        return o, lse
+
+    def attention_rows_bf16(self, q, k, v, rows, scale, causal, cu_seqlens=None):
+        """Attention for selected rows only.
+
+        rows are numbered like the lse layout: dense (b*H + h)*S + i, varlen
+        h*T + t.  Returns (o_rows float64 [n, D], lse_rows float64 [n]).
+        """
+        qb, kb, vb = _as_bits(q), _as_bits(k), _as_bits(v)
+        cu = _cu(cu_seqlens)
+        B, S, H, D = _dims(qb.shape, cu)
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        o = np.empty((len(rows), D), np.float64)
+        lse = np.empty(len(rows), np.float64)
+        rc = self.lib.oracle_attn_rows_bf16(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(rows),
+                                            len(rows), _ptr(o), _ptr(lse), B, H, S, D,
+                                            float(scale), int(bool(causal)), _ptr(cu))
+        if rc != 0:
+            raise ValueError("oracle_attn_rows_bf16 rejected its arguments")
+        return o, lse
+
+    def exp2(self, x) -> np.ndarray:
+        """2**x in float64 for float32 inputs (what the device polynomial approximates)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        y = np.empty(x.shape, np.float64)
+        self.lib.oracle_exp2(_ptr(x), _ptr(y), x.size)
+        return y
+
+    def bf16_to_f64(self, bits: int) -> float:
+        """Exact value of one bf16 bit pattern."""
+        return self.lib.oracle_bf16_to_f64(int(bits) & 0xFFFF)
+
+    def num_threads(self) -> int:
+        """Threads the oracle's OpenMP regions use."""
+        return self.lib.oracle_num_threads()
+
+
+_default = None
+
+
+def lib() -> OracleLib:
+    """The oracle built from attn_oracle.c (compiled on first use)."""
+    global _default
+    if _default is None:
+        _default = OracleLib(build())
+    return _default
+
+
+def attention_f64(*a, **kw):
+    return lib().attention_f64(*a, **kw)
+
+
+def attention_bf16(*a, **kw):
+    return lib().attention_bf16(*a, **kw)
+
+
+def attention_rows_bf16(*a, **kw):
+    return lib().attention_rows_bf16(*a, **kw)
+
+
+def exp2(x):
+    return lib().exp2(x)
+
+
+def bf16_to_f64(bits):
+    return lib().bf16_to_f64(bits)
+
+
+def num_threads():
+    return lib().num_threads()

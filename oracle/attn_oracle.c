@@ -1,0 +1,291 @@
+/*
+ * attn_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, double-precision CPU implementation of exact attention
+ * forward, O = softmax(scale * Q K^T + causal mask) V, plus the natural-log
+ * logsumexp of each row.  It exists to check the GPU library against; it is
+ * not part of the product.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load it.  It shares no source, header,
+ * table or constant with the HIP library.
+ *
+ * What it follows (FlashAttention-4 paper as translated on 171host.com):
+ *   - section 2.1 "Multi-head attention" names the operation; its formula was
+ *     lost from the page, so the textbook definition is written out here:
+ *     s_ij = scale * <q_i, k_j>, P = softmax over the allowed keys, O = P V;
+ *   - section 3.1.2: per row, take the maximum, subtract it, exponentiate,
+ *     then sum;  section 3.1.4: the output is normalised by that sum at the
+ *     end;
+ *   - section 3.3 (LPT for causal masking): scores above the diagonal are
+ *     masked, i.e. query i may use key j only when j <= i.
+ * The row is processed in two plain passes (max, then exp/sum/weighted sum);
+ * no blocking, no online rescaling, no reordering beyond that.
+ *
+ * Layouts (row-major, contiguous):
+ *   dense : q, k, v, o are [B, S, H, D]; lse is [B, H, S]
+ *   varlen: q, k, v, o are [T, H, D] with T = cu_seqlens[B]; lse is [H, T];
+ *           sequence b owns tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 and
+ *           attends only within itself (query and key lengths are equal).
+ * Inputs come either as double or as bfloat16 bit patterns (uint16), which
+ * are widened exactly to double (bf16 is the top half of an IEEE float).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Exact widening of one bfloat16 bit pattern. */
+double oracle_bf16_to_f64(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* A read-only tensor that is either double or bf16 bits. */
+typedef struct {
+    const void *p;
+    int is_bf16;
+} tensor_in;
+
+static inline double at(tensor_in t, int64_t i)
+{
+    if (t.is_bf16)
+        return oracle_bf16_to_f64(((const uint16_t *)t.p)[i]);
+    return ((const double *)t.p)[i];
+}
+
+/* Where a sequence lives: first token index and length. */
+typedef struct {
+    int64_t tok0;
+    int len;
+} seq_span;
+
+/*
+ * One query row i of one (sequence, head): two passes over the allowed keys.
+ * s must hold at least len doubles.  Writes D outputs to o_row and the
+ * row's logsumexp to *lse_out.
+ */
+static void attend_one_row(tensor_in q, tensor_in k, tensor_in v,
+                           double *o_row, double *lse_out,
+                           seq_span sp, int i, int h, int H, int D,
+                           double scale, int causal, double *s)
+{
+    const int nkeys = causal ? i + 1 : sp.len;
+    const int64_t qbase = ((sp.tok0 + i) * H + h) * (int64_t)D;
+
+    /* pass 1: scores and their maximum */
+    double m = -INFINITY;
+    for (int j = 0; j < nkeys; ++j) {
+        const int64_t kbase = ((sp.tok0 + j) * H + h) * (int64_t)D;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d)
+            dot += at(q, qbase + d) * at(k, kbase + d);
+        s[j] = scale * dot;
+        if (s[j] > m)
+            m = s[j];
+    }
+
+    /* pass 2: exponentiate against the maximum, sum, weight V */
+    double l = 0.0;
+    for (int j = 0; j < nkeys; ++j) {
+        s[j] = exp(s[j] - m);
+        l += s[j];
+    }
+    for (int d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int j = 0; j < nkeys; ++j)
+            acc += s[j] * at(v, ((sp.tok0 + j) * H + h) * (int64_t)D + d);
+        o_row[d] = acc / l;
+    }
+    *lse_out = m + log(l);
+}
+
+/* Span of sequence b: dense uses b*S .. b*S+S-1, varlen reads cu_seqlens. */
+static seq_span span_of(int b, int S, const int *cu_seqlens)
+{
+    seq_span sp;
+    if (cu_seqlens) {
+        sp.tok0 = cu_seqlens[b];
+        sp.len = cu_seqlens[b + 1] - cu_seqlens[b];
+    } else {
+        sp.tok0 = (int64_t)b * S;
+        sp.len = S;
+    }
+    return sp;
+}
+
+/*
+ * Map a row id, numbered like the lse layout, to (b, h, i).
+ *   dense : row = (b*H + h)*S + i
+ *   varlen: row = h*T + t, t a global token index; b is the sequence holding t
+ */
+static void decode_row(int64_t row, int B, int H, int S, const int *cu_seqlens,
+                       int *b, int *h, int *i)
+{
+    if (!cu_seqlens) {
+        *i = (int)(row % S);
+        *h = (int)((row / S) % H);
+        *b = (int)(row / ((int64_t)S * H));
+        return;
+    }
+    const int64_t T = cu_seqlens[B];
+    const int64_t t = row % T;
+    *h = (int)(row / T);
+    int bb = 0;
+    while (bb + 1 < B && cu_seqlens[bb + 1] <= t)
+        ++bb;
+    *b = bb;
+    *i = (int)(t - cu_seqlens[bb]);
+}
+
+static int max_len(int B, int S, const int *cu_seqlens)
+{
+    if (!cu_seqlens)
+        return S;
+    int mx = 0;
+    for (int b = 0; b < B; ++b) {
+        int L = cu_seqlens[b + 1] - cu_seqlens[b];
+        if (L > mx)
+            mx = L;
+    }
+    return mx;
+}
+
+/*
+ * Attention for an explicit list of rows.  o_rows is [n_rows, D] and
+ * lse_rows is [n_rows]; either may be NULL.  Returns 0, or -1 on bad input.
+ */
+static int attend_rows(tensor_in q, tensor_in k, tensor_in v,
+                       const int64_t *rows, int64_t n_rows,
+                       double *o_rows, double *lse_rows,
+                       int B, int H, int S, int D, double scale, int causal,
+                       const int *cu_seqlens)
+{
+    if (B <= 0 || H <= 0 || D <= 0 || (!cu_seqlens && S <= 0))
+        return -1;
+    const int Lmax = max_len(B, S, cu_seqlens);
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Lmax > 0 ? Lmax : 1));
+        double *o_tmp = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!s || !o_tmp) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 8)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int b, h, i;
+                decode_row(rows[r], B, H, S, cu_seqlens, &b, &h, &i);
+                seq_span sp = span_of(b, S, cu_seqlens);
+                double lse;
+                attend_one_row(q, k, v, o_tmp, &lse, sp, i, h, H, D, scale, causal, s);
+                if (o_rows)
+                    memcpy(o_rows + r * (int64_t)D, o_tmp, sizeof(double) * (size_t)D);
+                if (lse_rows)
+                    lse_rows[r] = lse;
+            }
+        }
+        free(s);
+        free(o_tmp);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Full attention: o in the q layout, lse in the lse layout (either may be
+ * NULL).  Every row of every (sequence, head) is computed.
+ */
+static int attend_all(tensor_in q, tensor_in k, tensor_in v, double *o, double *lse,
+                      int B, int H, int S, int D, double scale, int causal,
+                      const int *cu_seqlens)
+{
+    if (B <= 0 || H <= 0 || D <= 0 || (!cu_seqlens && S <= 0))
+        return -1;
+    const int64_t T = cu_seqlens ? cu_seqlens[B] : (int64_t)B * S;
+    const int64_t n_rows = T * H;
+    int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_rows > 0 ? n_rows : 1));
+    double *o_rows = (double *)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1) * D);
+    double *l_rows = (double *)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1));
+    if (!rows || !o_rows || !l_rows) {
+        free(rows);
+        free(o_rows);
+        free(l_rows);
+        return -1;
+    }
+    for (int64_t r = 0; r < n_rows; ++r)
+        rows[r] = r;
+    int rc = attend_rows(q, k, v, rows, n_rows, o_rows, l_rows, B, H, S, D, scale,
+                         causal, cu_seqlens);
+    if (rc == 0) {
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int b, h, i;
+            decode_row(r, B, H, S, cu_seqlens, &b, &h, &i);
+            seq_span sp = span_of(b, S, cu_seqlens);
+            if (o)
+                memcpy(o + ((sp.tok0 + i) * H + h) * (int64_t)D, o_rows + r * (int64_t)D,
+                       sizeof(double) * (size_t)D);
+            if (lse)
+                lse[r] = l_rows[r];
+        }
+    }
+    free(rows);
+    free(o_rows);
+    free(l_rows);
+    return rc;
+}
+
+/* ---- exported entry points (C ABI, loaded by ctypes from Python) ---- */
+
+int oracle_attn_fwd_f64(const double *q, const double *k, const double *v,
+                        double *o, double *lse, int B, int H, int S, int D,
+                        double scale, int causal, const int *cu_seqlens)
+{
+    tensor_in tq = {q, 0}, tk = {k, 0}, tv = {v, 0};
+    return attend_all(tq, tk, tv, o, lse, B, H, S, D, scale, causal, cu_seqlens);
+}
+
+int oracle_attn_fwd_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         double *o, double *lse, int B, int H, int S, int D,
+                         double scale, int causal, const int *cu_seqlens)
+{
+    tensor_in tq = {q, 1}, tk = {k, 1}, tv = {v, 1};
+    return attend_all(tq, tk, tv, o, lse, B, H, S, D, scale, causal, cu_seqlens);
+}
+
+int oracle_attn_rows_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                          const int64_t *rows, int64_t n_rows,
+                          double *o_rows, double *lse_rows,
+                          int B, int H, int S, int D, double scale, int causal,
+                          const int *cu_seqlens)
+{
+    tensor_in tq = {q, 1}, tk = {k, 1}, tv = {v, 1};
+    return attend_rows(tq, tk, tv, rows, n_rows, o_rows, lse_rows, B, H, S, D, scale,
+                       causal, cu_seqlens);
+}
+
+/*
+ * 2^x in double precision for float inputs: the definition that the
+ * device-side polynomial exp2 approximates (FlashAttention-4 paper,
+ * section 3.1.3, "Emulation of the exponential").
+ */
+void oracle_exp2(const float *x, double *y, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = exp2((double)x[i]);
+}
+
+/* Number of threads a parallel region of this library will use. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,185 @@
+"""Checks that pin the fp64 oracle to facts it does not compute itself.
+
+Each check takes an ``OracleLib``-like object (``attention_f64`` method) and
+raises AssertionError when the oracle disagrees with what the definition of
+attention fixes.  The checks come from closed forms, invariances and an
+independent 50-digit brute force; none re-types the oracle's own formula.
+They are used on the real oracle (test_oracle_pins.py) and on deliberately
+broken copies of it (test_oracle_mutants.py), which every one of these
+mistakes must trip.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import brute
+
+
+def _bf16_grid(rng, shape, std=1.0):
+    """Random values that are exactly representable in bf16 (8-bit mantissa)."""
+    x = rng.standard_normal(shape) * std
+    m, e = np.frexp(x)
+    m = np.round(m * 256.0) / 256.0
+    return np.ldexp(m, e)
+
+
+def check_brute_force_tiny(o):
+    """Two-pass oracle == 50-digit exp-without-max-subtraction on tiny inputs."""
+    rng = np.random.default_rng(11)
+    for causal in (False, True):
+        B, S, H, D = 2, 7, 2, 5
+        q, k, v = (_bf16_grid(rng, (B, S, H, D)) for _ in range(3))
+        scale = 0.37
+        got_o, got_l = o.attention_f64(q, k, v, scale, causal)
+        ref_o, ref_l = brute.attention(q, k, v, scale, causal)
+        assert np.max(np.abs(got_o - ref_o)) <= 1e-12, ("brute O", causal)
+        assert np.max(np.abs(got_l - ref_l)) <= 1e-12, ("brute LSE", causal)
+    # packed variable-length batch, causal
+    cu = [0, 3, 9, 10]
+    q, k, v = (_bf16_grid(rng, (10, 2, 4)) for _ in range(3))
+    got_o, got_l = o.attention_f64(q, k, v, 0.5, True, cu)
+    ref_o, ref_l = brute.attention(q, k, v, 0.5, True, cu)
+    assert np.max(np.abs(got_o - ref_o)) <= 1e-12, "brute varlen O"
+    assert np.max(np.abs(got_l - ref_l)) <= 1e-12, "brute varlen LSE"
+
+
+def check_equal_logits_mean_of_v(o):
+    """Q = 0 makes every logit equal: O_i is the mean of the allowed V rows
+    and LSE_i = ln(number of allowed keys)."""
+    rng = np.random.default_rng(12)
+    B, S, H, D = 2, 9, 3, 6
+    q = np.zeros((B, S, H, D))
+    k, v = rng.standard_normal((B, S, H, D)), rng.standard_normal((B, S, H, D))
+    for causal in (False, True):
+        got_o, got_l = o.attention_f64(q, k, v, 0.3, causal)
+        for i in range(S):
+            n = i + 1 if causal else S
+            mean = v[:, :n].mean(axis=1)
+            assert np.allclose(got_o[:, i], mean, rtol=0, atol=1e-13), ("mean of V", causal, i)
+            assert np.allclose(got_l[:, :, i], np.log(n), rtol=0, atol=1e-13), ("ln n", causal, i)
+
+
+def check_dominant_logit_selects_row(o):
+    """One logit 60 above all others: O_i = v_{j*} (to e^-60) and LSE_i = 60."""
+    rng = np.random.default_rng(13)
+    S, D, scale = 12, 12, 0.25
+    for causal in (False, True):
+        target = np.array([rng.integers(0, (i + 1) if causal else S) for i in range(S)])
+        q = np.zeros((1, S, 1, D))
+        k = np.zeros((1, S, 1, D))
+        for i in range(S):
+            q[0, i, 0, target[i]] = 1.0          # query i points at key target[i]
+        for j in range(S):
+            k[0, j, 0, j] = 60.0 / scale          # key j answers only direction j
+        v = rng.standard_normal((1, S, 1, D))
+        got_o, got_l = o.attention_f64(q, k, v, scale, causal)
+        for i in range(S):
+            assert np.allclose(got_o[0, i, 0], v[0, target[i], 0], rtol=0, atol=1e-20), \
+                ("dominant O", causal, i)
+            assert abs(got_l[0, 0, i] - 60.0) <= 1e-12, ("dominant LSE", causal, i)
+
+
+def check_causal_row0(o):
+    """Causal row 0 sees only key 0: O_0 = v_0 exactly, LSE_0 = scale*q_0.k_0."""
+    rng = np.random.default_rng(14)
+    B, S, H, D = 2, 8, 2, 7
+    q, k, v = (_bf16_grid(rng, (B, S, H, D)) for _ in range(3))
+    got_o, got_l = o.attention_f64(q, k, v, 0.21, True)
+    assert np.array_equal(got_o[:, 0], v[:, 0]), "causal row 0 O"
+    s00 = 0.21 * np.einsum("bhd,bhd->bh", q[:, 0], k[:, 0])
+    assert np.allclose(got_l[:, :, 0], s00, rtol=0, atol=1e-14), "causal row 0 LSE"
+
+
+def check_kv_permutation_invariance(o):
+    """Non-causal attention does not depend on the order of the (k_j, v_j) pairs."""
+    rng = np.random.default_rng(15)
+    B, S, H, D = 2, 11, 2, 6
+    q, k, v = (rng.standard_normal((B, S, H, D)) for _ in range(3))
+    perm = rng.permutation(S)
+    o1, l1 = o.attention_f64(q, k, v, 0.4, False)
+    o2, l2 = o.attention_f64(q, k[:, perm], v[:, perm], 0.4, False)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-13), "permutation O"
+    assert np.allclose(l1, l2, rtol=0, atol=1e-13), "permutation LSE"
+    # and it does depend on pairing: permuting V alone changes O
+    o3, _ = o.attention_f64(q, k, v[:, perm], 0.4, False)
+    assert not np.allclose(o1, o3, rtol=0, atol=1e-6), "pairing of K and V rows"
+
+
+def check_key_shift(o):
+    """k_j += u for all j: O unchanged, LSE_i += scale * q_i . u."""
+    rng = np.random.default_rng(16)
+    B, S, H, D = 1, 10, 2, 5
+    q, k, v = (rng.standard_normal((B, S, H, D)) for _ in range(3))
+    u = rng.standard_normal((H, D))
+    for causal in (False, True):
+        o1, l1 = o.attention_f64(q, k, v, 0.5, causal)
+        o2, l2 = o.attention_f64(q, k + u[None, None], v, 0.5, causal)
+        assert np.allclose(o1, o2, rtol=0, atol=1e-12), ("shift O", causal)
+        shift = 0.5 * np.einsum("bshd,hd->bhs", q, u)
+        assert np.allclose(l2 - l1, shift, rtol=0, atol=1e-12), ("shift LSE", causal)
+
+
+def check_affine_v(o):
+    """V -> V A + 1 b^T maps O -> O A + 1 b^T (softmax rows sum to one)."""
+    rng = np.random.default_rng(17)
+    B, S, H, D = 2, 9, 1, 4
+    q, k, v = (rng.standard_normal((B, S, H, D)) for _ in range(3))
+    A = rng.standard_normal((D, D))
+    bvec = rng.standard_normal(D)
+    for causal in (False, True):
+        o1, l1 = o.attention_f64(q, k, v, 0.7, causal)
+        o2, l2 = o.attention_f64(q, k, v @ A + bvec, 0.7, causal)
+        assert np.allclose(o2, o1 @ A + bvec, rtol=0, atol=1e-12), ("affine O", causal)
+        assert np.allclose(l1, l2, rtol=0, atol=0), ("affine LSE", causal)
+
+
+def check_causal_prefix(o):
+    """Causal row i equals non-causal attention over the first i+1 keys."""
+    rng = np.random.default_rng(18)
+    B, S, H, D = 1, 9, 2, 5
+    q, k, v = (rng.standard_normal((B, S, H, D)) for _ in range(3))
+    oc, lc = o.attention_f64(q, k, v, 0.45, True)
+    for i in range(S):
+        on, ln = o.attention_f64(q[:, :i + 1], k[:, :i + 1], v[:, :i + 1], 0.45, False)
+        assert np.allclose(oc[:, i], on[:, i], rtol=0, atol=1e-13), ("prefix O", i)
+        assert np.allclose(lc[:, :, i], ln[:, :, i], rtol=0, atol=1e-13), ("prefix LSE", i)
+
+
+def check_varlen_equals_dense_runs(o):
+    """A packed batch equals each sequence run on its own."""
+    rng = np.random.default_rng(19)
+    lens = [5, 1, 8, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    H, D = 2, 4
+    q, k, v = (rng.standard_normal((cu[-1], H, D)) for _ in range(3))
+    for causal in (False, True):
+        op, lp = o.attention_f64(q, k, v, 0.6, causal, cu)
+        for b, L in enumerate(lens):
+            sl = slice(cu[b], cu[b + 1])
+            od, ld = o.attention_f64(q[None, sl], k[None, sl], v[None, sl], 0.6, causal)
+            assert np.array_equal(op[sl], od[0]), ("varlen O", causal, b)
+            assert np.array_equal(lp[:, sl], ld[0]), ("varlen LSE", causal, b)
+
+
+def check_scale_is_a_logit_multiplier(o):
+    """attention(Q, scale=a) == attention(a*Q, scale=1) for a power of two a."""
+    rng = np.random.default_rng(20)
+    B, S, H, D = 1, 6, 2, 3
+    q, k, v = (rng.standard_normal((B, S, H, D)) for _ in range(3))
+    o1, l1 = o.attention_f64(q, k, v, 0.125, True)
+    o2, l2 = o.attention_f64(q * 0.125, k, v, 1.0, True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "scale"
+
+
+ALL_CHECKS = [
+    check_brute_force_tiny,
+    check_equal_logits_mean_of_v,
+    check_dominant_logit_selects_row,
+    check_causal_row0,
+    check_kv_permutation_invariance,
+    check_key_shift,
+    check_affine_v,
+    check_causal_prefix,
+    check_varlen_equals_dense_runs,
+    check_scale_is_a_logit_multiplier,
+]

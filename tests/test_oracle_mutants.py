@@ -1,0 +1,75 @@
+"""Plausible mistakes planted in a copy of the oracle must fail a pin.
+
+Each mutant is the oracle's C source with one small, realistic error (an
+off-by-one mask, a dropped scale, a transposed or mis-indexed operand, a
+wrong sign, a missing normalisation).  It is compiled to a temporary library
+on the CPU and run through the pins of oracle_pins.py; the test passes only
+if at least one pin rejects it.  This shows the pins would catch such a
+mistake in the real oracle.
+"""
+import os
+import subprocess
+import sys
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+for _p in (os.path.dirname(_HERE), _HERE):   # also run as a child script
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
+
+import pytest  # noqa: E402
+
+import oracle  # noqa: E402
+import oracle_pins  # noqa: E402
+
+# (name, text in attn_oracle.c, replacement)
+MUTANTS = [
+    ("mask_excludes_diagonal", "causal ? i + 1 : sp.len", "causal ? i : sp.len"),
+    ("mask_admits_next_key", "causal ? i + 1 : sp.len", "causal ? (i + 2 < sp.len ? i + 2 : sp.len) : sp.len"),
+    ("scale_dropped", "s[j] = scale * dot;", "s[j] = dot;"),
+    ("k_read_at_query_row", "dot += at(q, qbase + d) * at(k, kbase + d);",
+     "dot += at(q, qbase + d) * at(k, qbase + d);"),
+    ("exp_sign_flipped", "s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
+    ("lse_missing_max", "*lse_out = m + log(l);", "*lse_out = log(l);"),
+    ("normalisation_dropped", "o_row[d] = acc / l;", "o_row[d] = acc;"),
+    ("v_head_ignored", "acc += s[j] * at(v, ((sp.tok0 + j) * H + h) * (int64_t)D + d);",
+     "acc += s[j] * at(v, ((sp.tok0 + j) * H + 0) * (int64_t)D + d);"),
+    ("v_read_at_query_row", "acc += s[j] * at(v, ((sp.tok0 + j) * H + h) * (int64_t)D + d);",
+     "acc += s[j] * at(v, ((sp.tok0 + i) * H + h) * (int64_t)D + d);"),
+    ("dense_batch_offset_wrong", "sp.tok0 = (int64_t)b * S;", "sp.tok0 = (int64_t)b;"),
+    ("varlen_length_short", "sp.len = cu_seqlens[b + 1] - cu_seqlens[b];",
+     "sp.len = cu_seqlens[b + 1] - cu_seqlens[b] - (b > 0);"),
+    ("row_decode_swaps_h_i", "*i = (int)(row % S);\n        *h = (int)((row / S) % H);",
+     "*h = (int)(row % H);\n        *i = (int)((row / H) % S);"),
+    ("sum_skips_first_key", "for (int j = 0; j < nkeys; ++j) {\n        s[j] = exp(s[j] - m);\n        l += s[j];",
+     "for (int j = 0; j < nkeys; ++j) {\n        s[j] = exp(s[j] - m);\n        if (j) l += s[j];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new, tmp_path):
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) >= 1, "mutation anchor not found: " + name
+    mutated = src.replace(old, new, 1)
+    path = os.path.join(tmp_path, "mutant.c")
+    with open(path, "w") as f:
+        f.write(mutated)
+    lib = oracle.build(force=True, src=path, out=os.path.join(tmp_path, "libmutant.so"))
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), lib],
+                       capture_output=True, text=True, timeout=300)
+    assert "Error" not in r.stderr or r.returncode < 0, r.stderr[-2000:]
+    caught = r.returncode != 0 or r.stdout.strip() != ""
+    assert caught, "no pin caught mutant " + name
+
+
+def _run_pins(lib_path):
+    """Child-process entry: print the names of the pins the library fails."""
+    lib = oracle.OracleLib(lib_path)
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(lib)
+        except (AssertionError, ValueError, FloatingPointError):
+            print(check.__name__)
+
+
+if __name__ == "__main__":
+    _run_pins(sys.argv[1])

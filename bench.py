@@ -1,0 +1,202 @@
+"""Throughput of the exact attention forward on one MI355X.
+
+One step = one fa_fwd launch over the whole workload (all steps of the hot
+path: schedule, K/V loads, Q K^T, mask, softmax with conditional rescaling,
+exp2, P V, epilogue), inputs resident in HBM before the timed region.
+Default workload: causal attention, B=1, H=16, S=32768, D=128 (bf16 in,
+bf16 O + fp32 LSE out).  The metric is TFLOP/s with the usual convention
+4*B*H*S^2*D, halved for causal, and its fraction of the dense bf16 MFMA peak.
+The S=8192 causal workload (B=2, H=16, D=128) the metric also names is timed
+the same way and reported under "secondary".
+
+Timing follows the FlashAttention-4 paper's protocol (appendix A.1: warm up,
+then time repeated runs and report the mean): W untimed warm-up steps, then K
+timed steps bracketed by torch.cuda.synchronize(); each launch is also
+bracketed by HIP events on the launch stream for the per-launch kernel time
+used by the roofline figure.
+
+The cpu_baseline leg times the fp64 oracle (test infrastructure) on a
+bounded sample of query rows of the same workload on the host cores.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+DEFAULT_WORKLOAD = "long_b1h16s32768d128_causal"
+SECONDARY_WORKLOAD = "causal_b2h16s8192d128"
+
+
+def time_workload(fa, torch, w, steps, warmup, tuning=None):
+    from attn_inputs import make, flops
+    q, k, v, cu, S = make(w)
+    dev = torch.device("cuda:0")
+    dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
+    dcu = None if cu is None else torch.from_numpy(cu).to(dev)
+    o = torch.empty_like(dq)
+    T = dq.shape[0] if cu is not None else None
+    lse = torch.empty((w.H, T) if cu is not None else (w.B, w.H, w.S), dtype=torch.float32,
+                      device=dev)
+    fl = flops(w, cu)
+
+    def step():
+        fa.attention(dq, dk, dv, causal=w.causal, scale=w.scale, cu_seqlens=dcu,
+                     max_seqlen=S if cu is not None else None, out=o, lse_out=lse,
+                     tuning=tuning)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    return {
+        "flops": fl,
+        "ms_per_step": wall * 1e3 / steps,
+        "kernel_ms_mean": float(np.mean(kernel_ms)),
+        "kernel_ms_median": float(np.median(kernel_ms)),
+        "kernel_ms_min": float(np.min(kernel_ms)),
+        "inputs": (q, k, v, cu),
+    }
+
+
+def cpu_baseline(w, inputs, target_s=15.0):
+    """Time the fp64 oracle on a bounded, seeded sample of query rows."""
+    import oracle
+    q, k, v, cu = inputs
+    rng = np.random.default_rng(12345)
+    if cu is None:
+        nrows = w.B * w.H * w.S
+        keys_of = (lambda r: (r % w.S) + 1) if w.causal else (lambda r: np.full_like(r, w.S))
+    else:
+        T = int(cu[-1])
+        nrows = w.H * T
+        starts = np.asarray(cu[:-1])
+
+        def keys_of(r):
+            t = r % T
+            b = np.searchsorted(cu, t, side="right") - 1
+            L = cu[b + 1] - cu[b]
+            return (t - starts[b] + 1) if w.causal else L
+    # calibrate on a small batch, then size the sample to about target_s
+    n = 64
+    total_rows, total_flops, total_s = 0, 0.0, 0.0
+    while total_s < target_s and n > 0:
+        rows = rng.choice(nrows, n, replace=False)
+        t0 = time.perf_counter()
+        oracle.attention_rows_bf16(q, k, v, rows, w.scale, w.causal, cu)
+        dt = time.perf_counter() - t0
+        total_s += dt
+        total_rows += n
+        total_flops += float(np.sum(4.0 * w.D * keys_of(rows)))
+        rate = n / max(dt, 1e-6)
+        n = int(min(max(rate * (target_s - total_s), 0), 20000))
+    return {
+        "value": total_flops / total_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "%d random query rows (all their keys) of %s, fp64, %.1f s" % (
+            total_rows, w.name, total_s),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--exp2-emu", type=int, default=None)
+    ap.add_argument("--schedule", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the attention forward runs on a single MI355X "
+              "(every (sequence, head, row-tile) is independent; see the sharding notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_forward_04_amd as fa
+    from attn_inputs import WORKLOADS
+    if not torch.cuda.is_available():
+        print("no GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.load()
+
+    tuning = None
+    if args.tau is not None or args.exp2_emu is not None or args.schedule is not None:
+        tuning = fa.default_tuning()
+        if args.tau is not None:
+            tuning.tau = args.tau
+        if args.exp2_emu is not None:
+            tuning.exp2_emu = args.exp2_emu
+        if args.schedule is not None:
+            tuning.schedule = args.schedule
+
+    w = WORKLOADS[args.workload]
+    r = time_workload(fa, torch, w, args.steps, args.warmup, tuning)
+    value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
+    achieved = r["flops"] / (r["kernel_ms_mean"] * 1e-3) / 1e12
+    out = {
+        "metric": "attention fwd TFLOP/s (bf16) + % of MFMA peak, S=8k/32k D=128 causal",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   "causal": w.causal, "seed": w.seed, "flops_per_step": r["flops"]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel_ms_mean": round(r["kernel_ms_mean"], 4),
+                     "kernel_ms_median": round(r["kernel_ms_median"], 4),
+                     "kernel_ms_min": round(r["kernel_ms_min"], 4)},
+    }
+    if not args.no_secondary and args.workload == DEFAULT_WORKLOAD:
+        w2 = WORKLOADS[SECONDARY_WORKLOAD]
+        r2 = time_workload(fa, torch, w2, args.steps, args.warmup, tuning)
+        v2 = r2["flops"] / (r2["ms_per_step"] * 1e-3) / 1e12
+        out["secondary"] = {"workload": w2.name, "value": round(v2, 2), "unit": "TFLOP/s",
+                            "pct_of_peak": round(100 * v2 / PEAK_BF16_TFLOPS, 2),
+                            "ms_per_step": round(r2["ms_per_step"], 4),
+                            "kernel_ms_mean": round(r2["kernel_ms_mean"], 4)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, r["inputs"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+"""MI355X (gfx950) exact attention forward: Python binding of libfa_mi355x.so.
+
+Every computation runs in the HIP kernels of the shared library; this module
+only marshals arguments (torch is used for device memory and streams).  If
+the library is missing or no gfx950 GPU is present, calls raise instead of
+falling back to anything else.
+
+    o, lse = attention(q, k, v, causal=True)          # q, k, v: [B,S,H,D] bf16 on cuda
+    o, lse = attention(q, k, v, causal=True, cu_seqlens=cu, max_seqlen=S)  # [T,H,D]
+
+The C ABI it wraps is declared in include/fa.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+from . import build as _build
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_HIP = -3
+FA_ERR_NO_DEVICE = -4
+
+LIB_PATH = _build.LIB_PATH
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A non-zero fa_status from the library."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s failed: %s (%d)" % (fn, msg, status))
+        self.status = status
+
+
+class Tuning(ctypes.Structure):
+    """Mirror of struct fa_tuning (include/fa.h)."""
+    _fields_ = [("tau", ctypes.c_float), ("exp2_emu", ctypes.c_int),
+                ("schedule", ctypes.c_int), ("counters", ctypes.c_void_p)]
+
+
+def load(path: str = LIB_PATH):
+    """Load the shared library (building it first only if nothing is built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        _build.build(path)
+    lib = ctypes.CDLL(path)
+    P, I, F, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_longlong
+    lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P]
+    lib.fa_fwd.restype = I
+    lib.fa_fwd_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, ctypes.POINTER(Tuning)]
+    lib.fa_fwd_ex.restype = I
+    lib.fa_tuning_default.argtypes = []
+    lib.fa_tuning_default.restype = Tuning
+    lib.fa_exp2_emu.argtypes = [P, P, LL, P]
+    lib.fa_exp2_emu.restype = I
+    lib.fa_schedule.argtypes = [I, I, I, I, I, P, I, P, I, ctypes.POINTER(I), ctypes.POINTER(I)]
+    lib.fa_schedule.restype = I
+    lib.fa_num_workers.argtypes = [I, ctypes.POINTER(I)]
+    lib.fa_num_workers.restype = I
+    lib.fa_status_string.argtypes = [I]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = I
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != FA_OK:
+        raise FaError(fn, status, status_string(status))
+
+
+def default_tuning() -> Tuning:
+    return load().fa_tuning_default()
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
+              cu_seqlens=None, max_seqlen: Optional[int] = None, return_lse: bool = True,
+              out=None, lse_out=None, tuning: Optional[Tuning] = None, stream=None):
+    """Exact attention forward on the GPU.
+
+    q, k, v: contiguous bf16 CUDA tensors, [B,S,H,D] (dense) or [T,H,D]
+    (varlen, with cu_seqlens an int32 CUDA tensor of B+1 offsets and
+    max_seqlen the longest sequence).  Returns (o, lse): o like q (bf16),
+    lse fp32 [B,H,S] or [H,T] (None if return_lse is False).
+    """
+    import torch
+    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous bf16 CUDA tensor" % name)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("dense inputs are [B, S, H, D]")
+        B, S, H, D = q.shape
+        lse_shape = (B, H, S)
+        cu_ptr = None
+    else:
+        if q.dim() != 3:
+            raise ValueError("varlen inputs are [T, H, D]")
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be a contiguous int32 CUDA tensor")
+        if max_seqlen is None:
+            raise ValueError("varlen needs max_seqlen")
+        T, H, D = q.shape
+        B = cu_seqlens.numel() - 1
+        S = int(max_seqlen)
+        lse_shape = (H, T)
+        cu_ptr = cu_seqlens.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = out if out is not None else torch.empty_like(q)
+    lse = None
+    if return_lse:
+        lse = lse_out if lse_out is not None else torch.empty(lse_shape, dtype=torch.float32,
+                                                              device=q.device)
+    sp = _stream_ptr(stream)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+            lse.data_ptr() if lse is not None else None, B, H, S, D, float(scale),
+            int(bool(causal)), cu_ptr, sp)
+    if tuning is None:
+        rc = lib.fa_fwd(*args)
+        _check("fa_fwd", rc)
+    else:
+        rc = lib.fa_fwd_ex(*args, ctypes.byref(tuning))
+        _check("fa_fwd_ex", rc)
+    return o, lse
+
+
+def exp2_emu(x, stream=None):
+    """Device polynomial 2^x (the emulated exponential) on a float32 CUDA tensor."""
+    import torch
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 CUDA tensor")
+    y = torch.empty_like(x)
+    rc = load().fa_exp2_emu(x.data_ptr(), y.data_ptr(), x.numel(), _stream_ptr(stream))
+    _check("fa_exp2_emu", rc)
+    return y
+
+
+def schedule(B: int, H: int, S: int, D: int, causal: bool, workers: int,
+             cu_seqlens=None, max_rounds: int = 4096):
+    """Host-side persistent tile order: (tiles [workers, rounds] int32, BM).
+
+    Tile code = (seq * H + head) * ceil(S / BM) + mblock, -1 = idle.
+    cu_seqlens (optional) is a host sequence of B+1 offsets.
+    """
+    import numpy as np
+    lib = load()
+    tiles = np.full((workers, max_rounds), -2, dtype=np.int32)
+    cu = None
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    rounds, bm = ctypes.c_int(0), ctypes.c_int(0)
+    rc = lib.fa_schedule(B, H, S, D, int(bool(causal)), None if cu is None else cu.ctypes.data,
+                         workers, tiles.ctypes.data, max_rounds, ctypes.byref(rounds),
+                         ctypes.byref(bm))
+    _check("fa_schedule", rc)
+    return tiles[:, :rounds.value].copy(), bm.value
+
+
+def num_workers(D: int = 128) -> int:
+    """Persistent workgroups fa_fwd launches on the current device."""
+    n = ctypes.c_int(0)
+    _check("fa_num_workers", load().fa_num_workers(D, ctypes.byref(n)))
+    return n.value
+
+
+def version() -> int:
+    return load().fa_version()

@@ -1,0 +1,53 @@
+"""Ahead-of-time build of the gfx950 attention library (libfa_mi355x.so).
+
+hipcc compiles csrc/fa_fwd.hip for gfx950 into a shared library that sits
+next to this file; the Python binding loads it with ctypes.  Packed-FP32
+instruction selection is disabled (-packed-fp32-ops) on purpose.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = [os.path.join(CSRC, "fa_fwd.hip")]
+HEADERS = [os.path.join(CSRC, n) for n in ("fa_sched.h", "exp2_poly.h")] + \
+          [os.path.join(ROOT, "include", "fa.h")]
+LIB_NAME = "libfa_mi355x.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+
+def hipcc_command(out: str = LIB_PATH):
+    return [HIPCC, "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-inline-asm",
+            "-o", out] + SOURCES
+
+
+def build(out: str = LIB_PATH, verbose: bool = False) -> str:
+    """Compile the library (always recompiles) and return its path."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = hipcc_command(tmp)
+    if verbose:
+        print(" ".join(cmd))
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + r.stderr[-4000:])
+    os.replace(tmp, out)
+    return out
+
+
+def is_stale(path: str = LIB_PATH) -> bool:
+    if not os.path.exists(path):
+        return True
+    t = os.path.getmtime(path)
+    return any(os.path.getmtime(s) > t for s in SOURCES + HEADERS)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,717 @@
+// fa_fwd.hip -- exact attention forward for MI355X (gfx950): kernels and C ABI.
+//
+// O = softmax(scale * Q K^T + causal mask) V and LSE = ln sum exp, computed per
+// tile of query rows with an online softmax so the score matrix stays on
+// chip (FlashAttention-4 paper, sections 1 and 3.1; the engineering blog's
+// "life of a tile").  The gfx950 design:
+//
+//   workgroup  NW wavefronts of 64 lanes; wave w owns 32 query rows, so a
+//              tile is BM = 32*NW rows of one (sequence, head).
+//   Q          loaded once per tile into VGPRs as the B operand of
+//              v_mfma_f32_32x32x16_bf16 (lane l: row l%32, 8 consecutive d).
+//   K, V       streamed in blocks of BN = 64 keys through LDS with
+//              global_load_lds_dwordx4 (16 bytes per lane straight into LDS),
+//              double-buffered: block j+1 is in flight while block j is
+//              used.  Rows are stored with a 16-byte-chunk XOR swizzle so the
+//              MFMA operand reads do not collide on LDS banks.
+//   S^T = K Q^T  on MFMA (keys on the M side, query rows on N): every lane
+//              then holds 16 keys of ONE query row per 32-key sub-block, so a
+//              row maximum is an in-lane max plus one v_permlane32_swap with
+//              the other half-wave, and the row statistics are per lane.
+//   softmax    running row max m_ref in log2 units; a block whose maximum
+//              exceeds m_ref by more than tau in ANY row of the wave triggers
+//              a rescale of O and the row sums for the whole wave (paper
+//              section 3.1.4); otherwise m_ref is kept and the final
+//              normalisation absorbs the difference.  p = exp2(c*s - m_ref)
+//              with c = scale*log2(e), by v_exp_f32 or, for a fixed share of
+//              column slots, by the Cody-Waite degree-3 polynomial (paper
+//              section 3.1.3).  Two row sums: l32 = sum p (fp32, for the LSE)
+//              and lbf = sum bf16(p) (for the output, so that the rounding of
+//              P to bf16 cancels in O = sum bf16(p) v / lbf).
+//   O^T += V^T P^T  on MFMA: the S accumulator registers, rounded to bf16,
+//              are already the B operand (the contraction index runs over
+//              the keys in the order the S layout holds them); V^T comes from
+//              LDS with ds_read_b64_tr_b16, which transposes 16-bit elements
+//              across each 16-lane group.
+//   epilogue   O / lbf -> bf16, LSE = ln2 * (m_ref + log2 l32).
+//
+// Scheduling: a persistent grid walks tiles in longest-processing-time-first
+// order (fa_sched.h), or one workgroup per tile in natural order.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+
+#include "fa.h"
+#include "exp2_poly.h"
+#include "fa_sched.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kBN = 64;           // keys per KV block
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Polynomial exp2 (Cody-Waite split + degree-3 Horner, three FMAs).
+// x is clamped to -127 so that n >= -127; with C0 == 1 a clamped input gives
+// p = 1 and an exponent field of 0: exactly +0.  f = x - floor(x) is exact.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float exp2_poly(float x) {
+  x = fmaxf(x, -127.0f);
+  const float f = __builtin_amdgcn_fractf(x);  // x - floor(x), in [0, 1)
+  const float n = x - f;                        // floor(x), exact
+  float p = __builtin_fmaf(FA_EXP2_C3, f, FA_EXP2_C2);
+  p = __builtin_fmaf(p, f, FA_EXP2_C1);
+  p = __builtin_fmaf(p, f, FA_EXP2_C0);
+  const int bits = __float_as_int(p) + (static_cast<int>(n) << 23);
+  return __int_as_float(bits);
+}
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Swap a value with the lane 32 positions away (the other half-wave).
+__device__ __forceinline__ float swap_halves(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]);
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence.  __syncthreads() would also wait
+// for every outstanding global->LDS copy (vmcnt(0)), including the next
+// block's prefetch; the copies this barrier must cover are waited for
+// explicitly with wait_vmcnt<>() first.  The "memory" clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+// Barrier after this wave's LDS reads of a buffer have all returned, so no
+// read is still queued when another wave's copy starts overwriting it.
+__device__ __forceinline__ void barrier_after_reads() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16-byte chunk swizzle of an LDS row: chunk c of row r lives at c ^ swz(r).
+// For D >= 128 (rows of 16+ chunks) rows r..r+15 get distinct values (bank
+// spread for the K operand reads, 16 rows x one chunk) and rows 4a..4a+3
+// differ in bits 2-3 (spread for the transposed V reads, 4 rows x 4 chunks).
+// For D = 64 (8 chunks, two rows per 256 bytes) the same two properties hold
+// on the row-pair level.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+template <int D>
+struct Cfg {
+  static constexpr int NW = (D == 256) ? 4 : 8;  // waves per workgroup
+  static constexpr int BM = 32 * NW;             // query rows per tile
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int BLOCK_BYTES = kBN * D * 2;
+  static constexpr int LOADS = (kBN * CPR) / (NW * kWave);  // per wave, per tensor
+  static constexpr int THREADS = NW * kWave;
+  static_assert(LOADS * NW * kWave == kBN * CPR, "block must split evenly over waves");
+};
+
+// Kernel arguments.
+struct Args {
+  const __bf16 *q, *k, *v;
+  __bf16 *o;
+  float *lse;
+  const int *cu;            // varlen offsets or nullptr
+  int B, H, S;
+  float c;                  // scale * log2(e)
+  float tau;
+  unsigned long long *counters;
+  int workers;              // persistent: number of workgroups
+};
+
+// Issue the global->LDS copies of one K or V block (this wave's share).
+// The copies are issued from inline assembly so that the compiler does not
+// track them: it would otherwise wait for every outstanding copy (including
+// the prefetch of the next block) before any LDS read it cannot prove
+// disjoint.  Completion is waited for explicitly with wait_vmcnt<>(), which
+// is exact because the vector-memory counter retires loads in issue order.
+// LDS slot p (16 bytes) of the block holds row p / CPR, physical chunk
+// p % CPR, i.e. logical chunk (p % CPR) ^ swz(row).  Rows past the sequence
+// end read row L-1 (always in bounds; masked later).
+template <int D>
+__device__ __forceinline__ void issue_block(const __bf16 *base, long long tok0, int H, int h,
+                                            int n0, int L, char LDS_AS *dst, int wave, int lane) {
+  using C = Cfg<D>;
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int slot0 = (i * C::NW + wave) * kWave;  // first slot of this wave's instruction
+    const int p = slot0 + lane;
+    const int row = p / C::CPR;
+    const int pc = p % C::CPR;
+    const int c = pc ^ swz<D>(row);
+    int key = n0 + row;
+    key = key < L ? key : L - 1;
+    const __bf16 *src = base + ((tok0 + key) * H + h) * (long long)D + c * 8;
+    // M0 holds the wave-uniform LDS destination; lane l lands at M0 + 16*l.
+    const unsigned lds_addr =
+        (unsigned)(uintptr_t)(dst + __builtin_amdgcn_readfirstlane(slot0) * 16);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(lds_addr), "v"(src)
+        : "memory", "m0");
+  }
+}
+
+// K operand (A of S^T = K Q^T) for key sub-block kb, k-step s.
+template <int D>
+__device__ __forceinline__ bf16x8 read_k(const char LDS_AS *kbuf, int kb, int s, int lane) {
+  const int row = kb * 32 + (lane & 31);
+  const int c = 2 * s + (lane >> 5);
+  const char LDS_AS *p = kbuf + row * (D * 2) + ((c ^ swz<D>(row)) << 4);
+  return *(const bf16x8 LDS_AS *)p;
+}
+
+// V^T operand (A of O^T += V^T P^T) for 16-key step t and 32-wide d tile dt:
+// lane l gets d = 32*dt + l%32 and keys 16t + 4h + {0..3}, 16t + 8 + 4h + {0..3}
+// (h = l/32), matching the key order of the P operand taken from the S
+// accumulator layout.  Within a 16-lane group the transposed read hands lane
+// i element i%4 of the rows supplied by lanes 4e + i/4, so lane j supplies
+// key (j/4) and d-quad (j%4) of its group's 16 d values.
+template <int D>
+__device__ __forceinline__ bf16x8 read_vt(const char LDS_AS *vbuf, int t, int dt, int lane) {
+  const int j = lane & 15, g = lane >> 4, h = lane >> 5;
+  const int d = 32 * dt + 16 * (g & 1) + 4 * (j & 3);
+  const int c = d >> 3, half = (d >> 2) & 1;
+  const int key0 = 16 * t + 4 * h + (j >> 2);
+  const int key1 = key0 + 8;
+  const char LDS_AS *p0 = vbuf + key0 * (D * 2) + ((c ^ swz<D>(key0)) << 4) + (half << 3);
+  const char LDS_AS *p1 = vbuf + key1 * (D * 2) + ((c ^ swz<D>(key1)) << 4) + (half << 3);
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)p0);
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)p1);
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Per-wave state of one tile.
+template <int D>
+struct WaveState {
+  bf16x8 qf[D / 16];
+  f32x16 o[D / 32];
+  float m_ref, l32, lbf;
+};
+
+// One KV block for one wave: S^T = K Q^T, mask, statistics, exp, P V.
+template <int D, bool CAUSAL, int EMU, bool COUNT>
+__device__ __forceinline__ void block_step(WaveState<D> &st, const char LDS_AS *kbuf,
+                                           const char LDS_AS *vbuf, int lane, int n0, int row,
+                                           int L, bool need_mask, bool last_block, const Args &a) {
+  // ---- S^T = K Q^T : two 32-key sub-blocks, D/16 k-steps each
+  f32x16 sacc[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 kf = read_k<D>(kbuf, kb, s, lane);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[s], sacc[kb], 0, 0, 0);
+    }
+  }
+  // ---- mask: key index of sacc[kb][4i+j] is n0 + 32kb + 8i + 4h + j
+  const int h = lane >> 5;
+  if (need_mask) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = n0 + 32 * kb + 8 * (e >> 2) + 4 * h + (e & 3);
+        const bool masked = (key >= L) || (CAUSAL && key > row);
+        sacc[kb][e] = masked ? -INFINITY : sacc[kb][e];
+      }
+  }
+  // ---- block row max (raw scores; c > 0 so it commutes with scaling)
+  float mx = sacc[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+  mx = fmaxf(mx, swap_halves(mx));
+  const float m_blk = mx * a.c;  // -inf when the whole row of the block is masked
+  // ---- conditional rescale, decided for the whole wave
+  const bool need = m_blk > st.m_ref + a.tau;
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    const float m_new = fmaxf(st.m_ref, m_blk);
+    const float alpha = (st.m_ref == -INFINITY) ? 0.0f : exp2_hw(st.m_ref - m_new);
+    st.m_ref = m_new;
+    st.l32 *= alpha;
+    st.lbf *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.o[dt][e] *= alpha;
+    if constexpr (COUNT) {
+      if (lane == 0) atomicAdd(&a.counters[0], 1ull);
+    }
+  }
+  if constexpr (COUNT) {
+    if (lane == 0) atomicAdd(&a.counters[1], 1ull);
+  }
+  const float m_use = (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
+  // ---- p = exp2(c*s - m), sums, bf16 pack
+  bf16x8 pf[4];
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const float x0 = __builtin_fmaf(sacc[kb][e], a.c, -m_use);
+      const float x1 = __builtin_fmaf(sacc[kb][e + 1], a.c, -m_use);
+      float p0, p1;
+      if (EMU > 0 && !last_block && (e % EMU) == 0) p0 = exp2_poly(x0);
+      else p0 = exp2_hw(x0);
+      p1 = exp2_hw(x1);
+      st.l32 += p0 + p1;
+      const bf16x2 pb = {(__bf16)p0, (__bf16)p1};
+      st.lbf = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, st.lbf, false);
+      const int t = 2 * kb + (e >> 3);
+      pf[t][e & 7] = pb[0];
+      pf[t][(e & 7) + 1] = pb[1];
+    }
+  }
+  // ---- O^T += V^T P^T : D/32 d-tiles, 4 steps of 16 keys
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      bf16x8 vf = read_vt<D>(vbuf, t, dt, lane);
+      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], st.o[dt], 0, 0, 0);
+    }
+  }
+}
+
+// Process one tile (b, h, mb) with the whole workgroup.
+template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>
+__device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, char LDS_AS *lds) {
+  using C = Cfg<D>;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  long long tok0;
+  int L;
+  if constexpr (VARLEN) {
+    tok0 = a.cu[b];
+    int Lr = a.cu[b + 1] - a.cu[b];
+    L = Lr < 0 ? 0 : (Lr > a.S ? a.S : Lr);
+  } else {
+    tok0 = (long long)b * a.S;
+    L = a.S;
+  }
+  const int m0 = mb * C::BM;
+  if (m0 >= L) return;  // workgroup-uniform
+  const int H = a.H;
+  // rows of this wave and lane
+  const int wrow0 = m0 + wave * 32;
+  const int row = wrow0 + (lane & 31);
+  const bool wave_active = wrow0 < L;
+  const int wrow_last = (wrow0 + 31 < L - 1) ? wrow0 + 31 : L - 1;
+
+  // KV range shared by the workgroup
+  const int n_end = CAUSAL ? ((m0 + C::BM < L) ? m0 + C::BM : L) : L;
+  const int nblocks = fa::ceil_div(n_end, kBN);
+
+  char LDS_AS *kb0 = lds;
+  char LDS_AS *vb0 = lds + C::BLOCK_BYTES;
+  char LDS_AS *kb1 = lds + 2 * C::BLOCK_BYTES;
+  char LDS_AS *vb1 = lds + 3 * C::BLOCK_BYTES;
+
+  // Q fragments: lane l holds row (l%32), d = 16s + 8(l/32) .. +7
+  WaveState<D> st;
+  {
+    const int qrow = row < L ? row : L - 1;
+    const bf16x8 *qp = (const bf16x8 *)(a.q + ((tok0 + qrow) * H + h) * (long long)D + 8 * (lane >> 5));
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) st.qf[s] = qp[2 * s];
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st.o[dt][e] = 0.0f;
+  st.m_ref = -INFINITY;
+  st.l32 = 0.0f;
+  st.lbf = 0.0f;
+
+  issue_block<D>(a.k, tok0, H, h, 0, L, kb0, wave, lane);
+  issue_block<D>(a.v, tok0, H, h, 0, L, vb0, wave, lane);
+
+  for (int j = 0; j < nblocks; ++j) {
+    const int n0 = j * kBN;
+    char LDS_AS *kcur = (j & 1) ? kb1 : kb0;
+    char LDS_AS *vcur = (j & 1) ? vb1 : vb0;
+    if (j + 1 < nblocks) {
+      char LDS_AS *knext = (j & 1) ? kb0 : kb1;
+      char LDS_AS *vnext = (j & 1) ? vb0 : vb1;
+      issue_block<D>(a.k, tok0, H, h, n0 + kBN, L, knext, wave, lane);
+      issue_block<D>(a.v, tok0, H, h, n0 + kBN, L, vnext, wave, lane);
+      wait_vmcnt<2 * C::LOADS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_nofence();
+    // does this wave need this block, and does it need the mask?
+    const bool useful = wave_active && (!CAUSAL || n0 <= wrow_last);
+    if (useful) {
+      const bool need_mask = (n0 + kBN > L) || (CAUSAL && n0 + kBN - 1 > wrow0);
+      block_step<D, CAUSAL, EMU, COUNT>(st, kcur, vcur, lane, n0, row, L, need_mask,
+                                        j + 1 == nblocks, a);
+    }
+    barrier_after_reads();  // every wave is done reading this buffer
+  }
+
+  if (!wave_active) return;
+  // ---- epilogue: combine the two half-wave partial sums of each row
+  const float l32 = st.l32 + swap_halves(st.l32);
+  const float lbf = st.lbf + swap_halves(st.lbf);
+  if (row < L) {
+    const float inv = 1.0f / lbf;
+    const int hh = lane >> 5;
+    __bf16 *op = a.o + ((tok0 + row) * H + h) * (long long)D + 4 * hh;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 out = {(__bf16)(st.o[dt][4 * i + 0] * inv), (__bf16)(st.o[dt][4 * i + 1] * inv),
+                      (__bf16)(st.o[dt][4 * i + 2] * inv), (__bf16)(st.o[dt][4 * i + 3] * inv)};
+        *(bf16x4 *)(op + 32 * dt + 8 * i) = out;
+      }
+    if (a.lse != nullptr && hh == 0) {
+      const float lse = (st.m_ref + log2f(l32)) * kLn2;
+      if constexpr (VARLEN) a.lse[(long long)h * a.cu[a.B] + tok0 + row] = lse;
+      else a.lse[((long long)b * H + h) * a.S + row] = lse;
+    }
+  }
+}
+
+template <int D>
+constexpr int lds_bytes() { return 4 * Cfg<D>::BLOCK_BYTES; }
+
+// Persistent kernel: each workgroup walks its static LPT list.
+template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>
+__global__ __launch_bounds__(Cfg<D>::THREADS) void fa_fwd_persistent(Args a) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  char LDS_AS *lds = (char LDS_AS *)lds_raw;
+  using C = Cfg<D>;
+  fa::Sched s = fa::make_sched(a.B, a.H, a.S, C::BM, CAUSAL, VARLEN, a.workers);
+  fa::SchedTables t{nullptr, nullptr, nullptr};
+  if constexpr (VARLEN) {
+    int *tab = (int *)(lds_raw + lds_bytes<D>());
+    t.len = tab;
+    t.sorted = tab + fa::kMaxVarlenSeqs;
+    t.off = tab + 2 * fa::kMaxVarlenSeqs;
+    fa::tables_phase1(s, a.cu, t, threadIdx.x, blockDim.x);
+    __syncthreads();
+    fa::tables_phase2(s, t, threadIdx.x, blockDim.x);
+    __syncthreads();
+    fa::tables_phase3(s, t, threadIdx.x, blockDim.x);
+    __syncthreads();
+    __shared__ int n_items_sh;
+    if (threadIdx.x == 0) n_items_sh = fa::tables_phase4(s, t);
+    __syncthreads();
+    s.n_items = n_items_sh;
+  }
+  int x, w, W;
+  fa::worker_slot(s, blockIdx.x, a.workers, &x, &w, &W);
+  const int npos = fa::group_positions(s);
+  for (int r = 0;; ++r) {
+    const int p = fa::snake_position(r, w, W);
+    if (p >= npos) break;
+    const fa::Tile tl = fa::decode_position(s, t, x, p);
+    run_tile<D, CAUSAL, VARLEN, EMU, COUNT>(a, tl.b, tl.h, tl.mb, lds);
+  }
+}
+
+// One workgroup per tile, natural (b, h, mb) order.
+template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>
+__global__ __launch_bounds__(Cfg<D>::THREADS) void fa_fwd_grid(Args a) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  char LDS_AS *lds = (char LDS_AS *)lds_raw;
+  using C = Cfg<D>;
+  const int nmb = fa::ceil_div(a.S, C::BM);
+  const int id = blockIdx.x;
+  const int mb = id % nmb;
+  const int h = (id / nmb) % a.H;
+  const int b = id / (nmb * a.H);
+  run_tile<D, CAUSAL, VARLEN, EMU, COUNT>(a, b, h, mb, lds);
+}
+
+__global__ void exp2_emu_kernel(const float *x, float *y, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = exp2_poly(x[i]);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+struct DeviceInfo {
+  int ok = 0;
+  int cus = 0;
+};
+
+DeviceInfo g_dev[64];
+std::once_flag g_dev_once[64];
+
+int current_device(DeviceInfo **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FA_ERR_NO_DEVICE;
+  std::call_once(g_dev_once[dev], [dev] {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return;
+    if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0) return;
+    g_dev[dev].cus = p.multiProcessorCount;
+    g_dev[dev].ok = 1;
+  });
+  if (!g_dev[dev].ok) return FA_ERR_NO_DEVICE;
+  *out = &g_dev[dev];
+  return FA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int validate(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+             int S, int D, float scale, int causal, const fa_tuning *t) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID_ARG;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (t) {
+    if (!(t->tau >= 0.0f) || !std::isfinite(t->tau)) return FA_ERR_INVALID_ARG;
+    if (t->exp2_emu != 0 && t->exp2_emu != 4 && t->exp2_emu != 8) return FA_ERR_INVALID_ARG;
+    if (t->schedule != 0 && t->schedule != 1) return FA_ERR_INVALID_ARG;
+  }
+  if (D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  // sizes must fit the 32-bit index arithmetic used for rows and tiles
+  if ((long long)B * S > (1LL << 31) - 1 || (long long)S * H > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+// Allow a kernel the dynamic LDS it needs (above the 64 KB default).
+template <typename K>
+bool allow_lds(K kern, size_t bytes) {
+  static std::mutex mu;
+  static std::map<const void *, size_t> granted;  // per kernel
+  std::lock_guard<std::mutex> lock(mu);
+  size_t &g = granted[(const void *)kern];
+  if (bytes <= g) return true;
+  if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)bytes) != hipSuccess)
+    return false;
+  g = bytes;
+  return true;
+}
+
+template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>
+int launch_variant(const Args &a0, int schedule, int cus, hipStream_t stream) {
+  using C = Cfg<D>;
+  Args a = a0;
+  size_t lds = lds_bytes<D>();
+  const int nmb = fa::ceil_div(a.S, C::BM);
+  bool persistent = (schedule == 0);
+  if (VARLEN && (a.B > fa::kMaxVarlenSeqs || nmb > fa::kMaxVarlenLevels)) persistent = false;
+  if (persistent) {
+    const int occ = 1;  // workgroups per CU
+    a.workers = cus * occ;
+    if (VARLEN) lds += sizeof(int) * (2 * fa::kMaxVarlenSeqs + fa::kMaxVarlenLevels + 1);
+    auto kern = fa_fwd_persistent<D, CAUSAL, VARLEN, EMU, COUNT>;
+    if (!allow_lds(kern, lds)) return FA_ERR_HIP;
+    hipLaunchKernelGGL(kern, dim3(a.workers), dim3(C::THREADS), lds, stream, a);
+  } else {
+    const long long grid = (long long)a.B * a.H * nmb;
+    if (grid > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    auto kern = fa_fwd_grid<D, CAUSAL, VARLEN, EMU, COUNT>;
+    if (!allow_lds(kern, lds)) return FA_ERR_HIP;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), lds, stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+int dispatch_emu(const Args &a, const fa_tuning &t, int cus, hipStream_t st) {
+  if (t.counters) return launch_variant<D, CAUSAL, VARLEN, 0, true>(a, t.schedule, cus, st);
+  switch (t.exp2_emu) {
+    case 8: return launch_variant<D, CAUSAL, VARLEN, 8, false>(a, t.schedule, cus, st);
+    case 4: return launch_variant<D, CAUSAL, VARLEN, 4, false>(a, t.schedule, cus, st);
+    default: return launch_variant<D, CAUSAL, VARLEN, 0, false>(a, t.schedule, cus, st);
+  }
+}
+
+template <int D>
+int dispatch_d(const Args &a, bool causal, bool varlen, const fa_tuning &t, int cus,
+               hipStream_t st) {
+  if (causal) {
+    return varlen ? dispatch_emu<D, true, true>(a, t, cus, st) : dispatch_emu<D, true, false>(a, t, cus, st);
+  }
+  return varlen ? dispatch_emu<D, false, true>(a, t, cus, st) : dispatch_emu<D, false, false>(a, t, cus, st);
+}
+
+template <int D>
+constexpr int bm_of() { return Cfg<D>::BM; }
+
+int bm_for(int D) {
+  switch (D) {
+    case 64: return bm_of<64>();
+    case 128: return bm_of<128>();
+    default: return bm_of<256>();
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_tuning fa_tuning_default(void) {
+  fa_tuning t;
+  t.tau = 8.0f;
+  t.exp2_emu = 0;
+  t.schedule = 0;
+  t.counters = nullptr;
+  return t;
+}
+
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+              int S, int D, float scale, int causal, const int *cu_seqlens, void *stream,
+              const fa_tuning *tuning) {
+  const fa_tuning t = tuning ? *tuning : fa_tuning_default();
+  int rc = validate(q, k, v, o, lse, B, H, S, D, scale, causal, &t);
+  if (rc != FA_OK) return rc;
+  DeviceInfo *dev = nullptr;
+  rc = current_device(&dev);
+  if (rc != FA_OK) return rc;
+  Args a;
+  a.q = (const __bf16 *)q;
+  a.k = (const __bf16 *)k;
+  a.v = (const __bf16 *)v;
+  a.o = (__bf16 *)o;
+  a.lse = lse;
+  a.cu = cu_seqlens;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.c = scale * kLog2e;
+  a.tau = t.tau;
+  a.counters = t.counters;
+  a.workers = 0;
+  hipStream_t st = (hipStream_t)stream;
+  const bool varlen = cu_seqlens != nullptr;
+  switch (D) {
+    case 64: return dispatch_d<64>(a, causal, varlen, t, dev->cus, st);
+    case 128: return dispatch_d<128>(a, causal, varlen, t, dev->cus, st);
+    default: return dispatch_d<256>(a, causal, varlen, t, dev->cus, st);
+  }
+}
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int S,
+           int D, float scale, int causal, const int *cu_seqlens, void *stream) {
+  return fa_fwd_ex(q, k, v, o, lse, B, H, S, D, scale, causal, cu_seqlens, stream, nullptr);
+}
+
+int fa_exp2_emu(const float *x, float *y, long long n, void *stream) {
+  if (n < 0) return FA_ERR_INVALID_ARG;
+  if (n == 0) return FA_OK;
+  if (!x || !y) return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(x) & 3) || (reinterpret_cast<uintptr_t>(y) & 3)) return FA_ERR_INVALID_ARG;
+  DeviceInfo *dev = nullptr;
+  int rc = current_device(&dev);
+  if (rc != FA_OK) return rc;
+  const long long blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(exp2_emu_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x, y, n);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_schedule(int B, int H, int S, int D, int causal, const int *cu_seqlens, int workers,
+                int *tiles, int max_rounds, int *rounds_out, int *bm_out) {
+  if (B <= 0 || H <= 0 || S <= 0 || workers <= 0 || !tiles || max_rounds <= 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  const int BM = bm_for(D);
+  const bool varlen = cu_seqlens != nullptr;
+  fa::Sched s = fa::make_sched(B, H, S, BM, causal, varlen, workers);
+  if (varlen && (B > fa::kMaxVarlenSeqs || s.nmb_max > fa::kMaxVarlenLevels)) return FA_ERR_UNSUPPORTED;
+  static thread_local int len[fa::kMaxVarlenSeqs], sorted[fa::kMaxVarlenSeqs],
+      off[fa::kMaxVarlenLevels + fa::kMaxVarlenSeqs + 1];
+  fa::SchedTables t{len, sorted, off};
+  if (varlen) {
+    fa::tables_phase1(s, cu_seqlens, t, 0, 1);
+    fa::tables_phase2(s, t, 0, 1);
+    fa::tables_phase3(s, t, 0, 1);
+    s.n_items = fa::tables_phase4(s, t);
+  }
+  const int npos = fa::group_positions(s);
+  int rounds = 0;
+  for (int wk = 0; wk < workers; ++wk) {
+    int x, w, W;
+    fa::worker_slot(s, wk, workers, &x, &w, &W);
+    for (int r = 0; r < max_rounds; ++r) {
+      const int p = fa::snake_position(r, w, W);
+      int code = -1;
+      if (p < npos) {
+        const fa::Tile tl = fa::decode_position(s, t, x, p);
+        code = (tl.b * H + tl.h) * s.nmb_max + tl.mb;
+        if (r + 1 > rounds) rounds = r + 1;
+      }
+      tiles[(long long)wk * max_rounds + r] = code;
+    }
+    // the worker must have finished within max_rounds
+    if (fa::snake_position(max_rounds, w, W) < npos) return FA_ERR_INVALID_ARG;
+  }
+  if (rounds_out) *rounds_out = rounds;
+  if (bm_out) *bm_out = BM;
+  return FA_OK;
+}
+
+int fa_num_workers(int D, int *workers_out) {
+  if (!workers_out) return FA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  DeviceInfo *dev = nullptr;
+  int rc = current_device(&dev);
+  if (rc != FA_OK) return rc;
+  *workers_out = dev->cus;
+  return FA_OK;
+}
+
+const char *fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported configuration";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
+    case FA_ERR_NO_DEVICE: return "FA_ERR_NO_DEVICE: no gfx950 device is current";
+    default: return "unknown fa_status";
+  }
+}
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

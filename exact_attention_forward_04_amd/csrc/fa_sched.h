@@ -1,0 +1,173 @@
+// fa_sched.h -- tile order for the persistent attention kernel (host and device).
+//
+// A tile is (sequence b, head h, m-block mb): BM query rows of one head.  The
+// persistent kernel launches a fixed number of workgroups ("workers"); each
+// walks a static list of tiles.  The order follows the FlashAttention-4
+// paper, section 3.3 (scheduling):
+//   - longest-processing-time first: for causal masking the m-blocks are
+//     visited in reverse, so the tiles with the most KV blocks start first;
+//     for variable-length batches the sequences are sorted by length
+//     (a virtual -> actual sequence map), longest first;
+//   - heads innermost within an m-block level, so the tiles running at the
+//     same time on one L2 share the same K/V;
+//   - heads are split across the 8 XCDs (each with its own L2) when H is a
+//     multiple of 8: XCD x owns heads x, x+8, ...; workgroup w runs on XCD
+//     w % 8 because the dispatcher deals workgroups to XCDs round-robin.
+// Within an XCD, workers take positions in "snake" order: round r gives
+// worker w position r*W + w on even rounds and r*W + W-1-w on odd rounds.
+//
+// Item order (an item is (b, mb); heads are expanded innermost):
+//   causal   : level l = 0..nmb_max-1 is m-block nmb_max-1-l; a level holds
+//              the sequences with more than that many m-blocks, in sorted
+//              order (for dense inputs: every sequence).
+//   noncausal: sequences in sorted order, each with its m-blocks ascending.
+//
+// The same code builds the tables on the host (tid = 0, nth = 1) for
+// fa_schedule() and in LDS on the device (tid = thread, nth = block size,
+// with a barrier between phases).
+#pragma once
+
+#ifndef FA_HD
+#define FA_HD __host__ __device__
+#endif
+
+namespace fa {
+
+constexpr int kXcds = 8;
+constexpr int kMaxVarlenSeqs = 1024;     // persistent varlen table limit (B)
+constexpr int kMaxVarlenLevels = 2048;   // persistent varlen table limit (nmb_max)
+
+struct SchedTables {
+  int *len;        // [B] clamped sequence lengths
+  int *sorted;     // [B] sequence index by rank (length descending, index ascending)
+  int *off;        // [nmb_max + 1] (causal: level offsets) or [B + 1] (noncausal: rank offsets)
+};
+
+struct Sched {
+  int B, H, S, BM;
+  int causal, varlen;
+  int nmb_max;     // ceil(S / BM)
+  int groups;      // kXcds or 1
+  int hpg;         // heads per group
+  int n_items;     // number of (b, mb) items
+};
+
+FA_HD inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+FA_HD inline Sched make_sched(int B, int H, int S, int BM, int causal, int varlen, int workers) {
+  Sched s;
+  s.B = B; s.H = H; s.S = S; s.BM = BM; s.causal = causal; s.varlen = varlen;
+  s.nmb_max = ceil_div(S, BM);
+  s.groups = (H % kXcds == 0 && workers % kXcds == 0) ? kXcds : 1;
+  s.hpg = H / s.groups;
+  s.n_items = B * s.nmb_max;  // dense; varlen fills it from the tables
+  return s;
+}
+
+// ---- varlen table construction, in phases (barrier between phases) ----
+
+// Phase 1: clamped lengths.
+FA_HD inline void tables_phase1(const Sched &s, const int *cu, SchedTables t, int tid, int nth) {
+  for (int b = tid; b < s.B; b += nth) {
+    int L = cu[b + 1] - cu[b];
+    L = L < 0 ? 0 : (L > s.S ? s.S : L);
+    t.len[b] = L;
+  }
+}
+
+// Phase 2: rank of each sequence (length descending, index ascending).
+FA_HD inline void tables_phase2(const Sched &s, SchedTables t, int tid, int nth) {
+  for (int b = tid; b < s.B; b += nth) {
+    const int Lb = t.len[b];
+    int rank = 0;
+    for (int c = 0; c < s.B; ++c) {
+      const int Lc = t.len[c];
+      rank += (Lc > Lb) || (Lc == Lb && c < b);
+    }
+    t.sorted[rank] = b;
+  }
+}
+
+// Phase 3: per-level (causal) or per-rank (noncausal) item counts into off[i+1].
+FA_HD inline void tables_phase3(const Sched &s, SchedTables t, int tid, int nth) {
+  if (s.causal) {
+    for (int l = tid; l < s.nmb_max; l += nth) {
+      const int mb = s.nmb_max - 1 - l;
+      int cnt = 0;
+      for (int r = 0; r < s.B; ++r) cnt += ceil_div(t.len[t.sorted[r]], s.BM) > mb;
+      t.off[l + 1] = cnt;
+    }
+  } else {
+    for (int r = tid; r < s.B; r += nth) t.off[r + 1] = ceil_div(t.len[t.sorted[r]], s.BM);
+  }
+  if (tid == 0) t.off[0] = 0;
+}
+
+// Phase 4 (one thread): inclusive prefix sum; returns the item count.
+FA_HD inline int tables_phase4(const Sched &s, SchedTables t) {
+  const int n = s.causal ? s.nmb_max : s.B;
+  for (int i = 0; i < n; ++i) t.off[i + 1] += t.off[i];
+  return t.off[n];
+}
+
+// ---- decode ----
+
+struct Tile {
+  int b, h, mb;
+};
+
+// Item index -> (b, mb).
+FA_HD inline void decode_item(const Sched &s, const SchedTables &t, int it, int *b, int *mb) {
+  if (!s.varlen) {
+    if (s.causal) {
+      const int l = it / s.B;
+      *b = it - l * s.B;
+      *mb = s.nmb_max - 1 - l;
+    } else {
+      *b = it / s.nmb_max;
+      *mb = it - *b * s.nmb_max;
+    }
+    return;
+  }
+  const int n = s.causal ? s.nmb_max : s.B;
+  int lo = 0, hi = n;  // find the last i with off[i] <= it
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (t.off[mid] <= it) lo = mid; else hi = mid;
+  }
+  const int r = it - t.off[lo];
+  if (s.causal) {
+    *b = t.sorted[r];
+    *mb = s.nmb_max - 1 - lo;
+  } else {
+    *b = t.sorted[lo];
+    *mb = r;
+  }
+}
+
+// Position p (within group x's list) -> tile.
+FA_HD inline Tile decode_position(const Sched &s, const SchedTables &t, int x, int p) {
+  Tile tl;
+  const int it = p / s.hpg;
+  const int hi = p - it * s.hpg;
+  decode_item(s, t, it, &tl.b, &tl.mb);
+  tl.h = x + s.groups * hi;
+  return tl;
+}
+
+// Number of positions in each group's list.
+FA_HD inline int group_positions(const Sched &s) { return s.n_items * s.hpg; }
+
+// Worker -> (group, index within group, workers in group).
+FA_HD inline void worker_slot(const Sched &s, int worker, int workers, int *x, int *w, int *W) {
+  *x = worker % s.groups;
+  *w = worker / s.groups;
+  *W = workers / s.groups;
+}
+
+// Snake position of worker w (of W) in round r.
+FA_HD inline int snake_position(int r, int w, int W) {
+  return r * W + ((r & 1) ? (W - 1 - w) : w);
+}
+
+}  // namespace fa

@@ -1,0 +1,160 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact attention forward library
+ * (libfa_mi355x.so).
+ *
+ * The operation is the one the FlashAttention-4 pages centre on: exact
+ * multi-head attention forward, O = softmax(scale * Q K^T + causal mask) V,
+ * computed in tiles with an online softmax so the S x S score matrix never
+ * reaches device memory (FlashAttention-4 paper, sections 1, 2.1 and 3.1;
+ * the usage guide's "what it is" section).  Each row's natural-log
+ * logsumexp is returned as well.
+ *
+ * Conventions shared by every entry point:
+ *   - Device pointers are allocated, owned and freed by the caller.  The
+ *     library keeps no pointer after a call returns, apart from work it has
+ *     enqueued on the caller's stream, and allocates no device memory.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Every call is asynchronous: it enqueues kernels and returns without
+ *     synchronising.  Results are valid once the stream has reached them.
+ *   - Arguments are validated on the host before any HIP call, so a bad
+ *     argument is reported without touching the GPU.  No call aborts or
+ *     throws; each returns an fa_status.
+ *   - Calls are thread-safe; concurrent calls on different streams are
+ *     independent.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size, bad scale, ... */
+    FA_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement (e.g. D) */
+    FA_ERR_HIP = -3,           /* a HIP runtime call or kernel launch failed */
+    FA_ERR_NO_DEVICE = -4      /* no gfx950 device is current */
+} fa_status;
+
+/*
+ * fa_fwd -- exact attention forward.
+ *
+ * Computes, for every sequence b, head h and query row i,
+ *   s_ij   = scale * <q_i, k_j>  for the allowed keys j
+ *            (all j < L_b; with causal=1 only j <= i, i.e. scores above the
+ *            diagonal are masked as in the FlashAttention-4 paper,
+ *            section 3.3, LPT scheduling for causal masking)
+ *   o_i    = sum_j softmax_j(s_ij) v_j                        (bf16 output)
+ *   lse_i  = ln sum_j exp(s_ij)                                (fp32 output)
+ *
+ * Layouts (row-major, contiguous, 16-byte aligned base pointers):
+ *   dense  (cu_seqlens == NULL): q, k, v, o are bf16 [B, S, H, D];
+ *                                lse is fp32 [B, H, S]
+ *   varlen (cu_seqlens != NULL): q, k, v, o are bf16 [T, H, D] with
+ *                                T = cu_seqlens[B]; lse is fp32 [H, T].
+ *          Sequence b owns tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 and
+ *          attends within itself (query and key lengths are equal).  S is
+ *          the maximum sequence length.  cu_seqlens is an int32 device array
+ *          of B+1 entries; its contents are not read on the host, so the
+ *          caller guarantees cu_seqlens[0] == 0, non-decreasing entries,
+ *          every length <= S, and T matching the tensors.  (The kernel clamps
+ *          each length to [0, S] to keep its own tables in bounds.)
+ *
+ * Arguments:
+ *   q, k, v   read-only inputs; o, lse write-only outputs that must not alias
+ *             the inputs.  lse may be NULL (not written).
+ *   B, H, S   >= 1.  D in {64, 128, 256} (FA_ERR_UNSUPPORTED otherwise; the
+ *             usage guide's interface limit is D <= 256).
+ *   scale     finite and > 0 (1/sqrt(D) is the usual choice).
+ *   causal    0 or 1.
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_NO_DEVICE or
+ * FA_ERR_HIP.  On an error nothing has been enqueued unless the error is
+ * FA_ERR_HIP from the launch itself.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int S, int D, float scale, int causal,
+           const int *cu_seqlens, void *stream);
+
+/*
+ * Experiment knobs for fa_fwd_ex.  fa_fwd uses fa_tuning_default().
+ *
+ *   tau        Rescale threshold in log2 units (>= 0).  The running row
+ *              maximum used for the exponentials is moved, and the output
+ *              and row sums rescaled, only when some row of a wavefront sees
+ *              a block maximum more than tau above it; otherwise the stale
+ *              maximum is kept (FlashAttention-4 paper, section 3.1.4,
+ *              skipping online-softmax rescaling: the final normalisation
+ *              corrects the skipped steps; the decision is taken for the
+ *              whole wavefront so it never diverges).  tau = 0 is the
+ *              textbook online softmax.  Default 8 (factor 256).
+ *   exp2_emu   Share of exponentials evaluated by the degree-3 polynomial
+ *              instead of v_exp_f32 (paper section 3.1.3, partial emulation):
+ *              0 = none, 8 = one column slot in 8 (12.5 %), 4 = one in 4
+ *              (25 %).  Other values are FA_ERR_INVALID_ARG.
+ *   schedule   0 = persistent workgroups walking the tiles in
+ *              longest-processing-time-first order (paper section 3.3);
+ *              1 = one workgroup per tile in natural (batch, head, m-block)
+ *              order.  Both give bitwise identical results.
+ *   counters   NULL, or a device array of 2 uint64 that the call adds to:
+ *              [0] wavefront-level rescale events, [1] wavefront-block steps
+ *              (their ratio is the rescale rate).  Slower; for measurement.
+ */
+typedef struct fa_tuning {
+    float tau;
+    int exp2_emu;
+    int schedule;
+    unsigned long long *counters;
+} fa_tuning;
+
+fa_tuning fa_tuning_default(void);
+
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int H, int S, int D, float scale, int causal,
+              const int *cu_seqlens, void *stream, const fa_tuning *tuning);
+
+/*
+ * fa_exp2_emu -- test hook: y[i] = the device's polynomial 2^x[i] for n
+ * floats (device pointers, 4-byte aligned).  The function is the one the
+ * attention kernel uses for its emulated exponentials: Cody-Waite
+ * reduction x = n + f with n = floor(x), f in [0, 1), then a degree-3 Horner
+ * polynomial for 2^f (three FMAs) and an exponent add (paper section 3.1.3;
+ * the engineering blog's approximate-exponent section).  Inputs below -127
+ * are clamped to -127, which yields exactly +0; for x in (-127, -126) the
+ * result is a subnormal below 2^-126.  n >= 0.
+ */
+int fa_exp2_emu(const float *x, float *y, long long n, void *stream);
+
+/*
+ * fa_schedule -- host-only view of the persistent tile order (no GPU use).
+ *
+ * Fills tiles[w * max_rounds + r] with the tile that persistent workgroup w
+ * processes in its round r, or -1 when it has no more work, for a launch of
+ * `workers` workgroups.  A tile is encoded as
+ *   ((seq * H + head) * n_mblocks_max + mblock)
+ * with n_mblocks_max = ceil(S / BM) and BM the row-tile height chosen for D.
+ * cu_seqlens, if not NULL, is a HOST int32 array of B+1 entries.  *rounds_out
+ * receives the number of rounds used and *bm_out the BM used.  Returns
+ * FA_ERR_INVALID_ARG when max_rounds is too small or an argument is invalid.
+ */
+int fa_schedule(int B, int H, int S, int D, int causal, const int *cu_seqlens,
+                int workers, int *tiles, int max_rounds, int *rounds_out, int *bm_out);
+
+/* Number of persistent workgroups fa_fwd launches on the current device. */
+int fa_num_workers(int D, int *workers_out);
+
+/* Human-readable name of an fa_status value (static string, never NULL). */
+const char *fa_status_string(int status);
+
+/* Library ABI version: 100 * major + minor. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,112 @@
+"""Host-side checks of the persistent tile order (fa_schedule; CPU only).
+
+The order is the FlashAttention-4 paper's longest-processing-time-first
+schedule (section 3.3): every tile is processed exactly once, the cost of
+the tiles a worker meets never increases from one round to the next for
+causal masking (m-blocks in reverse), and the makespan is close to the
+ideal total/workers.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import exact_attention_forward_04_amd as fa
+from attn_inputs import WORKLOADS, make, varlen_lengths, cu_seqlens_of
+
+BN = 64
+
+
+def tile_cost(code, H, S, bm, causal, lens):
+    nmb = math.ceil(S / bm)
+    mb = code % nmb
+    b = code // (nmb * H)
+    L = lens[b]
+    kv = min(L, (mb + 1) * bm) if causal else L
+    return math.ceil(kv / BN)
+
+
+def all_tiles(B, H, S, bm, lens):
+    nmb = math.ceil(S / bm)
+    out = set()
+    for b in range(B):
+        for h in range(H):
+            for mb in range(math.ceil(lens[b] / bm)):
+                out.add((b * H + h) * nmb + mb)
+    return out
+
+
+CASES = [
+    # (B, H, S, D, causal, lens or None, workers)
+    (2, 16, 2048, 128, True, None, 256),
+    (2, 16, 2048, 128, False, None, 256),
+    (1, 16, 32768, 128, True, None, 256),
+    (2, 16, 8192, 128, True, None, 256),
+    (2, 16, 8192, 256, False, None, 256),
+    (1, 8, 512, 64, True, None, 256),
+    (1, 2, 128, 64, False, None, 256),
+    (3, 5, 1000, 128, True, None, 256),      # H not a multiple of 8
+    (3, 5, 1000, 128, True, None, 13),       # workers not a multiple of 8
+    (16, 32, 8192, 128, True, "C4", 256),
+    (5, 8, 3000, 128, True, [1, 0, 3000, 257, 999], 256),
+    (5, 8, 3000, 128, False, [1, 0, 3000, 257, 999], 256),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_every_tile_exactly_once(case):
+    B, H, S, D, causal, lens, workers = case
+    if lens == "C4":
+        lens = list(varlen_lengths(16, 512, 8192, WORKLOADS["varlen_16x512to8192_h32d128_causal"].seed))
+        S = max(lens)
+    cu = None if lens is None else cu_seqlens_of(lens)
+    L = [S] * B if lens is None else list(lens)
+    tiles, bm = fa.schedule(B, H, S, D, causal, workers, cu_seqlens=cu)
+    seen = tiles[tiles >= 0].tolist()
+    assert len(seen) == len(set(seen)), "a tile is processed twice"
+    assert set(seen) == all_tiles(B, H, S, bm, L), "a tile is missing or foreign"
+    # idle slots only at the end of a worker's list
+    for row in tiles:
+        idle = np.flatnonzero(row < 0)
+        if idle.size:
+            assert np.all(row[idle[0]:] < 0)
+    # LPT (causal): within each worker the costs never increase
+    if causal:
+        for row in tiles:
+            c = [tile_cost(t, H, S, bm, causal, L) for t in row if t >= 0]
+            assert all(c[i] >= c[i + 1] for i in range(len(c) - 1)), c
+
+
+@pytest.mark.parametrize("case", [c for c in CASES if c[4]])
+def test_makespan_near_ideal(case):
+    B, H, S, D, causal, lens, workers = case
+    if lens == "C4":
+        lens = list(varlen_lengths(16, 512, 8192, WORKLOADS["varlen_16x512to8192_h32d128_causal"].seed))
+        S = max(lens)
+    cu = None if lens is None else cu_seqlens_of(lens)
+    L = [S] * B if lens is None else list(lens)
+    tiles, bm = fa.schedule(B, H, S, D, causal, workers, cu_seqlens=cu)
+    per_worker = [sum(tile_cost(t, H, S, bm, causal, L) + 2 for t in row if t >= 0) for row in tiles]
+    total = sum(per_worker)
+    ideal = max(total / workers, max(tile_cost(t, H, S, bm, causal, L) + 2
+                                      for t in tiles.ravel() if t >= 0))
+    ratio = max(per_worker) / ideal
+    # small problems cannot be balanced better than one round of tiles
+    rounds = tiles.shape[1]
+    assert ratio <= (1.10 if rounds >= 4 else 1.6), (ratio, rounds)
+
+
+def test_xcd_grouping_keeps_heads_on_one_xcd():
+    # H % 8 == 0: worker w (XCD w % 8) only sees heads h with h % 8 == w % 8
+    B, H, S = 2, 16, 8192
+    tiles, bm = fa.schedule(B, H, S, 128, True, 256)
+    nmb = math.ceil(S / bm)
+    for w, row in enumerate(tiles):
+        for t in row[row >= 0]:
+            h = (t // nmb) % H
+            assert h % 8 == w % 8
+
+
+def test_schedule_rejects_small_round_budget():
+    with pytest.raises(fa.FaError):
+        fa.schedule(1, 16, 32768, 128, True, 256, max_rounds=2)

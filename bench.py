@@ -133,6 +133,9 @@ def main():
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--exp2-emu", type=int, default=None)
     ap.add_argument("--schedule", type=int, default=None)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times); used to "
+                         "scale the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the attention forward runs on a single MI355X "
@@ -147,6 +150,16 @@ def main():
         print("no GPU", file=sys.stderr)
         sys.exit(1)
     fa.load()
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
+        return
 
     tuning = None
     if args.tau is not None or args.exp2_emu is not None or args.schedule is not None:

@@ -67,12 +67,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 // ---------------------------------------------------------------------------
 // Polynomial exp2 (Cody-Waite split + degree-3 Horner, three FMAs).
 // x is clamped to -127 so that n >= -127; with C0 == 1 a clamped input gives
-// p = 1 and an exponent field of 0: exactly +0.  f = x - floor(x) is exact.
+// p = 1 and an exponent field of 0: exactly +0.  n = floor(x) is exact and
+// f = x - n lies in [0, 1]: it rounds to exactly 1 only for tiny negative x,
+// where p(1) ~ 2 with the same relative error.  (v_fract_f32 is not used:
+// it clamps f below 1, after which x - f is no longer an integer.)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float exp2_poly(float x) {
   x = fmaxf(x, -127.0f);
-  const float f = __builtin_amdgcn_fractf(x);  // x - floor(x), in [0, 1)
-  const float n = x - f;                        // floor(x), exact
+  const float n = floorf(x);
+  const float f = x - n;
   float p = __builtin_fmaf(FA_EXP2_C3, f, FA_EXP2_C2);
   p = __builtin_fmaf(p, f, FA_EXP2_C1);
   p = __builtin_fmaf(p, f, FA_EXP2_C0);
@@ -82,10 +85,18 @@ __device__ __forceinline__ float exp2_poly(float x) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Swap a value with the lane 32 positions away (the other half-wave).
-__device__ __forceinline__ float swap_halves(float v) {
+// Combine a value with the one held 32 lanes away (the other half-wave).
+// v_permlane32_swap(v, v) exchanges the upper half of its first operand with
+// the lower half of its second: lanes 0-31 get {own, partner} and lanes
+// 32-63 get {partner, own}, so the symmetric combination of both results is
+// the same on the two lanes of a pair.
+__device__ __forceinline__ float max_halves(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
@@ -256,7 +267,7 @@ __device__ __forceinline__ void block_step(WaveState<D> &st, const char LDS_AS *
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
-  mx = fmaxf(mx, swap_halves(mx));
+  mx = max_halves(mx);
   const float m_blk = mx * a.c;  // -inf when the whole row of the block is masked
   // ---- conditional rescale, decided for the whole wave
   const bool need = m_blk > st.m_ref + a.tau;
@@ -389,8 +400,8 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
 
   if (!wave_active) return;
   // ---- epilogue: combine the two half-wave partial sums of each row
-  const float l32 = st.l32 + swap_halves(st.l32);
-  const float lbf = st.lbf + swap_halves(st.lbf);
+  const float l32 = sum_halves(st.l32);
+  const float lbf = sum_halves(st.lbf);
   if (row < L) {
     const float inv = 1.0f / lbf;
     const int hh = lane >> 5;

@@ -37,8 +37,8 @@ def fma32(a, b, c):
 def device_model(x):
     c = coeffs()
     x = np.maximum(x.astype(np.float32), np.float32(-127.0))
-    f = (x - np.floor(x)).astype(np.float32)
-    n = (x - f).astype(np.float32)
+    n = np.floor(x).astype(np.float32)
+    f = (x - n).astype(np.float32)       # in [0, 1]; exactly 1 only for tiny negative x
     p = fma32(np.full_like(f, c[3]), f, np.full_like(f, c[2]))
     p = fma32(p, f, np.full_like(f, c[1]))
     p = fma32(p, f, np.full_like(f, c[0]))
@@ -66,6 +66,16 @@ def test_within_two_bf16_ulp_dense_sample():
     # integers are exact powers of two
     ints = np.arange(-126, 9, dtype=np.float32)
     assert np.array_equal(device_model(ints).astype(np.float64), np.ldexp(1.0, ints.astype(int)))
+
+
+def test_tiny_negative_and_subnormal_inputs():
+    # x just below zero: floor(x) = -1 and x - floor(x) rounds to 1.0; the
+    # result must still be ~1 (a clamped fraction would give ~2 instead)
+    x = np.array([-1e-10, -1e-30, -1.4e-45, -6e-8, -0.0, 1e-30, 1.4e-45], np.float32)
+    ref = oracle.exp2(x)
+    y = device_model(x).astype(np.float64)
+    err = np.abs(bf16_round(y) - ref) / ulp_bf16(ref)
+    assert err.max() <= 2.0, err
 
 
 def test_clamped_inputs_give_zero():

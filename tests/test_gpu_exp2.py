@@ -61,6 +61,15 @@ def test_exhaustive_negative_range():
     print("[gpu-case] exp2 poly worst error over (0, 8]: %.3f bf16 ulp" % worst_pos, flush=True)
 
 
+def test_tiny_negative_inputs():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    x = torch.tensor([-1e-10, -1e-30, -1.4e-45, -6e-8, -0.0], device="cuda")
+    y = fa.exp2_emu(x).cpu().numpy()
+    ref = oracle.exp2(x.cpu().numpy())
+    assert np.all(np.abs(bf16_of_f32(y) - ref) / ulp_bf16(ref) <= 2.0), y
+
+
 def test_clamp_gives_zero():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")

@@ -133,7 +133,14 @@ __device__ __forceinline__ int swz(int r) {
 
 template <int D>
 struct Cfg {
+  // D <= 128: eight waves (two per SIMD) in one workgroup per CU, run as two
+  // halves that alternate matrix-product and softmax phases (run_tile).
+  // D = 256 needs the whole register file (O alone is 128 VGPRs per lane):
+  // four waves, one per SIMD, in the plain per-block sequence.
   static constexpr int NW = (D == 256) ? 4 : 8;  // waves per workgroup
+  static constexpr int OCC = 1;                  // workgroups per CU
+  static constexpr bool PINGPONG = (NW == 8);    // two halves alternate MFMA and VALU phases
+  static constexpr int WAVES_PER_SIMD = NW * OCC / 4;
   static constexpr int BM = 32 * NW;             // query rows per tile
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int BLOCK_BYTES = kBN * D * 2;
@@ -156,48 +163,102 @@ struct Args {
 };
 
 // Issue the global->LDS copies of one K or V block (this wave's share).
-// The copies are issued from inline assembly so that the compiler does not
-// track them: it would otherwise wait for every outstanding copy (including
-// the prefetch of the next block) before any LDS read it cannot prove
-// disjoint.  Completion is waited for explicitly with wait_vmcnt<>(), which
-// is exact because the vector-memory counter retires loads in issue order.
 // LDS slot p (16 bytes) of the block holds row p / CPR, physical chunk
-// p % CPR, i.e. logical chunk (p % CPR) ^ swz(row).  Rows past the sequence
-// end read row L-1 (always in bounds; masked later).
+// p % CPR, i.e. logical chunk (p % CPR) ^ swz(row).  The copies are issued
+// from inline assembly so that the compiler does not track them: it would
+// otherwise wait for every outstanding copy (including the prefetch of the
+// next block) before any LDS read it cannot prove disjoint.  Completion is
+// waited for explicitly with wait_vmcnt<>(), which is exact because the
+// vector-memory counter retires loads in issue order.
 template <int D>
-__device__ __forceinline__ void issue_block(const __bf16 *base, long long tok0, int H, int h,
-                                            int n0, int L, char LDS_AS *dst, int wave, int lane) {
+struct BlockLoader {
   using C = Cfg<D>;
-#pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int slot0 = (i * C::NW + wave) * kWave;  // first slot of this wave's instruction
-    const int p = slot0 + lane;
-    const int row = p / C::CPR;
-    const int pc = p % C::CPR;
-    const int c = pc ^ swz<D>(row);
-    int key = n0 + row;
-    key = key < L ? key : L - 1;
-    const __bf16 *src = base + ((tok0 + key) * H + h) * (long long)D + c * 8;
-    // M0 holds the wave-uniform LDS destination; lane l lands at M0 + 16*l.
-    const unsigned lds_addr =
-        (unsigned)(uintptr_t)(dst + __builtin_amdgcn_readfirstlane(slot0) * 16);
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off"
-        :
-        : "s"(lds_addr), "v"(src)
-        : "memory", "m0");
-  }
-}
+  int off[C::LOADS];  // element offset of this lane's slot from the block's first row
+  int wave, lane;
 
-// K operand (A of S^T = K Q^T) for key sub-block kb, k-step s.
+  __device__ __forceinline__ int slot0(int i) const { return (i * C::NW + wave) * kWave; }
+  __device__ __forceinline__ int row_of(int i) const { return (slot0(i) + lane) / C::CPR; }
+
+  __device__ __forceinline__ void init(int H, int wave_, int lane_) {
+    wave = __builtin_amdgcn_readfirstlane(wave_);
+    lane = lane_;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int p = slot0(i) + lane;
+      const int row = p / C::CPR;
+      const int c = (p % C::CPR) ^ swz<D>(row);
+      off[i] = row * H * D + c * 8;
+    }
+  }
+
+  // Copy rows n0 .. n0+BN-1 of one (sequence, head) of K or V into dst.
+  // Rows at or past L read row L-1 instead (in bounds; masked later).
+  __device__ __forceinline__ void issue(const __bf16 *base, long long tok0, int H, int h, int n0,
+                                        int L, char LDS_AS *dst) const {
+    const __bf16 *blk = base + ((tok0 + n0) * H + h) * (long long)D;
+    const bool full = n0 + kBN <= L;  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const __bf16 *src;
+      if (full) {
+        src = blk + off[i];
+      } else {
+        const int row = row_of(i);
+        const int r = (n0 + row < L) ? row : L - 1 - n0;
+        src = blk + off[i] + (long long)(r - row) * H * D;
+      }
+      const unsigned lds_addr = (unsigned)(uintptr_t)dst + (unsigned)slot0(i) * 16u;
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %1, off"
+          :
+          : "s"(lds_addr), "v"(src)
+          : "memory", "m0");
+    }
+  }
+};
+
+// LDS operand addressing.  With the swizzle above, the byte offset of the
+// K operand of lane l for sub-block kb and k-step s is
+//   row*2D + ((2s + h) ^ swz(row)) * 16,   row = 32kb + l%32, h = l/32,
+// and since 2s occupies other bits than h and swz(row) = swz(l%32), this is
+//   ((KY + buf) ^ 32s) + kb*32*2D   with the per-lane constant
+//   KY = (l%32)*2D | (16h ^ 16 swz(l%32)).
+// (This needs the K/V buffers to start at multiples of 2D*64 bytes of LDS:
+// the kernels declare no static LDS, so the dynamic allocation starts at 0.)
+// Likewise the transposed V read r (r = 0, 1) for 16-key step t and d tile
+// dt is ((VW_r + buf) ^ 64dt) + t*16*2D.  Buffers start at multiples of
+// 2D*64 bytes, so adding the buffer base commutes with the XOR.  Each read
+// is then one v_xor plus an instruction offset, with three base registers.
 template <int D>
-__device__ __forceinline__ bf16x8 read_k(const char LDS_AS *kbuf, int kb, int s, int lane) {
-  const int row = kb * 32 + (lane & 31);
-  const int c = 2 * s + (lane >> 5);
-  const char LDS_AS *p = kbuf + row * (D * 2) + ((c ^ swz<D>(row)) << 4);
-  return *(const bf16x8 LDS_AS *)p;
+struct LdsAddr {
+  unsigned ky, vw0, vw1;
+  __device__ __forceinline__ void init(int lane) {
+    const int row = lane & 31, h = lane >> 5;
+    ky = (unsigned)(row * (2 * D)) | (unsigned)((16 * h) ^ (swz<D>(row) << 4));
+    const int j = lane & 15, g = lane >> 4;
+    const int cl = 2 * (g & 1) + ((j & 3) >> 1);
+    unsigned w[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int kk = 4 * h + (j >> 2) + 8 * r;
+      const int sw = swz<D>(kk);
+      const int z = ((sw & ~3) << 4) | ((cl ^ (sw & 3)) << 4);
+      w[r] = (unsigned)(kk * (2 * D)) | (unsigned)z | (unsigned)((j & 1) * 8);
+    }
+    vw0 = w[0];
+    vw1 = w[1];
+  }
+};
+
+__device__ __forceinline__ unsigned lds_u32(const char LDS_AS *p) { return (unsigned)(uintptr_t)p; }
+
+// K operand (A of S^T = K Q^T) for key sub-block kb, k-step s; ka = KY + buffer.
+template <int D>
+__device__ __forceinline__ bf16x8 read_k(unsigned ka, int kb, int s) {
+  const unsigned addr = (ka ^ (unsigned)(32 * s)) + (unsigned)(kb * 32 * 2 * D);
+  return *(const bf16x8 LDS_AS *)(uintptr_t)addr;
 }
 
 // V^T operand (A of O^T += V^T P^T) for 16-key step t and 32-wide d tile dt:
@@ -205,18 +266,14 @@ __device__ __forceinline__ bf16x8 read_k(const char LDS_AS *kbuf, int kb, int s,
 // (h = l/32), matching the key order of the P operand taken from the S
 // accumulator layout.  Within a 16-lane group the transposed read hands lane
 // i element i%4 of the rows supplied by lanes 4e + i/4, so lane j supplies
-// key (j/4) and d-quad (j%4) of its group's 16 d values.
+// key (j/4) and d-quad (j%4) of its group's 16 d values.  va_r = VW_r + buffer.
 template <int D>
-__device__ __forceinline__ bf16x8 read_vt(const char LDS_AS *vbuf, int t, int dt, int lane) {
-  const int j = lane & 15, g = lane >> 4, h = lane >> 5;
-  const int d = 32 * dt + 16 * (g & 1) + 4 * (j & 3);
-  const int c = d >> 3, half = (d >> 2) & 1;
-  const int key0 = 16 * t + 4 * h + (j >> 2);
-  const int key1 = key0 + 8;
-  const char LDS_AS *p0 = vbuf + key0 * (D * 2) + ((c ^ swz<D>(key0)) << 4) + (half << 3);
-  const char LDS_AS *p1 = vbuf + key1 * (D * 2) + ((c ^ swz<D>(key1)) << 4) + (half << 3);
-  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)p0);
-  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)p1);
+__device__ __forceinline__ bf16x8 read_vt(unsigned va0, unsigned va1, int t, int dt) {
+  const unsigned off = (unsigned)(t * 16 * 2 * D);
+  const unsigned p0 = (va0 ^ (unsigned)(64 * dt)) + off;
+  const unsigned p1 = (va1 ^ (unsigned)(64 * dt)) + off;
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(uintptr_t)p0);
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(uintptr_t)p1);
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8, r);
@@ -225,31 +282,52 @@ __device__ __forceinline__ bf16x8 read_vt(const char LDS_AS *vbuf, int t, int dt
 // Per-wave state of one tile.
 template <int D>
 struct WaveState {
-  bf16x8 qf[D / 16];
-  f32x16 o[D / 32];
+  bf16x8 qf[D / 16];  // Q rows of this wave (B operand of S^T = K Q^T)
+  f32x16 o[D / 32];   // O^T accumulators
+  f32x16 s[2];        // S^T of the block between its product and its softmax
+  bf16x8 p[4];        // bf16 P of the block between its softmax and its PV product
   float m_ref, l32, lbf;
 };
 
-// One KV block for one wave: S^T = K Q^T, mask, statistics, exp, P V.
-template <int D, bool CAUSAL, int EMU, bool COUNT>
-__device__ __forceinline__ void block_step(WaveState<D> &st, const char LDS_AS *kbuf,
-                                           const char LDS_AS *vbuf, int lane, int n0, int row,
-                                           int L, bool need_mask, bool last_block, const Args &a) {
-  // ---- S^T = K Q^T : two 32-key sub-blocks, D/16 k-steps each
-  f32x16 sacc[2];
+// S^T = K Q^T for one 64-key block: two 32-key sub-blocks, D/16 k-steps each.
+// The K operands are read kPrefK k-steps ahead of their products (the
+// scheduling barriers keep that order), so LDS latency hides behind the
+// matrix unit instead of stalling each product.
+constexpr int kPrefK = 2;
+template <int D>
+__device__ __forceinline__ void qk_step(WaveState<D> &st, const LdsAddr<D> &la,
+                                        const char LDS_AS *kbuf) {
+  constexpr int NS = D / 16;
+  const unsigned ka = la.ky + lds_u32(kbuf);
+  bf16x8 kf[NS][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
+    for (int e = 0; e < 16; ++e) st.s[kb][e] = 0.0f;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 kf = read_k<D>(kbuf, kb, s, lane);
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[s], sacc[kb], 0, 0, 0);
-    }
+  for (int s = 0; s < kPrefK && s < NS; ++s) {
+    kf[s][0] = read_k<D>(ka, 0, s);
+    kf[s][1] = read_k<D>(ka, 1, s);
   }
-  // ---- mask: key index of sacc[kb][4i+j] is n0 + 32kb + 8i + 4h + j
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s + kPrefK < NS) {
+      kf[s + kPrefK][0] = read_k<D>(ka, 0, s + kPrefK);
+      kf[s + kPrefK][1] = read_k<D>(ka, 1, s + kPrefK);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    st.s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][0], st.qf[s], st.s[0], 0, 0, 0);
+    st.s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][1], st.qf[s], st.s[1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Mask, row statistics, conditional rescale, exp2, row sums and bf16 packing
+// of one block (scores in st.s, probabilities out to st.p).
+template <int D, bool CAUSAL, int EMU, bool COUNT>
+__device__ __forceinline__ void softmax_step(WaveState<D> &st, int lane, int n0, int row, int L,
+                                             bool need_mask, bool last_block, const Args &a) {
+  // ---- mask: key index of s[kb][4i+j] is n0 + 32kb + 8i + 4h + j
   const int h = lane >> 5;
   if (need_mask) {
 #pragma unroll
@@ -258,15 +336,15 @@ __device__ __forceinline__ void block_step(WaveState<D> &st, const char LDS_AS *
       for (int e = 0; e < 16; ++e) {
         const int key = n0 + 32 * kb + 8 * (e >> 2) + 4 * h + (e & 3);
         const bool masked = (key >= L) || (CAUSAL && key > row);
-        sacc[kb][e] = masked ? -INFINITY : sacc[kb][e];
+        st.s[kb][e] = masked ? -INFINITY : st.s[kb][e];
       }
   }
   // ---- block row max (raw scores; c > 0 so it commutes with scaling)
-  float mx = sacc[0][0];
+  float mx = st.s[0][0];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st.s[kb][e]);
   mx = max_halves(mx);
   const float m_blk = mx * a.c;  // -inf when the whole row of the block is masked
   // ---- conditional rescale, decided for the whole wave
@@ -289,15 +367,14 @@ __device__ __forceinline__ void block_step(WaveState<D> &st, const char LDS_AS *
     if (lane == 0) atomicAdd(&a.counters[1], 1ull);
   }
   const float m_use = (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
-  // ---- p = exp2(c*s - m), sums, bf16 pack
-  bf16x8 pf[4];
+  // ---- p = exp2(c*s - m), sums, bf16 pack into the PV operand layout
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
-      const float x0 = __builtin_fmaf(sacc[kb][e], a.c, -m_use);
-      const float x1 = __builtin_fmaf(sacc[kb][e + 1], a.c, -m_use);
+      const float x0 = __builtin_fmaf(st.s[kb][e], a.c, -m_use);
+      const float x1 = __builtin_fmaf(st.s[kb][e + 1], a.c, -m_use);
       float p0, p1;
       if (EMU > 0 && !last_block && (e % EMU) == 0) p0 = exp2_poly(x0);
       else p0 = exp2_hw(x0);
@@ -306,27 +383,69 @@ __device__ __forceinline__ void block_step(WaveState<D> &st, const char LDS_AS *
       const bf16x2 pb = {(__bf16)p0, (__bf16)p1};
       st.lbf = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, st.lbf, false);
       const int t = 2 * kb + (e >> 3);
-      pf[t][e & 7] = pb[0];
-      pf[t][(e & 7) + 1] = pb[1];
-    }
-  }
-  // ---- O^T += V^T P^T : D/32 d-tiles, 4 steps of 16 keys
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      bf16x8 vf = read_vt<D>(vbuf, t, dt, lane);
-      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], st.o[dt], 0, 0, 0);
+      st.p[t][e & 7] = pb[0];
+      st.p[t][(e & 7) + 1] = pb[1];
     }
   }
 }
 
+// O^T += V^T P^T for one block: D/32 d-tiles, 4 steps of 16 keys.  The V^T
+// operands of key step t+1 are read while the products of step t run.
+template <int D>
+__device__ __forceinline__ void pv_step(WaveState<D> &st, const LdsAddr<D> &la,
+                                        const char LDS_AS *vbuf) {
+  constexpr int NT = D / 32;
+  const unsigned va0 = la.vw0 + lds_u32(vbuf), va1 = la.vw1 + lds_u32(vbuf);
+  bf16x8 vf[4][NT];
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) vf[0][dt] = read_vt<D>(va0, va1, 0, dt);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (t + 1 < 4) {
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) vf[t + 1][dt] = read_vt<D>(va0, va1, t + 1, dt);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt)
+      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t][dt], st.p[t], st.o[dt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Which KV blocks a wave (32 rows from wrow0) needs, and which need masking.
+struct WaveRows {
+  int wrow0, wrow_last;   // first and last valid row of the wave
+  bool active;
+  int last_block;         // index of the wave's last useful block
+  __device__ __forceinline__ bool useful(int j, bool causal) const {
+    return active && (!causal || j * kBN <= wrow_last);
+  }
+  __device__ __forceinline__ bool need_mask(int j, int L, bool causal) const {
+    const int n0 = j * kBN;
+    return (n0 + kBN > L) || (causal && n0 + kBN - 1 > wrow0);
+  }
+};
+
 // Process one tile (b, h, mb) with the whole workgroup.
+//
+// Eight-wave workgroups (D <= 128) run a two-phase "ping-pong" per KV block
+// (the FlashAttention-4 paper, section 3.1.2: two output tiles per CTA, the
+// matrix unit working on one while the other does its softmax).  Half 0
+// (waves 0-3, one per SIMD) and half 1 (waves 4-7) hold different rows; in
+// every phase one half issues matrix products and the other its softmax, so
+// each SIMD always has one wave on MFMA and one on VALU:
+//   interval j, phase 1:  half 0: S_j = K_j Q^T, O += V_{j-1} P_{j-1}   half 1: softmax_{j-1}
+//   interval j, phase 2:  half 0: softmax_j                             half 1: S_j, O += V_{j-1} P_{j-1}
+// K/V blocks rotate through three LDS buffers: block j+1 is copied while the
+// workgroup still reads K_j and V_{j-1}.
+// Four-wave workgroups (D = 256) run the plain sequence per block with two
+// buffers.
 template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>
 __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, char LDS_AS *lds) {
   using C = Cfg<D>;
   const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   long long tok0;
   int L;
   if constexpr (VARLEN) {
@@ -340,20 +459,17 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   const int m0 = mb * C::BM;
   if (m0 >= L) return;  // workgroup-uniform
   const int H = a.H;
-  // rows of this wave and lane
-  const int wrow0 = m0 + wave * 32;
-  const int row = wrow0 + (lane & 31);
-  const bool wave_active = wrow0 < L;
-  const int wrow_last = (wrow0 + 31 < L - 1) ? wrow0 + 31 : L - 1;
+  WaveRows wr;
+  wr.wrow0 = m0 + wave * 32;
+  wr.active = wr.wrow0 < L;
+  wr.wrow_last = (wr.wrow0 + 31 < L - 1) ? wr.wrow0 + 31 : L - 1;
+  const int row = wr.wrow0 + (lane & 31);
 
   // KV range shared by the workgroup
   const int n_end = CAUSAL ? ((m0 + C::BM < L) ? m0 + C::BM : L) : L;
   const int nblocks = fa::ceil_div(n_end, kBN);
-
-  char LDS_AS *kb0 = lds;
-  char LDS_AS *vb0 = lds + C::BLOCK_BYTES;
-  char LDS_AS *kb1 = lds + 2 * C::BLOCK_BYTES;
-  char LDS_AS *vb1 = lds + 3 * C::BLOCK_BYTES;
+  wr.last_block = CAUSAL ? ((wr.wrow_last / kBN < nblocks - 1) ? wr.wrow_last / kBN : nblocks - 1)
+                         : nblocks - 1;
 
   // Q fragments: lane l holds row (l%32), d = 16s + 8(l/32) .. +7
   WaveState<D> st;
@@ -362,6 +478,11 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     const bf16x8 *qp = (const bf16x8 *)(a.q + ((tok0 + qrow) * H + h) * (long long)D + 8 * (lane >> 5));
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) st.qf[s] = qp[2 * s];
+    // Opaque to the compiler: Q stays in registers for the whole tile instead
+    // of being re-fetched inside the KV loop (a re-fetch would share the
+    // in-order vector-memory counter with the K/V prefetch and wait for it).
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(st.qf[s]));
   }
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -371,34 +492,86 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   st.l32 = 0.0f;
   st.lbf = 0.0f;
 
-  issue_block<D>(a.k, tok0, H, h, 0, L, kb0, wave, lane);
-  issue_block<D>(a.v, tok0, H, h, 0, L, vb0, wave, lane);
+  BlockLoader<D> ld;
+  ld.init(H, wave, lane);
+  LdsAddr<D> la;
+  la.init(lane);
 
-  for (int j = 0; j < nblocks; ++j) {
-    const int n0 = j * kBN;
-    char LDS_AS *kcur = (j & 1) ? kb1 : kb0;
-    char LDS_AS *vcur = (j & 1) ? vb1 : vb0;
-    if (j + 1 < nblocks) {
-      char LDS_AS *knext = (j & 1) ? kb0 : kb1;
-      char LDS_AS *vnext = (j & 1) ? vb0 : vb1;
-      issue_block<D>(a.k, tok0, H, h, n0 + kBN, L, knext, wave, lane);
-      issue_block<D>(a.v, tok0, H, h, n0 + kBN, L, vnext, wave, lane);
-      wait_vmcnt<2 * C::LOADS>();
-    } else {
+  if constexpr (C::PINGPONG) {
+    const int half = wave / 4;
+    auto kbuf = [&](int j) { return lds + (2 * (j % 3)) * C::BLOCK_BYTES; };
+    auto vbuf = [&](int j) { return lds + (2 * (j % 3) + 1) * C::BLOCK_BYTES; };
+    // Start of interval it: this wave's copies of block it have landed,
+    // then the barrier makes everyone's visible (and ends interval it-1, so
+    // the buffer of block it-2 is free for block it+1).
+    auto interval_start = [&](int it) {
       wait_vmcnt<0>();
+      barrier_after_reads();
+      if (it + 1 < nblocks) {
+        ld.issue(a.k, tok0, H, h, (it + 1) * kBN, L, kbuf(it + 1));
+        ld.issue(a.v, tok0, H, h, (it + 1) * kBN, L, vbuf(it + 1));
+      }
+    };
+    auto softmax = [&](int j) {
+      softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, j * kBN, row, L, wr.need_mask(j, L, CAUSAL),
+                                          j == wr.last_block, a);
+    };
+    ld.issue(a.k, tok0, H, h, 0, L, kbuf(0));
+    ld.issue(a.v, tok0, H, h, 0, L, vbuf(0));
+    // The two halves run separate loops that meet at the same barriers.
+    if (half == 0) {
+      for (int it = 0; it <= nblocks; ++it) {
+        interval_start(it);
+        const bool cur = it < nblocks && wr.useful(it, CAUSAL);
+        if (cur) qk_step<D>(st, la, kbuf(it));
+        __builtin_amdgcn_sched_barrier(0);
+        if (it > 0 && wr.useful(it - 1, CAUSAL)) pv_step<D>(st, la, vbuf(it - 1));
+        barrier_nofence();
+        if (cur) softmax(it);
+      }
+    } else {
+      for (int it = 0; it <= nblocks; ++it) {
+        interval_start(it);
+        const bool prev = it > 0 && wr.useful(it - 1, CAUSAL);
+        if (prev) softmax(it - 1);
+        barrier_nofence();
+        if (it < nblocks && wr.useful(it, CAUSAL)) qk_step<D>(st, la, kbuf(it));
+        __builtin_amdgcn_sched_barrier(0);
+        if (prev) pv_step<D>(st, la, vbuf(it - 1));
+      }
     }
-    barrier_nofence();
-    // does this wave need this block, and does it need the mask?
-    const bool useful = wave_active && (!CAUSAL || n0 <= wrow_last);
-    if (useful) {
-      const bool need_mask = (n0 + kBN > L) || (CAUSAL && n0 + kBN - 1 > wrow0);
-      block_step<D, CAUSAL, EMU, COUNT>(st, kcur, vcur, lane, n0, row, L, need_mask,
-                                        j + 1 == nblocks, a);
+  } else {
+    char LDS_AS *kb0 = lds;
+    char LDS_AS *vb0 = lds + C::BLOCK_BYTES;
+    char LDS_AS *kb1 = lds + 2 * C::BLOCK_BYTES;
+    char LDS_AS *vb1 = lds + 3 * C::BLOCK_BYTES;
+    ld.issue(a.k, tok0, H, h, 0, L, kb0);
+    ld.issue(a.v, tok0, H, h, 0, L, vb0);
+    for (int j = 0; j < nblocks; ++j) {
+      const int n0 = j * kBN;
+      char LDS_AS *kcur = (j & 1) ? kb1 : kb0;
+      char LDS_AS *vcur = (j & 1) ? vb1 : vb0;
+      if (j + 1 < nblocks) {
+        char LDS_AS *knext = (j & 1) ? kb0 : kb1;
+        char LDS_AS *vnext = (j & 1) ? vb0 : vb1;
+        ld.issue(a.k, tok0, H, h, n0 + kBN, L, knext);
+        ld.issue(a.v, tok0, H, h, n0 + kBN, L, vnext);
+        wait_vmcnt<2 * C::LOADS>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      barrier_nofence();
+      if (wr.useful(j, CAUSAL)) {
+        qk_step<D>(st, la, kcur);
+        softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, n0, row, L, wr.need_mask(j, L, CAUSAL),
+                                            j == wr.last_block, a);
+        pv_step<D>(st, la, vcur);
+      }
+      barrier_after_reads();  // every wave is done reading this buffer
     }
-    barrier_after_reads();  // every wave is done reading this buffer
   }
 
-  if (!wave_active) return;
+  if (!wr.active) return;
   // ---- epilogue: combine the two half-wave partial sums of each row
   const float l32 = sum_halves(st.l32);
   const float lbf = sum_halves(st.lbf);
@@ -424,11 +597,11 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
 }
 
 template <int D>
-constexpr int lds_bytes() { return 4 * Cfg<D>::BLOCK_BYTES; }
+constexpr int lds_bytes() { return (Cfg<D>::PINGPONG ? 6 : 4) * Cfg<D>::BLOCK_BYTES; }
 
 // Persistent kernel: each workgroup walks its static LPT list.
 template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>
-__global__ __launch_bounds__(Cfg<D>::THREADS) void fa_fwd_persistent(Args a) {
+__global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fwd_persistent(Args a) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   char LDS_AS *lds = (char LDS_AS *)lds_raw;
   using C = Cfg<D>;
@@ -445,10 +618,10 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void fa_fwd_persistent(Args a) {
     __syncthreads();
     fa::tables_phase3(s, t, threadIdx.x, blockDim.x);
     __syncthreads();
-    __shared__ int n_items_sh;
-    if (threadIdx.x == 0) n_items_sh = fa::tables_phase4(s, t);
+    int *n_items_sh = t.off + fa::kMaxVarlenLevels + 1;
+    if (threadIdx.x == 0) *n_items_sh = fa::tables_phase4(s, t);
     __syncthreads();
-    s.n_items = n_items_sh;
+    s.n_items = *n_items_sh;
   }
   int x, w, W;
   fa::worker_slot(s, blockIdx.x, a.workers, &x, &w, &W);
@@ -463,7 +636,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS) void fa_fwd_persistent(Args a) {
 
 // One workgroup per tile, natural (b, h, mb) order.
 template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>
-__global__ __launch_bounds__(Cfg<D>::THREADS) void fa_fwd_grid(Args a) {
+__global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fwd_grid(Args a) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   char LDS_AS *lds = (char LDS_AS *)lds_raw;
   using C = Cfg<D>;
@@ -551,9 +724,8 @@ int launch_variant(const Args &a0, int schedule, int cus, hipStream_t stream) {
   bool persistent = (schedule == 0);
   if (VARLEN && (a.B > fa::kMaxVarlenSeqs || nmb > fa::kMaxVarlenLevels)) persistent = false;
   if (persistent) {
-    const int occ = 1;  // workgroups per CU
-    a.workers = cus * occ;
-    if (VARLEN) lds += sizeof(int) * (2 * fa::kMaxVarlenSeqs + fa::kMaxVarlenLevels + 1);
+    a.workers = cus * C::OCC;
+    if (VARLEN) lds += sizeof(int) * (2 * fa::kMaxVarlenSeqs + fa::kMaxVarlenLevels + 2);
     auto kern = fa_fwd_persistent<D, CAUSAL, VARLEN, EMU, COUNT>;
     if (!allow_lds(kern, lds)) return FA_ERR_HIP;
     hipLaunchKernelGGL(kern, dim3(a.workers), dim3(C::THREADS), lds, stream, a);
@@ -708,7 +880,7 @@ int fa_num_workers(int D, int *workers_out) {
   DeviceInfo *dev = nullptr;
   int rc = current_device(&dev);
   if (rc != FA_OK) return rc;
-  *workers_out = dev->cus;
+  *workers_out = dev->cus * (D == 256 ? Cfg<256>::OCC : (D == 128 ? Cfg<128>::OCC : Cfg<64>::OCC));
   return FA_OK;
 }
 

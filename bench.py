@@ -35,6 +35,37 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of the kernel sources (csrc/*.hip, csrc/*.h), to tell whether a
+    stored counter measurement still describes the current kernel."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_forward_04_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE profile
+    (scaled by the copy-kernel calibration), or None if there is none for this
+    workload or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    return rec.get("hbm_bytes")
+
+
 DEFAULT_WORKLOAD = "long_b1h16s32768d128_causal"
 SECONDARY_WORKLOAD = "causal_b2h16s8192d128"
 
@@ -133,6 +164,12 @@ def main():
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--exp2-emu", type=int, default=None)
     ap.add_argument("--schedule", type=int, default=None)
+    ap.add_argument("--table", action="store_true",
+                    help="time every named workload (one JSON line each) instead of the "
+                         "single bench line")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="only time torch's bf16 matmul (hipBLASLt) on large shapes, as context "
+                         "for the MFMA fraction the attention kernel reaches")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times); used to "
                          "scale the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
@@ -161,6 +198,25 @@ def main():
         print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
         return
 
+    if args.gemm_reference:
+        for (m, n, kk) in [(4096, 4096, 4096), (8192, 8192, 8192), (16384, 16384, 8192)]:
+            a = torch.randn(m, kk, dtype=torch.bfloat16, device="cuda")
+            b = torch.randn(kk, n, dtype=torch.bfloat16, device="cuda")
+            for _ in range(5):
+                c = a @ b
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(20):
+                c = a @ b
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 20
+            print(json.dumps({"gemm_bf16": [m, n, kk], "ms": round(ms, 4),
+                              "TFLOP/s": round(2.0 * m * n * kk / ms / 1e9, 1)}), flush=True)
+            del a, b, c
+        return
+
     tuning = None
     if args.tau is not None or args.exp2_emu is not None or args.schedule is not None:
         tuning = fa.default_tuning()
@@ -170,6 +226,17 @@ def main():
             tuning.exp2_emu = args.exp2_emu
         if args.schedule is not None:
             tuning.schedule = args.schedule
+
+    if args.table:
+        for name, wl in WORKLOADS.items():
+            rr = time_workload(fa, torch, wl, args.steps, args.warmup, tuning)
+            v = rr["flops"] / (rr["kernel_ms_mean"] * 1e-3) / 1e12
+            print(json.dumps({"workload": name, "kernel_ms_mean": round(rr["kernel_ms_mean"], 4),
+                              "kernel_ms_median": round(rr["kernel_ms_median"], 4),
+                              "TFLOP/s": round(v, 1),
+                              "pct_of_peak": round(100 * v / PEAK_BF16_TFLOPS, 2),
+                              "flops": rr["flops"]}), flush=True)
+        return
 
     w = WORKLOADS[args.workload]
     r = time_workload(fa, torch, w, args.steps, args.warmup, tuning)
@@ -193,7 +260,8 @@ def main():
                    "causal": w.causal, "seed": w.seed, "flops_per_step": r["flops"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name),
                      "kernel_ms_mean": round(r["kernel_ms_mean"], 4),
                      "kernel_ms_median": round(r["kernel_ms_median"], 4),
                      "kernel_ms_min": round(r["kernel_ms_min"], 4)},

@@ -437,7 +437,7 @@ struct WaveRows {
 // each SIMD always has one wave on MFMA and one on VALU:
 //   interval j, phase 1:  half 0: S_j = K_j Q^T, O += V_{j-1} P_{j-1}   half 1: softmax_{j-1}
 //   interval j, phase 2:  half 0: softmax_j                             half 1: S_j, O += V_{j-1} P_{j-1}
-// K/V blocks rotate through three LDS buffers: block j+1 is copied while the
+// K/V blocks rotate through four LDS buffers: block j+2 is copied while the
 // workgroup still reads K_j and V_{j-1}.
 // Four-wave workgroups (D = 256) run the plain sequence per block with two
 // buffers.
@@ -499,17 +499,19 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
 
   if constexpr (C::PINGPONG) {
     const int half = wave / 4;
-    auto kbuf = [&](int j) { return lds + (2 * (j % 3)) * C::BLOCK_BYTES; };
-    auto vbuf = [&](int j) { return lds + (2 * (j % 3) + 1) * C::BLOCK_BYTES; };
-    // Start of interval it: this wave's copies of block it have landed,
-    // then the barrier makes everyone's visible (and ends interval it-1, so
-    // the buffer of block it-2 is free for block it+1).
+    auto kbuf = [&](int j) { return lds + (2 * (j & 3)) * C::BLOCK_BYTES; };
+    auto vbuf = [&](int j) { return lds + (2 * (j & 3) + 1) * C::BLOCK_BYTES; };
+    // Start of interval it: this wave's copies of block it have landed
+    // (block it+1 may still be in flight), then the barrier makes everyone's
+    // visible and ends interval it-1, so the buffer of block it-2 is free for
+    // block it+2: copies run two intervals ahead of their use.
     auto interval_start = [&](int it) {
-      wait_vmcnt<0>();
+      if (it + 1 < nblocks) wait_vmcnt<2 * C::LOADS>();
+      else wait_vmcnt<0>();
       barrier_after_reads();
-      if (it + 1 < nblocks) {
-        ld.issue(a.k, tok0, H, h, (it + 1) * kBN, L, kbuf(it + 1));
-        ld.issue(a.v, tok0, H, h, (it + 1) * kBN, L, vbuf(it + 1));
+      if (it + 2 < nblocks) {
+        ld.issue(a.k, tok0, H, h, (it + 2) * kBN, L, kbuf(it + 2));
+        ld.issue(a.v, tok0, H, h, (it + 2) * kBN, L, vbuf(it + 2));
       }
     };
     auto softmax = [&](int j) {
@@ -518,6 +520,10 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     };
     ld.issue(a.k, tok0, H, h, 0, L, kbuf(0));
     ld.issue(a.v, tok0, H, h, 0, L, vbuf(0));
+    if (nblocks > 1) {
+      ld.issue(a.k, tok0, H, h, kBN, L, kbuf(1));
+      ld.issue(a.v, tok0, H, h, kBN, L, vbuf(1));
+    }
     // The two halves run separate loops that meet at the same barriers.
     if (half == 0) {
       for (int it = 0; it <= nblocks; ++it) {
@@ -597,7 +603,7 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
 }
 
 template <int D>
-constexpr int lds_bytes() { return (Cfg<D>::PINGPONG ? 6 : 4) * Cfg<D>::BLOCK_BYTES; }
+constexpr int lds_bytes() { return (Cfg<D>::PINGPONG ? 8 : 4) * Cfg<D>::BLOCK_BYTES; }
 
 // Persistent kernel: each workgroup walks its static LPT list.
 template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>

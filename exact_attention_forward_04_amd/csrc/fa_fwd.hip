@@ -11,9 +11,10 @@
 //              v_mfma_f32_32x32x16_bf16 (lane l: row l%32, 8 consecutive d).
 //   K, V       streamed in blocks of BN = 64 keys through LDS with
 //              global_load_lds_dwordx4 (16 bytes per lane straight into LDS),
-//              double-buffered: block j+1 is in flight while block j is
-//              used.  Rows are stored with a 16-byte-chunk XOR swizzle so the
-//              MFMA operand reads do not collide on LDS banks.
+//              copied two blocks ahead of their use through a ring of four
+//              buffers (D = 256: double-buffered).  Rows are stored with a
+//              16-byte-chunk XOR swizzle so the MFMA operand reads do not
+//              collide on LDS banks.
 //   S^T = K Q^T  on MFMA (keys on the M side, query rows on N): every lane
 //              then holds 16 keys of ONE query row per 32-key sub-block, so a
 //              row maximum is an in-lane max plus one v_permlane32_swap with
@@ -25,15 +26,15 @@
 //              normalisation absorbs the difference.  p = exp2(c*s - m_ref)
 //              with c = scale*log2(e), by v_exp_f32 or, for a fixed share of
 //              column slots, by the Cody-Waite degree-3 polynomial (paper
-//              section 3.1.3).  Two row sums: l32 = sum p (fp32, for the LSE)
-//              and lbf = sum bf16(p) (for the output, so that the rounding of
-//              P to bf16 cancels in O = sum bf16(p) v / lbf).
+//              section 3.1.3).  The row sum l = sum p is kept in fp32 from
+//              the unrounded p (paper section 3.1.2 sums after the exp);
+//              P is rounded to bf16 only as the operand of the PV product.
 //   O^T += V^T P^T  on MFMA: the S accumulator registers, rounded to bf16,
 //              are already the B operand (the contraction index runs over
 //              the keys in the order the S layout holds them); V^T comes from
 //              LDS with ds_read_b64_tr_b16, which transposes 16-bit elements
 //              across each 16-lane group.
-//   epilogue   O / lbf -> bf16, LSE = ln2 * (m_ref + log2 l32).
+//   epilogue   O / l -> bf16, LSE = ln2 * (m_ref + log2 l).
 //
 // Scheduling: a persistent grid walks tiles in longest-processing-time-first
 // order (fa_sched.h), or one workgroup per tile in natural order.
@@ -173,7 +174,8 @@ struct Args {
 template <int D>
 struct BlockLoader {
   using C = Cfg<D>;
-  int off[C::LOADS];  // element offset of this lane's slot from the block's first row
+  unsigned voff[C::LOADS];  // byte offset of this lane's 16-byte chunk from the block's first row
+  unsigned row_bytes;       // H*D*2: distance between consecutive tokens of a head
   int wave, lane;
 
   __device__ __forceinline__ int slot0(int i) const { return (i * C::NW + wave) * kWave; }
@@ -182,40 +184,49 @@ struct BlockLoader {
   __device__ __forceinline__ void init(int H, int wave_, int lane_) {
     wave = __builtin_amdgcn_readfirstlane(wave_);
     lane = lane_;
+    row_bytes = (unsigned)H * (unsigned)D * 2u;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int p = slot0(i) + lane;
       const int row = p / C::CPR;
       const int c = (p % C::CPR) ^ swz<D>(row);
-      off[i] = row * H * D + c * 8;
+      voff[i] = (unsigned)row * row_bytes + (unsigned)c * 16u;
     }
   }
 
-  // Copy rows n0 .. n0+BN-1 of one (sequence, head) of K or V into dst.
-  // Rows at or past L read row L-1 instead (in bounds; masked later).
+  // One 16-byte-per-lane copy: global (SGPR base + 32-bit lane offset) -> LDS
+  // at m0 + 16*lane.
+  static __device__ __forceinline__ void dma16(const char *blk, unsigned voff_, unsigned lds_addr) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(lds_addr), "v"(voff_), "s"(blk)
+        : "memory", "m0");
+  }
+
+  // Copy this wave's chunk i of rows n0 .. n0+BN-1 of one (sequence, head)
+  // of K or V into dst.  Rows at or past L read row L-1 instead (in bounds;
+  // masked later).  The full-block test is on scalars only: one scalar branch.
+  __device__ __forceinline__ void issue_one(const __bf16 *base, long long tok0, int H, int h,
+                                            int n0, int L, char LDS_AS *dst, int i) const {
+    const char *blk = (const char *)(base + ((tok0 + n0) * H + h) * (long long)D);
+    const unsigned lds_addr = (unsigned)(uintptr_t)dst + (unsigned)slot0(i) * 16u;
+    if (n0 + kBN <= L) {
+      dma16(blk, voff[i], lds_addr);
+    } else {
+      const int last = L - 1 - n0;  // >= 0: blocks start below L
+      const int row = row_of(i);
+      const int r = row < last ? row : last;
+      dma16(blk, voff[i] - (unsigned)(row - r) * row_bytes, lds_addr);
+    }
+  }
+  // All of this wave's chunks of one block.
   __device__ __forceinline__ void issue(const __bf16 *base, long long tok0, int H, int h, int n0,
                                         int L, char LDS_AS *dst) const {
-    const __bf16 *blk = base + ((tok0 + n0) * H + h) * (long long)D;
-    const bool full = n0 + kBN <= L;  // wave-uniform
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const __bf16 *src;
-      if (full) {
-        src = blk + off[i];
-      } else {
-        const int row = row_of(i);
-        const int r = (n0 + row < L) ? row : L - 1 - n0;
-        src = blk + off[i] + (long long)(r - row) * H * D;
-      }
-      const unsigned lds_addr = (unsigned)(uintptr_t)dst + (unsigned)slot0(i) * 16u;
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "s_nop 0\n\t"
-          "global_load_lds_dwordx4 %1, off"
-          :
-          : "s"(lds_addr), "v"(src)
-          : "memory", "m0");
-    }
+    for (int i = 0; i < C::LOADS; ++i) issue_one(base, tok0, H, h, n0, L, dst, i);
   }
 };
 
@@ -286,7 +297,7 @@ struct WaveState {
   f32x16 o[D / 32];   // O^T accumulators
   f32x16 s[2];        // S^T of the block between its product and its softmax
   bf16x8 p[4];        // bf16 P of the block between its softmax and its PV product
-  float m_ref, l32, lbf;
+  float m_ref, l32;
 };
 
 // S^T = K Q^T for one 64-key block: two 32-key sub-blocks, D/16 k-steps each.
@@ -323,10 +334,14 @@ __device__ __forceinline__ void qk_step(WaveState<D> &st, const LdsAddr<D> &la,
 }
 
 // Mask, row statistics, conditional rescale, exp2, row sums and bf16 packing
-// of one block (scores in st.s, probabilities out to st.p).
-template <int D, bool CAUSAL, int EMU, bool COUNT>
+// of one block (scores in st.s, probabilities out to st.p).  side(0) runs
+// before the row max and side(1) before the exp loop: the caller hangs its
+// K/V copies there, off the path of the other half's matrix products.
+template <int D, bool CAUSAL, int EMU, bool COUNT, typename Side>
 __device__ __forceinline__ void softmax_step(WaveState<D> &st, int lane, int n0, int row, int L,
-                                             bool need_mask, bool last_block, const Args &a) {
+                                             bool need_mask, bool last_block, const Args &a,
+                                             Side &&side) {
+  side(0);
   // ---- mask: key index of s[kb][4i+j] is n0 + 32kb + 8i + 4h + j
   const int h = lane >> 5;
   if (need_mask) {
@@ -354,7 +369,6 @@ __device__ __forceinline__ void softmax_step(WaveState<D> &st, int lane, int n0,
     const float alpha = (st.m_ref == -INFINITY) ? 0.0f : exp2_hw(st.m_ref - m_new);
     st.m_ref = m_new;
     st.l32 *= alpha;
-    st.lbf *= alpha;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -367,8 +381,10 @@ __device__ __forceinline__ void softmax_step(WaveState<D> &st, int lane, int n0,
     if (lane == 0) atomicAdd(&a.counters[1], 1ull);
   }
   const float m_use = (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
-  // ---- p = exp2(c*s - m), sums, bf16 pack into the PV operand layout
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  side(1);
+  // ---- p = exp2(c*s - m), row sum (one partial sum per key sub-block, to
+  // halve the dependent chain), bf16 pack into the PV operand layout
+  float lsum[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -379,14 +395,14 @@ __device__ __forceinline__ void softmax_step(WaveState<D> &st, int lane, int n0,
       if (EMU > 0 && !last_block && (e % EMU) == 0) p0 = exp2_poly(x0);
       else p0 = exp2_hw(x0);
       p1 = exp2_hw(x1);
-      st.l32 += p0 + p1;
+      lsum[kb] += p0 + p1;
       const bf16x2 pb = {(__bf16)p0, (__bf16)p1};
-      st.lbf = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, st.lbf, false);
       const int t = 2 * kb + (e >> 3);
       st.p[t][e & 7] = pb[0];
       st.p[t][(e & 7) + 1] = pb[1];
     }
   }
+  st.l32 += lsum[0] + lsum[1];
 }
 
 // O^T += V^T P^T for one block: D/32 d-tiles, 4 steps of 16 keys.  The V^T
@@ -490,7 +506,6 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     for (int e = 0; e < 16; ++e) st.o[dt][e] = 0.0f;
   st.m_ref = -INFINITY;
   st.l32 = 0.0f;
-  st.lbf = 0.0f;
 
   BlockLoader<D> ld;
   ld.init(H, wave, lane);
@@ -509,14 +524,29 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       if (it + 1 < nblocks) wait_vmcnt<2 * C::LOADS>();
       else wait_vmcnt<0>();
       barrier_after_reads();
-      if (it + 2 < nblocks) {
-        ld.issue(a.k, tok0, H, h, (it + 2) * kBN, L, kbuf(it + 2));
-        ld.issue(a.v, tok0, H, h, (it + 2) * kBN, L, vbuf(it + 2));
-      }
     };
-    auto softmax = [&](int j) {
-      softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, j * kBN, row, L, wr.need_mask(j, L, CAUSAL),
-                                          j == wr.last_block, a);
+    // This wave's copies of block it+2 (K on side 0, V on side 1), issued
+    // from its softmax phase of interval it.  All eight waves issuing right
+    // after the barrier would queue 32 KB on the CU's vector-memory path at
+    // once and hold the waves that start matrix products behind it.
+    // Part 0: this wave's K copies of block it+2; part 1: its V copies.
+    auto copies = [&](int it) {
+      return [&, it](int part) {
+        if (it + 2 < nblocks) {
+          if (part == 0) ld.issue(a.k, tok0, H, h, (it + 2) * kBN, L, kbuf(it + 2));
+          else ld.issue(a.v, tok0, H, h, (it + 2) * kBN, L, vbuf(it + 2));
+        }
+      };
+    };
+    auto softmax_phase = [&](bool run, int j, int it) {
+      auto side = copies(it);
+      if (run) {
+        softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, j * kBN, row, L, wr.need_mask(j, L, CAUSAL),
+                                            j == wr.last_block, a, side);
+      } else {
+        side(0);
+        side(1);
+      }
     };
     ld.issue(a.k, tok0, H, h, 0, L, kbuf(0));
     ld.issue(a.v, tok0, H, h, 0, L, vbuf(0));
@@ -533,13 +563,13 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
         __builtin_amdgcn_sched_barrier(0);
         if (it > 0 && wr.useful(it - 1, CAUSAL)) pv_step<D>(st, la, vbuf(it - 1));
         barrier_nofence();
-        if (cur) softmax(it);
+        softmax_phase(cur, it, it);
       }
     } else {
       for (int it = 0; it <= nblocks; ++it) {
         interval_start(it);
         const bool prev = it > 0 && wr.useful(it - 1, CAUSAL);
-        if (prev) softmax(it - 1);
+        softmax_phase(prev, it - 1, it);
         barrier_nofence();
         if (it < nblocks && wr.useful(it, CAUSAL)) qk_step<D>(st, la, kbuf(it));
         __builtin_amdgcn_sched_barrier(0);
@@ -570,7 +600,7 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       if (wr.useful(j, CAUSAL)) {
         qk_step<D>(st, la, kcur);
         softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, n0, row, L, wr.need_mask(j, L, CAUSAL),
-                                            j == wr.last_block, a);
+                                            j == wr.last_block, a, [](int) {});
         pv_step<D>(st, la, vcur);
       }
       barrier_after_reads();  // every wave is done reading this buffer
@@ -580,9 +610,8 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   if (!wr.active) return;
   // ---- epilogue: combine the two half-wave partial sums of each row
   const float l32 = sum_halves(st.l32);
-  const float lbf = sum_halves(st.lbf);
   if (row < L) {
-    const float inv = 1.0f / lbf;
+    const float inv = 1.0f / l32;
     const int hh = lane >> 5;
     __bf16 *op = a.o + ((tok0 + row) * H + h) * (long long)D + 4 * hh;
 #pragma unroll

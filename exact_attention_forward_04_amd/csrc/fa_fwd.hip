@@ -61,6 +61,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kBN = 64;           // keys per KV block
+constexpr int kMatrixPrio = 2;    // wave priority (s_setprio) of a ping-pong matrix phase
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -448,15 +449,18 @@ struct WaveRows {
 // Eight-wave workgroups (D <= 128) run a two-phase "ping-pong" per KV block
 // (the FlashAttention-4 paper, section 3.1.2: two output tiles per CTA, the
 // matrix unit working on one while the other does its softmax).  Half 0
-// (waves 0-3, one per SIMD) and half 1 (waves 4-7) hold different rows; in
-// every phase one half issues matrix products and the other its softmax, so
-// each SIMD always has one wave on MFMA and one on VALU:
-//   interval j, phase 1:  half 0: S_j = K_j Q^T, O += V_{j-1} P_{j-1}   half 1: softmax_{j-1}
-//   interval j, phase 2:  half 0: softmax_j                             half 1: S_j, O += V_{j-1} P_{j-1}
-// K/V blocks rotate through four LDS buffers: block j+2 is copied while the
-// workgroup still reads K_j and V_{j-1}.
-// Four-wave workgroups (D = 256) run the plain sequence per block with two
-// buffers.
+// (waves 0-3, one per SIMD) and half 1 (waves 4-7) hold different rows.
+// After the barrier that opens interval j they run
+//   half 0:  S_j = K_j Q^T, O += V_{j-1} P_{j-1}   then   softmax_j
+//   half 1:  softmax_{j-1}                         then   S_j = K_j Q^T, O += V_{j-1} P_{j-1}
+// so each SIMD has one wave on MFMA while the other is on VALU.  The matrix
+// phase runs at raised wave priority, which keeps the matrix unit fed when
+// both waves of a SIMD have an instruction ready; no barrier separates the
+// two phases (the halves keep their offset on their own, and a barrier there
+// only added the wait for the slower half).  K/V blocks rotate through four
+// LDS buffers: block j+2 is copied while the workgroup still reads K_j and
+// V_{j-1}.  Four-wave workgroups (D = 256) run the plain sequence per block
+// with two buffers.
 template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>
 __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, char LDS_AS *lds) {
   using C = Cfg<D>;
@@ -559,10 +563,11 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       for (int it = 0; it <= nblocks; ++it) {
         interval_start(it);
         const bool cur = it < nblocks && wr.useful(it, CAUSAL);
+        __builtin_amdgcn_s_setprio(kMatrixPrio);
         if (cur) qk_step<D>(st, la, kbuf(it));
         __builtin_amdgcn_sched_barrier(0);
         if (it > 0 && wr.useful(it - 1, CAUSAL)) pv_step<D>(st, la, vbuf(it - 1));
-        barrier_nofence();
+        __builtin_amdgcn_s_setprio(0);
         softmax_phase(cur, it, it);
       }
     } else {
@@ -570,10 +575,11 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
         interval_start(it);
         const bool prev = it > 0 && wr.useful(it - 1, CAUSAL);
         softmax_phase(prev, it - 1, it);
-        barrier_nofence();
+        __builtin_amdgcn_s_setprio(kMatrixPrio);
         if (it < nblocks && wr.useful(it, CAUSAL)) qk_step<D>(st, la, kbuf(it));
         __builtin_amdgcn_sched_barrier(0);
         if (prev) pv_step<D>(st, la, vbuf(it - 1));
+        __builtin_amdgcn_s_setprio(0);
       }
     }
   } else {

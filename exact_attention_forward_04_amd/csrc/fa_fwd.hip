@@ -345,14 +345,17 @@ __device__ __forceinline__ void softmax_step(WaveState<D> &st, int lane, int n0,
   side(0);
   // ---- mask: key index of s[kb][4i+j] is n0 + 32kb + 8i + 4h + j
   const int h = lane >> 5;
+  // A key is kept iff key < L and (non-causal or key <= row), i.e. iff its
+  // in-block offset 32kb + 8(e>>2) + (e&3), a constant, is below the per-lane
+  // limit lim: one compare and one select per score.
   if (need_mask) {
+    const int lim = (CAUSAL ? (row + 1 < L ? row + 1 : L) : L) - n0 - 4 * h;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = n0 + 32 * kb + 8 * (e >> 2) + 4 * h + (e & 3);
-        const bool masked = (key >= L) || (CAUSAL && key > row);
-        st.s[kb][e] = masked ? -INFINITY : st.s[kb][e];
+        const int off = 32 * kb + 8 * (e >> 2) + (e & 3);
+        st.s[kb][e] = off < lim ? st.s[kb][e] : -INFINITY;
       }
   }
   // ---- block row max (raw scores; c > 0 so it commutes with scaling)

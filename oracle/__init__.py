@@ -68,6 +68,11 @@ def _dims(q_shape, cu):
     return B, S, H, D
 
 
+def _kv_heads(k_shape, cu):
+    """Number of K/V heads: axis 2 of a dense [B,S,Hkv,D] K, axis 1 of varlen [T,Hkv,D]."""
+    return k_shape[2] if cu is None else k_shape[1]
+
+
 def _shapes(B, S, H, D, cu):
     if cu is None:
         return (B, S, H, D), (B, H, S)
@@ -82,9 +87,9 @@ class OracleLib:
         lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
-        lib.oracle_attn_fwd_f64.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, P]
-        lib.oracle_attn_fwd_bf16.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, P]
-        lib.oracle_attn_rows_bf16.argtypes = [P, P, P, P, i64, P, P, i32, i32, i32, i32,
+        lib.oracle_attn_fwd_f64.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, f64, i32, P]
+        lib.oracle_attn_fwd_bf16.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, f64, i32, P]
+        lib.oracle_attn_rows_bf16.argtypes = [P, P, P, P, i64, P, P, i32, i32, i32, i32, i32,
                                               f64, i32, P]
         for fn in (lib.oracle_attn_fwd_f64, lib.oracle_attn_fwd_bf16, lib.oracle_attn_rows_bf16):
             fn.restype = i32
@@ -98,7 +103,8 @@ class OracleLib:
         self.path = path
 
     def attention_f64(self, q, k, v, scale, causal, cu_seqlens=None):
-        """Attention on float64 inputs; q, k, v are [B,S,H,D] (or [T,H,D] varlen).
+        """Attention on float64 inputs; q is [B,S,H,D] (or [T,H,D] varlen), k and v
+        have the same layout with Hkv heads (Hkv divides H; Hkv = H is plain MHA).
 
         Returns (o float64 like q, lse float64 [B,H,S] or [H,T]).
         """
@@ -111,7 +117,8 @@ class OracleLib:
         o = np.empty(o_shape, np.float64)
         lse = np.empty(l_shape, np.float64)
         rc = self.lib.oracle_attn_fwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                          B, H, S, D, float(scale), int(bool(causal)), _ptr(cu))
+                                          B, H, _kv_heads(k.shape, cu), S, D, float(scale),
+                                          int(bool(causal)), _ptr(cu))
         if rc != 0:
             raise ValueError("oracle_attn_fwd_f64 rejected its arguments")
         return o, lse
@@ -128,7 +135,8 @@ class OracleLib:
         o = np.empty(o_shape, np.float64)
         lse = np.empty(l_shape, np.float64)
         rc = self.lib.oracle_attn_fwd_bf16(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(o), _ptr(lse),
-                                           B, H, S, D, float(scale), int(bool(causal)), _ptr(cu))
+                                           B, H, _kv_heads(kb.shape, cu), S, D, float(scale),
+                                           int(bool(causal)), _ptr(cu))
         if rc != 0:
             raise ValueError("oracle_attn_fwd_bf16 rejected its arguments")
         return o, lse
@@ -146,7 +154,8 @@ class OracleLib:
         o = np.empty((len(rows), D), np.float64)
         lse = np.empty(len(rows), np.float64)
         rc = self.lib.oracle_attn_rows_bf16(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(rows),
-                                            len(rows), _ptr(o), _ptr(lse), B, H, S, D,
+                                            len(rows), _ptr(o), _ptr(lse), B, H,
+                                            _kv_heads(kb.shape, cu), S, D,
                                             float(scale), int(bool(causal)), _ptr(cu))
         if rc != 0:
             raise ValueError("oracle_attn_rows_bf16 rejected its arguments")

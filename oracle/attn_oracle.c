@@ -21,10 +21,15 @@
  * no blocking, no online rescaling, no reordering beyond that.
  *
  * Layouts (row-major, contiguous):
- *   dense : q, k, v, o are [B, S, H, D]; lse is [B, H, S]
- *   varlen: q, k, v, o are [T, H, D] with T = cu_seqlens[B]; lse is [H, T];
- *           sequence b owns tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 and
- *           attends only within itself (query and key lengths are equal).
+ *   dense : q, o are [B, S, H, D]; k, v are [B, S, Hkv, D]; lse is [B, H, S]
+ *   varlen: q, o are [T, H, D], k, v are [T, Hkv, D] with T = cu_seqlens[B];
+ *           lse is [H, T]; sequence b owns tokens cu_seqlens[b] ..
+ *           cu_seqlens[b+1]-1 and attends only within itself (query and key
+ *           lengths are equal).
+ * Grouped-query attention (the paper's section 3.3 reports LPT results for
+ * MQA): Hkv divides H and query head h reads K/V head h / (H / Hkv), i.e.
+ * each run of H/Hkv consecutive query heads shares one K/V head.  Hkv = H is
+ * plain multi-head attention, Hkv = 1 is multi-query attention.
  * Inputs come either as double or as bfloat16 bit patterns (uint16), which
  * are widened exactly to double (bf16 is the top half of an IEEE float).
  */
@@ -71,16 +76,17 @@ typedef struct {
  */
 static void attend_one_row(tensor_in q, tensor_in k, tensor_in v,
                            double *o_row, double *lse_out,
-                           seq_span sp, int i, int h, int H, int D,
+                           seq_span sp, int i, int h, int H, int Hkv, int D,
                            double scale, int causal, double *s)
 {
     const int nkeys = causal ? i + 1 : sp.len;
     const int64_t qbase = ((sp.tok0 + i) * H + h) * (int64_t)D;
+    const int hk = h / (H / Hkv);  /* the K/V head of query head h */
 
     /* pass 1: scores and their maximum */
     double m = -INFINITY;
     for (int j = 0; j < nkeys; ++j) {
-        const int64_t kbase = ((sp.tok0 + j) * H + h) * (int64_t)D;
+        const int64_t kbase = ((sp.tok0 + j) * Hkv + hk) * (int64_t)D;
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
             dot += at(q, qbase + d) * at(k, kbase + d);
@@ -98,7 +104,7 @@ static void attend_one_row(tensor_in q, tensor_in k, tensor_in v,
     for (int d = 0; d < D; ++d) {
         double acc = 0.0;
         for (int j = 0; j < nkeys; ++j)
-            acc += s[j] * at(v, ((sp.tok0 + j) * H + h) * (int64_t)D + d);
+            acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)D + d);
         o_row[d] = acc / l;
     }
     *lse_out = m + log(l);
@@ -162,10 +168,10 @@ static int max_len(int B, int S, const int *cu_seqlens)
 static int attend_rows(tensor_in q, tensor_in k, tensor_in v,
                        const int64_t *rows, int64_t n_rows,
                        double *o_rows, double *lse_rows,
-                       int B, int H, int S, int D, double scale, int causal,
+                       int B, int H, int Hkv, int S, int D, double scale, int causal,
                        const int *cu_seqlens)
 {
-    if (B <= 0 || H <= 0 || D <= 0 || (!cu_seqlens && S <= 0))
+    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || D <= 0 || (!cu_seqlens && S <= 0))
         return -1;
     const int Lmax = max_len(B, S, cu_seqlens);
     int bad = 0;
@@ -183,7 +189,7 @@ static int attend_rows(tensor_in q, tensor_in k, tensor_in v,
                 decode_row(rows[r], B, H, S, cu_seqlens, &b, &h, &i);
                 seq_span sp = span_of(b, S, cu_seqlens);
                 double lse;
-                attend_one_row(q, k, v, o_tmp, &lse, sp, i, h, H, D, scale, causal, s);
+                attend_one_row(q, k, v, o_tmp, &lse, sp, i, h, H, Hkv, D, scale, causal, s);
                 if (o_rows)
                     memcpy(o_rows + r * (int64_t)D, o_tmp, sizeof(double) * (size_t)D);
                 if (lse_rows)
@@ -201,10 +207,10 @@ static int attend_rows(tensor_in q, tensor_in k, tensor_in v,
  * NULL).  Every row of every (sequence, head) is computed.
  */
 static int attend_all(tensor_in q, tensor_in k, tensor_in v, double *o, double *lse,
-                      int B, int H, int S, int D, double scale, int causal,
+                      int B, int H, int Hkv, int S, int D, double scale, int causal,
                       const int *cu_seqlens)
 {
-    if (B <= 0 || H <= 0 || D <= 0 || (!cu_seqlens && S <= 0))
+    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || D <= 0 || (!cu_seqlens && S <= 0))
         return -1;
     const int64_t T = cu_seqlens ? cu_seqlens[B] : (int64_t)B * S;
     const int64_t n_rows = T * H;
@@ -219,7 +225,7 @@ static int attend_all(tensor_in q, tensor_in k, tensor_in v, double *o, double *
     }
     for (int64_t r = 0; r < n_rows; ++r)
         rows[r] = r;
-    int rc = attend_rows(q, k, v, rows, n_rows, o_rows, l_rows, B, H, S, D, scale,
+    int rc = attend_rows(q, k, v, rows, n_rows, o_rows, l_rows, B, H, Hkv, S, D, scale,
                          causal, cu_seqlens);
     if (rc == 0) {
         for (int64_t r = 0; r < n_rows; ++r) {
@@ -239,32 +245,33 @@ static int attend_all(tensor_in q, tensor_in k, tensor_in v, double *o, double *
     return rc;
 }
 
-/* ---- exported entry points (C ABI, loaded by ctypes from Python) ---- */
+/* ---- exported entry points (C ABI, loaded by ctypes from Python) ----
+ * Hkv is the number of K/V heads (Hkv = H for multi-head attention). */
 
 int oracle_attn_fwd_f64(const double *q, const double *k, const double *v,
-                        double *o, double *lse, int B, int H, int S, int D,
+                        double *o, double *lse, int B, int H, int Hkv, int S, int D,
                         double scale, int causal, const int *cu_seqlens)
 {
     tensor_in tq = {q, 0}, tk = {k, 0}, tv = {v, 0};
-    return attend_all(tq, tk, tv, o, lse, B, H, S, D, scale, causal, cu_seqlens);
+    return attend_all(tq, tk, tv, o, lse, B, H, Hkv, S, D, scale, causal, cu_seqlens);
 }
 
 int oracle_attn_fwd_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                         double *o, double *lse, int B, int H, int S, int D,
+                         double *o, double *lse, int B, int H, int Hkv, int S, int D,
                          double scale, int causal, const int *cu_seqlens)
 {
     tensor_in tq = {q, 1}, tk = {k, 1}, tv = {v, 1};
-    return attend_all(tq, tk, tv, o, lse, B, H, S, D, scale, causal, cu_seqlens);
+    return attend_all(tq, tk, tv, o, lse, B, H, Hkv, S, D, scale, causal, cu_seqlens);
 }
 
 int oracle_attn_rows_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                           const int64_t *rows, int64_t n_rows,
                           double *o_rows, double *lse_rows,
-                          int B, int H, int S, int D, double scale, int causal,
+                          int B, int H, int Hkv, int S, int D, double scale, int causal,
                           const int *cu_seqlens)
 {
     tensor_in tq = {q, 1}, tk = {k, 1}, tv = {v, 1};
-    return attend_rows(tq, tk, tv, rows, n_rows, o_rows, lse_rows, B, H, S, D, scale,
+    return attend_rows(tq, tk, tv, rows, n_rows, o_rows, lse_rows, B, H, Hkv, S, D, scale,
                        causal, cu_seqlens);
 }
 

@@ -22,7 +22,8 @@ DIGITS = 50
 
 
 def attention(q, k, v, scale, causal, cu_seqlens=None):
-    """q, k, v: float arrays [B,S,H,D] (dense) or [T,H,D] (varlen).
+    """q: float array [B,S,H,D] (dense) or [T,H,D] (varlen); k, v the same with
+    Hkv heads, Hkv dividing H (query head h reads K/V head h // (H // Hkv)).
 
     Returns (o, lse) as numpy float64 arrays in the oracle's layouts
     (o like q; lse [B,H,S] or [H,T]).  Inputs must be exactly representable
@@ -36,7 +37,9 @@ def attention(q, k, v, scale, causal, cu_seqlens=None):
     if cu_seqlens is None:
         B, S, H, D = q.shape
         spans = [(b * S, S) for b in range(B)]
-        qf, kf, vf = (x.reshape(B * S, H, D) for x in (q, k, v))
+        Hkv = k.shape[2]
+        qf = q.reshape(B * S, H, D)
+        kf, vf = (x.reshape(B * S, Hkv, D) for x in (k, v))
         T = B * S
     else:
         cu = [int(c) for c in cu_seqlens]
@@ -44,21 +47,24 @@ def attention(q, k, v, scale, causal, cu_seqlens=None):
         spans = [(cu[b], cu[b + 1] - cu[b]) for b in range(B)]
         qf, kf, vf = q, k, v
         T, H, D = q.shape
+        Hkv = k.shape[1]
+    group = H // Hkv
     o = np.zeros((T, H, D), np.float64)
     lse_t = np.zeros((H, T), np.float64)
     for (t0, L) in spans:
         for h in range(H):
+            hk = h // group
             for i in range(L):
                 keys = range(i + 1) if causal else range(L)
                 w = []
                 for j in keys:
-                    dot = sum(Fraction(float(qf[t0 + i, h, d])) * Fraction(float(kf[t0 + j, h, d]))
+                    dot = sum(Fraction(float(qf[t0 + i, h, d])) * Fraction(float(kf[t0 + j, hk, d]))
                               for d in range(D))
                     s = sc * dot
                     w.append(mpmath.exp(mpmath.mpf(s.numerator) / s.denominator))
                 z = mpmath.fsum(w)
                 for d in range(D):
-                    num = mpmath.fsum(wj * mpmath.mpf(float(vf[t0 + j, h, d]))
+                    num = mpmath.fsum(wj * mpmath.mpf(float(vf[t0 + j, hk, d]))
                                       for wj, j in zip(w, keys))
                     o[t0 + i, h, d] = float(num / z)
                 lse_t[h, t0 + i] = float(mpmath.log(z))

@@ -171,6 +171,42 @@ def check_scale_is_a_logit_multiplier(o):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "scale"
 
 
+def check_gqa_brute_force_tiny(o):
+    """Grouped-query attention (Hkv < H) == the 50-digit brute force, dense and varlen."""
+    rng = np.random.default_rng(21)
+    for causal in (False, True):
+        B, S, H, Hkv, D = 1, 6, 4, 2, 3
+        q = _bf16_grid(rng, (B, S, H, D))
+        k, v = (_bf16_grid(rng, (B, S, Hkv, D)) for _ in range(2))
+        got_o, got_l = o.attention_f64(q, k, v, 0.41, causal)
+        ref_o, ref_l = brute.attention(q, k, v, 0.41, causal)
+        assert np.max(np.abs(got_o - ref_o)) <= 1e-12, ("gqa brute O", causal)
+        assert np.max(np.abs(got_l - ref_l)) <= 1e-12, ("gqa brute LSE", causal)
+    cu = [0, 4, 5, 9]                 # multi-query (one K/V head), varlen, causal
+    q = _bf16_grid(rng, (9, 3, 4))
+    k, v = (_bf16_grid(rng, (9, 1, 4)) for _ in range(2))
+    got_o, got_l = o.attention_f64(q, k, v, 0.5, True, cu)
+    ref_o, ref_l = brute.attention(q, k, v, 0.5, True, cu)
+    assert np.max(np.abs(got_o - ref_o)) <= 1e-12, "mqa brute varlen O"
+    assert np.max(np.abs(got_l - ref_l)) <= 1e-12, "mqa brute varlen LSE"
+
+
+def check_gqa_equals_repeated_kv(o):
+    """Sharing a K/V head among H/Hkv consecutive query heads is the same as
+    multi-head attention on K and V with each head repeated H/Hkv times in a
+    row: the multi-head path gives the identical result, bit for bit."""
+    rng = np.random.default_rng(22)
+    B, S, H, D = 2, 7, 6, 4
+    q = rng.standard_normal((B, S, H, D))
+    for Hkv in (1, 2, 3):
+        k, v = (rng.standard_normal((B, S, Hkv, D)) for _ in range(2))
+        kr, vr = (np.repeat(x, H // Hkv, axis=2) for x in (k, v))
+        for causal in (False, True):
+            o1, l1 = o.attention_f64(q, k, v, 0.3, causal)
+            o2, l2 = o.attention_f64(q, kr, vr, 0.3, causal)
+            assert np.array_equal(o1, o2) and np.array_equal(l1, l2), ("gqa repeat", Hkv, causal)
+
+
 ALL_CHECKS = [
     check_brute_force_tiny,
     check_equal_logits_mean_of_v,
@@ -182,4 +218,6 @@ ALL_CHECKS = [
     check_causal_prefix,
     check_varlen_equals_dense_runs,
     check_scale_is_a_logit_multiplier,
+    check_gqa_brute_force_tiny,
+    check_gqa_equals_repeated_kv,
 ]

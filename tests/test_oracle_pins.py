@@ -93,6 +93,13 @@ def test_rejects_bad_shapes():
         oracle.lib().attention_f64(z[:, :0], z[:, :0], z[:, :0], 1.0, False)
 
 
+def test_rejects_kv_heads_not_dividing_q_heads():
+    q = np.zeros((1, 4, 4, 2))
+    k = v = np.zeros((1, 4, 3, 2))
+    with pytest.raises(ValueError):
+        oracle.attention_f64(q, k, v, 0.5, False)
+
+
 def test_golden_tiny_bruteforce():
     """Stored 50-digit values (tests/golden/tiny_bruteforce.json)."""
     import json

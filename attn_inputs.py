@@ -6,8 +6,9 @@ the two sides always see the same bf16 bits.
 
 Recipe: a CPU ``torch.Generator`` seeded with the workload's seed draws
 standard normals in float32 in the order Q, K, V (shape [B,S,H,D], or
-[T,H,D] for packed variable-length batches); each tensor is multiplied by
-its standard deviation and rounded to bfloat16 with round-to-nearest-even.
+[T,H,D] for packed variable-length batches; K and V have H_kv heads for
+grouped-query workloads); each tensor is multiplied by its standard
+deviation and rounded to bfloat16 with round-to-nearest-even.
 Variable-length batches draw their lengths first from
 ``numpy.random.default_rng(seed).integers(lo, hi, n, endpoint=True)``.
 """
@@ -35,6 +36,11 @@ class Workload:
     kv_std: float = 1.0
     varlen: Optional[tuple] = None   # (n_seqs, lo, hi) drawn uniformly, inclusive
     lengths: tuple = field(default=())
+    Hkv: int = 0                     # K/V heads for grouped-query attention (0: same as H)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def scale(self) -> float:
@@ -51,12 +57,16 @@ def cu_seqlens_of(lengths) -> np.ndarray:
     return np.concatenate([[0], np.cumsum(np.asarray(lengths, np.int64))]).astype(np.int32)
 
 
-def draw_qkv(shape, seed: int, q_std: float = 1.0, kv_std: float = 1.0):
-    """Q, K, V as CPU bf16 tensors of the given shape (drawn in that order)."""
+def draw_qkv(shape, seed: int, q_std: float = 1.0, kv_std: float = 1.0, kv_heads=None):
+    """Q, K, V as CPU bf16 tensors (drawn in that order).  Q has the given
+    shape; K and V too, or kv_heads heads on the head axis (second to last)."""
     g = torch.Generator(device="cpu").manual_seed(int(seed))
+    kv_shape = list(shape)
+    if kv_heads is not None:
+        kv_shape[-2] = int(kv_heads)
     out = []
-    for std in (q_std, kv_std, kv_std):
-        x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    for std, shp in ((q_std, shape), (kv_std, kv_shape), (kv_std, kv_shape)):
+        x = torch.randn(*shp, generator=g, dtype=torch.float32)
         if std != 1.0:
             x = x * std
         out.append(x.to(torch.bfloat16))
@@ -69,13 +79,13 @@ def make(w: Workload):
         n, lo, hi = w.varlen
         lens = varlen_lengths(n, lo, hi, w.seed)
         cu = cu_seqlens_of(lens)
-        q, k, v = draw_qkv((int(cu[-1]), w.H, w.D), w.seed, w.q_std, w.kv_std)
+        q, k, v = draw_qkv((int(cu[-1]), w.H, w.D), w.seed, w.q_std, w.kv_std, w.kv_heads)
         return q, k, v, cu, int(lens.max())
     if w.lengths:
         cu = cu_seqlens_of(w.lengths)
-        q, k, v = draw_qkv((int(cu[-1]), w.H, w.D), w.seed, w.q_std, w.kv_std)
+        q, k, v = draw_qkv((int(cu[-1]), w.H, w.D), w.seed, w.q_std, w.kv_std, w.kv_heads)
         return q, k, v, cu, int(max(w.lengths))
-    q, k, v = draw_qkv((w.B, w.S, w.H, w.D), w.seed, w.q_std, w.kv_std)
+    q, k, v = draw_qkv((w.B, w.S, w.H, w.D), w.seed, w.q_std, w.kv_std, w.kv_heads)
     return q, k, v, None, w.S
 
 
@@ -92,8 +102,9 @@ def flops(w: Workload, cu=None) -> float:
 # The workloads: a tiny non-causal case the oracle finishes instantly; dense
 # 2k heads (both masks); 32k causal long context; a packed variable-length
 # causal batch; wide heads with high-spread logits; 8k causal (the other
-# sequence length the throughput metric names); and the install-check shape
-# (1, 8, 512, 64) causal from the FlashAttention-4 usage guide.
+# sequence length the throughput metric names); the install-check shape
+# (1, 8, 512, 64) causal from the FlashAttention-4 usage guide; and
+# grouped-query attention at 8k causal (32 query heads sharing 8 K/V heads).
 WORKLOADS = {
     "tiny_b1h2s128d64": Workload("tiny_b1h2s128d64", 1, 128, 2, 64, False, seed=1),
     "dense_b2h16s2048d128": Workload("dense_b2h16s2048d128", 2, 2048, 16, 128, False, seed=2),
@@ -108,4 +119,6 @@ WORKLOADS = {
                                             False, seed=5, q_std=3.0),
     "causal_b2h16s8192d128": Workload("causal_b2h16s8192d128", 2, 8192, 16, 128, True, seed=6),
     "smoke_b1h8s512d64_causal": Workload("smoke_b1h8s512d64_causal", 1, 512, 8, 64, True, seed=7),
+    "gqa_b2h32kv8s8192d128_causal": Workload("gqa_b2h32kv8s8192d128_causal", 2, 8192, 32, 128,
+                                             True, seed=8, Hkv=8),
 }

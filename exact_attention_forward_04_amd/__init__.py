@@ -56,6 +56,8 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd.restype = I
     lib.fa_fwd_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, ctypes.POINTER(Tuning)]
     lib.fa_fwd_ex.restype = I
+    lib.fa_fwd_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, P, ctypes.POINTER(Tuning)]
+    lib.fa_fwd_gqa.restype = I
     lib.fa_tuning_default.argtypes = []
     lib.fa_tuning_default.restype = Tuning
     lib.fa_exp2_emu.argtypes = [P, P, LL, P]
@@ -98,16 +100,23 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
 
     q, k, v: contiguous bf16 CUDA tensors, [B,S,H,D] (dense) or [T,H,D]
     (varlen, with cu_seqlens an int32 CUDA tensor of B+1 offsets and
-    max_seqlen the longest sequence).  Returns (o, lse): o like q (bf16),
-    lse fp32 [B,H,S] or [H,T] (None if return_lse is False).
+    max_seqlen the longest sequence).  k and v may have fewer heads H_kv than
+    q (grouped-query attention; H_kv divides H and query head h reads K/V
+    head h // (H // H_kv)).  Returns (o, lse): o like q (bf16), lse fp32
+    [B,H,S] or [H,T] (None if return_lse is False).
     """
     import torch
     lib = load()
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("%s must be a contiguous bf16 CUDA tensor" % name)
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must have the same shape")
+    head_axis = 2 if cu_seqlens is None else 1
+    if k.shape != v.shape or k.dim() != q.dim() or any(
+            k.shape[i] != q.shape[i] for i in range(q.dim()) if i != head_axis):
+        raise ValueError("k and v must have q's shape apart from the number of heads")
+    H_kv = k.shape[head_axis]
+    if H_kv < 1 or q.shape[head_axis] % H_kv != 0:
+        raise ValueError("the K/V head count must divide the query head count")
     if cu_seqlens is None:
         if q.dim() != 4:
             raise ValueError("dense inputs are [B, S, H, D]")
@@ -137,7 +146,11 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
             lse.data_ptr() if lse is not None else None, B, H, S, D, float(scale),
             int(bool(causal)), cu_ptr, sp)
-    if tuning is None:
+    if H_kv != H:
+        gargs = args[:7] + (H_kv,) + args[7:]
+        rc = lib.fa_fwd_gqa(*gargs, ctypes.byref(tuning) if tuning is not None else None)
+        _check("fa_fwd_gqa", rc)
+    elif tuning is None:
         rc = lib.fa_fwd(*args)
         _check("fa_fwd", rc)
     else:

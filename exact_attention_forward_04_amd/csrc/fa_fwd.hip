@@ -158,6 +158,7 @@ struct Args {
   float *lse;
   const int *cu;            // varlen offsets or nullptr
   int B, H, S;
+  int Hkv;                  // K/V heads (divides H); query head h reads K/V head h / (H / Hkv)
   float c;                  // scale * log2(e)
   float tau;
   unsigned long long *counters;
@@ -482,6 +483,8 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   const int m0 = mb * C::BM;
   if (m0 >= L) return;  // workgroup-uniform
   const int H = a.H;
+  const int Hk = a.Hkv;              // K/V row layout: [.., Hk, D]
+  const int hk = h / (H / Hk);       // the K/V head this query head reads
   WaveRows wr;
   wr.wrow0 = m0 + wave * 32;
   wr.active = wr.wrow0 < L;
@@ -515,7 +518,7 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   st.l32 = 0.0f;
 
   BlockLoader<D> ld;
-  ld.init(H, wave, lane);
+  ld.init(Hk, wave, lane);
   LdsAddr<D> la;
   la.init(lane);
 
@@ -540,8 +543,8 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     auto copies = [&](int it) {
       return [&, it](int part) {
         if (it + 2 < nblocks) {
-          if (part == 0) ld.issue(a.k, tok0, H, h, (it + 2) * kBN, L, kbuf(it + 2));
-          else ld.issue(a.v, tok0, H, h, (it + 2) * kBN, L, vbuf(it + 2));
+          if (part == 0) ld.issue(a.k, tok0, Hk, hk, (it + 2) * kBN, L, kbuf(it + 2));
+          else ld.issue(a.v, tok0, Hk, hk, (it + 2) * kBN, L, vbuf(it + 2));
         }
       };
     };
@@ -555,11 +558,11 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
         side(1);
       }
     };
-    ld.issue(a.k, tok0, H, h, 0, L, kbuf(0));
-    ld.issue(a.v, tok0, H, h, 0, L, vbuf(0));
+    ld.issue(a.k, tok0, Hk, hk, 0, L, kbuf(0));
+    ld.issue(a.v, tok0, Hk, hk, 0, L, vbuf(0));
     if (nblocks > 1) {
-      ld.issue(a.k, tok0, H, h, kBN, L, kbuf(1));
-      ld.issue(a.v, tok0, H, h, kBN, L, vbuf(1));
+      ld.issue(a.k, tok0, Hk, hk, kBN, L, kbuf(1));
+      ld.issue(a.v, tok0, Hk, hk, kBN, L, vbuf(1));
     }
     // The two halves run separate loops that meet at the same barriers.
     if (half == 0) {
@@ -590,8 +593,8 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     char LDS_AS *vb0 = lds + C::BLOCK_BYTES;
     char LDS_AS *kb1 = lds + 2 * C::BLOCK_BYTES;
     char LDS_AS *vb1 = lds + 3 * C::BLOCK_BYTES;
-    ld.issue(a.k, tok0, H, h, 0, L, kb0);
-    ld.issue(a.v, tok0, H, h, 0, L, vb0);
+    ld.issue(a.k, tok0, Hk, hk, 0, L, kb0);
+    ld.issue(a.v, tok0, Hk, hk, 0, L, vb0);
     for (int j = 0; j < nblocks; ++j) {
       const int n0 = j * kBN;
       char LDS_AS *kcur = (j & 1) ? kb1 : kb0;
@@ -599,8 +602,8 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       if (j + 1 < nblocks) {
         char LDS_AS *knext = (j & 1) ? kb0 : kb1;
         char LDS_AS *vnext = (j & 1) ? vb0 : vb1;
-        ld.issue(a.k, tok0, H, h, n0 + kBN, L, knext);
-        ld.issue(a.v, tok0, H, h, n0 + kBN, L, vnext);
+        ld.issue(a.k, tok0, Hk, hk, n0 + kBN, L, knext);
+        ld.issue(a.v, tok0, Hk, hk, n0 + kBN, L, vnext);
         wait_vmcnt<2 * C::LOADS>();
       } else {
         wait_vmcnt<0>();
@@ -726,11 +729,12 @@ int current_device(DeviceInfo **out) {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 int validate(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-             int S, int D, float scale, int causal, const fa_tuning *t) {
+             int Hkv, int S, int D, float scale, int causal, const fa_tuning *t) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID_ARG;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return FA_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA_ERR_INVALID_ARG;
+  if (Hkv <= 0 || H % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (t) {
@@ -826,11 +830,11 @@ fa_tuning fa_tuning_default(void) {
   return t;
 }
 
-int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-              int S, int D, float scale, int causal, const int *cu_seqlens, void *stream,
-              const fa_tuning *tuning) {
+int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+               int H_kv, int S, int D, float scale, int causal, const int *cu_seqlens,
+               void *stream, const fa_tuning *tuning) {
   const fa_tuning t = tuning ? *tuning : fa_tuning_default();
-  int rc = validate(q, k, v, o, lse, B, H, S, D, scale, causal, &t);
+  int rc = validate(q, k, v, o, lse, B, H, H_kv, S, D, scale, causal, &t);
   if (rc != FA_OK) return rc;
   DeviceInfo *dev = nullptr;
   rc = current_device(&dev);
@@ -844,6 +848,7 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, 
   a.cu = cu_seqlens;
   a.B = B;
   a.H = H;
+  a.Hkv = H_kv;
   a.S = S;
   a.c = scale * kLog2e;
   a.tau = t.tau;
@@ -858,9 +863,15 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, 
   }
 }
 
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+              int S, int D, float scale, int causal, const int *cu_seqlens, void *stream,
+              const fa_tuning *tuning) {
+  return fa_fwd_gqa(q, k, v, o, lse, B, H, H, S, D, scale, causal, cu_seqlens, stream, tuning);
+}
+
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int S,
            int D, float scale, int causal, const int *cu_seqlens, void *stream) {
-  return fa_fwd_ex(q, k, v, o, lse, B, H, S, D, scale, causal, cu_seqlens, stream, nullptr);
+  return fa_fwd_gqa(q, k, v, o, lse, B, H, H, S, D, scale, causal, cu_seqlens, stream, nullptr);
 }
 
 int fa_exp2_emu(const float *x, float *y, long long n, void *stream) {
@@ -939,6 +950,6 @@ const char *fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 101; }
 
 }  // extern "C"

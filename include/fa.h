@@ -118,6 +118,23 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               const int *cu_seqlens, void *stream, const fa_tuning *tuning);
 
 /*
+ * fa_fwd_gqa -- grouped-query attention forward (the FlashAttention-4 paper,
+ * section 3.3, reports its LPT scheduling results for MQA as well as MHA).
+ *
+ * Same operation, layouts, arguments and errors as fa_fwd_ex, except that k
+ * and v carry H_kv heads:
+ *   dense  k, v bf16 [B, S, H_kv, D];   varlen  k, v bf16 [T, H_kv, D]
+ * while q, o and lse keep H heads.  H_kv >= 1 must divide H
+ * (FA_ERR_INVALID_ARG otherwise); query head h reads K/V head
+ * h / (H / H_kv), so each run of H/H_kv consecutive query heads shares one
+ * K/V head.  H_kv = H is fa_fwd_ex itself, H_kv = 1 is multi-query attention.
+ * tuning may be NULL (fa_tuning_default()).
+ */
+int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
+               int B, int H, int H_kv, int S, int D, float scale, int causal,
+               const int *cu_seqlens, void *stream, const fa_tuning *tuning);
+
+/*
  * fa_exp2_emu -- test hook: y[i] = the device's polynomial 2^x[i] for n
  * floats (device pointers, 4-byte aligned).  The function is the one the
  * attention kernel uses for its emulated exponentials: Cody-Waite
@@ -150,7 +167,7 @@ int fa_num_workers(int D, int *workers_out);
 /* Human-readable name of an fa_status value (static string, never NULL). */
 const char *fa_status_string(int status);
 
-/* Library ABI version: 100 * major + minor. */
+/* Library ABI version: 100 * major + minor (101: fa_fwd_gqa added). */
 int fa_version(void);
 
 #ifdef __cplusplus

@@ -81,12 +81,26 @@ def test_tuning_validation():
         assert rc == fa.FA_ERR_INVALID_ARG, (field, val)
 
 
+@pytest.mark.parametrize("H,H_kv,expect", [
+    (4, 3, fa.FA_ERR_INVALID_ARG),   # K/V heads must divide the query heads
+    (4, 0, fa.FA_ERR_INVALID_ARG),
+    (4, -2, fa.FA_ERR_INVALID_ARG),
+    (2, 4, fa.FA_ERR_INVALID_ARG),   # more K/V heads than query heads
+])
+def test_gqa_head_validation(H, H_kv, expect):
+    lib = fa.load()
+    rc = lib.fa_fwd_gqa(A, A, A, A, A, 1, H, H_kv, 8, 128, 0.1, 1, None, None, None)
+    assert rc == expect
+
+
 def test_valid_call_without_gpu_reports_no_device():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert call() == fa.FA_ERR_NO_DEVICE
     assert fa.load().fa_exp2_emu(A, A, 16, None) == fa.FA_ERR_NO_DEVICE
+    assert fa.load().fa_fwd_gqa(A, A, A, A, A, 1, 8, 2, 8, 128, 0.1, 1, None, None,
+                                None) == fa.FA_ERR_NO_DEVICE
 
 
 def test_exp2_emu_argument_checks():

@@ -131,6 +131,7 @@ def gather_rows(o, lse, rows, w, cu):
     ("long_b1h16s32768d128_causal", 384),
     ("varlen_16x512to8192_h32d128_causal", 512),
     ("wide_b2h16s8192d256_spread3", 512),
+    ("gqa_b2h32kv8s8192d128_causal", 512),
 ])
 def test_named_sampled(name, n):
     w = WORKLOADS[name]
@@ -161,7 +162,8 @@ def _cell_distance_t(o_bf16, ref):
 
 
 @pytest.mark.parametrize("name", ["wide_b2h16s8192d256_spread3", "causal_b2h16s8192d128",
-                                  "dense_b2h16s2048d128", "dense_b2h16s2048d128_causal"])
+                                  "dense_b2h16s2048d128", "dense_b2h16s2048d128_causal",
+                                  "gqa_b2h32kv8s8192d128_causal"])
 def test_all_outputs_vs_fp32_reference(name):
     w = WORKLOADS[name]
     q, k, v, cu, S = make(w)
@@ -169,11 +171,12 @@ def test_all_outputs_vs_fp32_reference(name):
     o, lse = run_gpu(q, k, v, w.causal, w.scale)
     dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
     worst, total, count, lse_worst = 0.0, 0.0, 0, 0.0
+    group = w.H // w.kv_heads
     for b in range(w.B):
         for h in range(w.H):
-            K = dk[b, :, h].float().contiguous()
+            K = dk[b, :, h // group].float().contiguous()
             Kt = K.t().contiguous()
-            V = dv[b, :, h].float().contiguous()
+            V = dv[b, :, h // group].float().contiguous()
             for r0 in range(0, w.S, 4096):
                 r1 = min(w.S, r0 + 4096)
                 s = (dq[b, r0:r1, h].float() @ Kt) * w.scale
@@ -192,6 +195,52 @@ def test_all_outputs_vs_fp32_reference(name):
                 lse_worst = max(lse_worst, (lse[b, h, r0:r1] - lse_ref).abs().max().item())
     note(name, "max cell distance %.3e, mean |dO| %.3e, max |dLSE| %.3e" % (worst, total / count, lse_worst))
     assert worst <= 1e-2 and total / count <= 1e-3 and lse_worst <= 1e-3
+
+
+# ---- grouped-query attention (K/V heads shared by consecutive query heads)
+
+GQA_SMALL = [
+    # (B, S, H, H_kv, D)
+    (2, 700, 8, 2, 128),
+    (1, 513, 4, 1, 64),      # multi-query
+    (1, 300, 4, 2, 256),
+    (2, 257, 6, 3, 128),
+]
+
+
+@pytest.mark.parametrize("shape", GQA_SMALL, ids=lambda s: "B%dS%dH%dKV%dD%d" % s)
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_small_full(shape, causal):
+    B, S, H, Hkv, D = shape
+    q, k, v = draw_qkv((B, S, H, D), seed=200 + S + H, kv_heads=Hkv)
+    full_check(q, k, v, causal, 1.0 / math.sqrt(D), what="gqa-small")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_varlen_small_full(causal):
+    lens = [1, 0, 300, 64, 65, 777, 2]
+    cu = cu_seqlens_of(lens)
+    q, k, v = draw_qkv((int(cu[-1]), 4, 128), seed=211, kv_heads=2)
+    full_check(q, k, v, causal, 1.0 / math.sqrt(128), cu=cu, S=max(lens), what="gqa-varlen")
+
+
+def test_gqa_equals_mha_on_repeated_kv():
+    """Reading a shared K/V head is the same work as multi-head attention on
+    K/V with each head repeated: the two launches agree bit for bit."""
+    q, k, v = draw_qkv((2, 1500, 8, 128), seed=221, kv_heads=2)
+    kr, vr = (x.repeat_interleave(4, dim=2).contiguous() for x in (k, v))
+    for causal in (False, True):
+        note("gqa vs repeated kv, causal", causal)
+        o1, l1 = run_gpu(q, k, v, causal, 0.088)
+        o2, l2 = run_gpu(q, kr, vr, causal, 0.088)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    lens = [900, 33, 2048, 1, 511]
+    cu = cu_seqlens_of(lens)
+    q, k, v = draw_qkv((int(cu[-1]), 6, 64), seed=222, kv_heads=1)
+    kr, vr = (x.repeat_interleave(6, dim=1).contiguous() for x in (k, v))
+    o1, l1 = run_gpu(q, k, v, True, 0.1, cu, max(lens))
+    o2, l2 = run_gpu(q, kr, vr, True, 0.1, cu, max(lens))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 # ---- invariances

@@ -64,6 +64,9 @@ def load(path: str = LIB_PATH):
     lib.fa_exp2_emu.restype = I
     lib.fa_schedule.argtypes = [I, I, I, I, I, P, I, P, I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.fa_schedule.restype = I
+    lib.fa_schedule_gqa.argtypes = [I, I, I, I, I, I, P, I, P, I, ctypes.POINTER(I),
+                                    ctypes.POINTER(I)]
+    lib.fa_schedule_gqa.restype = I
     lib.fa_num_workers.argtypes = [I, ctypes.POINTER(I)]
     lib.fa_num_workers.restype = I
     lib.fa_status_string.argtypes = [I]
@@ -171,11 +174,12 @@ def exp2_emu(x, stream=None):
 
 
 def schedule(B: int, H: int, S: int, D: int, causal: bool, workers: int,
-             cu_seqlens=None, max_rounds: int = 4096):
+             cu_seqlens=None, max_rounds: int = 4096, H_kv: Optional[int] = None):
     """Host-side persistent tile order: (tiles [workers, rounds] int32, BM).
 
     Tile code = (seq * H + head) * ceil(S / BM) + mblock, -1 = idle.
-    cu_seqlens (optional) is a host sequence of B+1 offsets.
+    cu_seqlens (optional) is a host sequence of B+1 offsets; H_kv (optional)
+    the number of K/V heads for grouped-query attention.
     """
     import numpy as np
     lib = load()
@@ -184,10 +188,16 @@ def schedule(B: int, H: int, S: int, D: int, causal: bool, workers: int,
     if cu_seqlens is not None:
         cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
     rounds, bm = ctypes.c_int(0), ctypes.c_int(0)
-    rc = lib.fa_schedule(B, H, S, D, int(bool(causal)), None if cu is None else cu.ctypes.data,
-                         workers, tiles.ctypes.data, max_rounds, ctypes.byref(rounds),
-                         ctypes.byref(bm))
-    _check("fa_schedule", rc)
+    cu_ptr = None if cu is None else cu.ctypes.data
+    if H_kv is None:
+        rc = lib.fa_schedule(B, H, S, D, int(bool(causal)), cu_ptr, workers, tiles.ctypes.data,
+                             max_rounds, ctypes.byref(rounds), ctypes.byref(bm))
+        _check("fa_schedule", rc)
+    else:
+        rc = lib.fa_schedule_gqa(B, H, H_kv, S, D, int(bool(causal)), cu_ptr, workers,
+                                 tiles.ctypes.data, max_rounds, ctypes.byref(rounds),
+                                 ctypes.byref(bm))
+        _check("fa_schedule_gqa", rc)
     return tiles[:, :rounds.value].copy(), bm.value
 
 

@@ -652,7 +652,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fw
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   char LDS_AS *lds = (char LDS_AS *)lds_raw;
   using C = Cfg<D>;
-  fa::Sched s = fa::make_sched(a.B, a.H, a.S, C::BM, CAUSAL, VARLEN, a.workers);
+  fa::Sched s = fa::make_sched(a.B, a.H, a.Hkv, a.S, C::BM, CAUSAL, VARLEN, a.workers);
   fa::SchedTables t{nullptr, nullptr, nullptr};
   if constexpr (VARLEN) {
     int *tab = (int *)(lds_raw + lds_bytes<D>());
@@ -890,12 +890,19 @@ int fa_exp2_emu(const float *x, float *y, long long n, void *stream) {
 
 int fa_schedule(int B, int H, int S, int D, int causal, const int *cu_seqlens, int workers,
                 int *tiles, int max_rounds, int *rounds_out, int *bm_out) {
+  return fa_schedule_gqa(B, H, H, S, D, causal, cu_seqlens, workers, tiles, max_rounds,
+                         rounds_out, bm_out);
+}
+
+int fa_schedule_gqa(int B, int H, int H_kv, int S, int D, int causal, const int *cu_seqlens,
+                    int workers, int *tiles, int max_rounds, int *rounds_out, int *bm_out) {
   if (B <= 0 || H <= 0 || S <= 0 || workers <= 0 || !tiles || max_rounds <= 0) return FA_ERR_INVALID_ARG;
+  if (H_kv <= 0 || H % H_kv != 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
   const int BM = bm_for(D);
   const bool varlen = cu_seqlens != nullptr;
-  fa::Sched s = fa::make_sched(B, H, S, BM, causal, varlen, workers);
+  fa::Sched s = fa::make_sched(B, H, H_kv, S, BM, causal, varlen, workers);
   if (varlen && (B > fa::kMaxVarlenSeqs || s.nmb_max > fa::kMaxVarlenLevels)) return FA_ERR_UNSUPPORTED;
   static thread_local int len[fa::kMaxVarlenSeqs], sorted[fa::kMaxVarlenSeqs],
       off[fa::kMaxVarlenLevels + fa::kMaxVarlenSeqs + 1];

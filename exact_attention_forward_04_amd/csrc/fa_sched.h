@@ -13,6 +13,11 @@
 //   - heads are split across the 8 XCDs (each with its own L2) when H is a
 //     multiple of 8: XCD x owns heads x, x+8, ...; workgroup w runs on XCD
 //     w % 8 because the dispatcher deals workgroups to XCDs round-robin.
+//     With grouped-query attention (G = H / Hkv query heads per K/V head)
+//     and Hkv a multiple of 8, XCD x owns the K/V heads x, x+8, ... and all
+//     G query heads of each, visited one K/V head at a time (the survey of
+//     the paper's section 3.3: walk every query head of one K/V head before
+//     moving on), so a K/V head is read into one L2 only.
 // Within an XCD, workers take positions in "snake" order: round r gives
 // worker w position r*W + w on even rounds and r*W + W-1-w on odd rounds.
 //
@@ -45,6 +50,8 @@ struct SchedTables {
 
 struct Sched {
   int B, H, S, BM;
+  int G;           // query heads per K/V head (1: multi-head attention)
+  int kv_grouped;  // XCD groups follow K/V heads (Hkv a multiple of the group count)
   int causal, varlen;
   int nmb_max;     // ceil(S / BM)
   int groups;      // kXcds or 1
@@ -54,11 +61,14 @@ struct Sched {
 
 FA_HD inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-FA_HD inline Sched make_sched(int B, int H, int S, int BM, int causal, int varlen, int workers) {
+FA_HD inline Sched make_sched(int B, int H, int Hkv, int S, int BM, int causal, int varlen,
+                              int workers) {
   Sched s;
   s.B = B; s.H = H; s.S = S; s.BM = BM; s.causal = causal; s.varlen = varlen;
+  s.G = H / Hkv;
   s.nmb_max = ceil_div(S, BM);
   s.groups = (H % kXcds == 0 && workers % kXcds == 0) ? kXcds : 1;
+  s.kv_grouped = (Hkv % s.groups == 0);
   s.hpg = H / s.groups;
   s.n_items = B * s.nmb_max;  // dense; varlen fills it from the tables
   return s;
@@ -151,7 +161,13 @@ FA_HD inline Tile decode_position(const Sched &s, const SchedTables &t, int x, i
   const int it = p / s.hpg;
   const int hi = p - it * s.hpg;
   decode_item(s, t, it, &tl.b, &tl.mb);
-  tl.h = x + s.groups * hi;
+  if (s.kv_grouped) {
+    // hi -> (K/V head x + groups*kvl, query head g of it); g innermost
+    const int kvl = hi / s.G;
+    tl.h = (x + s.groups * kvl) * s.G + (hi - kvl * s.G);
+  } else {
+    tl.h = x + s.groups * hi;
+  }
   return tl;
 }
 

@@ -161,6 +161,17 @@ int fa_exp2_emu(const float *x, float *y, long long n, void *stream);
 int fa_schedule(int B, int H, int S, int D, int causal, const int *cu_seqlens,
                 int workers, int *tiles, int max_rounds, int *rounds_out, int *bm_out);
 
+/*
+ * fa_schedule_gqa -- fa_schedule for grouped-query attention with H_kv K/V
+ * heads (H_kv divides H; FA_ERR_INVALID_ARG otherwise).  Tiles are still
+ * (sequence, query head, m-block).  When H_kv is a multiple of 8, the heads
+ * are split across the 8 XCDs by K/V head, so all query heads sharing a K/V
+ * head run on one XCD, one K/V head at a time.  fa_schedule is the
+ * H_kv = H case.
+ */
+int fa_schedule_gqa(int B, int H, int H_kv, int S, int D, int causal, const int *cu_seqlens,
+                    int workers, int *tiles, int max_rounds, int *rounds_out, int *bm_out);
+
 /* Number of persistent workgroups fa_fwd launches on the current device. */
 int fa_num_workers(int D, int *workers_out);
 

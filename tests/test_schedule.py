@@ -107,6 +107,57 @@ def test_xcd_grouping_keeps_heads_on_one_xcd():
             assert h % 8 == w % 8
 
 
+GQA_CASES = [
+    # (B, H, H_kv, S, D, causal, lens or None, workers)
+    (2, 32, 8, 8192, 128, True, None, 256),      # K/V heads a multiple of 8: grouped by K/V head
+    (2, 32, 16, 4096, 128, False, None, 256),
+    (1, 32, 4, 8192, 128, True, None, 256),      # fewer K/V heads than XCDs
+    (1, 16, 1, 4096, 64, True, None, 256),       # multi-query
+    (5, 24, 8, 3000, 128, True, [1, 0, 3000, 257, 999], 256),
+    (3, 12, 3, 1000, 128, True, None, 13),
+]
+
+
+@pytest.mark.parametrize("case", GQA_CASES)
+def test_gqa_every_tile_exactly_once_and_lpt(case):
+    B, H, H_kv, S, D, causal, lens, workers = case
+    cu = None if lens is None else cu_seqlens_of(lens)
+    L = [S] * B if lens is None else list(lens)
+    tiles, bm = fa.schedule(B, H, S, D, causal, workers, cu_seqlens=cu, H_kv=H_kv)
+    seen = tiles[tiles >= 0].tolist()
+    assert len(seen) == len(set(seen)), "a tile is processed twice"
+    assert set(seen) == all_tiles(B, H, S, bm, L), "a tile is missing or foreign"
+    if causal:
+        for row in tiles:
+            c = [tile_cost(t, H, S, bm, causal, L) for t in row if t >= 0]
+            assert all(c[i] >= c[i + 1] for i in range(len(c) - 1)), c
+
+
+def test_gqa_query_heads_of_a_kv_head_share_an_xcd():
+    # H_kv % 8 == 0: worker w (XCD w % 8) only sees query heads whose K/V head
+    # is congruent to w mod 8, and consecutive positions walk the query heads
+    # of one K/V head before moving to the next
+    B, H, H_kv, S = 2, 32, 8, 8192
+    G = H // H_kv
+    tiles, bm = fa.schedule(B, H, S, 128, True, 256, H_kv=H_kv)
+    nmb = math.ceil(S / bm)
+    for w, row in enumerate(tiles):
+        for t in row[row >= 0]:
+            h = (t // nmb) % H
+            assert (h // G) % 8 == w % 8
+    # round 0 of the workers of XCD 0 (workers 0, 8, 16, ...): G consecutive
+    # workers hold the G query heads of one K/V head
+    first = [tiles[w, 0] for w in range(0, 256, 8)]
+    heads = [(t // nmb) % H for t in first]
+    for i in range(0, len(heads) - G + 1, G):
+        assert len({h // G for h in heads[i:i + G]}) == 1, heads
+
+
+def test_gqa_schedule_rejects_bad_kv_heads():
+    with pytest.raises(fa.FaError):
+        fa.schedule(1, 12, 1024, 128, True, 256, H_kv=5)
+
+
 def test_schedule_rejects_small_round_budget():
     with pytest.raises(fa.FaError):
         fa.schedule(1, 16, 32768, 128, True, 256, max_rounds=2)

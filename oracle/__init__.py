@@ -73,11 +73,12 @@ def _kv_heads(k_shape, cu):
     return k_shape[2] if cu is None else k_shape[1]
 
 
-def _shapes(B, S, H, D, cu):
+def _shapes(B, S, H, Dv, cu):
+    """Shapes of o (head dimension Dv, the v dimension) and lse."""
     if cu is None:
-        return (B, S, H, D), (B, H, S)
+        return (B, S, H, Dv), (B, H, S)
     T = int(cu[-1])
-    return (T, H, D), (H, T)
+    return (T, H, Dv), (H, T)
 
 
 class OracleLib:
@@ -87,10 +88,12 @@ class OracleLib:
         lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
-        lib.oracle_attn_fwd_f64.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, f64, i32, P]
-        lib.oracle_attn_fwd_bf16.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, f64, i32, P]
+        lib.oracle_attn_fwd_f64.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, f64,
+                                            i32, P]
+        lib.oracle_attn_fwd_bf16.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, f64,
+                                             i32, P]
         lib.oracle_attn_rows_bf16.argtypes = [P, P, P, P, i64, P, P, i32, i32, i32, i32, i32,
-                                              f64, i32, P]
+                                              i32, f64, i32, P]
         for fn in (lib.oracle_attn_fwd_f64, lib.oracle_attn_fwd_bf16, lib.oracle_attn_rows_bf16):
             fn.restype = i32
         lib.oracle_exp2.argtypes = [P, P, i64]
@@ -104,20 +107,22 @@ class OracleLib:
 
     def attention_f64(self, q, k, v, scale, causal, cu_seqlens=None):
         """Attention on float64 inputs; q is [B,S,H,D] (or [T,H,D] varlen), k and v
-        have the same layout with Hkv heads (Hkv divides H; Hkv = H is plain MHA).
+        have the same layout with Hkv heads (Hkv divides H; Hkv = H is plain MHA);
+        v may have its own head dimension Dv.
 
-        Returns (o float64 like q, lse float64 [B,H,S] or [H,T]).
+        Returns (o float64 [..., Dv] like q, lse float64 [B,H,S] or [H,T]).
         """
         q = np.ascontiguousarray(q, dtype=np.float64)
         k = np.ascontiguousarray(k, dtype=np.float64)
         v = np.ascontiguousarray(v, dtype=np.float64)
         cu = _cu(cu_seqlens)
         B, S, H, D = _dims(q.shape, cu)
-        o_shape, l_shape = _shapes(B, S, H, D, cu)
+        Dv = v.shape[-1]
+        o_shape, l_shape = _shapes(B, S, H, Dv, cu)
         o = np.empty(o_shape, np.float64)
         lse = np.empty(l_shape, np.float64)
         rc = self.lib.oracle_attn_fwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                          B, H, _kv_heads(k.shape, cu), S, D, float(scale),
+                                          B, H, _kv_heads(k.shape, cu), S, D, Dv, float(scale),
                                           int(bool(causal)), _ptr(cu))
         if rc != 0:
             raise ValueError("oracle_attn_fwd_f64 rejected its arguments")
@@ -131,11 +136,12 @@ class OracleLib:
         qb, kb, vb = _as_bits(q), _as_bits(k), _as_bits(v)
         cu = _cu(cu_seqlens)
         B, S, H, D = _dims(qb.shape, cu)
-        o_shape, l_shape = _shapes(B, S, H, D, cu)
+        Dv = vb.shape[-1]
+        o_shape, l_shape = _shapes(B, S, H, Dv, cu)
         o = np.empty(o_shape, np.float64)
         lse = np.empty(l_shape, np.float64)
         rc = self.lib.oracle_attn_fwd_bf16(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(o), _ptr(lse),
-                                           B, H, _kv_heads(kb.shape, cu), S, D, float(scale),
+                                           B, H, _kv_heads(kb.shape, cu), S, D, Dv, float(scale),
                                            int(bool(causal)), _ptr(cu))
         if rc != 0:
             raise ValueError("oracle_attn_fwd_bf16 rejected its arguments")
@@ -150,12 +156,13 @@ class OracleLib:
         qb, kb, vb = _as_bits(q), _as_bits(k), _as_bits(v)
         cu = _cu(cu_seqlens)
         B, S, H, D = _dims(qb.shape, cu)
+        Dv = vb.shape[-1]
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
-        o = np.empty((len(rows), D), np.float64)
+        o = np.empty((len(rows), Dv), np.float64)
         lse = np.empty(len(rows), np.float64)
         rc = self.lib.oracle_attn_rows_bf16(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(rows),
                                             len(rows), _ptr(o), _ptr(lse), B, H,
-                                            _kv_heads(kb.shape, cu), S, D,
+                                            _kv_heads(kb.shape, cu), S, D, Dv,
                                             float(scale), int(bool(causal)), _ptr(cu))
         if rc != 0:
             raise ValueError("oracle_attn_rows_bf16 rejected its arguments")

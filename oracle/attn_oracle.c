@@ -30,6 +30,9 @@
  * MQA): Hkv divides H and query head h reads K/V head h / (H / Hkv), i.e.
  * each run of H/Hkv consecutive query heads shares one K/V head.  Hkv = H is
  * plain multi-head attention, Hkv = 1 is multi-query attention.
+ * Head dimensions: q and k rows have D entries, v and o rows Dv entries
+ * (the paper's section 5.1 also benchmarks the (192, 128) pair of
+ * DeepSeek V3); Dv = D is the usual case.
  * Inputs come either as double or as bfloat16 bit patterns (uint16), which
  * are widened exactly to double (bf16 is the top half of an IEEE float).
  */
@@ -76,7 +79,7 @@ typedef struct {
  */
 static void attend_one_row(tensor_in q, tensor_in k, tensor_in v,
                            double *o_row, double *lse_out,
-                           seq_span sp, int i, int h, int H, int Hkv, int D,
+                           seq_span sp, int i, int h, int H, int Hkv, int D, int Dv,
                            double scale, int causal, double *s)
 {
     const int nkeys = causal ? i + 1 : sp.len;
@@ -101,10 +104,10 @@ static void attend_one_row(tensor_in q, tensor_in k, tensor_in v,
         s[j] = exp(s[j] - m);
         l += s[j];
     }
-    for (int d = 0; d < D; ++d) {
+    for (int d = 0; d < Dv; ++d) {
         double acc = 0.0;
         for (int j = 0; j < nkeys; ++j)
-            acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)D + d);
+            acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)Dv + d);
         o_row[d] = acc / l;
     }
     *lse_out = m + log(l);
@@ -168,17 +171,18 @@ static int max_len(int B, int S, const int *cu_seqlens)
 static int attend_rows(tensor_in q, tensor_in k, tensor_in v,
                        const int64_t *rows, int64_t n_rows,
                        double *o_rows, double *lse_rows,
-                       int B, int H, int Hkv, int S, int D, double scale, int causal,
+                       int B, int H, int Hkv, int S, int D, int Dv, double scale, int causal,
                        const int *cu_seqlens)
 {
-    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || D <= 0 || (!cu_seqlens && S <= 0))
+    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || D <= 0 || Dv <= 0 ||
+        (!cu_seqlens && S <= 0))
         return -1;
     const int Lmax = max_len(B, S, cu_seqlens);
     int bad = 0;
 #pragma omp parallel
     {
         double *s = (double *)malloc(sizeof(double) * (size_t)(Lmax > 0 ? Lmax : 1));
-        double *o_tmp = (double *)malloc(sizeof(double) * (size_t)D);
+        double *o_tmp = (double *)malloc(sizeof(double) * (size_t)Dv);
         if (!s || !o_tmp) {
 #pragma omp atomic write
             bad = 1;
@@ -189,9 +193,9 @@ static int attend_rows(tensor_in q, tensor_in k, tensor_in v,
                 decode_row(rows[r], B, H, S, cu_seqlens, &b, &h, &i);
                 seq_span sp = span_of(b, S, cu_seqlens);
                 double lse;
-                attend_one_row(q, k, v, o_tmp, &lse, sp, i, h, H, Hkv, D, scale, causal, s);
+                attend_one_row(q, k, v, o_tmp, &lse, sp, i, h, H, Hkv, D, Dv, scale, causal, s);
                 if (o_rows)
-                    memcpy(o_rows + r * (int64_t)D, o_tmp, sizeof(double) * (size_t)D);
+                    memcpy(o_rows + r * (int64_t)Dv, o_tmp, sizeof(double) * (size_t)Dv);
                 if (lse_rows)
                     lse_rows[r] = lse;
             }
@@ -207,15 +211,16 @@ static int attend_rows(tensor_in q, tensor_in k, tensor_in v,
  * NULL).  Every row of every (sequence, head) is computed.
  */
 static int attend_all(tensor_in q, tensor_in k, tensor_in v, double *o, double *lse,
-                      int B, int H, int Hkv, int S, int D, double scale, int causal,
+                      int B, int H, int Hkv, int S, int D, int Dv, double scale, int causal,
                       const int *cu_seqlens)
 {
-    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || D <= 0 || (!cu_seqlens && S <= 0))
+    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || D <= 0 || Dv <= 0 ||
+        (!cu_seqlens && S <= 0))
         return -1;
     const int64_t T = cu_seqlens ? cu_seqlens[B] : (int64_t)B * S;
     const int64_t n_rows = T * H;
     int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_rows > 0 ? n_rows : 1));
-    double *o_rows = (double *)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1) * D);
+    double *o_rows = (double *)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1) * Dv);
     double *l_rows = (double *)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1));
     if (!rows || !o_rows || !l_rows) {
         free(rows);
@@ -225,7 +230,7 @@ static int attend_all(tensor_in q, tensor_in k, tensor_in v, double *o, double *
     }
     for (int64_t r = 0; r < n_rows; ++r)
         rows[r] = r;
-    int rc = attend_rows(q, k, v, rows, n_rows, o_rows, l_rows, B, H, Hkv, S, D, scale,
+    int rc = attend_rows(q, k, v, rows, n_rows, o_rows, l_rows, B, H, Hkv, S, D, Dv, scale,
                          causal, cu_seqlens);
     if (rc == 0) {
         for (int64_t r = 0; r < n_rows; ++r) {
@@ -233,8 +238,8 @@ static int attend_all(tensor_in q, tensor_in k, tensor_in v, double *o, double *
             decode_row(r, B, H, S, cu_seqlens, &b, &h, &i);
             seq_span sp = span_of(b, S, cu_seqlens);
             if (o)
-                memcpy(o + ((sp.tok0 + i) * H + h) * (int64_t)D, o_rows + r * (int64_t)D,
-                       sizeof(double) * (size_t)D);
+                memcpy(o + ((sp.tok0 + i) * H + h) * (int64_t)Dv, o_rows + r * (int64_t)Dv,
+                       sizeof(double) * (size_t)Dv);
             if (lse)
                 lse[r] = l_rows[r];
         }
@@ -246,32 +251,33 @@ static int attend_all(tensor_in q, tensor_in k, tensor_in v, double *o, double *
 }
 
 /* ---- exported entry points (C ABI, loaded by ctypes from Python) ----
- * Hkv is the number of K/V heads (Hkv = H for multi-head attention). */
+ * Hkv is the number of K/V heads (Hkv = H for multi-head attention); D is the
+ * q/k head dimension and Dv the v/o head dimension. */
 
 int oracle_attn_fwd_f64(const double *q, const double *k, const double *v,
-                        double *o, double *lse, int B, int H, int Hkv, int S, int D,
+                        double *o, double *lse, int B, int H, int Hkv, int S, int D, int Dv,
                         double scale, int causal, const int *cu_seqlens)
 {
     tensor_in tq = {q, 0}, tk = {k, 0}, tv = {v, 0};
-    return attend_all(tq, tk, tv, o, lse, B, H, Hkv, S, D, scale, causal, cu_seqlens);
+    return attend_all(tq, tk, tv, o, lse, B, H, Hkv, S, D, Dv, scale, causal, cu_seqlens);
 }
 
 int oracle_attn_fwd_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                         double *o, double *lse, int B, int H, int Hkv, int S, int D,
+                         double *o, double *lse, int B, int H, int Hkv, int S, int D, int Dv,
                          double scale, int causal, const int *cu_seqlens)
 {
     tensor_in tq = {q, 1}, tk = {k, 1}, tv = {v, 1};
-    return attend_all(tq, tk, tv, o, lse, B, H, Hkv, S, D, scale, causal, cu_seqlens);
+    return attend_all(tq, tk, tv, o, lse, B, H, Hkv, S, D, Dv, scale, causal, cu_seqlens);
 }
 
 int oracle_attn_rows_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                           const int64_t *rows, int64_t n_rows,
                           double *o_rows, double *lse_rows,
-                          int B, int H, int Hkv, int S, int D, double scale, int causal,
+                          int B, int H, int Hkv, int S, int D, int Dv, double scale, int causal,
                           const int *cu_seqlens)
 {
     tensor_in tq = {q, 1}, tk = {k, 1}, tv = {v, 1};
-    return attend_rows(tq, tk, tv, rows, n_rows, o_rows, lse_rows, B, H, Hkv, S, D, scale,
+    return attend_rows(tq, tk, tv, rows, n_rows, o_rows, lse_rows, B, H, Hkv, S, D, Dv, scale,
                        causal, cu_seqlens);
 }
 

@@ -23,7 +23,8 @@ DIGITS = 50
 
 def attention(q, k, v, scale, causal, cu_seqlens=None):
     """q: float array [B,S,H,D] (dense) or [T,H,D] (varlen); k, v the same with
-    Hkv heads, Hkv dividing H (query head h reads K/V head h // (H // Hkv)).
+    Hkv heads, Hkv dividing H (query head h reads K/V head h // (H // Hkv));
+    v may have its own head dimension Dv.
 
     Returns (o, lse) as numpy float64 arrays in the oracle's layouts
     (o like q; lse [B,H,S] or [H,T]).  Inputs must be exactly representable
@@ -39,7 +40,8 @@ def attention(q, k, v, scale, causal, cu_seqlens=None):
         spans = [(b * S, S) for b in range(B)]
         Hkv = k.shape[2]
         qf = q.reshape(B * S, H, D)
-        kf, vf = (x.reshape(B * S, Hkv, D) for x in (k, v))
+        kf = k.reshape(B * S, Hkv, D)
+        vf = v.reshape(B * S, Hkv, v.shape[-1])
         T = B * S
     else:
         cu = [int(c) for c in cu_seqlens]
@@ -49,7 +51,8 @@ def attention(q, k, v, scale, causal, cu_seqlens=None):
         T, H, D = q.shape
         Hkv = k.shape[1]
     group = H // Hkv
-    o = np.zeros((T, H, D), np.float64)
+    Dv = v.shape[-1]
+    o = np.zeros((T, H, Dv), np.float64)
     lse_t = np.zeros((H, T), np.float64)
     for (t0, L) in spans:
         for h in range(H):
@@ -63,13 +66,13 @@ def attention(q, k, v, scale, causal, cu_seqlens=None):
                     s = sc * dot
                     w.append(mpmath.exp(mpmath.mpf(s.numerator) / s.denominator))
                 z = mpmath.fsum(w)
-                for d in range(D):
+                for d in range(Dv):
                     num = mpmath.fsum(wj * mpmath.mpf(float(vf[t0 + j, hk, d]))
                                       for wj, j in zip(w, keys))
                     o[t0 + i, h, d] = float(num / z)
                 lse_t[h, t0 + i] = float(mpmath.log(z))
     if cu_seqlens is None:
-        o = o.reshape(B, S, H, D)
+        o = o.reshape(B, S, H, Dv)
         lse = lse_t.reshape(H, B, S).transpose(1, 0, 2).copy()
         return o, lse
     return o, lse_t

@@ -207,6 +207,36 @@ def check_gqa_equals_repeated_kv(o):
             assert np.array_equal(o1, o2) and np.array_equal(l1, l2), ("gqa repeat", Hkv, causal)
 
 
+def check_value_dim_brute_force_tiny(o):
+    """A value head dimension Dv different from the q/k one == the 50-digit brute force."""
+    rng = np.random.default_rng(23)
+    for causal in (False, True):
+        B, S, H, Hkv, D, Dv = 1, 6, 2, 1, 5, 3
+        q = _bf16_grid(rng, (B, S, H, D))
+        k = _bf16_grid(rng, (B, S, Hkv, D))
+        v = _bf16_grid(rng, (B, S, Hkv, Dv))
+        got_o, got_l = o.attention_f64(q, k, v, 0.45, causal)
+        ref_o, ref_l = brute.attention(q, k, v, 0.45, causal)
+        assert got_o.shape == (B, S, H, Dv)
+        assert np.max(np.abs(got_o - ref_o)) <= 1e-12, ("dv brute O", causal)
+        assert np.max(np.abs(got_l - ref_l)) <= 1e-12, ("dv brute LSE", causal)
+
+
+def check_value_columns_are_independent(o):
+    """Each output column depends only on the same column of V: attention on V
+    equals the first Dv columns of attention on V padded with extra columns,
+    and the LSE ignores V entirely (bit for bit in both cases)."""
+    rng = np.random.default_rng(24)
+    B, S, H, D, Dv = 2, 7, 2, 6, 3
+    q, k = (rng.standard_normal((B, S, H, D)) for _ in range(2))
+    v = rng.standard_normal((B, S, H, Dv))
+    vpad = np.concatenate([v, rng.standard_normal((B, S, H, 5))], axis=-1)
+    for causal in (False, True):
+        o1, l1 = o.attention_f64(q, k, v, 0.2, causal)
+        o2, l2 = o.attention_f64(q, k, vpad, 0.2, causal)
+        assert np.array_equal(o1, o2[..., :Dv]) and np.array_equal(l1, l2), ("dv columns", causal)
+
+
 ALL_CHECKS = [
     check_brute_force_tiny,
     check_equal_logits_mean_of_v,
@@ -220,4 +250,6 @@ ALL_CHECKS = [
     check_scale_is_a_logit_multiplier,
     check_gqa_brute_force_tiny,
     check_gqa_equals_repeated_kv,
+    check_value_dim_brute_force_tiny,
+    check_value_columns_are_independent,
 ]

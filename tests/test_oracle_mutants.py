@@ -31,10 +31,12 @@ MUTANTS = [
     ("exp_sign_flipped", "s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
     ("lse_missing_max", "*lse_out = m + log(l);", "*lse_out = log(l);"),
     ("normalisation_dropped", "o_row[d] = acc / l;", "o_row[d] = acc;"),
-    ("v_head_ignored", "acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)D + d);",
-     "acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + 0) * (int64_t)D + d);"),
-    ("v_read_at_query_row", "acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)D + d);",
-     "acc += s[j] * at(v, ((sp.tok0 + i) * Hkv + hk) * (int64_t)D + d);"),
+    ("v_head_ignored", "acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)Dv + d);",
+     "acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + 0) * (int64_t)Dv + d);"),
+    ("v_read_at_query_row", "acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)Dv + d);",
+     "acc += s[j] * at(v, ((sp.tok0 + i) * Hkv + hk) * (int64_t)Dv + d);"),
+    ("v_row_stride_of_q", "acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)Dv + d);",
+     "acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)D + d);"),
     ("kv_head_interleaved", "const int hk = h / (H / Hkv);", "const int hk = h % Hkv;"),
     ("kv_head_stride_of_q", "const int64_t kbase = ((sp.tok0 + j) * Hkv + hk) * (int64_t)D;",
      "const int64_t kbase = ((sp.tok0 + j) * H + hk) * (int64_t)D;"),

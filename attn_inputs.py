@@ -7,8 +7,9 @@ the two sides always see the same bf16 bits.
 Recipe: a CPU ``torch.Generator`` seeded with the workload's seed draws
 standard normals in float32 in the order Q, K, V (shape [B,S,H,D], or
 [T,H,D] for packed variable-length batches; K and V have H_kv heads for
-grouped-query workloads); each tensor is multiplied by its standard
-deviation and rounded to bfloat16 with round-to-nearest-even.
+grouped-query workloads, and V has Dv columns where the value head
+dimension differs); each tensor is multiplied by its standard deviation and
+rounded to bfloat16 with round-to-nearest-even.
 Variable-length batches draw their lengths first from
 ``numpy.random.default_rng(seed).integers(lo, hi, n, endpoint=True)``.
 """
@@ -37,10 +38,15 @@ class Workload:
     varlen: Optional[tuple] = None   # (n_seqs, lo, hi) drawn uniformly, inclusive
     lengths: tuple = field(default=())
     Hkv: int = 0                     # K/V heads for grouped-query attention (0: same as H)
+    Dv: int = 0                      # value/output head dimension (0: same as D)
 
     @property
     def kv_heads(self) -> int:
         return self.Hkv or self.H
+
+    @property
+    def head_dim_v(self) -> int:
+        return self.Dv or self.D
 
     @property
     def scale(self) -> float:
@@ -57,15 +63,20 @@ def cu_seqlens_of(lengths) -> np.ndarray:
     return np.concatenate([[0], np.cumsum(np.asarray(lengths, np.int64))]).astype(np.int32)
 
 
-def draw_qkv(shape, seed: int, q_std: float = 1.0, kv_std: float = 1.0, kv_heads=None):
+def draw_qkv(shape, seed: int, q_std: float = 1.0, kv_std: float = 1.0, kv_heads=None,
+             v_dim=None):
     """Q, K, V as CPU bf16 tensors (drawn in that order).  Q has the given
-    shape; K and V too, or kv_heads heads on the head axis (second to last)."""
+    shape; K and V too, or kv_heads heads on the head axis (second to last);
+    V has v_dim columns when given."""
     g = torch.Generator(device="cpu").manual_seed(int(seed))
     kv_shape = list(shape)
     if kv_heads is not None:
         kv_shape[-2] = int(kv_heads)
+    v_shape = list(kv_shape)
+    if v_dim is not None:
+        v_shape[-1] = int(v_dim)
     out = []
-    for std, shp in ((q_std, shape), (kv_std, kv_shape), (kv_std, kv_shape)):
+    for std, shp in ((q_std, shape), (kv_std, kv_shape), (kv_std, v_shape)):
         x = torch.randn(*shp, generator=g, dtype=torch.float32)
         if std != 1.0:
             x = x * std
@@ -79,23 +90,28 @@ def make(w: Workload):
         n, lo, hi = w.varlen
         lens = varlen_lengths(n, lo, hi, w.seed)
         cu = cu_seqlens_of(lens)
-        q, k, v = draw_qkv((int(cu[-1]), w.H, w.D), w.seed, w.q_std, w.kv_std, w.kv_heads)
+        q, k, v = draw_qkv((int(cu[-1]), w.H, w.D), w.seed, w.q_std, w.kv_std, w.kv_heads,
+                           w.head_dim_v)
         return q, k, v, cu, int(lens.max())
     if w.lengths:
         cu = cu_seqlens_of(w.lengths)
-        q, k, v = draw_qkv((int(cu[-1]), w.H, w.D), w.seed, w.q_std, w.kv_std, w.kv_heads)
+        q, k, v = draw_qkv((int(cu[-1]), w.H, w.D), w.seed, w.q_std, w.kv_std, w.kv_heads,
+                           w.head_dim_v)
         return q, k, v, cu, int(max(w.lengths))
-    q, k, v = draw_qkv((w.B, w.S, w.H, w.D), w.seed, w.q_std, w.kv_std, w.kv_heads)
+    q, k, v = draw_qkv((w.B, w.S, w.H, w.D), w.seed, w.q_std, w.kv_std, w.kv_heads,
+                       w.head_dim_v)
     return q, k, v, None, w.S
 
 
 def flops(w: Workload, cu=None) -> float:
-    """Algorithmic flops: 4*B*H*S^2*D, halved for causal (varlen: sum over sequences)."""
+    """Algorithmic flops: 2*B*H*S^2*(D + Dv) (= 4*B*H*S^2*D for equal head
+    dimensions), halved for causal (varlen: sum over sequences)."""
+    dsum = w.D + w.head_dim_v
     if cu is not None:
         lens = np.diff(np.asarray(cu, np.int64))
-        tot = float(np.sum(lens.astype(np.float64) ** 2)) * 4.0 * w.H * w.D
+        tot = float(np.sum(lens.astype(np.float64) ** 2)) * 2.0 * w.H * dsum
     else:
-        tot = 4.0 * w.B * w.H * float(w.S) ** 2 * w.D
+        tot = 2.0 * w.B * w.H * float(w.S) ** 2 * dsum
     return tot / 2.0 if w.causal else tot
 
 
@@ -104,7 +120,8 @@ def flops(w: Workload, cu=None) -> float:
 # causal batch; wide heads with high-spread logits; 8k causal (the other
 # sequence length the throughput metric names); the install-check shape
 # (1, 8, 512, 64) causal from the FlashAttention-4 usage guide; and
-# grouped-query attention at 8k causal (32 query heads sharing 8 K/V heads).
+# grouped-query attention at 8k causal (32 query heads sharing 8 K/V heads);
+# and the (192, 128) head dimensions of DeepSeek V3 at 8k causal.
 WORKLOADS = {
     "tiny_b1h2s128d64": Workload("tiny_b1h2s128d64", 1, 128, 2, 64, False, seed=1),
     "dense_b2h16s2048d128": Workload("dense_b2h16s2048d128", 2, 2048, 16, 128, False, seed=2),
@@ -121,4 +138,6 @@ WORKLOADS = {
     "smoke_b1h8s512d64_causal": Workload("smoke_b1h8s512d64_causal", 1, 512, 8, 64, True, seed=7),
     "gqa_b2h32kv8s8192d128_causal": Workload("gqa_b2h32kv8s8192d128_causal", 2, 8192, 32, 128,
                                              True, seed=8, Hkv=8),
+    "hd192v128_b2h16s8192_causal": Workload("hd192v128_b2h16s8192_causal", 2, 8192, 16, 192,
+                                            True, seed=9, Dv=128),
 }

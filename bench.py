@@ -76,7 +76,7 @@ def time_workload(fa, torch, w, steps, warmup, tuning=None):
     dev = torch.device("cuda:0")
     dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
     dcu = None if cu is None else torch.from_numpy(cu).to(dev)
-    o = torch.empty_like(dq)
+    o = torch.empty(tuple(dq.shape[:-1]) + (w.head_dim_v,), dtype=dq.dtype, device=dev)
     T = dq.shape[0] if cu is not None else None
     lse = torch.empty((w.H, T) if cu is not None else (w.B, w.H, w.S), dtype=torch.float32,
                       device=dev)
@@ -140,7 +140,7 @@ def cpu_baseline(w, inputs, target_s=15.0):
         dt = time.perf_counter() - t0
         total_s += dt
         total_rows += n
-        total_flops += float(np.sum(4.0 * w.D * keys_of(rows)))
+        total_flops += float(np.sum(2.0 * (w.D + w.head_dim_v) * keys_of(rows)))
         rate = n / max(dt, 1e-6)
         n = int(min(max(rate * (target_s - total_s), 0), 20000))
     return {

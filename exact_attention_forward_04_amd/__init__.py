@@ -58,6 +58,8 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd_ex.restype = I
     lib.fa_fwd_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, P, ctypes.POINTER(Tuning)]
     lib.fa_fwd_gqa.restype = I
+    lib.fa_fwd_hd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, ctypes.POINTER(Tuning)]
+    lib.fa_fwd_hd.restype = I
     lib.fa_tuning_default.argtypes = []
     lib.fa_tuning_default.restype = Tuning
     lib.fa_exp2_emu.argtypes = [P, P, LL, P]
@@ -105,8 +107,9 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
     (varlen, with cu_seqlens an int32 CUDA tensor of B+1 offsets and
     max_seqlen the longest sequence).  k and v may have fewer heads H_kv than
     q (grouped-query attention; H_kv divides H and query head h reads K/V
-    head h // (H // H_kv)).  Returns (o, lse): o like q (bf16), lse fp32
-    [B,H,S] or [H,T] (None if return_lse is False).
+    head h // (H // H_kv)), and v may have its own head dimension D_v (the
+    (192, 128) pair).  Returns (o, lse): o like q with D_v columns (bf16),
+    lse fp32 [B,H,S] or [H,T] (None if return_lse is False).
     """
     import torch
     lib = load()
@@ -114,10 +117,13 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("%s must be a contiguous bf16 CUDA tensor" % name)
     head_axis = 2 if cu_seqlens is None else 1
-    if k.shape != v.shape or k.dim() != q.dim() or any(
-            k.shape[i] != q.shape[i] for i in range(q.dim()) if i != head_axis):
-        raise ValueError("k and v must have q's shape apart from the number of heads")
+    if k.dim() != q.dim() or v.dim() != q.dim() or any(
+            k.shape[i] != q.shape[i] for i in range(q.dim()) if i != head_axis) or any(
+            v.shape[i] != k.shape[i] for i in range(q.dim() - 1)):
+        raise ValueError("k must have q's shape apart from the number of heads, "
+                         "and v k's shape apart from the head dimension")
     H_kv = k.shape[head_axis]
+    D_v = v.shape[-1]
     if H_kv < 1 or q.shape[head_axis] % H_kv != 0:
         raise ValueError("the K/V head count must divide the query head count")
     if cu_seqlens is None:
@@ -140,7 +146,10 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
         cu_ptr = cu_seqlens.data_ptr()
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    o = out if out is not None else torch.empty_like(q)
+    o_shape = tuple(q.shape[:-1]) + (D_v,)
+    o = out if out is not None else torch.empty(o_shape, dtype=q.dtype, device=q.device)
+    if tuple(o.shape) != o_shape:
+        raise ValueError("out must have shape %s" % (o_shape,))
     lse = None
     if return_lse:
         lse = lse_out if lse_out is not None else torch.empty(lse_shape, dtype=torch.float32,
@@ -149,7 +158,11 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
             lse.data_ptr() if lse is not None else None, B, H, S, D, float(scale),
             int(bool(causal)), cu_ptr, sp)
-    if H_kv != H:
+    if D_v != D:
+        hargs = args[:7] + (H_kv,) + args[7:9] + (D_v,) + args[9:]
+        rc = lib.fa_fwd_hd(*hargs, ctypes.byref(tuning) if tuning is not None else None)
+        _check("fa_fwd_hd", rc)
+    elif H_kv != H:
         gargs = args[:7] + (H_kv,) + args[7:]
         rc = lib.fa_fwd_gqa(*gargs, ctypes.byref(tuning) if tuning is not None else None)
         _check("fa_fwd_gqa", rc)

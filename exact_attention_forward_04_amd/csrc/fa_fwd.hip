@@ -47,6 +47,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <utility>
 
 #include "fa.h"
 #include "exp2_poly.h"
@@ -133,22 +134,27 @@ __device__ __forceinline__ int swz(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
+// Kernel instances are named by the q/k head dimension D; the v/o head
+// dimension DV equals D except for D = 192, which is the (192, 128) pair the
+// FlashAttention-4 paper benchmarks for DeepSeek V3 (section 5.1).
+template <int D>
+constexpr int head_dim_v() { return D == 192 ? 128 : D; }
+
 template <int D>
 struct Cfg {
-  // D <= 128: eight waves (two per SIMD) in one workgroup per CU, run as two
+  // D <= 192: eight waves (two per SIMD) in one workgroup per CU, run as two
   // halves that alternate matrix-product and softmax phases (run_tile).
   // D = 256 needs the whole register file (O alone is 128 VGPRs per lane):
   // four waves, one per SIMD, in the plain per-block sequence.
+  static constexpr int DV = head_dim_v<D>();
   static constexpr int NW = (D == 256) ? 4 : 8;  // waves per workgroup
   static constexpr int OCC = 1;                  // workgroups per CU
   static constexpr bool PINGPONG = (NW == 8);    // two halves alternate MFMA and VALU phases
   static constexpr int WAVES_PER_SIMD = NW * OCC / 4;
   static constexpr int BM = 32 * NW;             // query rows per tile
-  static constexpr int CPR = D / 8;              // 16-byte chunks per row
-  static constexpr int BLOCK_BYTES = kBN * D * 2;
-  static constexpr int LOADS = (kBN * CPR) / (NW * kWave);  // per wave, per tensor
+  static constexpr int K_BYTES = kBN * D * 2;    // one K block in LDS
+  static constexpr int V_BYTES = kBN * DV * 2;   // one V block in LDS
   static constexpr int THREADS = NW * kWave;
-  static_assert(LOADS * NW * kWave == kBN * CPR, "block must split evenly over waves");
 };
 
 // Kernel arguments.
@@ -173,25 +179,54 @@ struct Args {
 // next block) before any LDS read it cannot prove disjoint.  Completion is
 // waited for explicitly with wait_vmcnt<>(), which is exact because the
 // vector-memory counter retires loads in issue order.
-template <int D>
+template <int W, int NW>
 struct BlockLoader {
-  using C = Cfg<D>;
-  unsigned voff[C::LOADS];  // byte offset of this lane's 16-byte chunk from the block's first row
-  unsigned row_bytes;       // H*D*2: distance between consecutive tokens of a head
+  // Rows are W bf16 wide; W = 192 rows are stored as two LDS parts: chunks
+  // 0-15 of every row in a 128-wide layout (16 KiB, slots 0..1023) and
+  // chunks 16-23 in a 64-wide layout (8 KiB, slots 1024..1535), so that each
+  // part keeps the power-of-two row pitch the operand addressing relies on.
+  static constexpr int CPR = W / 8;                           // 16-byte chunks per row
+  static constexpr int LOADS = (kBN * CPR) / (NW * kWave);    // per wave
+  static_assert(LOADS * NW * kWave == kBN * CPR, "block must split evenly over waves");
+  static_assert(W != 192 || (1024 % (NW * kWave)) == 0, "no copy may straddle the two parts");
+  unsigned voff[LOADS];  // byte offset of this lane's 16-byte chunk from the block's first row
+  unsigned row_bytes;    // Hk*W*2: distance between consecutive tokens of a head
   int wave, lane;
 
-  __device__ __forceinline__ int slot0(int i) const { return (i * C::NW + wave) * kWave; }
-  __device__ __forceinline__ int row_of(int i) const { return (slot0(i) + lane) / C::CPR; }
+  __device__ __forceinline__ int slot0(int i) const { return (i * NW + wave) * kWave; }
+  // Slot p of the block -> (row, logical chunk).
+  static __device__ __forceinline__ void row_chunk(int p, int &row, int &c) {
+    if constexpr (W == 192) {
+      if (p < 1024) {
+        row = p / 16;
+        c = (p % 16) ^ swz<128>(row);
+      } else {
+        const int q = p - 1024;
+        row = q / 8;
+        c = 16 + ((q % 8) ^ swz<64>(row));
+      }
+    } else {
+      row = p / CPR;
+      c = (p % CPR) ^ swz<W>(row);
+    }
+  }
+  __device__ __forceinline__ int row_of(int i) const {
+    int row, c;
+    row_chunk(slot0(i) + lane, row, c);
+    return row;
+  }
+  // Copy i goes to the second part of a W = 192 block (compile-time: the
+  // copies of one index i cover slots i*NW*64 .. (i+1)*NW*64-1 over the waves).
+  static constexpr bool second_part(int i) { return W == 192 && i * NW * kWave >= 1024; }
 
-  __device__ __forceinline__ void init(int H, int wave_, int lane_) {
+  __device__ __forceinline__ void init(int Hk, int wave_, int lane_) {
     wave = __builtin_amdgcn_readfirstlane(wave_);
     lane = lane_;
-    row_bytes = (unsigned)H * (unsigned)D * 2u;
+    row_bytes = (unsigned)Hk * (unsigned)W * 2u;
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int p = slot0(i) + lane;
-      const int row = p / C::CPR;
-      const int c = (p % C::CPR) ^ swz<D>(row);
+    for (int i = 0; i < LOADS; ++i) {
+      int row, c;
+      row_chunk(slot0(i) + lane, row, c);
       voff[i] = (unsigned)row * row_bytes + (unsigned)c * 16u;
     }
   }
@@ -208,27 +243,38 @@ struct BlockLoader {
         : "memory", "m0");
   }
 
-  // Copy this wave's chunk i of rows n0 .. n0+BN-1 of one (sequence, head)
-  // of K or V into dst.  Rows at or past L read row L-1 instead (in bounds;
-  // masked later).  The full-block test is on scalars only: one scalar branch.
-  __device__ __forceinline__ void issue_one(const __bf16 *base, long long tok0, int H, int h,
-                                            int n0, int L, char LDS_AS *dst, int i) const {
-    const char *blk = (const char *)(base + ((tok0 + n0) * H + h) * (long long)D);
-    const unsigned lds_addr = (unsigned)(uintptr_t)dst + (unsigned)slot0(i) * 16u;
+  // Copy this wave's chunk i of rows n0 .. n0+BN-1 of one (sequence, K/V
+  // head) of K or V into the LDS block dst (dst2: its second part, W = 192).
+  // Rows at or past L read row L-1 instead (in bounds; masked later).  The
+  // full-block test is on scalars only: one scalar branch.
+  template <int I>
+  __device__ __forceinline__ void issue_one(const __bf16 *base, long long tok0, int Hk, int hk,
+                                            int n0, int L, char LDS_AS *dst,
+                                            char LDS_AS *dst2) const {
+    const char *blk = (const char *)(base + ((tok0 + n0) * Hk + hk) * (long long)W);
+    const unsigned lds_addr =
+        second_part(I) ? (unsigned)(uintptr_t)dst2 + (unsigned)(slot0(I) - 1024) * 16u
+                       : (unsigned)(uintptr_t)dst + (unsigned)slot0(I) * 16u;
     if (n0 + kBN <= L) {
-      dma16(blk, voff[i], lds_addr);
+      dma16(blk, voff[I], lds_addr);
     } else {
       const int last = L - 1 - n0;  // >= 0: blocks start below L
-      const int row = row_of(i);
+      const int row = row_of(I);
       const int r = row < last ? row : last;
-      dma16(blk, voff[i] - (unsigned)(row - r) * row_bytes, lds_addr);
+      dma16(blk, voff[I] - (unsigned)(row - r) * row_bytes, lds_addr);
     }
   }
   // All of this wave's chunks of one block.
-  __device__ __forceinline__ void issue(const __bf16 *base, long long tok0, int H, int h, int n0,
-                                        int L, char LDS_AS *dst) const {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) issue_one(base, tok0, H, h, n0, L, dst, i);
+  __device__ __forceinline__ void issue(const __bf16 *base, long long tok0, int Hk, int hk, int n0,
+                                        int L, char LDS_AS *dst,
+                                        char LDS_AS *dst2 = nullptr) const {
+    issue_all(base, tok0, Hk, hk, n0, L, dst, dst2, std::make_integer_sequence<int, LOADS>{});
+  }
+  template <int... I>
+  __device__ __forceinline__ void issue_all(const __bf16 *base, long long tok0, int Hk, int hk,
+                                            int n0, int L, char LDS_AS *dst, char LDS_AS *dst2,
+                                            std::integer_sequence<int, I...>) const {
+    (issue_one<I>(base, tok0, Hk, hk, n0, L, dst, dst2), ...);
   }
 };
 
@@ -244,21 +290,33 @@ struct BlockLoader {
 // dt is ((VW_r + buf) ^ 64dt) + t*16*2D.  Buffers start at multiples of
 // 2D*64 bytes, so adding the buffer base commutes with the XOR.  Each read
 // is then one v_xor plus an instruction offset, with three base registers.
+// For D = 192 the K layout has two parts (128- and 64-wide, see
+// BlockLoader): k-steps 0-7 read the first with KY, k-steps 8-11 the second
+// with KY2 (each part's own pitch and swizzle).  V uses the DV-wide layout.
+template <int W>
+__device__ __forceinline__ unsigned k_lane_const(int lane) {
+  const int row = lane & 31, h = lane >> 5;
+  return (unsigned)(row * (2 * W)) | (unsigned)((16 * h) ^ (swz<W>(row) << 4));
+}
+
 template <int D>
 struct LdsAddr {
-  unsigned ky, vw0, vw1;
+  static constexpr int KW = (D == 192) ? 128 : D;  // pitch of the (first) K part
+  static constexpr int DV = head_dim_v<D>();
+  unsigned ky, ky2, vw0, vw1;
   __device__ __forceinline__ void init(int lane) {
-    const int row = lane & 31, h = lane >> 5;
-    ky = (unsigned)(row * (2 * D)) | (unsigned)((16 * h) ^ (swz<D>(row) << 4));
+    const int h = lane >> 5;
+    ky = k_lane_const<KW>(lane);
+    ky2 = (D == 192) ? k_lane_const<64>(lane) : 0u;
     const int j = lane & 15, g = lane >> 4;
     const int cl = 2 * (g & 1) + ((j & 3) >> 1);
     unsigned w[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int kk = 4 * h + (j >> 2) + 8 * r;
-      const int sw = swz<D>(kk);
+      const int sw = swz<DV>(kk);
       const int z = ((sw & ~3) << 4) | ((cl ^ (sw & 3)) << 4);
-      w[r] = (unsigned)(kk * (2 * D)) | (unsigned)z | (unsigned)((j & 1) * 8);
+      w[r] = (unsigned)(kk * (2 * DV)) | (unsigned)z | (unsigned)((j & 1) * 8);
     }
     vw0 = w[0];
     vw1 = w[1];
@@ -267,11 +325,23 @@ struct LdsAddr {
 
 __device__ __forceinline__ unsigned lds_u32(const char LDS_AS *p) { return (unsigned)(uintptr_t)p; }
 
-// K operand (A of S^T = K Q^T) for key sub-block kb, k-step s; ka = KY + buffer.
-template <int D>
+// K operand (A of S^T = K Q^T) for key sub-block kb, k-step s of a W-wide
+// layout; ka = KY + buffer.
+template <int W>
 __device__ __forceinline__ bf16x8 read_k(unsigned ka, int kb, int s) {
-  const unsigned addr = (ka ^ (unsigned)(32 * s)) + (unsigned)(kb * 32 * 2 * D);
+  const unsigned addr = (ka ^ (unsigned)(32 * s)) + (unsigned)(kb * 32 * 2 * W);
   return *(const bf16x8 LDS_AS *)(uintptr_t)addr;
+}
+// k-step s of a D-instance K block: ka addresses the first part, ka2 the
+// second part of a D = 192 block.
+template <int D>
+__device__ __forceinline__ bf16x8 read_k_step(unsigned ka, unsigned ka2, int kb, int s) {
+  if constexpr (D == 192) {
+    if (s >= 8) return read_k<64>(ka2, kb, s - 8);
+    return read_k<128>(ka, kb, s);
+  } else {
+    return read_k<D>(ka, kb, s);
+  }
 }
 
 // V^T operand (A of O^T += V^T P^T) for 16-key step t and 32-wide d tile dt:
@@ -295,8 +365,8 @@ __device__ __forceinline__ bf16x8 read_vt(unsigned va0, unsigned va1, int t, int
 // Per-wave state of one tile.
 template <int D>
 struct WaveState {
-  bf16x8 qf[D / 16];  // Q rows of this wave (B operand of S^T = K Q^T)
-  f32x16 o[D / 32];   // O^T accumulators
+  bf16x8 qf[D / 16];                // Q rows of this wave (B operand of S^T = K Q^T)
+  f32x16 o[head_dim_v<D>() / 32];   // O^T accumulators
   f32x16 s[2];        // S^T of the block between its product and its softmax
   bf16x8 p[4];        // bf16 P of the block between its softmax and its PV product
   float m_ref, l32;
@@ -309,9 +379,10 @@ struct WaveState {
 constexpr int kPrefK = 2;
 template <int D>
 __device__ __forceinline__ void qk_step(WaveState<D> &st, const LdsAddr<D> &la,
-                                        const char LDS_AS *kbuf) {
+                                        const char LDS_AS *kbuf, const char LDS_AS *kbuf2) {
   constexpr int NS = D / 16;
   const unsigned ka = la.ky + lds_u32(kbuf);
+  const unsigned ka2 = la.ky2 + lds_u32(kbuf2);
   bf16x8 kf[NS][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -319,14 +390,14 @@ __device__ __forceinline__ void qk_step(WaveState<D> &st, const LdsAddr<D> &la,
     for (int e = 0; e < 16; ++e) st.s[kb][e] = 0.0f;
 #pragma unroll
   for (int s = 0; s < kPrefK && s < NS; ++s) {
-    kf[s][0] = read_k<D>(ka, 0, s);
-    kf[s][1] = read_k<D>(ka, 1, s);
+    kf[s][0] = read_k_step<D>(ka, ka2, 0, s);
+    kf[s][1] = read_k_step<D>(ka, ka2, 1, s);
   }
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     if (s + kPrefK < NS) {
-      kf[s + kPrefK][0] = read_k<D>(ka, 0, s + kPrefK);
-      kf[s + kPrefK][1] = read_k<D>(ka, 1, s + kPrefK);
+      kf[s + kPrefK][0] = read_k_step<D>(ka, ka2, 0, s + kPrefK);
+      kf[s + kPrefK][1] = read_k_step<D>(ka, ka2, 1, s + kPrefK);
     }
     __builtin_amdgcn_sched_barrier(0);
     st.s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][0], st.qf[s], st.s[0], 0, 0, 0);
@@ -375,7 +446,7 @@ __device__ __forceinline__ void softmax_step(WaveState<D> &st, int lane, int n0,
     st.m_ref = m_new;
     st.l32 *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < head_dim_v<D>() / 32; ++dt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) st.o[dt][e] *= alpha;
     if constexpr (COUNT) {
@@ -415,16 +486,17 @@ __device__ __forceinline__ void softmax_step(WaveState<D> &st, int lane, int n0,
 template <int D>
 __device__ __forceinline__ void pv_step(WaveState<D> &st, const LdsAddr<D> &la,
                                         const char LDS_AS *vbuf) {
-  constexpr int NT = D / 32;
+  constexpr int DV = head_dim_v<D>();
+  constexpr int NT = DV / 32;
   const unsigned va0 = la.vw0 + lds_u32(vbuf), va1 = la.vw1 + lds_u32(vbuf);
   bf16x8 vf[4][NT];
 #pragma unroll
-  for (int dt = 0; dt < NT; ++dt) vf[0][dt] = read_vt<D>(va0, va1, 0, dt);
+  for (int dt = 0; dt < NT; ++dt) vf[0][dt] = read_vt<DV>(va0, va1, 0, dt);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     if (t + 1 < 4) {
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt) vf[t + 1][dt] = read_vt<D>(va0, va1, t + 1, dt);
+      for (int dt = 0; dt < NT; ++dt) vf[t + 1][dt] = read_vt<DV>(va0, va1, t + 1, dt);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -463,8 +535,33 @@ struct WaveRows {
 // two phases (the halves keep their offset on their own, and a barrier there
 // only added the wait for the slower half).  K/V blocks rotate through four
 // LDS buffers: block j+2 is copied while the workgroup still reads K_j and
-// V_{j-1}.  Four-wave workgroups (D = 256) run the plain sequence per block
-// with two buffers.
+// V_{j-1}.  (D = 192 keeps K in a ring of three, since K_{j-1} is no longer
+// read in interval j, and V in a ring of four; see KvLayout.)  Four-wave
+// workgroups (D = 256) run the plain sequence per block with two buffers.
+// LDS placement of the K/V ring of a ping-pong instance.  Every part starts
+// at a multiple of its 64-row block size, as the operand addressing needs.
+//   D = 64, 128: four slots of [K block | V block], K_j and V_j in slot j%4.
+//   D = 192:     V_j in slot j%4 (4 x 16 KiB at 0), K_j in slot j%3 with its
+//                128-wide part (3 x 16 KiB at 64 KiB) and 64-wide part
+//                (3 x 8 KiB at 112 KiB): 136 KiB in all.
+template <int D>
+struct KvLayout {
+  using C = Cfg<D>;
+  static constexpr int BYTES = (D == 192) ? 136 * 1024 : 4 * (C::K_BYTES + C::V_BYTES);
+  static __device__ __forceinline__ char LDS_AS *k(char LDS_AS *lds, int j) {
+    if constexpr (D == 192) return lds + 64 * 1024 + (j % 3) * 16 * 1024;
+    else return lds + (j & 3) * (C::K_BYTES + C::V_BYTES);
+  }
+  static __device__ __forceinline__ char LDS_AS *k2(char LDS_AS *lds, int j) {
+    if constexpr (D == 192) return lds + 112 * 1024 + (j % 3) * 8 * 1024;
+    else return lds;  // unused
+  }
+  static __device__ __forceinline__ char LDS_AS *v(char LDS_AS *lds, int j) {
+    if constexpr (D == 192) return lds + (j & 3) * 16 * 1024;
+    else return lds + (j & 3) * (C::K_BYTES + C::V_BYTES) + C::K_BYTES;
+  }
+};
+
 template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>
 __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, char LDS_AS *lds) {
   using C = Cfg<D>;
@@ -510,28 +607,39 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(st.qf[s]));
   }
+  constexpr int DV = C::DV;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < DV / 32; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) st.o[dt][e] = 0.0f;
   st.m_ref = -INFINITY;
   st.l32 = 0.0f;
 
-  BlockLoader<D> ld;
-  ld.init(Hk, wave, lane);
+  // K and V loaders (one object when both rows have the same width)
+  BlockLoader<D, C::NW> ldk;
+  ldk.init(Hk, wave, lane);
+  BlockLoader<DV, C::NW> ldv_own;
+  if constexpr (DV != D) ldv_own.init(Hk, wave, lane);
+  const auto &ldv = [&]() -> const BlockLoader<DV, C::NW> & {
+    if constexpr (DV != D) return ldv_own;
+    else return ldk;
+  }();
+  constexpr int LOADS_BLOCK = BlockLoader<D, C::NW>::LOADS + BlockLoader<DV, C::NW>::LOADS;
   LdsAddr<D> la;
   la.init(lane);
 
   if constexpr (C::PINGPONG) {
     const int half = wave / 4;
-    auto kbuf = [&](int j) { return lds + (2 * (j & 3)) * C::BLOCK_BYTES; };
-    auto vbuf = [&](int j) { return lds + (2 * (j & 3) + 1) * C::BLOCK_BYTES; };
+    using KV = KvLayout<D>;
+    auto kbuf = [&](int j) { return KV::k(lds, j); };
+    auto kbuf2 = [&](int j) { return KV::k2(lds, j); };
+    auto vbuf = [&](int j) { return KV::v(lds, j); };
     // Start of interval it: this wave's copies of block it have landed
     // (block it+1 may still be in flight), then the barrier makes everyone's
     // visible and ends interval it-1, so the buffer of block it-2 is free for
     // block it+2: copies run two intervals ahead of their use.
     auto interval_start = [&](int it) {
-      if (it + 1 < nblocks) wait_vmcnt<2 * C::LOADS>();
+      if (it + 1 < nblocks) wait_vmcnt<LOADS_BLOCK>();
       else wait_vmcnt<0>();
       barrier_after_reads();
     };
@@ -543,8 +651,8 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     auto copies = [&](int it) {
       return [&, it](int part) {
         if (it + 2 < nblocks) {
-          if (part == 0) ld.issue(a.k, tok0, Hk, hk, (it + 2) * kBN, L, kbuf(it + 2));
-          else ld.issue(a.v, tok0, Hk, hk, (it + 2) * kBN, L, vbuf(it + 2));
+          if (part == 0) ldk.issue(a.k, tok0, Hk, hk, (it + 2) * kBN, L, kbuf(it + 2), kbuf2(it + 2));
+          else ldv.issue(a.v, tok0, Hk, hk, (it + 2) * kBN, L, vbuf(it + 2));
         }
       };
     };
@@ -558,11 +666,11 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
         side(1);
       }
     };
-    ld.issue(a.k, tok0, Hk, hk, 0, L, kbuf(0));
-    ld.issue(a.v, tok0, Hk, hk, 0, L, vbuf(0));
+    ldk.issue(a.k, tok0, Hk, hk, 0, L, kbuf(0), kbuf2(0));
+    ldv.issue(a.v, tok0, Hk, hk, 0, L, vbuf(0));
     if (nblocks > 1) {
-      ld.issue(a.k, tok0, Hk, hk, kBN, L, kbuf(1));
-      ld.issue(a.v, tok0, Hk, hk, kBN, L, vbuf(1));
+      ldk.issue(a.k, tok0, Hk, hk, kBN, L, kbuf(1), kbuf2(1));
+      ldv.issue(a.v, tok0, Hk, hk, kBN, L, vbuf(1));
     }
     // The two halves run separate loops that meet at the same barriers.
     if (half == 0) {
@@ -570,7 +678,7 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
         interval_start(it);
         const bool cur = it < nblocks && wr.useful(it, CAUSAL);
         __builtin_amdgcn_s_setprio(kMatrixPrio);
-        if (cur) qk_step<D>(st, la, kbuf(it));
+        if (cur) qk_step<D>(st, la, kbuf(it), kbuf2(it));
         __builtin_amdgcn_sched_barrier(0);
         if (it > 0 && wr.useful(it - 1, CAUSAL)) pv_step<D>(st, la, vbuf(it - 1));
         __builtin_amdgcn_s_setprio(0);
@@ -582,19 +690,20 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
         const bool prev = it > 0 && wr.useful(it - 1, CAUSAL);
         softmax_phase(prev, it - 1, it);
         __builtin_amdgcn_s_setprio(kMatrixPrio);
-        if (it < nblocks && wr.useful(it, CAUSAL)) qk_step<D>(st, la, kbuf(it));
+        if (it < nblocks && wr.useful(it, CAUSAL)) qk_step<D>(st, la, kbuf(it), kbuf2(it));
         __builtin_amdgcn_sched_barrier(0);
         if (prev) pv_step<D>(st, la, vbuf(it - 1));
         __builtin_amdgcn_s_setprio(0);
       }
     }
   } else {
+    static_assert(D == DV, "the serial path keeps K and V blocks of one size");
     char LDS_AS *kb0 = lds;
-    char LDS_AS *vb0 = lds + C::BLOCK_BYTES;
-    char LDS_AS *kb1 = lds + 2 * C::BLOCK_BYTES;
-    char LDS_AS *vb1 = lds + 3 * C::BLOCK_BYTES;
-    ld.issue(a.k, tok0, Hk, hk, 0, L, kb0);
-    ld.issue(a.v, tok0, Hk, hk, 0, L, vb0);
+    char LDS_AS *vb0 = lds + C::K_BYTES;
+    char LDS_AS *kb1 = lds + 2 * C::K_BYTES;
+    char LDS_AS *vb1 = lds + 3 * C::K_BYTES;
+    ldk.issue(a.k, tok0, Hk, hk, 0, L, kb0);
+    ldv.issue(a.v, tok0, Hk, hk, 0, L, vb0);
     for (int j = 0; j < nblocks; ++j) {
       const int n0 = j * kBN;
       char LDS_AS *kcur = (j & 1) ? kb1 : kb0;
@@ -602,15 +711,15 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       if (j + 1 < nblocks) {
         char LDS_AS *knext = (j & 1) ? kb0 : kb1;
         char LDS_AS *vnext = (j & 1) ? vb0 : vb1;
-        ld.issue(a.k, tok0, Hk, hk, n0 + kBN, L, knext);
-        ld.issue(a.v, tok0, Hk, hk, n0 + kBN, L, vnext);
-        wait_vmcnt<2 * C::LOADS>();
+        ldk.issue(a.k, tok0, Hk, hk, n0 + kBN, L, knext);
+        ldv.issue(a.v, tok0, Hk, hk, n0 + kBN, L, vnext);
+        wait_vmcnt<LOADS_BLOCK>();
       } else {
         wait_vmcnt<0>();
       }
       barrier_nofence();
       if (wr.useful(j, CAUSAL)) {
-        qk_step<D>(st, la, kcur);
+        qk_step<D>(st, la, kcur, kcur);
         softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, n0, row, L, wr.need_mask(j, L, CAUSAL),
                                             j == wr.last_block, a, [](int) {});
         pv_step<D>(st, la, vcur);
@@ -625,9 +734,9 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   if (row < L) {
     const float inv = 1.0f / l32;
     const int hh = lane >> 5;
-    __bf16 *op = a.o + ((tok0 + row) * H + h) * (long long)D + 4 * hh;
+    __bf16 *op = a.o + ((tok0 + row) * H + h) * (long long)DV + 4 * hh;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < DV / 32; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -644,7 +753,9 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
 }
 
 template <int D>
-constexpr int lds_bytes() { return (Cfg<D>::PINGPONG ? 8 : 4) * Cfg<D>::BLOCK_BYTES; }
+constexpr int lds_bytes() {
+  return Cfg<D>::PINGPONG ? KvLayout<D>::BYTES : 4 * Cfg<D>::K_BYTES;
+}
 
 // Persistent kernel: each workgroup walks its static LPT list.
 template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>
@@ -728,12 +839,18 @@ int current_device(DeviceInfo **out) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Supported (q/k, v/o) head-dimension pairs; the kernel instance is named by
+// the q/k dimension.
+bool supported_dims(int D, int Dv) {
+  return (D == Dv && (D == 64 || D == 128 || D == 256)) || (D == 192 && Dv == 128);
+}
+
 int validate(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-             int Hkv, int S, int D, float scale, int causal, const fa_tuning *t) {
+             int Hkv, int S, int D, int Dv, float scale, int causal, const fa_tuning *t) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID_ARG;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return FA_ERR_INVALID_ARG;
-  if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || S <= 0 || D <= 0 || Dv <= 0) return FA_ERR_INVALID_ARG;
   if (Hkv <= 0 || H % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
@@ -742,7 +859,7 @@ int validate(const void *q, const void *k, const void *v, void *o, float *lse, i
     if (t->exp2_emu != 0 && t->exp2_emu != 4 && t->exp2_emu != 8) return FA_ERR_INVALID_ARG;
     if (t->schedule != 0 && t->schedule != 1) return FA_ERR_INVALID_ARG;
   }
-  if (D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  if (!supported_dims(D, Dv)) return FA_ERR_UNSUPPORTED;
   // sizes must fit the 32-bit index arithmetic used for rows and tiles
   if ((long long)B * S > (1LL << 31) - 1 || (long long)S * H > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
   return FA_OK;
@@ -813,6 +930,7 @@ int bm_for(int D) {
   switch (D) {
     case 64: return bm_of<64>();
     case 128: return bm_of<128>();
+    case 192: return bm_of<192>();
     default: return bm_of<256>();
   }
 }
@@ -830,11 +948,11 @@ fa_tuning fa_tuning_default(void) {
   return t;
 }
 
-int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-               int H_kv, int S, int D, float scale, int causal, const int *cu_seqlens,
-               void *stream, const fa_tuning *tuning) {
+int fa_fwd_hd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+              int H_kv, int S, int D, int D_v, float scale, int causal, const int *cu_seqlens,
+              void *stream, const fa_tuning *tuning) {
   const fa_tuning t = tuning ? *tuning : fa_tuning_default();
-  int rc = validate(q, k, v, o, lse, B, H, H_kv, S, D, scale, causal, &t);
+  int rc = validate(q, k, v, o, lse, B, H, H_kv, S, D, D_v, scale, causal, &t);
   if (rc != FA_OK) return rc;
   DeviceInfo *dev = nullptr;
   rc = current_device(&dev);
@@ -859,8 +977,16 @@ int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
   switch (D) {
     case 64: return dispatch_d<64>(a, causal, varlen, t, dev->cus, st);
     case 128: return dispatch_d<128>(a, causal, varlen, t, dev->cus, st);
+    case 192: return dispatch_d<192>(a, causal, varlen, t, dev->cus, st);
     default: return dispatch_d<256>(a, causal, varlen, t, dev->cus, st);
   }
+}
+
+int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+               int H_kv, int S, int D, float scale, int causal, const int *cu_seqlens,
+               void *stream, const fa_tuning *tuning) {
+  return fa_fwd_hd(q, k, v, o, lse, B, H, H_kv, S, D, D, scale, causal, cu_seqlens, stream,
+                   tuning);
 }
 
 int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
@@ -899,7 +1025,7 @@ int fa_schedule_gqa(int B, int H, int H_kv, int S, int D, int causal, const int 
   if (B <= 0 || H <= 0 || S <= 0 || workers <= 0 || !tiles || max_rounds <= 0) return FA_ERR_INVALID_ARG;
   if (H_kv <= 0 || H % H_kv != 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-  if (D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128 && D != 192 && D != 256) return FA_ERR_UNSUPPORTED;
   const int BM = bm_for(D);
   const bool varlen = cu_seqlens != nullptr;
   fa::Sched s = fa::make_sched(B, H, H_kv, S, BM, causal, varlen, workers);
@@ -938,11 +1064,11 @@ int fa_schedule_gqa(int B, int H, int H_kv, int S, int D, int causal, const int 
 
 int fa_num_workers(int D, int *workers_out) {
   if (!workers_out) return FA_ERR_INVALID_ARG;
-  if (D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128 && D != 192 && D != 256) return FA_ERR_UNSUPPORTED;
   DeviceInfo *dev = nullptr;
   int rc = current_device(&dev);
   if (rc != FA_OK) return rc;
-  *workers_out = dev->cus * (D == 256 ? Cfg<256>::OCC : (D == 128 ? Cfg<128>::OCC : Cfg<64>::OCC));
+  *workers_out = dev->cus * (D == 256 ? Cfg<256>::OCC : Cfg<128>::OCC);  // OCC = 1 for every D
   return FA_OK;
 }
 
@@ -957,6 +1083,6 @@ const char *fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 101; }
+int fa_version(void) { return 102; }
 
 }  // extern "C"

@@ -135,6 +135,22 @@ int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
                const int *cu_seqlens, void *stream, const fa_tuning *tuning);
 
 /*
+ * fa_fwd_hd -- fa_fwd_gqa with separate q/k and v/o head dimensions.
+ *
+ * q and k rows have D entries, v and o rows D_v entries:
+ *   dense  q [B,S,H,D], k [B,S,H_kv,D], v [B,S,H_kv,D_v], o [B,S,H,D_v]
+ *   varlen q [T,H,D],   k [T,H_kv,D],   v [T,H_kv,D_v],   o [T,H,D_v]
+ * The scores use D (scale is typically 1/sqrt(D)); the output has D_v
+ * columns.  Supported pairs: D = D_v in {64, 128, 256}, and (D, D_v) =
+ * (192, 128), the DeepSeek V3 shape the FlashAttention-4 paper benchmarks
+ * (section 5.1); anything else is FA_ERR_UNSUPPORTED.  fa_fwd_gqa is the
+ * D_v = D case.
+ */
+int fa_fwd_hd(const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int H, int H_kv, int S, int D, int D_v, float scale, int causal,
+              const int *cu_seqlens, void *stream, const fa_tuning *tuning);
+
+/*
  * fa_exp2_emu -- test hook: y[i] = the device's polynomial 2^x[i] for n
  * floats (device pointers, 4-byte aligned).  The function is the one the
  * attention kernel uses for its emulated exponentials: Cody-Waite
@@ -153,7 +169,8 @@ int fa_exp2_emu(const float *x, float *y, long long n, void *stream);
  * processes in its round r, or -1 when it has no more work, for a launch of
  * `workers` workgroups.  A tile is encoded as
  *   ((seq * H + head) * n_mblocks_max + mblock)
- * with n_mblocks_max = ceil(S / BM) and BM the row-tile height chosen for D.
+ * with n_mblocks_max = ceil(S / BM) and BM the row-tile height chosen for D
+ * (the q/k head dimension: 64, 128, 192 or 256).
  * cu_seqlens, if not NULL, is a HOST int32 array of B+1 entries.  *rounds_out
  * receives the number of rounds used and *bm_out the BM used.  Returns
  * FA_ERR_INVALID_ARG when max_rounds is too small or an argument is invalid.
@@ -178,7 +195,7 @@ int fa_num_workers(int D, int *workers_out);
 /* Human-readable name of an fa_status value (static string, never NULL). */
 const char *fa_status_string(int status);
 
-/* Library ABI version: 100 * major + minor (101: fa_fwd_gqa added). */
+/* Library ABI version: 100 * major + minor (101: fa_fwd_gqa; 102: fa_fwd_hd). */
 int fa_version(void);
 
 #ifdef __cplusplus

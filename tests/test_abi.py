@@ -93,6 +93,22 @@ def test_gqa_head_validation(H, H_kv, expect):
     assert rc == expect
 
 
+@pytest.mark.parametrize("D,D_v,expect", [
+    (192, 192, fa.FA_ERR_UNSUPPORTED),
+    (128, 64, fa.FA_ERR_UNSUPPORTED),
+    (256, 128, fa.FA_ERR_UNSUPPORTED),
+    (192, 0, fa.FA_ERR_INVALID_ARG),
+])
+def test_head_dim_pair_validation(D, D_v, expect):
+    lib = fa.load()
+    rc = lib.fa_fwd_hd(A, A, A, A, A, 1, 2, 2, 8, D, D_v, 0.1, 1, None, None, None)
+    assert rc == expect
+
+
+def test_fa_fwd_rejects_d192_without_a_value_dimension():
+    assert call(D=192) == fa.FA_ERR_UNSUPPORTED
+
+
 def test_valid_call_without_gpu_reports_no_device():
     import torch
     if torch.cuda.is_available():
@@ -101,6 +117,8 @@ def test_valid_call_without_gpu_reports_no_device():
     assert fa.load().fa_exp2_emu(A, A, 16, None) == fa.FA_ERR_NO_DEVICE
     assert fa.load().fa_fwd_gqa(A, A, A, A, A, 1, 8, 2, 8, 128, 0.1, 1, None, None,
                                 None) == fa.FA_ERR_NO_DEVICE
+    assert fa.load().fa_fwd_hd(A, A, A, A, A, 1, 8, 2, 8, 192, 128, 0.1, 1, None, None,
+                               None) == fa.FA_ERR_NO_DEVICE
 
 
 def test_exp2_emu_argument_checks():

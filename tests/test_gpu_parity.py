@@ -132,6 +132,7 @@ def gather_rows(o, lse, rows, w, cu):
     ("varlen_16x512to8192_h32d128_causal", 512),
     ("wide_b2h16s8192d256_spread3", 512),
     ("gqa_b2h32kv8s8192d128_causal", 512),
+    ("hd192v128_b2h16s8192_causal", 512),
 ])
 def test_named_sampled(name, n):
     w = WORKLOADS[name]
@@ -163,7 +164,7 @@ def _cell_distance_t(o_bf16, ref):
 
 @pytest.mark.parametrize("name", ["wide_b2h16s8192d256_spread3", "causal_b2h16s8192d128",
                                   "dense_b2h16s2048d128", "dense_b2h16s2048d128_causal",
-                                  "gqa_b2h32kv8s8192d128_causal"])
+                                  "gqa_b2h32kv8s8192d128_causal", "hd192v128_b2h16s8192_causal"])
 def test_all_outputs_vs_fp32_reference(name):
     w = WORKLOADS[name]
     q, k, v, cu, S = make(w)
@@ -241,6 +242,45 @@ def test_gqa_equals_mha_on_repeated_kv():
     o1, l1 = run_gpu(q, k, v, True, 0.1, cu, max(lens))
     o2, l2 = run_gpu(q, kr, vr, True, 0.1, cu, max(lens))
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---- separate value head dimension: (D, D_v) = (192, 128)
+
+HD_SMALL = [
+    # (B, S, H, H_kv, D, D_v)
+    (2, 700, 3, 3, 192, 128),
+    (1, 513, 4, 2, 192, 128),
+    (1, 65, 2, 1, 192, 128),
+]
+
+
+@pytest.mark.parametrize("shape", HD_SMALL, ids=lambda s: "B%dS%dH%dKV%dD%dV%d" % s)
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dims_192_128_small_full(shape, causal):
+    B, S, H, Hkv, D, Dv = shape
+    q, k, v = draw_qkv((B, S, H, D), seed=300 + S, kv_heads=Hkv, v_dim=Dv)
+    o, _ = full_check(q, k, v, causal, 1.0 / math.sqrt(D), what="hd-small")
+    assert tuple(o.shape) == (B, S, H, Dv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dims_192_128_varlen_small_full(causal):
+    lens = [1, 0, 300, 64, 65, 777, 2]
+    cu = cu_seqlens_of(lens)
+    q, k, v = draw_qkv((int(cu[-1]), 2, 192), seed=311, v_dim=128)
+    full_check(q, k, v, causal, 1.0 / math.sqrt(192), cu=cu, S=max(lens), what="hd-varlen")
+
+
+def test_head_dims_192_128_value_columns_independent():
+    """Each output column is the same weighted sum of one V column wherever
+    that column sits: reversing the order of V's columns reverses O's columns
+    bit for bit, and leaves the LSE (which V does not enter) unchanged."""
+    q, k, v = draw_qkv((1, 900, 2, 192), seed=321, v_dim=128)
+    o1, l1 = run_gpu(q, k, v, True, 0.07)
+    v2 = torch.flip(v, dims=[-1]).contiguous()     # permuted value columns
+    o2, l2 = run_gpu(q, k, v2, True, 0.07)
+    assert torch.equal(l1, l2)
+    assert torch.equal(torch.flip(o2, dims=[-1]), o1)
 
 
 # ---- invariances

@@ -43,6 +43,7 @@ CASES = [
     (1, 16, 32768, 128, True, None, 256),
     (2, 16, 8192, 128, True, None, 256),
     (2, 16, 8192, 256, False, None, 256),
+    (2, 16, 8192, 192, True, None, 256),     # (192, 128) head dimensions
     (1, 8, 512, 64, True, None, 256),
     (1, 2, 128, 64, False, None, 256),
     (3, 5, 1000, 128, True, None, 256),      # H not a multiple of 8

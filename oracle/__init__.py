@@ -57,27 +57,32 @@ def _cu(cu_seqlens):
     return np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
 
 
-def _dims(q_shape, cu):
-    """(B, S, H, D) from a dense [B,S,H,D] shape, or varlen [T,H,D] + cu_seqlens."""
-    if cu is None:
-        B, S, H, D = q_shape
-        return B, S, H, D
-    _, H, D = q_shape
-    B = len(cu) - 1
-    S = int(np.max(np.diff(cu))) if B > 0 else 0
-    return B, S, H, D
+def _maxlen(cu) -> int:
+    return int(np.max(np.diff(cu))) if len(cu) > 1 else 0
 
 
-def _kv_heads(k_shape, cu):
-    """Number of K/V heads: axis 2 of a dense [B,S,Hkv,D] K, axis 1 of varlen [T,Hkv,D]."""
-    return k_shape[2] if cu is None else k_shape[1]
+def _layout(q_shape, k_shape, v_shape, cu_q, cu_k):
+    """Sizes (B, H, Hkv, Sq, Sk, D, Dv) of a call.
+
+    dense : q [B,Sq,H,D], k [B,Sk,Hkv,D], v [B,Sk,Hkv,Dv]
+    varlen: q [Tq,H,D], k [Tk,Hkv,D], v [Tk,Hkv,Dv]; Sq, Sk the longest lengths
+    """
+    if cu_q is None:
+        B, Sq, H, D = q_shape
+        Sk, Hkv = k_shape[1], k_shape[2]
+    else:
+        _, H, D = q_shape
+        Hkv = k_shape[1]
+        B = len(cu_q) - 1
+        Sq, Sk = _maxlen(cu_q), _maxlen(cu_k)
+    return B, H, Hkv, Sq, Sk, D, v_shape[-1]
 
 
-def _shapes(B, S, H, Dv, cu):
-    """Shapes of o (head dimension Dv, the v dimension) and lse."""
-    if cu is None:
-        return (B, S, H, Dv), (B, H, S)
-    T = int(cu[-1])
+def _out_shapes(B, H, Sq, Dv, cu_q):
+    """Shapes of o (Dv columns) and lse."""
+    if cu_q is None:
+        return (B, Sq, H, Dv), (B, H, Sq)
+    T = int(cu_q[-1])
     return (T, H, Dv), (H, T)
 
 
@@ -88,12 +93,10 @@ class OracleLib:
         lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
-        lib.oracle_attn_fwd_f64.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, f64,
-                                            i32, P]
-        lib.oracle_attn_fwd_bf16.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, f64,
-                                             i32, P]
-        lib.oracle_attn_rows_bf16.argtypes = [P, P, P, P, i64, P, P, i32, i32, i32, i32, i32,
-                                              i32, f64, i32, P]
+        dims = [i32] * 7  # B, H, Hkv, Sq, Sk, D, Dv
+        lib.oracle_attn_fwd_f64.argtypes = [P, P, P, P, P] + dims + [f64, i32, P, P]
+        lib.oracle_attn_fwd_bf16.argtypes = [P, P, P, P, P] + dims + [f64, i32, P, P]
+        lib.oracle_attn_rows_bf16.argtypes = [P, P, P, P, i64, P, P] + dims + [f64, i32, P, P]
         for fn in (lib.oracle_attn_fwd_f64, lib.oracle_attn_fwd_bf16, lib.oracle_attn_rows_bf16):
             fn.restype = i32
         lib.oracle_exp2.argtypes = [P, P, i64]
@@ -105,65 +108,62 @@ class OracleLib:
         self.lib = lib
         self.path = path
 
-    def attention_f64(self, q, k, v, scale, causal, cu_seqlens=None):
-        """Attention on float64 inputs; q is [B,S,H,D] (or [T,H,D] varlen), k and v
-        have the same layout with Hkv heads (Hkv divides H; Hkv = H is plain MHA);
-        v may have its own head dimension Dv.
+    def attention_f64(self, q, k, v, scale, causal, cu_seqlens=None, cu_seqlens_k=None):
+        """Attention on float64 inputs.
 
-        Returns (o float64 [..., Dv] like q, lse float64 [B,H,S] or [H,T]).
+        q is [B,Sq,H,D] (or [T,H,D] varlen); k has the same layout with Hkv
+        heads (Hkv divides H) and its own length; v is k with Dv columns.
+        cu_seqlens are the varlen query offsets and cu_seqlens_k the key
+        offsets (default: the same).  Causal masking is aligned to the
+        bottom-right corner.  Returns (o float64 like q with Dv columns, lse
+        float64 [B,H,Sq] or [H,T]).
         """
         q = np.ascontiguousarray(q, dtype=np.float64)
         k = np.ascontiguousarray(k, dtype=np.float64)
         v = np.ascontiguousarray(v, dtype=np.float64)
-        cu = _cu(cu_seqlens)
-        B, S, H, D = _dims(q.shape, cu)
-        Dv = v.shape[-1]
-        o_shape, l_shape = _shapes(B, S, H, Dv, cu)
-        o = np.empty(o_shape, np.float64)
-        lse = np.empty(l_shape, np.float64)
-        rc = self.lib.oracle_attn_fwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                          B, H, _kv_heads(k.shape, cu), S, D, Dv, float(scale),
-                                          int(bool(causal)), _ptr(cu))
-        if rc != 0:
-            raise ValueError("oracle_attn_fwd_f64 rejected its arguments")
-        return o, lse
+        return self._run(self.lib.oracle_attn_fwd_f64, q, k, v, scale, causal, cu_seqlens,
+                         cu_seqlens_k, "oracle_attn_fwd_f64")
 
-    def attention_bf16(self, q, k, v, scale, causal, cu_seqlens=None):
+    def attention_bf16(self, q, k, v, scale, causal, cu_seqlens=None, cu_seqlens_k=None):
         """Attention on bf16 inputs (torch bf16 CPU tensors or uint16 bit arrays).
 
         Shapes as in attention_f64; the result is float64.
         """
         qb, kb, vb = _as_bits(q), _as_bits(k), _as_bits(v)
-        cu = _cu(cu_seqlens)
-        B, S, H, D = _dims(qb.shape, cu)
-        Dv = vb.shape[-1]
-        o_shape, l_shape = _shapes(B, S, H, Dv, cu)
+        return self._run(self.lib.oracle_attn_fwd_bf16, qb, kb, vb, scale, causal, cu_seqlens,
+                         cu_seqlens_k, "oracle_attn_fwd_bf16")
+
+    def _run(self, fn, q, k, v, scale, causal, cu_seqlens, cu_seqlens_k, name):
+        cu_q = _cu(cu_seqlens)
+        cu_k = _cu(cu_seqlens_k) if cu_seqlens_k is not None else cu_q
+        B, H, Hkv, Sq, Sk, D, Dv = _layout(q.shape, k.shape, v.shape, cu_q, cu_k)
+        o_shape, l_shape = _out_shapes(B, H, Sq, Dv, cu_q)
         o = np.empty(o_shape, np.float64)
         lse = np.empty(l_shape, np.float64)
-        rc = self.lib.oracle_attn_fwd_bf16(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(o), _ptr(lse),
-                                           B, H, _kv_heads(kb.shape, cu), S, D, Dv, float(scale),
-                                           int(bool(causal)), _ptr(cu))
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Sq, Sk, D, Dv,
+                float(scale), int(bool(causal)), _ptr(cu_q), _ptr(cu_k))
         if rc != 0:
-            raise ValueError("oracle_attn_fwd_bf16 rejected its arguments")
+            raise ValueError(name + " rejected its arguments")
         return o, lse
 
-    def attention_rows_bf16(self, q, k, v, rows, scale, causal, cu_seqlens=None):
+    def attention_rows_bf16(self, q, k, v, rows, scale, causal, cu_seqlens=None,
+                            cu_seqlens_k=None):
         """Attention for selected rows only.
 
-        rows are numbered like the lse layout: dense (b*H + h)*S + i, varlen
-        h*T + t.  Returns (o_rows float64 [n, D], lse_rows float64 [n]).
+        rows are numbered like the lse layout: dense (b*H + h)*Sq + i, varlen
+        h*Tq + t.  Returns (o_rows float64 [n, Dv], lse_rows float64 [n]).
         """
         qb, kb, vb = _as_bits(q), _as_bits(k), _as_bits(v)
-        cu = _cu(cu_seqlens)
-        B, S, H, D = _dims(qb.shape, cu)
-        Dv = vb.shape[-1]
+        cu_q = _cu(cu_seqlens)
+        cu_k = _cu(cu_seqlens_k) if cu_seqlens_k is not None else cu_q
+        B, H, Hkv, Sq, Sk, D, Dv = _layout(qb.shape, kb.shape, vb.shape, cu_q, cu_k)
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
         o = np.empty((len(rows), Dv), np.float64)
         lse = np.empty(len(rows), np.float64)
         rc = self.lib.oracle_attn_rows_bf16(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(rows),
-                                            len(rows), _ptr(o), _ptr(lse), B, H,
-                                            _kv_heads(kb.shape, cu), S, D, Dv,
-                                            float(scale), int(bool(causal)), _ptr(cu))
+                                            len(rows), _ptr(o), _ptr(lse), B, H, Hkv, Sq, Sk,
+                                            D, Dv, float(scale), int(bool(causal)),
+                                            _ptr(cu_q), _ptr(cu_k))
         if rc != 0:
             raise ValueError("oracle_attn_rows_bf16 rejected its arguments")
         return o, lse

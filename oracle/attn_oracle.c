@@ -21,11 +21,16 @@
  * no blocking, no online rescaling, no reordering beyond that.
  *
  * Layouts (row-major, contiguous):
- *   dense : q, o are [B, S, H, D]; k, v are [B, S, Hkv, D]; lse is [B, H, S]
- *   varlen: q, o are [T, H, D], k, v are [T, Hkv, D] with T = cu_seqlens[B];
- *           lse is [H, T]; sequence b owns tokens cu_seqlens[b] ..
- *           cu_seqlens[b+1]-1 and attends only within itself (query and key
- *           lengths are equal).
+ *   dense : q, o are [B, Sq, H, D]; k, v are [B, Sk, Hkv, D]; lse is [B, H, Sq]
+ *   varlen: q, o are [Tq, H, D] with Tq = cu_q[B]; k, v are [Tk, Hkv, D] with
+ *           Tk = cu_k[B]; lse is [H, Tq].  Sequence b owns query tokens
+ *           cu_q[b] .. cu_q[b+1]-1 and key tokens cu_k[b] .. cu_k[b+1]-1 and
+ *           attends only within itself.
+ * Query and key lengths may differ (Lq, Lk).  The causal mask is aligned to
+ * the bottom-right corner: query i may use key j when j <= i + Lk - Lq, so
+ * the last query sees every key (for Lq = Lk this is the plain j <= i).  A
+ * row that may use no key (Lq > Lk, i < Lq - Lk) has output 0 and LSE -inf
+ * (the empty sum).
  * Grouped-query attention (the paper's section 3.3 reports LPT results for
  * MQA): Hkv divides H and query head h reads K/V head h / (H / Hkv), i.e.
  * each run of H/Hkv consecutive query heads shares one K/V head.  Hkv = H is
@@ -72,24 +77,41 @@ typedef struct {
     int len;
 } seq_span;
 
+/* Sizes of one call.  cu_q / cu_k are NULL for dense inputs. */
+typedef struct {
+    int B, H, Hkv, Sq, Sk, D, Dv;
+    const int *cu_q, *cu_k;
+} attn_shape;
+
 /*
  * One query row i of one (sequence, head): two passes over the allowed keys.
- * s must hold at least len doubles.  Writes D outputs to o_row and the
+ * s must hold at least spk.len doubles.  Writes Dv outputs to o_row and the
  * row's logsumexp to *lse_out.
  */
 static void attend_one_row(tensor_in q, tensor_in k, tensor_in v,
                            double *o_row, double *lse_out,
-                           seq_span sp, int i, int h, int H, int Hkv, int D, int Dv,
+                           seq_span spq, seq_span spk, int i, int h, const attn_shape *sh,
                            double scale, int causal, double *s)
 {
-    const int nkeys = causal ? i + 1 : sp.len;
-    const int64_t qbase = ((sp.tok0 + i) * H + h) * (int64_t)D;
+    const int H = sh->H, Hkv = sh->Hkv, D = sh->D, Dv = sh->Dv;
+    int nkeys = spk.len;
+    if (causal) {
+        const int last = i + spk.len - spq.len;  /* bottom-right alignment */
+        nkeys = last + 1 < 0 ? 0 : (last + 1 < spk.len ? last + 1 : spk.len);
+    }
+    const int64_t qbase = ((spq.tok0 + i) * H + h) * (int64_t)D;
     const int hk = h / (H / Hkv);  /* the K/V head of query head h */
+    if (nkeys == 0) {
+        for (int d = 0; d < Dv; ++d)
+            o_row[d] = 0.0;
+        *lse_out = -INFINITY;
+        return;
+    }
 
     /* pass 1: scores and their maximum */
     double m = -INFINITY;
     for (int j = 0; j < nkeys; ++j) {
-        const int64_t kbase = ((sp.tok0 + j) * Hkv + hk) * (int64_t)D;
+        const int64_t kbase = ((spk.tok0 + j) * Hkv + hk) * (int64_t)D;
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
             dot += at(q, qbase + d) * at(k, kbase + d);
@@ -107,19 +129,19 @@ static void attend_one_row(tensor_in q, tensor_in k, tensor_in v,
     for (int d = 0; d < Dv; ++d) {
         double acc = 0.0;
         for (int j = 0; j < nkeys; ++j)
-            acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)Dv + d);
+            acc += s[j] * at(v, ((spk.tok0 + j) * Hkv + hk) * (int64_t)Dv + d);
         o_row[d] = acc / l;
     }
     *lse_out = m + log(l);
 }
 
-/* Span of sequence b: dense uses b*S .. b*S+S-1, varlen reads cu_seqlens. */
-static seq_span span_of(int b, int S, const int *cu_seqlens)
+/* Span of sequence b: dense uses b*S .. b*S+S-1, varlen reads cu. */
+static seq_span span_of(int b, int S, const int *cu)
 {
     seq_span sp;
-    if (cu_seqlens) {
-        sp.tok0 = cu_seqlens[b];
-        sp.len = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (cu) {
+        sp.tok0 = cu[b];
+        sp.len = cu[b + 1] - cu[b];
     } else {
         sp.tok0 = (int64_t)b * S;
         sp.len = S;
@@ -129,55 +151,67 @@ static seq_span span_of(int b, int S, const int *cu_seqlens)
 
 /*
  * Map a row id, numbered like the lse layout, to (b, h, i).
- *   dense : row = (b*H + h)*S + i
- *   varlen: row = h*T + t, t a global token index; b is the sequence holding t
+ *   dense : row = (b*H + h)*Sq + i
+ *   varlen: row = h*Tq + t, t a global query token index; b the sequence holding t
  */
-static void decode_row(int64_t row, int B, int H, int S, const int *cu_seqlens,
-                       int *b, int *h, int *i)
+static void decode_row(int64_t row, const attn_shape *sh, int *b, int *h, int *i)
 {
-    if (!cu_seqlens) {
+    const int B = sh->B, H = sh->H, S = sh->Sq;
+    const int *cu = sh->cu_q;
+    if (!cu) {
         *i = (int)(row % S);
         *h = (int)((row / S) % H);
         *b = (int)(row / ((int64_t)S * H));
         return;
     }
-    const int64_t T = cu_seqlens[B];
+    const int64_t T = cu[B];
     const int64_t t = row % T;
     *h = (int)(row / T);
     int bb = 0;
-    while (bb + 1 < B && cu_seqlens[bb + 1] <= t)
+    while (bb + 1 < B && cu[bb + 1] <= t)
         ++bb;
     *b = bb;
-    *i = (int)(t - cu_seqlens[bb]);
+    *i = (int)(t - cu[bb]);
 }
 
-static int max_len(int B, int S, const int *cu_seqlens)
+static int max_len(int B, int S, const int *cu)
 {
-    if (!cu_seqlens)
+    if (!cu)
         return S;
     int mx = 0;
     for (int b = 0; b < B; ++b) {
-        int L = cu_seqlens[b + 1] - cu_seqlens[b];
+        int L = cu[b + 1] - cu[b];
         if (L > mx)
             mx = L;
     }
     return mx;
 }
 
+static int shape_ok(const attn_shape *sh)
+{
+    if (sh->B <= 0 || sh->H <= 0 || sh->Hkv <= 0 || sh->H % sh->Hkv != 0 || sh->D <= 0 ||
+        sh->Dv <= 0)
+        return 0;
+    if ((sh->cu_q == NULL) != (sh->cu_k == NULL))
+        return 0;
+    if (!sh->cu_q && (sh->Sq <= 0 || sh->Sk <= 0))
+        return 0;
+    return 1;
+}
+
 /*
- * Attention for an explicit list of rows.  o_rows is [n_rows, D] and
+ * Attention for an explicit list of rows.  o_rows is [n_rows, Dv] and
  * lse_rows is [n_rows]; either may be NULL.  Returns 0, or -1 on bad input.
  */
 static int attend_rows(tensor_in q, tensor_in k, tensor_in v,
                        const int64_t *rows, int64_t n_rows,
                        double *o_rows, double *lse_rows,
-                       int B, int H, int Hkv, int S, int D, int Dv, double scale, int causal,
-                       const int *cu_seqlens)
+                       const attn_shape *sh, double scale, int causal)
 {
-    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || D <= 0 || Dv <= 0 ||
-        (!cu_seqlens && S <= 0))
+    if (!shape_ok(sh))
         return -1;
-    const int Lmax = max_len(B, S, cu_seqlens);
+    const int Lmax = max_len(sh->B, sh->Sk, sh->cu_k);
+    const int Dv = sh->Dv;
     int bad = 0;
 #pragma omp parallel
     {
@@ -190,10 +224,11 @@ static int attend_rows(tensor_in q, tensor_in k, tensor_in v,
 #pragma omp for schedule(dynamic, 8)
             for (int64_t r = 0; r < n_rows; ++r) {
                 int b, h, i;
-                decode_row(rows[r], B, H, S, cu_seqlens, &b, &h, &i);
-                seq_span sp = span_of(b, S, cu_seqlens);
+                decode_row(rows[r], sh, &b, &h, &i);
+                seq_span spq = span_of(b, sh->Sq, sh->cu_q);
+                seq_span spk = span_of(b, sh->Sk, sh->cu_k);
                 double lse;
-                attend_one_row(q, k, v, o_tmp, &lse, sp, i, h, H, Hkv, D, Dv, scale, causal, s);
+                attend_one_row(q, k, v, o_tmp, &lse, spq, spk, i, h, sh, scale, causal, s);
                 if (o_rows)
                     memcpy(o_rows + r * (int64_t)Dv, o_tmp, sizeof(double) * (size_t)Dv);
                 if (lse_rows)
@@ -207,17 +242,16 @@ static int attend_rows(tensor_in q, tensor_in k, tensor_in v,
 }
 
 /*
- * Full attention: o in the q layout, lse in the lse layout (either may be
- * NULL).  Every row of every (sequence, head) is computed.
+ * Full attention: o in the q layout (with Dv columns), lse in the lse layout
+ * (either may be NULL).  Every row of every (sequence, head) is computed.
  */
 static int attend_all(tensor_in q, tensor_in k, tensor_in v, double *o, double *lse,
-                      int B, int H, int Hkv, int S, int D, int Dv, double scale, int causal,
-                      const int *cu_seqlens)
+                      const attn_shape *sh, double scale, int causal)
 {
-    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || D <= 0 || Dv <= 0 ||
-        (!cu_seqlens && S <= 0))
+    if (!shape_ok(sh))
         return -1;
-    const int64_t T = cu_seqlens ? cu_seqlens[B] : (int64_t)B * S;
+    const int H = sh->H, Dv = sh->Dv;
+    const int64_t T = sh->cu_q ? sh->cu_q[sh->B] : (int64_t)sh->B * sh->Sq;
     const int64_t n_rows = T * H;
     int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_rows > 0 ? n_rows : 1));
     double *o_rows = (double *)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1) * Dv);
@@ -230,15 +264,14 @@ static int attend_all(tensor_in q, tensor_in k, tensor_in v, double *o, double *
     }
     for (int64_t r = 0; r < n_rows; ++r)
         rows[r] = r;
-    int rc = attend_rows(q, k, v, rows, n_rows, o_rows, l_rows, B, H, Hkv, S, D, Dv, scale,
-                         causal, cu_seqlens);
+    int rc = attend_rows(q, k, v, rows, n_rows, o_rows, l_rows, sh, scale, causal);
     if (rc == 0) {
         for (int64_t r = 0; r < n_rows; ++r) {
             int b, h, i;
-            decode_row(r, B, H, S, cu_seqlens, &b, &h, &i);
-            seq_span sp = span_of(b, S, cu_seqlens);
+            decode_row(r, sh, &b, &h, &i);
+            seq_span spq = span_of(b, sh->Sq, sh->cu_q);
             if (o)
-                memcpy(o + ((sp.tok0 + i) * H + h) * (int64_t)Dv, o_rows + r * (int64_t)Dv,
+                memcpy(o + ((spq.tok0 + i) * H + h) * (int64_t)Dv, o_rows + r * (int64_t)Dv,
                        sizeof(double) * (size_t)Dv);
             if (lse)
                 lse[r] = l_rows[r];
@@ -252,33 +285,39 @@ static int attend_all(tensor_in q, tensor_in k, tensor_in v, double *o, double *
 
 /* ---- exported entry points (C ABI, loaded by ctypes from Python) ----
  * Hkv is the number of K/V heads (Hkv = H for multi-head attention); D is the
- * q/k head dimension and Dv the v/o head dimension. */
+ * q/k head dimension and Dv the v/o head dimension; Sq and Sk are the dense
+ * query and key lengths; cu_q and cu_k (both NULL for dense inputs) the
+ * varlen query and key offsets. */
 
 int oracle_attn_fwd_f64(const double *q, const double *k, const double *v,
-                        double *o, double *lse, int B, int H, int Hkv, int S, int D, int Dv,
-                        double scale, int causal, const int *cu_seqlens)
+                        double *o, double *lse, int B, int H, int Hkv, int Sq, int Sk,
+                        int D, int Dv, double scale, int causal, const int *cu_q,
+                        const int *cu_k)
 {
     tensor_in tq = {q, 0}, tk = {k, 0}, tv = {v, 0};
-    return attend_all(tq, tk, tv, o, lse, B, H, Hkv, S, D, Dv, scale, causal, cu_seqlens);
+    attn_shape sh = {B, H, Hkv, Sq, Sk, D, Dv, cu_q, cu_k};
+    return attend_all(tq, tk, tv, o, lse, &sh, scale, causal);
 }
 
 int oracle_attn_fwd_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                         double *o, double *lse, int B, int H, int Hkv, int S, int D, int Dv,
-                         double scale, int causal, const int *cu_seqlens)
+                         double *o, double *lse, int B, int H, int Hkv, int Sq, int Sk,
+                         int D, int Dv, double scale, int causal, const int *cu_q,
+                         const int *cu_k)
 {
     tensor_in tq = {q, 1}, tk = {k, 1}, tv = {v, 1};
-    return attend_all(tq, tk, tv, o, lse, B, H, Hkv, S, D, Dv, scale, causal, cu_seqlens);
+    attn_shape sh = {B, H, Hkv, Sq, Sk, D, Dv, cu_q, cu_k};
+    return attend_all(tq, tk, tv, o, lse, &sh, scale, causal);
 }
 
 int oracle_attn_rows_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                           const int64_t *rows, int64_t n_rows,
                           double *o_rows, double *lse_rows,
-                          int B, int H, int Hkv, int S, int D, int Dv, double scale, int causal,
-                          const int *cu_seqlens)
+                          int B, int H, int Hkv, int Sq, int Sk, int D, int Dv,
+                          double scale, int causal, const int *cu_q, const int *cu_k)
 {
     tensor_in tq = {q, 1}, tk = {k, 1}, tv = {v, 1};
-    return attend_rows(tq, tk, tv, rows, n_rows, o_rows, lse_rows, B, H, Hkv, S, D, Dv, scale,
-                       causal, cu_seqlens);
+    attn_shape sh = {B, H, Hkv, Sq, Sk, D, Dv, cu_q, cu_k};
+    return attend_rows(tq, tk, tv, rows, n_rows, o_rows, lse_rows, &sh, scale, causal);
 }
 
 /*

@@ -237,6 +237,61 @@ def check_value_columns_are_independent(o):
         assert np.array_equal(o1, o2[..., :Dv]) and np.array_equal(l1, l2), ("dv columns", causal)
 
 
+def check_qk_lengths_brute_force_tiny(o):
+    """Query and key lengths that differ (bottom-right causal alignment,
+    rows with no key) == the 50-digit brute force, dense and varlen."""
+    rng = np.random.default_rng(25)
+    for (Sq, Sk) in ((3, 7), (7, 4)):
+        for causal in (False, True):
+            q = _bf16_grid(rng, (2, Sq, 2, 3))
+            k, v = (_bf16_grid(rng, (2, Sk, 1, 3)) for _ in range(2))
+            got_o, got_l = o.attention_f64(q, k, v, 0.6, causal)
+            ref_o, ref_l = brute.attention(q, k, v, 0.6, causal)
+            assert np.max(np.abs(got_o - ref_o)) <= 1e-12, ("qk brute O", Sq, Sk, causal)
+            assert np.array_equal(np.isinf(got_l), np.isinf(ref_l)), ("qk brute empty", Sq, Sk)
+            fin = np.isfinite(ref_l)
+            assert np.max(np.abs(got_l[fin] - ref_l[fin])) <= 1e-12, ("qk brute LSE", Sq, Sk)
+    cu_q, cu_k = [0, 2, 5, 6, 6], [0, 4, 5, 9, 11]
+    q = _bf16_grid(rng, (6, 2, 4))
+    k, v = (_bf16_grid(rng, (11, 2, 4)) for _ in range(2))
+    for causal in (False, True):
+        got_o, got_l = o.attention_f64(q, k, v, 0.5, causal, cu_q, cu_k)
+        ref_o, ref_l = brute.attention(q, k, v, 0.5, causal, cu_q, cu_k)
+        assert np.max(np.abs(got_o - ref_o)) <= 1e-12, ("qk brute varlen O", causal)
+        fin = np.isfinite(ref_l)
+        assert np.array_equal(fin, np.isfinite(got_l)), "qk brute varlen empty"
+        assert np.max(np.abs(got_l[fin] - ref_l[fin])) <= 1e-12, ("qk brute varlen LSE", causal)
+
+
+def check_short_queries_are_the_last_rows_of_self_attention(o):
+    """Lq queries against Lk >= Lq keys (bottom-right causal) are exactly the
+    last Lq rows of self-attention over Lk queries that end with them (the
+    earlier queries are arbitrary), bit for bit; non-causal likewise."""
+    rng = np.random.default_rng(26)
+    Lk, Lq, H, D = 9, 3, 2, 4
+    k, v = (rng.standard_normal((1, Lk, H, D)) for _ in range(2))
+    qfull = rng.standard_normal((1, Lk, H, D))
+    for causal in (False, True):
+        o1, l1 = o.attention_f64(qfull[:, Lk - Lq:], k, v, 0.4, causal)
+        o2, l2 = o.attention_f64(qfull, k, v, 0.4, causal)
+        assert np.array_equal(o1, o2[:, Lk - Lq:]), ("suffix O", causal)
+        assert np.array_equal(l1, l2[:, :, Lk - Lq:]), ("suffix LSE", causal)
+
+
+def check_rows_without_keys(o):
+    """Causal with more queries than keys: the first Lq - Lk rows may use no
+    key and are O = 0, LSE = -inf exactly; the others attend normally."""
+    rng = np.random.default_rng(27)
+    Lq, Lk = 6, 2
+    q = rng.standard_normal((1, Lq, 1, 3))
+    k, v = (rng.standard_normal((1, Lk, 1, 3)) for _ in range(2))
+    got_o, got_l = o.attention_f64(q, k, v, 0.5, True)
+    assert np.all(got_o[0, :Lq - Lk] == 0.0) and np.all(got_l[0, 0, :Lq - Lk] == -np.inf)
+    assert np.all(np.isfinite(got_l[0, 0, Lq - Lk:]))
+    # row Lq-Lk sees exactly key 0: its output is v_0
+    assert np.array_equal(got_o[0, Lq - Lk, 0], v[0, 0, 0]), "first non-empty row"
+
+
 ALL_CHECKS = [
     check_brute_force_tiny,
     check_equal_logits_mean_of_v,
@@ -252,4 +307,7 @@ ALL_CHECKS = [
     check_gqa_equals_repeated_kv,
     check_value_dim_brute_force_tiny,
     check_value_columns_are_independent,
+    check_qk_lengths_brute_force_tiny,
+    check_short_queries_are_the_last_rows_of_self_attention,
+    check_rows_without_keys,
 ]

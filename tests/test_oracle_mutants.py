@@ -23,26 +23,31 @@ import oracle_pins  # noqa: E402
 
 # (name, text in attn_oracle.c, replacement)
 MUTANTS = [
-    ("mask_excludes_diagonal", "causal ? i + 1 : sp.len", "causal ? i : sp.len"),
-    ("mask_admits_next_key", "causal ? i + 1 : sp.len", "causal ? (i + 2 < sp.len ? i + 2 : sp.len) : sp.len"),
+    ("mask_excludes_diagonal", "const int last = i + spk.len - spq.len;",
+     "const int last = i + spk.len - spq.len - 1;"),
+    ("mask_admits_next_key", "const int last = i + spk.len - spq.len;",
+     "const int last = i + spk.len - spq.len + 1;"),
+    ("causal_top_left_alignment", "const int last = i + spk.len - spq.len;", "const int last = i;"),
+    ("empty_row_not_special", "if (nkeys == 0) {", "if (0) {"),
+    ("key_span_from_query_offsets", "seq_span spk = span_of(b, sh->Sk, sh->cu_k);",
+     "seq_span spk = span_of(b, sh->Sq, sh->cu_q);"),
     ("scale_dropped", "s[j] = scale * dot;", "s[j] = dot;"),
     ("k_read_at_query_row", "dot += at(q, qbase + d) * at(k, kbase + d);",
      "dot += at(q, qbase + d) * at(k, qbase + d);"),
     ("exp_sign_flipped", "s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
     ("lse_missing_max", "*lse_out = m + log(l);", "*lse_out = log(l);"),
     ("normalisation_dropped", "o_row[d] = acc / l;", "o_row[d] = acc;"),
-    ("v_head_ignored", "acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)Dv + d);",
-     "acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + 0) * (int64_t)Dv + d);"),
-    ("v_read_at_query_row", "acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)Dv + d);",
-     "acc += s[j] * at(v, ((sp.tok0 + i) * Hkv + hk) * (int64_t)Dv + d);"),
-    ("v_row_stride_of_q", "acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)Dv + d);",
-     "acc += s[j] * at(v, ((sp.tok0 + j) * Hkv + hk) * (int64_t)D + d);"),
+    ("v_head_ignored", "acc += s[j] * at(v, ((spk.tok0 + j) * Hkv + hk) * (int64_t)Dv + d);",
+     "acc += s[j] * at(v, ((spk.tok0 + j) * Hkv + 0) * (int64_t)Dv + d);"),
+    ("v_read_at_query_row", "acc += s[j] * at(v, ((spk.tok0 + j) * Hkv + hk) * (int64_t)Dv + d);",
+     "acc += s[j] * at(v, ((spk.tok0 + i) * Hkv + hk) * (int64_t)Dv + d);"),
+    ("v_row_stride_of_q", "acc += s[j] * at(v, ((spk.tok0 + j) * Hkv + hk) * (int64_t)Dv + d);",
+     "acc += s[j] * at(v, ((spk.tok0 + j) * Hkv + hk) * (int64_t)D + d);"),
     ("kv_head_interleaved", "const int hk = h / (H / Hkv);", "const int hk = h % Hkv;"),
-    ("kv_head_stride_of_q", "const int64_t kbase = ((sp.tok0 + j) * Hkv + hk) * (int64_t)D;",
-     "const int64_t kbase = ((sp.tok0 + j) * H + hk) * (int64_t)D;"),
+    ("kv_head_stride_of_q", "const int64_t kbase = ((spk.tok0 + j) * Hkv + hk) * (int64_t)D;",
+     "const int64_t kbase = ((spk.tok0 + j) * H + hk) * (int64_t)D;"),
     ("dense_batch_offset_wrong", "sp.tok0 = (int64_t)b * S;", "sp.tok0 = (int64_t)b;"),
-    ("varlen_length_short", "sp.len = cu_seqlens[b + 1] - cu_seqlens[b];",
-     "sp.len = cu_seqlens[b + 1] - cu_seqlens[b] - (b > 0);"),
+    ("varlen_length_short", "sp.len = cu[b + 1] - cu[b];", "sp.len = cu[b + 1] - cu[b] - (b > 0);"),
     ("row_decode_swaps_h_i", "*i = (int)(row % S);\n        *h = (int)((row / S) % H);",
      "*h = (int)(row % H);\n        *i = (int)((row / H) % S);"),
     ("sum_skips_first_key", "for (int j = 0; j < nkeys; ++j) {\n        s[j] = exp(s[j] - m);\n        l += s[j];",

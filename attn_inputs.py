@@ -39,6 +39,7 @@ class Workload:
     lengths: tuple = field(default=())
     Hkv: int = 0                     # K/V heads for grouped-query attention (0: same as H)
     Dv: int = 0                      # value/output head dimension (0: same as D)
+    q_range: tuple = field(default=())  # varlen with query lengths of their own: (lo, hi)
 
     @property
     def kv_heads(self) -> int:
@@ -84,8 +85,37 @@ def draw_qkv(shape, seed: int, q_std: float = 1.0, kv_std: float = 1.0, kv_heads
     return tuple(out)
 
 
+def qk_lengths(w: Workload):
+    """(query lengths, key lengths) of a workload whose queries have lengths of
+    their own: key lengths as for varlen, query lengths uniform on q_range
+    (inclusive, drawn with seed + 1) and capped at the key length."""
+    n, lo, hi = w.varlen
+    lens_k = varlen_lengths(n, lo, hi, w.seed)
+    qlo, qhi = w.q_range
+    lens_q = np.minimum(varlen_lengths(n, qlo, qhi, w.seed + 1), lens_k)
+    return lens_q, lens_k
+
+
+def make_qk(w: Workload):
+    """(q, k, v, cu_q, cu_k, Sq, Sk) for a workload with separate query and key
+    lengths; Q is drawn with the query token count, K and V with the key's."""
+    lens_q, lens_k = qk_lengths(w)
+    cu_q, cu_k = cu_seqlens_of(lens_q), cu_seqlens_of(lens_k)
+    g = torch.Generator(device="cpu").manual_seed(int(w.seed))
+    shapes = ((int(cu_q[-1]), w.H, w.D), (int(cu_k[-1]), w.kv_heads, w.D),
+              (int(cu_k[-1]), w.kv_heads, w.head_dim_v))
+    out = []
+    for std, shp in zip((w.q_std, w.kv_std, w.kv_std), shapes):
+        x = torch.randn(*shp, generator=g, dtype=torch.float32)
+        if std != 1.0:
+            x = x * std
+        out.append(x.to(torch.bfloat16))
+    return out[0], out[1], out[2], cu_q, cu_k, int(lens_q.max()), int(lens_k.max())
+
+
 def make(w: Workload):
     """(q, k, v, cu_seqlens or None, S) for a workload; tensors are CPU bf16."""
+    assert not w.q_range, "workloads with their own query lengths use make_qk"
     if w.varlen is not None:
         n, lo, hi = w.varlen
         lens = varlen_lengths(n, lo, hi, w.seed)
@@ -105,8 +135,14 @@ def make(w: Workload):
 
 def flops(w: Workload, cu=None) -> float:
     """Algorithmic flops: 2*B*H*S^2*(D + Dv) (= 4*B*H*S^2*D for equal head
-    dimensions), halved for causal (varlen: sum over sequences)."""
+    dimensions), halved for causal (varlen: sum over sequences).  With query
+    lengths of their own: 2*H*(D + Dv)*sum(Lq*Lk), causal keeping Lq*Lk -
+    Lq^2/2 per sequence (the bottom-right triangle, the same convention)."""
     dsum = w.D + w.head_dim_v
+    if w.q_range:
+        lq, lk = (x.astype(np.float64) for x in qk_lengths(w))
+        pairs = lq * lk - (lq * lq / 2.0 if w.causal else 0.0)
+        return float(np.sum(pairs)) * 2.0 * w.H * dsum
     if cu is not None:
         lens = np.diff(np.asarray(cu, np.int64))
         tot = float(np.sum(lens.astype(np.float64) ** 2)) * 2.0 * w.H * dsum
@@ -121,7 +157,8 @@ def flops(w: Workload, cu=None) -> float:
 # sequence length the throughput metric names); the install-check shape
 # (1, 8, 512, 64) causal from the FlashAttention-4 usage guide; and
 # grouped-query attention at 8k causal (32 query heads sharing 8 K/V heads);
-# and the (192, 128) head dimensions of DeepSeek V3 at 8k causal.
+# the (192, 128) head dimensions of DeepSeek V3 at 8k causal; and a mixed
+# prefill/decode batch whose queries are shorter than their keys.
 WORKLOADS = {
     "tiny_b1h2s128d64": Workload("tiny_b1h2s128d64", 1, 128, 2, 64, False, seed=1),
     "dense_b2h16s2048d128": Workload("dense_b2h16s2048d128", 2, 2048, 16, 128, False, seed=2),
@@ -140,4 +177,7 @@ WORKLOADS = {
                                              True, seed=8, Hkv=8),
     "hd192v128_b2h16s8192_causal": Workload("hd192v128_b2h16s8192_causal", 2, 8192, 16, 192,
                                             True, seed=9, Dv=128),
+    "mixed_16x_q1to2048_k512to8192_h16d128_causal": Workload(
+        "mixed_16x_q1to2048_k512to8192_h16d128_causal", 16, 8192, 16, 128, True, seed=10,
+        varlen=(16, 512, 8192), q_range=(1, 2048)),
 }

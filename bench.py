@@ -71,21 +71,26 @@ SECONDARY_WORKLOAD = "causal_b2h16s8192d128"
 
 
 def time_workload(fa, torch, w, steps, warmup, tuning=None):
-    from attn_inputs import make, flops
-    q, k, v, cu, S = make(w)
+    from attn_inputs import make, make_qk, flops
     dev = torch.device("cuda:0")
+    extra = {}
+    if w.q_range:   # queries with lengths of their own
+        q, k, v, cu, cu_k, S, S_k = make_qk(w)
+        extra = dict(cu_seqlens_k=torch.from_numpy(cu_k).to(dev), max_seqlen_k=S_k)
+    else:
+        q, k, v, cu, S = make(w)
     dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
     dcu = None if cu is None else torch.from_numpy(cu).to(dev)
     o = torch.empty(tuple(dq.shape[:-1]) + (w.head_dim_v,), dtype=dq.dtype, device=dev)
     T = dq.shape[0] if cu is not None else None
     lse = torch.empty((w.H, T) if cu is not None else (w.B, w.H, w.S), dtype=torch.float32,
                       device=dev)
-    fl = flops(w, cu)
+    fl = flops(w, None if w.q_range else cu)
 
     def step():
         fa.attention(dq, dk, dv, causal=w.causal, scale=w.scale, cu_seqlens=dcu,
                      max_seqlen=S if cu is not None else None, out=o, lse_out=lse,
-                     tuning=tuning)
+                     tuning=tuning, **extra)
 
     for _ in range(warmup):
         step()

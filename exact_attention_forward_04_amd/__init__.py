@@ -60,6 +60,9 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd_gqa.restype = I
     lib.fa_fwd_hd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, ctypes.POINTER(Tuning)]
     lib.fa_fwd_hd.restype = I
+    lib.fa_fwd_general.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, P, P,
+                                   ctypes.POINTER(Tuning)]
+    lib.fa_fwd_general.restype = I
     lib.fa_tuning_default.argtypes = []
     lib.fa_tuning_default.restype = Tuning
     lib.fa_exp2_emu.argtypes = [P, P, LL, P]
@@ -100,50 +103,62 @@ def _stream_ptr(stream) -> Optional[int]:
 
 def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
               cu_seqlens=None, max_seqlen: Optional[int] = None, return_lse: bool = True,
-              out=None, lse_out=None, tuning: Optional[Tuning] = None, stream=None):
+              out=None, lse_out=None, tuning: Optional[Tuning] = None, stream=None,
+              cu_seqlens_k=None, max_seqlen_k: Optional[int] = None):
     """Exact attention forward on the GPU.
 
-    q, k, v: contiguous bf16 CUDA tensors, [B,S,H,D] (dense) or [T,H,D]
-    (varlen, with cu_seqlens an int32 CUDA tensor of B+1 offsets and
-    max_seqlen the longest sequence).  k and v may have fewer heads H_kv than
-    q (grouped-query attention; H_kv divides H and query head h reads K/V
-    head h // (H // H_kv)), and v may have its own head dimension D_v (the
-    (192, 128) pair).  Returns (o, lse): o like q with D_v columns (bf16),
-    lse fp32 [B,H,S] or [H,T] (None if return_lse is False).
+    q, k, v: contiguous bf16 CUDA tensors.  Dense: q [B,Sq,H,D], k [B,Sk,H_kv,D],
+    v [B,Sk,H_kv,D_v].  Varlen: q [Tq,H,D], k [Tk,H_kv,D], v [Tk,H_kv,D_v] with
+    cu_seqlens (query offsets) an int32 CUDA tensor of B+1 entries and
+    max_seqlen the longest query length; cu_seqlens_k / max_seqlen_k give the
+    key offsets and longest key length when they differ from the queries'.
+    H_kv divides H (query head h reads K/V head h // (H // H_kv)); D_v may
+    differ from D for the (192, 128) pair.  With causal=True and query and key
+    lengths that differ the mask is aligned to the bottom-right corner.
+    Returns (o, lse): o like q with D_v columns (bf16), lse fp32 [B,H,Sq] or
+    [H,Tq] (None if return_lse is False).
     """
     import torch
     lib = load()
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("%s must be a contiguous bf16 CUDA tensor" % name)
-    head_axis = 2 if cu_seqlens is None else 1
-    if k.dim() != q.dim() or v.dim() != q.dim() or any(
-            k.shape[i] != q.shape[i] for i in range(q.dim()) if i != head_axis) or any(
-            v.shape[i] != k.shape[i] for i in range(q.dim() - 1)):
-        raise ValueError("k must have q's shape apart from the number of heads, "
-                         "and v k's shape apart from the head dimension")
-    H_kv = k.shape[head_axis]
-    D_v = v.shape[-1]
-    if H_kv < 1 or q.shape[head_axis] % H_kv != 0:
+    dense = cu_seqlens is None
+    if cu_seqlens_k is not None and dense:
+        raise ValueError("cu_seqlens_k needs cu_seqlens")
+    nd = 4 if dense else 3
+    if q.dim() != nd or k.dim() != nd or v.dim() != nd:
+        raise ValueError("dense inputs are [B, S, H, D]" if dense else "varlen inputs are [T, H, D]")
+    if k.shape[-1] != q.shape[-1] or tuple(v.shape[:-1]) != tuple(k.shape[:-1]) or (
+            dense and k.shape[0] != q.shape[0]):
+        raise ValueError("k must match q's batch and head dimension, v k's leading shape")
+    H, D = q.shape[-2], q.shape[-1]
+    H_kv, D_v = k.shape[-2], v.shape[-1]
+    if H_kv < 1 or H % H_kv != 0:
         raise ValueError("the K/V head count must divide the query head count")
-    if cu_seqlens is None:
-        if q.dim() != 4:
-            raise ValueError("dense inputs are [B, S, H, D]")
-        B, S, H, D = q.shape
+    if dense:
+        B, S = q.shape[0], q.shape[1]
+        S_k = k.shape[1]
         lse_shape = (B, H, S)
-        cu_ptr = None
+        cu_ptr = cu_k_ptr = None
     else:
-        if q.dim() != 3:
-            raise ValueError("varlen inputs are [T, H, D]")
-        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or not cu_seqlens.is_contiguous():
-            raise ValueError("cu_seqlens must be a contiguous int32 CUDA tensor")
+        for name, c in (("cu_seqlens", cu_seqlens), ("cu_seqlens_k", cu_seqlens_k)):
+            if c is not None and (c.dtype != torch.int32 or not c.is_cuda or not c.is_contiguous()):
+                raise ValueError("%s must be a contiguous int32 CUDA tensor" % name)
         if max_seqlen is None:
             raise ValueError("varlen needs max_seqlen")
-        T, H, D = q.shape
+        if cu_seqlens_k is None:
+            if k.shape[0] != q.shape[0]:
+                raise ValueError("different query and key token counts need cu_seqlens_k")
+            cu_seqlens_k, max_seqlen_k = cu_seqlens, max_seqlen
+        elif max_seqlen_k is None:
+            raise ValueError("cu_seqlens_k needs max_seqlen_k")
         B = cu_seqlens.numel() - 1
-        S = int(max_seqlen)
-        lse_shape = (H, T)
-        cu_ptr = cu_seqlens.data_ptr()
+        if cu_seqlens_k.numel() != B + 1:
+            raise ValueError("cu_seqlens and cu_seqlens_k must have the same length")
+        S, S_k = int(max_seqlen), int(max_seqlen_k)
+        lse_shape = (H, q.shape[0])
+        cu_ptr, cu_k_ptr = cu_seqlens.data_ptr(), cu_seqlens_k.data_ptr()
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o_shape = tuple(q.shape[:-1]) + (D_v,)
@@ -155,22 +170,26 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
         lse = lse_out if lse_out is not None else torch.empty(lse_shape, dtype=torch.float32,
                                                               device=q.device)
     sp = _stream_ptr(stream)
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-            lse.data_ptr() if lse is not None else None, B, H, S, D, float(scale),
-            int(bool(causal)), cu_ptr, sp)
-    if D_v != D:
-        hargs = args[:7] + (H_kv,) + args[7:9] + (D_v,) + args[9:]
-        rc = lib.fa_fwd_hd(*hargs, ctypes.byref(tuning) if tuning is not None else None)
+    tref = ctypes.byref(tuning) if tuning is not None else None
+    lse_ptr = lse.data_ptr() if lse is not None else None
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_ptr)
+    if S_k != S or cu_k_ptr != cu_ptr:
+        rc = lib.fa_fwd_general(*ptrs, B, H, H_kv, S, S_k, D, D_v, float(scale),
+                                int(bool(causal)), cu_ptr, cu_k_ptr, sp, tref)
+        _check("fa_fwd_general", rc)
+    elif D_v != D:
+        rc = lib.fa_fwd_hd(*ptrs, B, H, H_kv, S, D, D_v, float(scale), int(bool(causal)),
+                           cu_ptr, sp, tref)
         _check("fa_fwd_hd", rc)
     elif H_kv != H:
-        gargs = args[:7] + (H_kv,) + args[7:]
-        rc = lib.fa_fwd_gqa(*gargs, ctypes.byref(tuning) if tuning is not None else None)
+        rc = lib.fa_fwd_gqa(*ptrs, B, H, H_kv, S, D, float(scale), int(bool(causal)), cu_ptr,
+                            sp, tref)
         _check("fa_fwd_gqa", rc)
     elif tuning is None:
-        rc = lib.fa_fwd(*args)
+        rc = lib.fa_fwd(*ptrs, B, H, S, D, float(scale), int(bool(causal)), cu_ptr, sp)
         _check("fa_fwd", rc)
     else:
-        rc = lib.fa_fwd_ex(*args, ctypes.byref(tuning))
+        rc = lib.fa_fwd_ex(*ptrs, B, H, S, D, float(scale), int(bool(causal)), cu_ptr, sp, tref)
         _check("fa_fwd_ex", rc)
     return o, lse
 

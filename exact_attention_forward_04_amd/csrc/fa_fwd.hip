@@ -162,8 +162,10 @@ struct Args {
   const __bf16 *q, *k, *v;
   __bf16 *o;
   float *lse;
-  const int *cu;            // varlen offsets or nullptr
-  int B, H, S;
+  const int *cu;            // varlen query offsets or nullptr
+  const int *cu_k;          // varlen key offsets (cu for self-attention) or nullptr
+  int B, H, S;              // S: (longest) query length
+  int Sk;                   // (longest) key length
   int Hkv;                  // K/V heads (divides H); query head h reads K/V head h / (H / Hkv)
   float c;                  // scale * log2(e)
   float tau;
@@ -507,16 +509,20 @@ __device__ __forceinline__ void pv_step(WaveState<D> &st, const LdsAddr<D> &la,
 }
 
 // Which KV blocks a wave (32 rows from wrow0) needs, and which need masking.
+// The causal mask is aligned to the bottom-right corner: query row i may use
+// key j when j <= i + koff, koff = Lk - Lq (0 for self-attention).  krow0 and
+// krow_last are the last usable keys of the wave's first and last row.
 struct WaveRows {
   int wrow0, wrow_last;   // first and last valid row of the wave
+  int krow0, krow_last;   // wrow0 + koff, wrow_last + koff
   bool active;
-  int last_block;         // index of the wave's last useful block
+  int last_block;         // index of the wave's last useful block (-1: none)
   __device__ __forceinline__ bool useful(int j, bool causal) const {
-    return active && (!causal || j * kBN <= wrow_last);
+    return active && (!causal || j * kBN <= krow_last);
   }
-  __device__ __forceinline__ bool need_mask(int j, int L, bool causal) const {
+  __device__ __forceinline__ bool need_mask(int j, int Lk, bool causal) const {
     const int n0 = j * kBN;
-    return (n0 + kBN > L) || (causal && n0 + kBN - 1 > wrow0);
+    return (n0 + kBN > Lk) || (causal && n0 + kBN - 1 > krow0);
   }
 };
 
@@ -567,16 +573,22 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   using C = Cfg<D>;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
-  long long tok0;
-  int L;
+  long long tok0, ktok0;  // first query token, first key token of the sequence
+  int L, Lk;              // query length, key length
   if constexpr (VARLEN) {
     tok0 = a.cu[b];
-    int Lr = a.cu[b + 1] - a.cu[b];
+    const int Lr = a.cu[b + 1] - a.cu[b];
     L = Lr < 0 ? 0 : (Lr > a.S ? a.S : Lr);
+    ktok0 = a.cu_k[b];
+    const int Lkr = a.cu_k[b + 1] - a.cu_k[b];
+    Lk = Lkr < 0 ? 0 : (Lkr > a.Sk ? a.Sk : Lkr);
   } else {
     tok0 = (long long)b * a.S;
     L = a.S;
+    ktok0 = (long long)b * a.Sk;
+    Lk = a.Sk;
   }
+  const int koff = Lk - L;  // bottom-right causal alignment
   const int m0 = mb * C::BM;
   if (m0 >= L) return;  // workgroup-uniform
   const int H = a.H;
@@ -586,13 +598,23 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   wr.wrow0 = m0 + wave * 32;
   wr.active = wr.wrow0 < L;
   wr.wrow_last = (wr.wrow0 + 31 < L - 1) ? wr.wrow0 + 31 : L - 1;
+  wr.krow0 = wr.wrow0 + koff;
+  wr.krow_last = wr.wrow_last + koff;
   const int row = wr.wrow0 + (lane & 31);
 
-  // KV range shared by the workgroup
-  const int n_end = CAUSAL ? ((m0 + C::BM < L) ? m0 + C::BM : L) : L;
+  // KV range shared by the workgroup (0 blocks: no row of the tile has a key)
+  int n_end = Lk;
+  if (CAUSAL) {
+    const int e = m0 + C::BM + koff;
+    n_end = e < 0 ? 0 : (e < Lk ? e : Lk);
+  }
   const int nblocks = fa::ceil_div(n_end, kBN);
-  wr.last_block = CAUSAL ? ((wr.wrow_last / kBN < nblocks - 1) ? wr.wrow_last / kBN : nblocks - 1)
-                         : nblocks - 1;
+  if (CAUSAL) {
+    const int lb = wr.krow_last >= 0 ? wr.krow_last / kBN : -1;
+    wr.last_block = lb < nblocks - 1 ? lb : nblocks - 1;
+  } else {
+    wr.last_block = nblocks - 1;
+  }
 
   // Q fragments: lane l holds row (l%32), d = 16s + 8(l/32) .. +7
   WaveState<D> st;
@@ -651,26 +673,29 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     auto copies = [&](int it) {
       return [&, it](int part) {
         if (it + 2 < nblocks) {
-          if (part == 0) ldk.issue(a.k, tok0, Hk, hk, (it + 2) * kBN, L, kbuf(it + 2), kbuf2(it + 2));
-          else ldv.issue(a.v, tok0, Hk, hk, (it + 2) * kBN, L, vbuf(it + 2));
+          if (part == 0) ldk.issue(a.k, ktok0, Hk, hk, (it + 2) * kBN, Lk, kbuf(it + 2), kbuf2(it + 2));
+          else ldv.issue(a.v, ktok0, Hk, hk, (it + 2) * kBN, Lk, vbuf(it + 2));
         }
       };
     };
     auto softmax_phase = [&](bool run, int j, int it) {
       auto side = copies(it);
       if (run) {
-        softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, j * kBN, row, L, wr.need_mask(j, L, CAUSAL),
-                                            j == wr.last_block, a, side);
+        softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, j * kBN, row + koff, Lk,
+                                            wr.need_mask(j, Lk, CAUSAL), j == wr.last_block, a,
+                                            side);
       } else {
         side(0);
         side(1);
       }
     };
-    ldk.issue(a.k, tok0, Hk, hk, 0, L, kbuf(0), kbuf2(0));
-    ldv.issue(a.v, tok0, Hk, hk, 0, L, vbuf(0));
+    if (nblocks > 0) {
+      ldk.issue(a.k, ktok0, Hk, hk, 0, Lk, kbuf(0), kbuf2(0));
+      ldv.issue(a.v, ktok0, Hk, hk, 0, Lk, vbuf(0));
+    }
     if (nblocks > 1) {
-      ldk.issue(a.k, tok0, Hk, hk, kBN, L, kbuf(1), kbuf2(1));
-      ldv.issue(a.v, tok0, Hk, hk, kBN, L, vbuf(1));
+      ldk.issue(a.k, ktok0, Hk, hk, kBN, Lk, kbuf(1), kbuf2(1));
+      ldv.issue(a.v, ktok0, Hk, hk, kBN, Lk, vbuf(1));
     }
     // The two halves run separate loops that meet at the same barriers.
     if (half == 0) {
@@ -702,8 +727,10 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     char LDS_AS *vb0 = lds + C::K_BYTES;
     char LDS_AS *kb1 = lds + 2 * C::K_BYTES;
     char LDS_AS *vb1 = lds + 3 * C::K_BYTES;
-    ldk.issue(a.k, tok0, Hk, hk, 0, L, kb0);
-    ldv.issue(a.v, tok0, Hk, hk, 0, L, vb0);
+    if (nblocks > 0) {
+      ldk.issue(a.k, ktok0, Hk, hk, 0, Lk, kb0);
+      ldv.issue(a.v, ktok0, Hk, hk, 0, Lk, vb0);
+    }
     for (int j = 0; j < nblocks; ++j) {
       const int n0 = j * kBN;
       char LDS_AS *kcur = (j & 1) ? kb1 : kb0;
@@ -711,8 +738,8 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       if (j + 1 < nblocks) {
         char LDS_AS *knext = (j & 1) ? kb0 : kb1;
         char LDS_AS *vnext = (j & 1) ? vb0 : vb1;
-        ldk.issue(a.k, tok0, Hk, hk, n0 + kBN, L, knext);
-        ldv.issue(a.v, tok0, Hk, hk, n0 + kBN, L, vnext);
+        ldk.issue(a.k, ktok0, Hk, hk, n0 + kBN, Lk, knext);
+        ldv.issue(a.v, ktok0, Hk, hk, n0 + kBN, Lk, vnext);
         wait_vmcnt<LOADS_BLOCK>();
       } else {
         wait_vmcnt<0>();
@@ -720,8 +747,9 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       barrier_nofence();
       if (wr.useful(j, CAUSAL)) {
         qk_step<D>(st, la, kcur, kcur);
-        softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, n0, row, L, wr.need_mask(j, L, CAUSAL),
-                                            j == wr.last_block, a, [](int) {});
+        softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, n0, row + koff, Lk,
+                                            wr.need_mask(j, Lk, CAUSAL), j == wr.last_block, a,
+                                            [](int) {});
         pv_step<D>(st, la, vcur);
       }
       barrier_after_reads();  // every wave is done reading this buffer
@@ -732,7 +760,7 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   // ---- epilogue: combine the two half-wave partial sums of each row
   const float l32 = sum_halves(st.l32);
   if (row < L) {
-    const float inv = 1.0f / l32;
+    const float inv = l32 > 0.0f ? 1.0f / l32 : 0.0f;  // a row without keys: O = 0, LSE = -inf
     const int hh = lane >> 5;
     __bf16 *op = a.o + ((tok0 + row) * H + h) * (long long)DV + 4 * hh;
 #pragma unroll
@@ -846,11 +874,13 @@ bool supported_dims(int D, int Dv) {
 }
 
 int validate(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-             int Hkv, int S, int D, int Dv, float scale, int causal, const fa_tuning *t) {
+             int Hkv, int S, int Sk, int D, int Dv, float scale, int causal, const int *cu_q,
+             const int *cu_k, const fa_tuning *t) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID_ARG;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return FA_ERR_INVALID_ARG;
-  if (B <= 0 || H <= 0 || S <= 0 || D <= 0 || Dv <= 0) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || S <= 0 || Sk <= 0 || D <= 0 || Dv <= 0) return FA_ERR_INVALID_ARG;
+  if ((cu_q == nullptr) != (cu_k == nullptr)) return FA_ERR_INVALID_ARG;
   if (Hkv <= 0 || H % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
@@ -861,7 +891,8 @@ int validate(const void *q, const void *k, const void *v, void *o, float *lse, i
   }
   if (!supported_dims(D, Dv)) return FA_ERR_UNSUPPORTED;
   // sizes must fit the 32-bit index arithmetic used for rows and tiles
-  if ((long long)B * S > (1LL << 31) - 1 || (long long)S * H > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  const long long Smax = S > Sk ? S : Sk;
+  if ((long long)B * Smax > (1LL << 31) - 1 || Smax * H > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -948,11 +979,13 @@ fa_tuning fa_tuning_default(void) {
   return t;
 }
 
-int fa_fwd_hd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-              int H_kv, int S, int D, int D_v, float scale, int causal, const int *cu_seqlens,
-              void *stream, const fa_tuning *tuning) {
+int fa_fwd_general(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                   int H, int H_kv, int S_q, int S_k, int D, int D_v, float scale, int causal,
+                   const int *cu_seqlens_q, const int *cu_seqlens_k, void *stream,
+                   const fa_tuning *tuning) {
   const fa_tuning t = tuning ? *tuning : fa_tuning_default();
-  int rc = validate(q, k, v, o, lse, B, H, H_kv, S, D, D_v, scale, causal, &t);
+  int rc = validate(q, k, v, o, lse, B, H, H_kv, S_q, S_k, D, D_v, scale, causal, cu_seqlens_q,
+                    cu_seqlens_k, &t);
   if (rc != FA_OK) return rc;
   DeviceInfo *dev = nullptr;
   rc = current_device(&dev);
@@ -963,23 +996,32 @@ int fa_fwd_hd(const void *q, const void *k, const void *v, void *o, float *lse, 
   a.v = (const __bf16 *)v;
   a.o = (__bf16 *)o;
   a.lse = lse;
-  a.cu = cu_seqlens;
+  a.cu = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
   a.B = B;
   a.H = H;
   a.Hkv = H_kv;
-  a.S = S;
+  a.S = S_q;
+  a.Sk = S_k;
   a.c = scale * kLog2e;
   a.tau = t.tau;
   a.counters = t.counters;
   a.workers = 0;
   hipStream_t st = (hipStream_t)stream;
-  const bool varlen = cu_seqlens != nullptr;
+  const bool varlen = cu_seqlens_q != nullptr;
   switch (D) {
     case 64: return dispatch_d<64>(a, causal, varlen, t, dev->cus, st);
     case 128: return dispatch_d<128>(a, causal, varlen, t, dev->cus, st);
     case 192: return dispatch_d<192>(a, causal, varlen, t, dev->cus, st);
     default: return dispatch_d<256>(a, causal, varlen, t, dev->cus, st);
   }
+}
+
+int fa_fwd_hd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+              int H_kv, int S, int D, int D_v, float scale, int causal, const int *cu_seqlens,
+              void *stream, const fa_tuning *tuning) {
+  return fa_fwd_general(q, k, v, o, lse, B, H, H_kv, S, S, D, D_v, scale, causal, cu_seqlens,
+                        cu_seqlens, stream, tuning);
 }
 
 int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
@@ -1083,6 +1125,6 @@ const char *fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 102; }
+int fa_version(void) { return 103; }
 
 }  // extern "C"

@@ -151,6 +151,33 @@ int fa_fwd_hd(const void *q, const void *k, const void *v, void *o, float *lse,
               const int *cu_seqlens, void *stream, const fa_tuning *tuning);
 
 /*
+ * fa_fwd_general -- the complete parameter set: fa_fwd_hd with query and key
+ * lengths that may differ (decode and mixed prefill/decode batches; the
+ * FlashAttention-4 paper's section 3.3 motivates its varlen scheduling with
+ * such batches).
+ *
+ *   dense  (both offsets NULL): q, o [B, S_q, H, .]; k, v [B, S_k, H_kv, .];
+ *                               lse fp32 [B, H, S_q]
+ *   varlen (both non-NULL):     q, o [T_q, H, .]; k, v [T_k, H_kv, .] with
+ *          T_q = cu_seqlens_q[B], T_k = cu_seqlens_k[B]; lse fp32 [H, T_q].
+ *          Sequence b has query tokens cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *          and key tokens cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1; S_q and S_k
+ *          are the longest lengths (the same trust rules as fa_fwd apply to
+ *          both offset arrays).
+ * With causal = 1 the mask is aligned to the bottom-right corner: with
+ * lengths L_q and L_k, query i may use key j when j <= i + L_k - L_q, so the
+ * last query sees every key (for L_q = L_k this is fa_fwd's j <= i).  A row
+ * that may use no key (L_q > L_k and i < L_q - L_k, or L_k = 0) gets O = 0
+ * and LSE = -inf.  One offset array NULL and the other not is
+ * FA_ERR_INVALID_ARG.  fa_fwd_hd is the S_q = S_k, cu_seqlens_q =
+ * cu_seqlens_k case.
+ */
+int fa_fwd_general(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int H, int H_kv, int S_q, int S_k, int D, int D_v, float scale,
+                   int causal, const int *cu_seqlens_q, const int *cu_seqlens_k, void *stream,
+                   const fa_tuning *tuning);
+
+/*
  * fa_exp2_emu -- test hook: y[i] = the device's polynomial 2^x[i] for n
  * floats (device pointers, 4-byte aligned).  The function is the one the
  * attention kernel uses for its emulated exponentials: Cody-Waite
@@ -195,7 +222,8 @@ int fa_num_workers(int D, int *workers_out);
 /* Human-readable name of an fa_status value (static string, never NULL). */
 const char *fa_status_string(int status);
 
-/* Library ABI version: 100 * major + minor (101: fa_fwd_gqa; 102: fa_fwd_hd). */
+/* Library ABI version: 100 * major + minor (101: fa_fwd_gqa; 102: fa_fwd_hd;
+ * 103: fa_fwd_general). */
 int fa_version(void);
 
 #ifdef __cplusplus

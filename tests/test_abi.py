@@ -105,6 +105,18 @@ def test_head_dim_pair_validation(D, D_v, expect):
     assert rc == expect
 
 
+def test_general_entry_validation():
+    lib = fa.load()
+    # one offset array without the other
+    assert lib.fa_fwd_general(A, A, A, A, A, 2, 4, 2, 8, 16, 128, 128, 0.1, 1, A, None, None,
+                              None) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_general(A, A, A, A, A, 2, 4, 2, 8, 16, 128, 128, 0.1, 1, None, A, None,
+                              None) == fa.FA_ERR_INVALID_ARG
+    # key length must be positive
+    assert lib.fa_fwd_general(A, A, A, A, A, 2, 4, 2, 8, 0, 128, 128, 0.1, 1, None, None, None,
+                              None) == fa.FA_ERR_INVALID_ARG
+
+
 def test_fa_fwd_rejects_d192_without_a_value_dimension():
     assert call(D=192) == fa.FA_ERR_UNSUPPORTED
 
@@ -119,6 +131,8 @@ def test_valid_call_without_gpu_reports_no_device():
                                 None) == fa.FA_ERR_NO_DEVICE
     assert fa.load().fa_fwd_hd(A, A, A, A, A, 1, 8, 2, 8, 192, 128, 0.1, 1, None, None,
                                None) == fa.FA_ERR_NO_DEVICE
+    assert fa.load().fa_fwd_general(A, A, A, A, A, 1, 8, 2, 3, 900, 128, 128, 0.1, 1, None,
+                                    None, None, None) == fa.FA_ERR_NO_DEVICE
 
 
 def test_exp2_emu_argument_checks():

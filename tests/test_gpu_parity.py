@@ -18,7 +18,7 @@ import torch
 
 import exact_attention_forward_04_amd as fa
 import oracle
-from attn_inputs import WORKLOADS, Workload, make, draw_qkv, cu_seqlens_of
+from attn_inputs import WORKLOADS, Workload, make, make_qk, draw_qkv, cu_seqlens_of
 from parity import assert_close, compare, tensor_to_f64
 
 pytestmark = pytest.mark.gpu
@@ -281,6 +281,105 @@ def test_head_dims_192_128_value_columns_independent():
     o2, l2 = run_gpu(q, k, v2, True, 0.07)
     assert torch.equal(l1, l2)
     assert torch.equal(torch.flip(o2, dims=[-1]), o1)
+
+
+# ---- query and key lengths that differ (bottom-right causal alignment)
+
+def qk_check(q, k, v, causal, scale, cu_q=None, cu_k=None, Sq=None, Sk=None, what=""):
+    note(what, "q", tuple(q.shape), "k", tuple(k.shape), "causal", causal)
+    dq, dk, dv = (t.cuda() for t in (q, k, v))
+    kw = {}
+    if cu_q is not None:
+        kw = dict(cu_seqlens=torch.from_numpy(np.asarray(cu_q, np.int32)).cuda(), max_seqlen=Sq,
+                  cu_seqlens_k=torch.from_numpy(np.asarray(cu_k, np.int32)).cuda(),
+                  max_seqlen_k=Sk)
+    o, lse = fa.attention(dq, dk, dv, causal=causal, scale=scale, **kw)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_bf16(q, k, v, scale, causal, cu_q, cu_k)
+    lse_g = tensor_to_f64(lse)
+    empty = np.isneginf(lse_ref)
+    # rows that may use no key: exactly O = 0 and LSE = -inf
+    assert np.array_equal(np.isneginf(lse_g), empty), what
+    o_g = tensor_to_f64(o)
+    if empty.any():
+        if cu_q is None:
+            rows_o = o_g.transpose(0, 2, 1, 3)[empty]     # [B,H,Sq,Dv] -> empty rows
+        else:
+            rows_o = o_g.transpose(1, 0, 2)[empty]        # [H,Tq,Dv]
+        assert np.all(rows_o == 0.0), what
+    lse_g = np.where(empty, 0.0, lse_g)
+    lse_r = np.where(empty, 0.0, lse_ref)
+    st = compare(o_g, lse_g, o_ref, lse_r)
+    note(what, st, "empty rows", int(empty.sum()))
+    assert_close(st, what)
+
+
+QK_DENSE = [
+    # (B, Sq, Sk, H, H_kv, D, D_v)
+    (2, 300, 700, 4, 2, 128, 128),
+    (1, 700, 300, 2, 2, 128, 128),    # more queries than keys: leading rows see no key
+    (1, 1, 1000, 4, 1, 128, 128),     # a decode step
+    (2, 3, 513, 2, 2, 64, 64),
+    (1, 200, 900, 2, 2, 192, 128),
+    (1, 100, 333, 2, 2, 256, 256),
+]
+
+
+@pytest.mark.parametrize("shape", QK_DENSE, ids=lambda s: "B%dQ%dK%dH%dKV%dD%dV%d" % s)
+@pytest.mark.parametrize("causal", [False, True])
+def test_qk_lengths_dense_full(shape, causal):
+    B, Sq, Sk, H, Hkv, D, Dv = shape
+    g = torch.Generator().manual_seed(400 + Sq + Sk)
+    q = torch.randn(B, Sq, H, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, Sk, Hkv, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, Sk, Hkv, Dv, generator=g).to(torch.bfloat16)
+    qk_check(q, k, v, causal, 1.0 / math.sqrt(D), what="qk-dense")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_qk_lengths_varlen_full(causal, D):
+    lens_q = [1, 0, 300, 64, 65, 7, 2, 500]
+    lens_k = [100, 5, 300, 900, 0, 777, 2, 200]   # includes L_k = 0 and L_q > L_k
+    cu_q, cu_k = cu_seqlens_of(lens_q), cu_seqlens_of(lens_k)
+    g = torch.Generator().manual_seed(411 + D)
+    q = torch.randn(int(cu_q[-1]), 4, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(int(cu_k[-1]), 2, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(int(cu_k[-1]), 2, D, generator=g).to(torch.bfloat16)
+    qk_check(q, k, v, causal, 1.0 / math.sqrt(D), cu_q, cu_k, max(lens_q), max(lens_k),
+             what="qk-varlen")
+
+
+def test_qk_lengths_equal_is_self_attention():
+    """Separate but equal query and key offsets give the self-attention launch's
+    result bit for bit (the same kernel path, koff = 0)."""
+    lens = [900, 33, 2048, 1, 511]
+    cu = cu_seqlens_of(lens)
+    q, k, v = draw_qkv((int(cu[-1]), 4, 128), seed=421)
+    dq, dk, dv = (t.cuda() for t in (q, k, v))
+    dcu = torch.from_numpy(cu).cuda()
+    for causal in (False, True):
+        o1, l1 = fa.attention(dq, dk, dv, causal=causal, cu_seqlens=dcu, max_seqlen=max(lens))
+        o2, l2 = fa.attention(dq, dk, dv, causal=causal, cu_seqlens=dcu, max_seqlen=max(lens),
+                              cu_seqlens_k=dcu.clone(), max_seqlen_k=max(lens))
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_mixed_prefill_decode_workload_sampled():
+    w = WORKLOADS["mixed_16x_q1to2048_k512to8192_h16d128_causal"]
+    q, k, v, cu_q, cu_k, Sq, Sk = make_qk(w)
+    note(w.name, "gpu run")
+    o, lse = fa.attention(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=w.scale,
+                          cu_seqlens=torch.from_numpy(cu_q).cuda(), max_seqlen=Sq,
+                          cu_seqlens_k=torch.from_numpy(cu_k).cuda(), max_seqlen_k=Sk)
+    torch.cuda.synchronize()
+    rows = sample_rows(w, cu_q, 512, seed=w.seed)
+    o_ref, lse_ref = oracle.attention_rows_bf16(q, k, v, rows, w.scale, True, cu_q, cu_k)
+    o_g, lse_g = gather_rows(o, lse, rows, w, cu_q)
+    st = compare(o_g, lse_g, o_ref, lse_ref)
+    note(w.name, st)
+    assert_close(st, w.name)
 
 
 # ---- invariances

@@ -1,8 +1,9 @@
-"""Test infrastructure only: the fp64 CPU oracle for exact attention forward.
+"""Test infrastructure only: the fp64 CPU oracle for exact attention.
 
 The oracle is a plain, slow, double-precision C implementation of
-O = softmax(scale * Q K^T + causal mask) V and the row logsumexp
-(``attn_oracle.c``), plus a 50-digit brute-force evaluator for tiny inputs
+O = softmax(scale * Q K^T + causal mask) V and the row logsumexp, and of the
+gradients of sum <dO, O> with respect to Q, K and V (``attn_oracle.c``),
+plus a 50-digit brute-force evaluator for tiny forward inputs
 (``brute.py``).  It shares no code with the HIP library and never imports it.
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may use it; the product path must never route through it.
@@ -51,6 +52,13 @@ def _as_bits(t) -> np.ndarray:
     return np.ascontiguousarray(t.contiguous().view(torch.int16).numpy().view(np.uint16))
 
 
+def _is_bf16(t) -> bool:
+    if isinstance(t, np.ndarray):
+        return t.dtype == np.uint16
+    import torch
+    return isinstance(t, torch.Tensor) and t.dtype == torch.bfloat16
+
+
 def _cu(cu_seqlens):
     if cu_seqlens is None:
         return None
@@ -97,7 +105,13 @@ class OracleLib:
         lib.oracle_attn_fwd_f64.argtypes = [P, P, P, P, P] + dims + [f64, i32, P, P]
         lib.oracle_attn_fwd_bf16.argtypes = [P, P, P, P, P] + dims + [f64, i32, P, P]
         lib.oracle_attn_rows_bf16.argtypes = [P, P, P, P, i64, P, P] + dims + [f64, i32, P, P]
-        for fn in (lib.oracle_attn_fwd_f64, lib.oracle_attn_fwd_bf16, lib.oracle_attn_rows_bf16):
+        lib.oracle_attn_bwd_f64.argtypes = [P] * 10 + dims + [f64, i32, P, P]
+        lib.oracle_attn_bwd_bf16.argtypes = [P] * 10 + dims + [f64, i32, P, P]
+        lib.oracle_attn_bwd_rows_bf16.argtypes = ([P, P, P, P, P, i64, P, P, P, i64, P, P, P, P]
+                                                  + dims + [f64, i32, P, P])
+        for fn in (lib.oracle_attn_fwd_f64, lib.oracle_attn_fwd_bf16, lib.oracle_attn_rows_bf16,
+                   lib.oracle_attn_bwd_f64, lib.oracle_attn_bwd_bf16,
+                   lib.oracle_attn_bwd_rows_bf16):
             fn.restype = i32
         lib.oracle_exp2.argtypes = [P, P, i64]
         lib.oracle_exp2.restype = None
@@ -168,6 +182,69 @@ class OracleLib:
             raise ValueError("oracle_attn_rows_bf16 rejected its arguments")
         return o, lse
 
+    def attention_backward(self, q, k, v, dout, scale, causal, cu_seqlens=None,
+                           cu_seqlens_k=None, magnitudes=False):
+        """Gradients of sum <dout, O> with respect to q, k and v.
+
+        Inputs are float64 arrays (any float dtype is widened) or bf16 (torch
+        bf16 CPU tensors / uint16 bit arrays, all four alike); dout has o's
+        shape (q's with Dv columns).  Returns (dq, dk, dv) as float64 arrays
+        shaped like q, k, v; with magnitudes=True also (|dq|, |dk|, |dv|), the
+        sums of absolute values of each gradient's terms.
+        """
+        bf = _is_bf16(q)
+        if bf:
+            arrs = [_as_bits(t) for t in (q, k, v, dout)]
+            fn, name = self.lib.oracle_attn_bwd_bf16, "oracle_attn_bwd_bf16"
+        else:
+            arrs = [np.ascontiguousarray(t, dtype=np.float64) for t in (q, k, v, dout)]
+            fn, name = self.lib.oracle_attn_bwd_f64, "oracle_attn_bwd_f64"
+        qa, ka, va, ga = arrs
+        cu_q = _cu(cu_seqlens)
+        cu_k = _cu(cu_seqlens_k) if cu_seqlens_k is not None else cu_q
+        B, H, Hkv, Sq, Sk, D, Dv = _layout(qa.shape, ka.shape, va.shape, cu_q, cu_k)
+        o_shape, _ = _out_shapes(B, H, Sq, Dv, cu_q)
+        if tuple(ga.shape) != tuple(o_shape):
+            raise ValueError("dout must have o's shape %s" % (o_shape,))
+        outs = [np.empty(qa.shape), np.empty(ka.shape), np.empty(va.shape)]
+        mags = [np.empty(qa.shape), np.empty(ka.shape), np.empty(va.shape)] if magnitudes \
+            else [None, None, None]
+        rc = fn(_ptr(qa), _ptr(ka), _ptr(va), _ptr(ga), *[_ptr(x) for x in outs],
+                *[_ptr(x) for x in mags], B, H, Hkv, Sq, Sk, D, Dv, float(scale),
+                int(bool(causal)), _ptr(cu_q), _ptr(cu_k))
+        if rc != 0:
+            raise ValueError(name + " rejected its arguments")
+        return (tuple(outs) + tuple(mags)) if magnitudes else tuple(outs)
+
+    def attention_backward_rows_bf16(self, q, k, v, dout, q_rows, k_rows, scale, causal,
+                                     cu_seqlens=None, cu_seqlens_k=None):
+        """Backward for selected rows only (bf16 inputs).
+
+        q_rows are numbered like the lse layout (dense (b*H + h)*Sq + i,
+        varlen h*Tq + t); k_rows like it over the K/V heads (dense
+        (b*Hkv + hk)*Sk + j, varlen hk*Tk + t).  Returns float64
+        (dq [nq, D], |dq|, dk [nk, D], dv [nk, Dv], |dk|, |dv|).
+        """
+        qb, kb, vb, gb = (_as_bits(t) for t in (q, k, v, dout))
+        cu_q = _cu(cu_seqlens)
+        cu_k = _cu(cu_seqlens_k) if cu_seqlens_k is not None else cu_q
+        B, H, Hkv, Sq, Sk, D, Dv = _layout(qb.shape, kb.shape, vb.shape, cu_q, cu_k)
+        qr = np.ascontiguousarray(np.asarray(q_rows, dtype=np.int64))
+        kr = np.ascontiguousarray(np.asarray(k_rows, dtype=np.int64))
+        dq = np.empty((len(qr), D))
+        dqm = np.empty((len(qr), D))
+        dk = np.empty((len(kr), D))
+        dv = np.empty((len(kr), Dv))
+        dkm = np.empty((len(kr), D))
+        dvm = np.empty((len(kr), Dv))
+        rc = self.lib.oracle_attn_bwd_rows_bf16(
+            _ptr(qb), _ptr(kb), _ptr(vb), _ptr(gb), _ptr(qr), len(qr), _ptr(dq), _ptr(dqm),
+            _ptr(kr), len(kr), _ptr(dk), _ptr(dv), _ptr(dkm), _ptr(dvm), B, H, Hkv, Sq, Sk, D,
+            Dv, float(scale), int(bool(causal)), _ptr(cu_q), _ptr(cu_k))
+        if rc != 0:
+            raise ValueError("oracle_attn_bwd_rows_bf16 rejected its arguments")
+        return dq, dqm, dk, dv, dkm, dvm
+
     def exp2(self, x) -> np.ndarray:
         """2**x in float64 for float32 inputs (what the device polynomial approximates)."""
         x = np.ascontiguousarray(x, dtype=np.float32)
@@ -205,6 +282,14 @@ def attention_bf16(*a, **kw):
 
 def attention_rows_bf16(*a, **kw):
     return lib().attention_rows_bf16(*a, **kw)
+
+
+def attention_backward(*a, **kw):
+    return lib().attention_backward(*a, **kw)
+
+
+def attention_backward_rows_bf16(*a, **kw):
+    return lib().attention_backward_rows_bf16(*a, **kw)
 
 
 def exp2(x):

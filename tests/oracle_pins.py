@@ -292,6 +292,166 @@ def check_rows_without_keys(o):
     assert np.array_equal(got_o[0, Lq - Lk, 0], v[0, 0, 0]), "first non-empty row"
 
 
+# ---------------------------------------------------------------------------
+# Backward pass: gradients of F = sum <dO, O> with respect to Q, K and V.
+# ---------------------------------------------------------------------------
+
+def _objective(o, q, k, v, g, scale, causal, cu=None, cu_k=None):
+    out, _ = o.attention_f64(q, k, v, scale, causal, cu, cu_k)
+    return float(np.sum(out * g))
+
+
+def _bwd_cases(rng):
+    """(name, q, k, v, dout, scale, causal, cu_q, cu_k) covering MHA, GQA,
+    D != Dv, varlen and query/key lengths that differ."""
+    cases = []
+    for causal in (False, True):
+        B, S, H, D = 2, 6, 2, 4
+        q, k, v, g = (rng.standard_normal((B, S, H, D)) for _ in range(4))
+        cases.append(("mha", q, k, v, g, 0.45, causal, None, None))
+    q = rng.standard_normal((1, 5, 4, 3))
+    k, v = rng.standard_normal((1, 5, 2, 3)), rng.standard_normal((1, 5, 2, 2))
+    cases.append(("gqa_dv", q, k, v, rng.standard_normal((1, 5, 4, 2)), 0.6, True, None, None))
+    cu = [0, 3, 7, 8]
+    q, k, v, g = (rng.standard_normal((8, 2, 3)) for _ in range(4))
+    cases.append(("varlen", q, k, v, g, 0.5, True, cu, None))
+    q, g = rng.standard_normal((1, 3, 1, 3)), rng.standard_normal((1, 3, 1, 3))
+    k, v = rng.standard_normal((1, 5, 1, 3)), rng.standard_normal((1, 5, 1, 3))
+    cases.append(("qk_lengths", q, k, v, g, 0.7, True, None, None))
+    return cases
+
+
+def check_bwd_finite_differences(o):
+    """<dF/dX, U> of the backward equals the central difference of the
+    forward oracle along a random direction U, for X = Q, K, V (fp64:
+    the difference quotient is exact to O(eps^2))."""
+    rng = np.random.default_rng(31)
+    eps = 1e-5
+    for name, q, k, v, g, scale, causal, cu, cu_k in _bwd_cases(rng):
+        grads = o.attention_backward(q, k, v, g, scale, causal, cu, cu_k)
+        for idx, x in enumerate((q, k, v)):
+            u = rng.standard_normal(x.shape)
+            args = [q, k, v]
+            args[idx] = x + eps * u
+            fp = _objective(o, *args, g, scale, causal, cu, cu_k)
+            args[idx] = x - eps * u
+            fm = _objective(o, *args, g, scale, causal, cu, cu_k)
+            fd = (fp - fm) / (2 * eps)
+            an = float(np.sum(grads[idx] * u))
+            assert abs(fd - an) <= 1e-7 * (1 + abs(fd)), (name, "dq dk dv".split()[idx], fd, an)
+
+
+def check_bwd_torch_autograd(o):
+    """The backward equals torch's float64 autograd through a masked softmax
+    (a library differentiation of the textbook formula), with grouped K/V
+    heads expanded by repetition and the causal mask bottom-right aligned."""
+    import torch
+    rng = np.random.default_rng(32)
+    for name, q, k, v, g, scale, causal, cu, cu_k in _bwd_cases(rng):
+        got = o.attention_backward(q, k, v, g, scale, causal, cu, cu_k)
+        tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+        tg = torch.tensor(g, dtype=torch.float64)
+        if cu is None:
+            segs = [(tq, tk, tv, tg)]
+        else:
+            segs = [(tq[None, a:b], tk[None, a:b], tv[None, a:b], tg[None, a:b])
+                    for a, b in zip(cu[:-1], cu[1:])]
+        total = 0
+        for sq, sk, sv, sg in segs:
+            G = sq.shape[2] // sk.shape[2]
+            kk = sk.repeat_interleave(G, dim=2)
+            vv = sv.repeat_interleave(G, dim=2)
+            logits = torch.einsum("bihd,bjhd->bhij", sq, kk) * scale
+            Lq, Lk = sq.shape[1], sk.shape[1]
+            if causal:
+                ii = torch.arange(Lq)[:, None]
+                jj = torch.arange(Lk)[None, :]
+                logits = logits.masked_fill(jj > ii + (Lk - Lq), -float("inf"))
+            p = torch.softmax(logits, dim=-1)
+            out = torch.einsum("bhij,bjhd->bihd", p, vv)
+            total = total + (out * sg).sum()
+        total.backward()
+        for got_x, ref_x, nm in zip(got, (tq.grad, tk.grad, tv.grad), ("dq", "dk", "dv")):
+            assert np.max(np.abs(got_x - ref_x.numpy())) <= 1e-12, (name, nm)
+
+
+def check_bwd_single_key(o):
+    """With one key every probability is 1: O_i = v_0 whatever Q and K are,
+    so dQ = dK = 0 and dV_0 = sum_i dO_i."""
+    rng = np.random.default_rng(33)
+    q, g = rng.standard_normal((2, 1, 3, 4)), rng.standard_normal((2, 1, 3, 4))
+    k, v = rng.standard_normal((2, 1, 3, 4)), rng.standard_normal((2, 1, 3, 4))
+    for causal in (False, True):
+        dq, dk, dv = o.attention_backward(q, k, v, g, 0.5, causal)
+        assert np.max(np.abs(dq)) <= 1e-15 and np.max(np.abs(dk)) <= 1e-15, causal
+        assert np.allclose(dv, g, rtol=0, atol=1e-15), causal
+
+
+def check_bwd_uniform_probabilities(o):
+    """Q = 0 makes every allowed probability 1/n_i: then dK = 0,
+    dV_j = sum over the rows i that use j of dO_i / n_i, and
+    dQ_i = scale * (mean_j <dO_i, v_j> k_j - mean_j <dO_i, v_j> * mean_j k_j),
+    the covariance form of the softmax Jacobian at equal logits."""
+    rng = np.random.default_rng(34)
+    B, S, H, D = 1, 5, 1, 3
+    q = np.zeros((B, S, H, D))
+    k, v, g = (rng.standard_normal((B, S, H, D)) for _ in range(3))
+    scale = 0.8
+    for causal in (False, True):
+        dq, dk, dv, dqm, dkm, dvm = o.attention_backward(q, k, v, g, scale, causal,
+                                                         magnitudes=True)
+        assert np.max(np.abs(dk)) <= 1e-14, causal
+        for j in range(S):
+            rows = [i for i in range(S) if not causal or j <= i]
+            n = [(i + 1) if causal else S for i in rows]
+            ref = sum(g[0, i, 0] / ni for i, ni in zip(rows, n))
+            ref_mag = sum(np.abs(g[0, i, 0]) / ni for i, ni in zip(rows, n))
+            assert np.allclose(dv[0, j, 0], ref, rtol=0, atol=1e-14), ("dv", causal, j)
+            assert np.allclose(dvm[0, j, 0], ref_mag, rtol=0, atol=1e-14), ("|dv|", causal, j)
+        for i in range(S):
+            n = i + 1 if causal else S
+            kk, vv = k[0, :n, 0], v[0, :n, 0]
+            dp = vv @ g[0, i, 0]
+            ref = scale * ((dp[:, None] * kk).mean(0) - dp.mean() * kk.mean(0))
+            assert np.allclose(dq[0, i, 0], ref, rtol=0, atol=1e-14), ("dq", causal, i)
+        for got, mag in ((dq, dqm), (dk, dkm), (dv, dvm)):
+            assert np.all(np.abs(got) <= mag + 1e-15), "a gradient exceeds its magnitude"
+
+
+def check_bwd_rows_match_full(o):
+    """The row-list entry point returns the rows of the full backward, for
+    dense and varlen inputs with grouped K/V heads."""
+    rng = np.random.default_rng(35)
+
+    def bits(x):
+        return (np.ascontiguousarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+    for cu in (None, [0, 4, 9]):
+        shape_q = (2, 5, 4, 8) if cu is None else (9, 4, 8)
+        shape_k = shape_q[:-2] + (2, 8)
+        q, g = bits(_bf16_grid(rng, shape_q)), bits(_bf16_grid(rng, shape_q))
+        k, v = bits(_bf16_grid(rng, shape_k)), bits(_bf16_grid(rng, shape_k))
+        full = o.attention_backward(q, k, v, g, 0.35, True, cu, magnitudes=True)
+        dq, dk, dv, dqm, dkm, dvm = full
+        H, Hk = 4, 2
+        if cu is None:
+            qrows = [(b * H + h) * 5 + i for b, h, i in ((0, 0, 0), (1, 3, 4), (0, 2, 3))]
+            krows = [(b * Hk + h) * 5 + j for b, h, j in ((0, 0, 0), (1, 1, 4), (1, 0, 2))]
+            qsel = [dq[0, 0, 0], dq[1, 4, 3], dq[0, 3, 2]]
+            ksel = [(0, 0, 0), (1, 4, 1), (1, 2, 0)]
+        else:
+            T = 9
+            qrows = [h * T + t for h, t in ((0, 0), (3, 8), (2, 5))]
+            krows = [h * T + t for h, t in ((0, 0), (1, 8), (0, 4))]
+            qsel = [dq[0, 0], dq[8, 3], dq[5, 2]]
+            ksel = [(0, 0), (8, 1), (4, 0)]
+        r = o.attention_backward_rows_bf16(q, k, v, g, qrows, krows, 0.35, True, cu)
+        assert np.array_equal(r[0], np.stack(qsel)), ("dq rows", cu)
+        assert np.array_equal(r[2], np.stack([dk[t] for t in ksel])), ("dk rows", cu)
+        assert np.array_equal(r[3], np.stack([dv[t] for t in ksel])), ("dv rows", cu)
+        assert np.array_equal(r[5], np.stack([dvm[t] for t in ksel])), ("|dv| rows", cu)
+
+
 ALL_CHECKS = [
     check_brute_force_tiny,
     check_equal_logits_mean_of_v,
@@ -310,4 +470,9 @@ ALL_CHECKS = [
     check_qk_lengths_brute_force_tiny,
     check_short_queries_are_the_last_rows_of_self_attention,
     check_rows_without_keys,
+    check_bwd_finite_differences,
+    check_bwd_torch_autograd,
+    check_bwd_single_key,
+    check_bwd_uniform_probabilities,
+    check_bwd_rows_match_full,
 ]

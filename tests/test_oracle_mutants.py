@@ -52,6 +52,22 @@ MUTANTS = [
      "*h = (int)(row % H);\n        *i = (int)((row / H) % S);"),
     ("sum_skips_first_key", "for (int j = 0; j < nkeys; ++j) {\n        s[j] = exp(s[j] - m);\n        l += s[j];",
      "for (int j = 0; j < nkeys; ++j) {\n        s[j] = exp(s[j] - m);\n        if (j) l += s[j];"),
+    ("bwd_delta_dropped_in_dq", "const double ds = p[j] * (dp[j] - delta);",
+     "const double ds = p[j] * dp[j];"),
+    ("bwd_delta_dropped_in_dk", "const double ds = p * (dp - st->delta);", "const double ds = p * dp;"),
+    ("bwd_dk_scale_dropped", "dk_row[d] += scale * ds * qd;", "dk_row[d] += ds * qd;"),
+    ("bwd_dq_scale_dropped", "dq_row[d] = scale * g;", "dq_row[d] = g;"),
+    ("bwd_dv_weighted_by_ds", "dv_row[d] += p * gd;", "dv_row[d] += ds * gd;"),
+    ("bwd_dp_reads_k", "acc += at(dout, obase + d) * at(v, vbase + d);",
+     "acc += at(dout, obase + d) * at(k, vbase + d);"),
+    ("bwd_key_rows_start_late", "i0 = j - (spk.len - spq.len);", "i0 = j - (spk.len - spq.len) + 1;"),
+    ("bwd_key_rows_top_left", "i0 = j - (spk.len - spq.len);", "i0 = j;"),
+    ("bwd_group_first_head_only", "const int h = hk * G + g;", "const int h = hk * G;"),
+    ("bwd_probs_unnormalised", "p[j] = exp(p[j] - *lse);", "p[j] = exp(p[j] - m);"),
+    ("bwd_lse_sign", "const double p = exp(scale * s - st->lse);",
+     "const double p = exp(scale * s + st->lse);"),
+    ("bwd_key_row_decode_swaps", "*j = (int)(row % S);\n        *hk = (int)((row / S) % Hkv);",
+     "*hk = (int)(row % Hkv);\n        *j = (int)((row / Hkv) % S);"),
 ]
 
 

@@ -85,6 +85,16 @@ def draw_qkv(shape, seed: int, q_std: float = 1.0, kv_std: float = 1.0, kv_heads
     return tuple(out)
 
 
+def draw_dout(shape, seed: int, std: float = 1.0):
+    """The output gradient dO of a backward problem as a CPU bf16 tensor of
+    the given shape (o's), N(0, std^2), from its own seeded stream."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed) + 7919)
+    x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    if std != 1.0:
+        x = x * std
+    return x.to(torch.bfloat16)
+
+
 def qk_lengths(w: Workload):
     """(query lengths, key lengths) of a workload whose queries have lengths of
     their own: key lengths as for varlen, query lengths uniform on q_range

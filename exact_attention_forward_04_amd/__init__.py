@@ -1,4 +1,4 @@
-"""MI355X (gfx950) exact attention forward: Python binding of libfa_mi355x.so.
+"""MI355X (gfx950) exact attention: Python binding of libfa_mi355x.so.
 
 Every computation runs in the HIP kernels of the shared library; this module
 only marshals arguments (torch is used for device memory and streams).  If
@@ -7,6 +7,8 @@ falling back to anything else.
 
     o, lse = attention(q, k, v, causal=True)          # q, k, v: [B,S,H,D] bf16 on cuda
     o, lse = attention(q, k, v, causal=True, cu_seqlens=cu, max_seqlen=S)  # [T,H,D]
+    dq, dk, dv = attention_backward(q, k, v, o, lse, do, causal=True)
+    o = attention_fn(q, k, v, causal=True)            # autograd: o.backward(...) runs fa_bwd
 
 The C ABI it wraps is declared in include/fa.h.
 """
@@ -63,6 +65,8 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd_general.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, P, P,
                                    ctypes.POINTER(Tuning)]
     lib.fa_fwd_general.restype = I
+    lib.fa_bwd.argtypes = [P] * 10 + [I, I, I, I, I, F, I, P, P]
+    lib.fa_bwd.restype = I
     lib.fa_tuning_default.argtypes = []
     lib.fa_tuning_default.restype = Tuning
     lib.fa_exp2_emu.argtypes = [P, P, LL, P]
@@ -192,6 +196,108 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
         rc = lib.fa_fwd_ex(*ptrs, B, H, S, D, float(scale), int(bool(causal)), cu_ptr, sp, tref)
         _check("fa_fwd_ex", rc)
     return o, lse
+
+
+def attention_backward(q, k, v, o, lse, dout, causal: bool = False,
+                       scale: Optional[float] = None, cu_seqlens=None,
+                       max_seqlen: Optional[int] = None, dq=None, dk=None, dv=None, delta=None,
+                       stream=None):
+    """Exact attention backward on the GPU (the fa_bwd entry point).
+
+    q, k, v, causal, scale, cu_seqlens and max_seqlen as given to attention()
+    (query and key lengths equal, D_v = D); o and lse its outputs; dout the
+    gradient with respect to o (o's shape, contiguous bf16).  Returns
+    (dq, dk, dv) shaped like q, k, v (bf16).  dq/dk/dv/delta may be passed
+    in to reuse buffers (delta: fp32 scratch of lse's shape).
+    """
+    import torch
+    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous bf16 CUDA tensor" % name)
+    if lse is None or lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous():
+        raise ValueError("lse must be the forward's contiguous fp32 CUDA tensor")
+    dense = cu_seqlens is None
+    nd = 4 if dense else 3
+    if any(t.dim() != nd for t in (q, k, v, o, dout)):
+        raise ValueError("dense inputs are [B, S, H, D]" if dense else "varlen inputs are [T, H, D]")
+    if tuple(k.shape) != tuple(v.shape) or k.shape[:-2] != q.shape[:-2] or \
+            k.shape[-1] != q.shape[-1] or tuple(o.shape) != tuple(q.shape) or \
+            tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("q, o, dout must share a shape; k, v another with the same tokens and D")
+    H, D, H_kv = q.shape[-2], q.shape[-1], k.shape[-2]
+    if H_kv < 1 or H % H_kv != 0:
+        raise ValueError("the K/V head count must divide the query head count")
+    if dense:
+        B, S = q.shape[0], q.shape[1]
+        lse_shape = (B, H, S)
+        cu_ptr = None
+    else:
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or \
+                not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be a contiguous int32 CUDA tensor")
+        if max_seqlen is None:
+            raise ValueError("varlen needs max_seqlen")
+        B, S = cu_seqlens.numel() - 1, int(max_seqlen)
+        lse_shape = (H, q.shape[0])
+        cu_ptr = cu_seqlens.data_ptr()
+    if tuple(lse.shape) != lse_shape:
+        raise ValueError("lse must have shape %s" % (lse_shape,))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = dq if dq is not None else torch.empty_like(q)
+    dk = dk if dk is not None else torch.empty_like(k)
+    dv = dv if dv is not None else torch.empty_like(v)
+    delta = delta if delta is not None else torch.empty(lse_shape, dtype=torch.float32,
+                                                        device=q.device)
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if tuple(t.shape) != tuple(ref.shape) or t.dtype != torch.bfloat16:
+            raise ValueError("%s must be bf16 of shape %s" % (name, tuple(ref.shape)))
+    if tuple(delta.shape) != lse_shape or delta.dtype != torch.float32:
+        raise ValueError("delta must be fp32 of shape %s" % (lse_shape,))
+    rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    delta.data_ptr(), B, H, H_kv, S, D, float(scale), int(bool(causal)), cu_ptr,
+                    _stream_ptr(stream))
+    _check("fa_bwd", rc)
+    return dq, dk, dv
+
+
+def _autograd_function():
+    import torch
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, causal, scale, cu_seqlens, max_seqlen):
+            o, lse = attention(q, k, v, causal=causal, scale=scale, cu_seqlens=cu_seqlens,
+                               max_seqlen=max_seqlen)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.cfg = (causal, scale, cu_seqlens, max_seqlen)
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse = ctx.saved_tensors
+            causal, scale, cu_seqlens, max_seqlen = ctx.cfg
+            dq, dk, dv = attention_backward(q, k, v, o, lse, do.contiguous(), causal=causal,
+                                            scale=scale, cu_seqlens=cu_seqlens,
+                                            max_seqlen=max_seqlen)
+            return dq, dk, dv, None, None, None, None
+
+    return _Attention
+
+
+_attention_fn = None
+
+
+def attention_fn(q, k, v, causal: bool = False, scale: Optional[float] = None,
+                 cu_seqlens=None, max_seqlen: Optional[int] = None):
+    """attention() as a differentiable torch op: returns o, and o.backward()
+    computes the input gradients with fa_bwd."""
+    global _attention_fn
+    if _attention_fn is None:
+        _attention_fn = _autograd_function()
+    return _attention_fn.apply(q, k, v, causal, scale, cu_seqlens, max_seqlen)
 
 
 def exp2_emu(x, stream=None):

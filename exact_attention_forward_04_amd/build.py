@@ -1,6 +1,6 @@
 """Ahead-of-time build of the gfx950 attention library (libfa_mi355x.so).
 
-hipcc compiles csrc/fa_fwd.hip for gfx950 into a shared library that sits
+hipcc compiles csrc/fa_fwd.hip (forward) and csrc/fa_bwd.hip (backward) for gfx950 into a shared library that sits
 next to this file; the Python binding loads it with ctypes.  Packed-FP32
 instruction selection is disabled (-packed-fp32-ops) on purpose.
 """
@@ -12,8 +12,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, "fa_fwd.hip")]
-HEADERS = [os.path.join(CSRC, n) for n in ("fa_sched.h", "exp2_poly.h")] + \
+SOURCES = [os.path.join(CSRC, "fa_fwd.hip"), os.path.join(CSRC, "fa_bwd.hip")]
+HEADERS = [os.path.join(CSRC, n) for n in ("fa_sched.h", "exp2_poly.h", "fa_tile.h", "fa_host.h")] + \
           [os.path.join(ROOT, "include", "fa.h")]
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)

@@ -1,0 +1,543 @@
+// fa_bwd.hip -- exact attention backward for MI355X (gfx950): kernels and C ABI.
+//
+// Given Q, K, V, the forward's O and LSE and the output gradient dO, this
+// computes dQ, dK and dV, the gradients of sum <dO, O>.  Like the forward it
+// never stores a score matrix: each block of S is recomputed from Q and K
+// and consumed on chip (FlashAttention-4 paper, section 3.2: recompute S,
+// then the products that give dP, dV, dQ and dK).
+//
+// The gfx950 design splits the work into two kernels so that every gradient
+// row is owned by exactly one workgroup and reduced in its registers in a
+// fixed order:
+//
+//   fa_bwd_dq    one tile of 32*NW query rows of one head per workgroup, as
+//                in the forward; K and V stream through LDS in blocks of 64
+//                keys.  In its prologue it forms Delta_i = <dO_i, O_i> for
+//                its rows (stored for the second kernel).  Per block:
+//                  S^T = K Q^T,  dP^T = V dO^T               (MFMA)
+//                  P = exp2(c S - LSE log2 e),  dS = P (dP - Delta)
+//                  dQ^T += K^T dS^T                          (MFMA)
+//   fa_bwd_dkdv  one tile of 32*NW keys of one K/V head per workgroup; the
+//                Q, dO, LSE and Delta blocks of every query head that reads
+//                this K/V head stream through LDS in blocks of 64 rows.  Per
+//                block:
+//                  S = Q K^T,  dP = dO V^T                   (MFMA)
+//                  P, dS as above
+//                  dV^T += dO^T P,  dK^T += Q^T dS           (MFMA)
+//
+// In both kernels the wave's own 32 rows (query rows, or keys) sit in VGPRs
+// as the B operand of v_mfma_f32_32x32x16_bf16, so the lane index is the
+// row: S, dP, P and dS then hold 16 entries of the lane's row per 32-row
+// sub-block, and the bf16 P and dS registers are directly the B operands of
+// the products that contract over the streamed rows, whose A operands come
+// from LDS through ds_read_b64_tr_b16 (the same layout the forward uses for
+// V^T).
+//
+// The paper's kernel runs five products per block and adds dQ across
+// workgroups with atomics in global memory, with a semaphore-ordered mode
+// for reproducible results (section 3.2.4).  Here the dQ kernel recomputes S
+// and dP instead (seven products per block pair in all): no atomics, no
+// workspace beyond Delta, no ordering protocol, and bitwise reproducible
+// results in every mode.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "fa.h"
+#include "fa_host.h"
+#include "fa_sched.h"
+#include "fa_tile.h"
+
+namespace {
+
+template <int D>
+struct BwdCfg {
+  // dQ: eight waves (two per SIMD), 32 query rows each.
+  static constexpr int NW_DQ = 8;
+  // dK/dV: the two D-wide fp32 accumulators of a wave take 2*D/32*16 VGPRs
+  // (128 at D = 128), so D = 128 runs one wave per SIMD.
+  static constexpr int NW_KV = (D == 128) ? 4 : 8;
+  static constexpr int BM = 32 * NW_DQ;  // query rows per dQ tile
+  static constexpr int BN = 32 * NW_KV;  // keys per dK/dV tile
+  static constexpr int BLK = kBN * D * 2;  // bytes of one 64-row block in LDS
+  static constexpr int STATS = 2 * kBN * 4;  // LSE and Delta of one block
+  // LDS: two stages of [K | V] blocks (dQ), or of [Q | dO] blocks followed
+  // by two stages of statistics (dK/dV).  Blocks sit at multiples of BLK, as
+  // the operand addressing needs.
+  static constexpr int LDS_DQ = 4 * BLK;
+  static constexpr int LDS_KV = 4 * BLK + 2 * STATS;
+};
+
+struct BwdArgs {
+  const __bf16 *q, *k, *v, *o, *dout;
+  const float *lse;
+  __bf16 *dq, *dk, *dv;
+  float *delta;
+  const int *cu;  // varlen offsets (queries and keys alike) or nullptr
+  int B, H, Hkv, S;
+  float c;      // scale * log2(e)
+  float scale;
+};
+
+struct Span {
+  long long tok0;
+  int L;
+};
+
+template <bool VARLEN>
+__device__ __forceinline__ Span seq_of(const BwdArgs &a, int b) {
+  if constexpr (VARLEN) {
+    const int Lr = a.cu[b + 1] - a.cu[b];
+    return {(long long)a.cu[b], Lr < 0 ? 0 : (Lr > a.S ? a.S : Lr)};
+  } else {
+    return {(long long)b * a.S, a.S};
+  }
+}
+
+// Index of query row i of (b, h) in the LSE / Delta layout.
+template <bool VARLEN>
+__device__ __forceinline__ long long stat_index(const BwdArgs &a, int b, int h, long long tok0,
+                                                int i) {
+  if constexpr (VARLEN) return (long long)h * a.cu[a.B] + tok0 + i;
+  else return ((long long)b * a.H + h) * a.S + i;
+}
+
+// One 4-byte-per-lane copy: global (64-bit lane address) -> LDS at m0 + 4*lane.
+__device__ __forceinline__ void dma4(const float *gaddr, unsigned lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off"
+      :
+      : "s"(lds_addr), "v"(gaddr)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Store the transposed accumulators acc[dt] (row d = 32dt + 8i + 4(l/32) + j,
+// column = the lane's row) times f as bf16 into the lane's output row.
+template <int D>
+__device__ __forceinline__ void store_rows(__bf16 *row_ptr, const f32x16 *acc, float f, int hh) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  __bf16 *op = row_ptr + 4 * hh;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x4 out = {(__bf16)(acc[dt][4 * i + 0] * f), (__bf16)(acc[dt][4 * i + 1] * f),
+                    (__bf16)(acc[dt][4 * i + 2] * f), (__bf16)(acc[dt][4 * i + 3] * f)};
+      *(bf16x4 *)(op + 32 * dt + 8 * i) = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and Delta): one tile of BM query rows of head h.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(BwdCfg<D>::NW_DQ * kWave, BwdCfg<D>::NW_DQ / 4) void fa_bwd_dq(
+    BwdArgs a) {
+  using C = BwdCfg<D>;
+  constexpr int NW = C::NW_DQ;
+  constexpr int NS = D / 16;
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  char LDS_AS *lds = (char LDS_AS *)lds_raw;
+
+  // Tiles of one (b, h) are B*H launch slots apart, so with B*H a multiple
+  // of 8 they share an XCD (and its L2 copy of K and V).  Causal: the last
+  // (longest) m-blocks start first.
+  const int nmb = fa::ceil_div(a.S, C::BM);
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int r = blockIdx.x / BH;
+  const int mb = CAUSAL ? nmb - 1 - r : r;
+  const int b = bh / a.H, h = bh % a.H;
+  const Span sp = seq_of<VARLEN>(a, b);
+  const int L = sp.L;
+  const int m0 = mb * C::BM;
+  if (m0 >= L) return;  // workgroup-uniform
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int hh = lane >> 5;
+  const int hk = h / (a.H / a.Hkv);
+  const int wrow0 = m0 + 32 * wave;
+  const bool active = wrow0 < L;
+  const int wrow_last = (wrow0 + 31 < L - 1) ? wrow0 + 31 : L - 1;
+  const int row = wrow0 + (lane & 31);
+  const int rowc = row < L ? row : L - 1;  // rows past L read row L-1 (never stored)
+
+  // Q and dO rows as B operands (lane: row l%32, d = 16s + 8(l/32) + 0..7);
+  // Delta = <dO, O> of the row (two half-rows, then one permlane swap).
+  bf16x8 qf[NS], gf[NS];
+  float delta, lse2;
+  {
+    const long long si = stat_index<VARLEN>(a, b, h, sp.tok0, rowc);
+    lse2 = a.lse[si] * kLog2e;
+    const long long base = ((sp.tok0 + rowc) * a.H + h) * (long long)D + 8 * hh;
+    const bf16x8 *qp = (const bf16x8 *)(a.q + base);
+    const bf16x8 *gp = (const bf16x8 *)(a.dout + base);
+    const bf16x8 *op = (const bf16x8 *)(a.o + base);
+    float dsum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qf[s] = qp[2 * s];
+      gf[s] = gp[2 * s];
+      const bf16x8 of = op[2 * s];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)gf[s][e], (float)of[e], dsum);
+    }
+    delta = sum_halves(dsum);
+    if (hh == 0 && row < L) a.delta[si] = delta;
+    // Keep the operands in registers for the whole tile (a re-fetch inside
+    // the loop would wait behind the K/V copies on the vector-memory counter).
+#pragma unroll
+    for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(qf[s]), "+v"(gf[s]));
+    asm volatile("" : "+v"(lse2), "+v"(delta));
+  }
+
+  int n_end = L;
+  if (CAUSAL) n_end = (m0 + C::BM < L) ? m0 + C::BM : L;
+  const int nblocks = fa::ceil_div(n_end, kBN);
+
+  BlockLoader<D, NW> ld;
+  ld.init(a.Hkv, wave, lane);
+  constexpr int LOADS_BLOCK = 2 * BlockLoader<D, NW>::LOADS;
+  LdsAddr<D> la;
+  la.init(lane);
+  auto kbuf = [&](int j) { return lds + (j & 1) * 2 * C::BLK; };
+  auto vbuf = [&](int j) { return lds + (j & 1) * 2 * C::BLK + C::BLK; };
+  auto issue = [&](int j) {
+    ld.issue(a.k, sp.tok0, a.Hkv, hk, j * kBN, L, kbuf(j));
+    ld.issue(a.v, sp.tok0, a.Hkv, hk, j * kBN, L, vbuf(j));
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.0f;
+
+  if (nblocks > 0) issue(0);
+  for (int j = 0; j < nblocks; ++j) {
+    if (j + 1 < nblocks) {
+      issue(j + 1);
+      wait_vmcnt<LOADS_BLOCK>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_nofence();
+    const int n0 = j * kBN;
+    if (active && (!CAUSAL || n0 <= wrow_last)) {
+      // ---- S^T = K Q^T and dP^T = V dO^T (keys on the M side)
+      const unsigned ka = la.ky + lds_u32(kbuf(j));
+      const unsigned va = la.ky + lds_u32(vbuf(j));
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s[i][e] = 0.0f;
+          dp[i][e] = 0.0f;
+        }
+      // (S first, then dP: the scheduling barriers bound how many operand
+      // reads the compiler hoists, which keeps two waves per SIMD in VGPRs.)
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const bf16x8 k0 = read_k<D>(ka, 0, st), k1 = read_k<D>(ka, 1, st);
+        s[0] = mfma(k0, qf[st], s[0]);
+        s[1] = mfma(k1, qf[st], s[1]);
+        if (st % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const bf16x8 v0 = read_k<D>(va, 0, st), v1 = read_k<D>(va, 1, st);
+        dp[0] = mfma(v0, gf[st], dp[0]);
+        dp[1] = mfma(v1, gf[st], dp[1]);
+        if (st % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      // ---- P and dS.  Entry e of sub-block i is key n0 + 32i + 8(e>>2) +
+      // 4h + (e&3) of the lane's row; it is kept iff its in-block offset is
+      // below lim (key < L, and key <= row when causal).
+      const bool need_mask = (n0 + kBN > L) || (CAUSAL && n0 + kBN - 1 > wrow0);
+      const int lim = (CAUSAL ? (row + 1 < L ? row + 1 : L) : L) - n0 - 4 * hh;
+      bf16x8 ds8[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int off = 32 * i + 8 * (e >> 2) + (e & 3);
+          float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -lse2));
+          if (need_mask) p = off < lim ? p : 0.0f;
+          ds8[2 * i + (e >> 3)][e & 7] = (__bf16)(p * (dp[i][e] - delta));
+        }
+      // ---- dQ^T += K^T dS^T (K^T by transposed reads of the K block)
+      const unsigned kt0 = la.vw0 + lds_u32(kbuf(j)), kt1 = la.vw1 + lds_u32(kbuf(j));
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma(read_vt<D>(kt0, kt1, t, dt), ds8[t], acc[dt]);
+    }
+    barrier_after_reads();  // every wave is done with this stage
+  }
+
+  if (active && row < L)
+    store_rows<D>(a.dq + ((sp.tok0 + row) * a.H + h) * (long long)D, acc, a.scale, hh);
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV: one tile of BN keys of K/V head hk.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) void fa_bwd_dkdv(
+    BwdArgs a) {
+  using C = BwdCfg<D>;
+  constexpr int NW = C::NW_KV;
+  constexpr int NS = D / 16;
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  char LDS_AS *lds = (char LDS_AS *)lds_raw;
+
+  // Tiles of one (b, hk) are B*Hkv slots apart (same XCD when B*Hkv is a
+  // multiple of 8).  Causal: the first key tiles, which every later query
+  // row reads, are the longest and start first.
+  const int BK = a.B * a.Hkv;
+  const int bhk = blockIdx.x % BK;
+  const int nb = blockIdx.x / BK;
+  const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const Span sp = seq_of<VARLEN>(a, b);
+  const int L = sp.L;
+  const int n0t = nb * C::BN;
+  if (n0t >= L) return;  // workgroup-uniform
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int hh = lane >> 5;
+  const int G = a.H / a.Hkv;
+  const int key0 = n0t + 32 * wave;  // first key of this wave
+  const bool active = key0 < L;
+  const int key = key0 + (lane & 31);
+  const int keyc = key < L ? key : L - 1;  // keys past L read key L-1 (never stored)
+
+  // K and V rows as B operands (lane: key l%32, d = 16s + 8(l/32) + 0..7).
+  bf16x8 kf[NS], vf[NS];
+  {
+    const long long base = ((sp.tok0 + keyc) * a.Hkv + hk) * (long long)D + 8 * hh;
+    const bf16x8 *kp = (const bf16x8 *)(a.k + base);
+    const bf16x8 *vp = (const bf16x8 *)(a.v + base);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      kf[s] = kp[2 * s];
+      vf[s] = vp[2 * s];
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(kf[s]), "+v"(vf[s]));
+  }
+
+  // Query blocks: for each query head of the group, the 64-row blocks from
+  // the one holding the tile's first key (causal) to the end.
+  const int nqb = fa::ceil_div(L, kBN);
+  const int qb0 = CAUSAL ? n0t / kBN : 0;
+  const int per = nqb - qb0;
+  const int nblocks = G * per;
+
+  BlockLoader<D, NW> ld;
+  ld.init(a.H, wave, lane);
+  constexpr int LOADS_BLOCK = 2 * BlockLoader<D, NW>::LOADS;
+  LdsAddr<D> la;
+  la.init(lane);
+  auto qbuf = [&](int t) { return lds + (t & 1) * 2 * C::BLK; };
+  auto gbuf = [&](int t) { return lds + (t & 1) * 2 * C::BLK + C::BLK; };
+  auto sbuf = [&](int t) { return lds + 4 * C::BLK + (t & 1) * C::STATS; };
+  // Block t: Q and dO rows (every wave), LSE (wave 0) and Delta (wave 1) of
+  // its 64 rows, one row per lane, rows past L reading row L-1.
+  auto issue = [&](int t) {
+    const int h = hk * G + t / per;
+    const int m0 = (qb0 + t % per) * kBN;
+    ld.issue(a.q, sp.tok0, a.H, h, m0, L, qbuf(t));
+    ld.issue(a.dout, sp.tok0, a.H, h, m0, L, gbuf(t));
+    if (wave < 2) {
+      const int rr = m0 + lane < L ? m0 + lane : L - 1;
+      const float *src = (wave == 0 ? a.lse : a.delta) + stat_index<VARLEN>(a, b, h, sp.tok0, rr);
+      dma4(src, lds_u32(sbuf(t)) + (unsigned)wave * (kBN * 4));
+    }
+  };
+  // Wait for block t while block t+1 may still be in flight (waves 0 and 1
+  // issue one statistics copy per block on top of the row copies).
+  auto wait_block = [&](bool next_in_flight) {
+    if (!next_in_flight) wait_vmcnt<0>();
+    else if (wave < 2) wait_vmcnt<LOADS_BLOCK + 1>();
+    else wait_vmcnt<LOADS_BLOCK>();
+  };
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dk[dt][e] = 0.0f;
+      dv[dt][e] = 0.0f;
+    }
+
+  if (nblocks > 0) issue(0);
+  for (int t = 0; t < nblocks; ++t) {
+    if (t + 1 < nblocks) issue(t + 1);
+    wait_block(t + 1 < nblocks);
+    barrier_nofence();
+    const int m0 = (qb0 + t % per) * kBN;
+    if (active && (!CAUSAL || m0 + kBN - 1 >= key0)) {
+      // ---- S = Q K^T and dP = dO V^T (query rows on the M side)
+      const unsigned qa = la.ky + lds_u32(qbuf(t));
+      const unsigned ga = la.ky + lds_u32(gbuf(t));
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s[i][e] = 0.0f;
+          dp[i][e] = 0.0f;
+        }
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const bf16x8 q0 = read_k<D>(qa, 0, st), q1 = read_k<D>(qa, 1, st);
+        const bf16x8 g0 = read_k<D>(ga, 0, st), g1 = read_k<D>(ga, 1, st);
+        s[0] = mfma(q0, kf[st], s[0]);
+        s[1] = mfma(q1, kf[st], s[1]);
+        dp[0] = mfma(g0, vf[st], dp[0]);
+        dp[1] = mfma(g1, vf[st], dp[1]);
+      }
+      // ---- P and dS.  Entry e of sub-block i is query row m0 + 32i +
+      // 8(e>>2) + 4h + (e&3) against the lane's key; it is kept iff its
+      // in-block offset off satisfies lo <= off < hi (row < L, and row >=
+      // key when causal).  LSE and Delta of the four rows 4h + (0..3) of a
+      // group come from LDS as one 16-byte read each.
+      const float LDS_AS *lse_l = (const float LDS_AS *)sbuf(t);
+      const float LDS_AS *del_l = lse_l + kBN;
+      const bool need_mask = (m0 + kBN > L) || (CAUSAL && m0 < key0 + 31);
+      const int hi = L - m0 - 4 * hh;
+      const int lo = CAUSAL ? key - m0 - 4 * hh : INT_MIN;
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      bf16x8 p8[4], ds8[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int r0 = 32 * i + 8 * g4 + 4 * hh;
+          const f32x4 l4 = *(const f32x4 LDS_AS *)(lse_l + r0);
+          const f32x4 d4 = *(const f32x4 LDS_AS *)(del_l + r0);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int e = 4 * g4 + jj;
+            const int off = 32 * i + 8 * g4 + jj;
+            float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -l4[jj] * kLog2e));
+            if (need_mask) p = (off < hi && off >= lo) ? p : 0.0f;
+            const int tt = 2 * i + (e >> 3);
+            p8[tt][e & 7] = (__bf16)p;
+            ds8[tt][e & 7] = (__bf16)(p * (dp[i][e] - d4[jj]));
+          }
+        }
+      // ---- dV^T += dO^T P and dK^T += Q^T dS (transposed reads of the blocks)
+      const unsigned gt0 = la.vw0 + lds_u32(gbuf(t)), gt1 = la.vw1 + lds_u32(gbuf(t));
+      const unsigned qt0 = la.vw0 + lds_u32(qbuf(t)), qt1 = la.vw1 + lds_u32(qbuf(t));
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          dv[dt] = mfma(read_vt<D>(gt0, gt1, tt, dt), p8[tt], dv[dt]);
+          dk[dt] = mfma(read_vt<D>(qt0, qt1, tt, dt), ds8[tt], dk[dt]);
+        }
+    }
+    barrier_after_reads();  // every wave is done with this stage
+  }
+
+  if (active && key < L) {
+    const long long rowoff = ((sp.tok0 + key) * a.Hkv + hk) * (long long)D;
+    store_rows<D>(a.dk + rowoff, dk, a.scale, hh);
+    store_rows<D>(a.dv + rowoff, dv, 1.0f, hh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+int validate_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
+                 int Hkv, int S, int D, float scale, int causal) {
+  const void *bufs[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void *p : bufs)
+    if (!p || !aligned16(p)) return FA_ERR_INVALID_ARG;
+  if (!lse || !delta) return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3) || (reinterpret_cast<uintptr_t>(delta) & 3))
+    return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA_ERR_INVALID_ARG;
+  if (Hkv <= 0 || H % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * S > (1LL << 31) - 1 || (long long)S * H > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+int launch_bwd(const BwdArgs &a, hipStream_t st) {
+  using C = BwdCfg<D>;
+  const long long g1 = (long long)a.B * a.H * fa::ceil_div(a.S, C::BM);
+  const long long g2 = (long long)a.B * a.Hkv * fa::ceil_div(a.S, C::BN);
+  if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  auto k1 = fa_bwd_dq<D, CAUSAL, VARLEN>;
+  auto k2 = fa_bwd_dkdv<D, CAUSAL, VARLEN>;
+  if (!allow_lds(k1, C::LDS_DQ) || !allow_lds(k2, C::LDS_KV)) return FA_ERR_HIP;
+  // dQ first: it also writes Delta, which the dK/dV kernel reads.
+  hipLaunchKernelGGL(k1, dim3((unsigned)g1), dim3(C::NW_DQ * kWave), C::LDS_DQ, st, a);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  hipLaunchKernelGGL(k2, dim3((unsigned)g2), dim3(C::NW_KV * kWave), C::LDS_KV, st, a);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+template <int D>
+int dispatch_bwd(const BwdArgs &a, bool causal, bool varlen, hipStream_t st) {
+  if (causal) return varlen ? launch_bwd<D, true, true>(a, st) : launch_bwd<D, true, false>(a, st);
+  return varlen ? launch_bwd<D, false, true>(a, st) : launch_bwd<D, false, false>(a, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H, int H_kv,
+           int S, int D, float scale, int causal, const int *cu_seqlens, void *stream) {
+  int rc = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, S, D, scale, causal);
+  if (rc != FA_OK) return rc;
+  DeviceInfo *dev = nullptr;
+  rc = current_device(&dev);
+  if (rc != FA_OK) return rc;
+  BwdArgs a;
+  a.q = (const __bf16 *)q;
+  a.k = (const __bf16 *)k;
+  a.v = (const __bf16 *)v;
+  a.o = (const __bf16 *)o;
+  a.dout = (const __bf16 *)dout;
+  a.lse = lse;
+  a.dq = (__bf16 *)dq;
+  a.dk = (__bf16 *)dk;
+  a.dv = (__bf16 *)dv;
+  a.delta = delta;
+  a.cu = cu_seqlens;
+  a.B = B;
+  a.H = H;
+  a.Hkv = H_kv;
+  a.S = S;
+  a.c = scale * kLog2e;
+  a.scale = scale;
+  hipStream_t st = (hipStream_t)stream;
+  const bool varlen = cu_seqlens != nullptr;
+  if (D == 64) return dispatch_bwd<64>(a, causal, varlen, st);
+  return dispatch_bwd<128>(a, causal, varlen, st);
+}
+
+}  // extern "C"

@@ -178,6 +178,45 @@ int fa_fwd_general(const void *q, const void *k, const void *v, void *o, float *
                    const fa_tuning *tuning);
 
 /*
+ * fa_bwd -- exact attention backward (FlashAttention-4 paper, section 3.2,
+ * "attention backward pass": S is recomputed block by block from Q and K,
+ * then dP, dV, dQ and dK follow from it).
+ *
+ * With P_ij = exp(scale * <q_i, k_j> - lse_i) over the allowed keys (the
+ * forward's probabilities) and dO the gradient of a loss with respect to o,
+ * computes the gradients of that loss:
+ *   delta_i = <dO_i, o_i>                                      (fp32 output)
+ *   dS_ij   = P_ij (<dO_i, v_j> - delta_i)
+ *   dq_i    = scale * sum_j dS_ij k_j                          (bf16 output)
+ *   dk_j    = scale * sum_(h, i) dS_ij q_i                     (bf16 output)
+ *   dv_j    = sum_(h, i) P_ij dO_i                             (bf16 output)
+ * where (h, i) runs over the rows of every query head that reads K/V head
+ * j's head (grouped-query attention sums the group's contributions).
+ *
+ * q, k, v, cu_seqlens, B, H, H_kv, S, D, scale and causal are those of the
+ * forward call that produced o and lse (query and key lengths are equal).
+ * Layouts (16-byte aligned base pointers; lse and delta 4-byte aligned):
+ *   q, o, dout, dq: bf16 [B, S, H, D]    (varlen [T, H, D])
+ *   k, v, dk, dv:   bf16 [B, S, H_kv, D] (varlen [T, H_kv, D])
+ *   lse, delta:     fp32 [B, H, S]       (varlen [H, T])
+ * o and lse are read as the forward wrote them (lse in natural-log units).
+ * delta is caller-owned scratch that this call fills; dq, dk, dv and delta
+ * must not alias any input.  Every gradient row is accumulated by one
+ * workgroup in a fixed order, so results are bitwise reproducible, without
+ * atomics.  Supported D: 64 and 128.
+ *
+ * Errors (nothing is launched): FA_ERR_INVALID_ARG for a null or misaligned
+ * pointer, a size <= 0, H not a multiple of H_kv, a non-finite or
+ * non-positive scale or causal not 0/1; FA_ERR_UNSUPPORTED for another D or
+ * sizes beyond 32-bit row indexing; FA_ERR_NO_DEVICE when no gfx950 is
+ * current; FA_ERR_HIP for a failed launch.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
+           int H_kv, int S, int D, float scale, int causal, const int *cu_seqlens,
+           void *stream);
+
+/*
  * fa_exp2_emu -- test hook: y[i] = the device's polynomial 2^x[i] for n
  * floats (device pointers, 4-byte aligned).  The function is the one the
  * attention kernel uses for its emulated exponentials: Cody-Waite
@@ -223,7 +262,7 @@ int fa_num_workers(int D, int *workers_out);
 const char *fa_status_string(int status);
 
 /* Library ABI version: 100 * major + minor (101: fa_fwd_gqa; 102: fa_fwd_hd;
- * 103: fa_fwd_general). */
+ * 103: fa_fwd_general; 104: fa_bwd). */
 int fa_version(void);
 
 #ifdef __cplusplus

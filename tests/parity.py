@@ -95,3 +95,38 @@ def assert_close(st, what=""):
     assert st["o_mean"] <= O_MEAN, ("mean |dO|", what, st)
     if "lse_max" in st:
         assert st["lse_max"] <= LSE_MAX, ("max |dLSE|", what, st)
+
+
+# ---- backward (gradients dQ, dK, dV; bf16 outputs)
+#
+# Gate, derived from the arithmetic: a gradient g is a sum of terms whose
+# bf16 operands (P or dS, and O inside Delta = <dO, O>) carry a relative
+# rounding error of at most u = 2^-8 each, so its error before the output
+# rounding is at most about u * A, with A the sum of the terms' absolute
+# values (the oracle returns A next to g); the output rounding adds at most
+# u * |g|.  The gate allows twice the operand term, for fp32 accumulation
+# and exp2 error:  |g_gpu - g| <= 2^-8 |g| + 2^-7 A  elementwise, and a
+# relative RMS error ||g_gpu - g|| / ||g|| <= 1e-2 over the tensor (an
+# emulation of the kernel's rounding in fp32 gives 2.3e-3 to 3.2e-3).
+GRAD_REL_RMS = 1e-2
+
+
+def compare_grad(g_gpu, g_ref, mag):
+    g_gpu = np.asarray(g_gpu, np.float64)
+    g_ref = np.asarray(g_ref, np.float64)
+    mag = np.asarray(mag, np.float64)
+    err = np.abs(g_gpu - g_ref)
+    bound = 2.0 ** -8 * np.abs(g_ref) + 2.0 ** -7 * mag
+    nrm = float(np.sqrt((g_ref ** 2).sum()))
+    return {
+        "max_err": float(err.max()) if err.size else 0.0,
+        "bound_use": float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0,
+        "rel_rms": float(np.sqrt((err ** 2).sum()) / nrm) if nrm > 0 else float(err.max(initial=0.0)),
+        "finite": bool(np.all(np.isfinite(g_gpu))),
+    }
+
+
+def assert_grad_close(st, what=""):
+    assert st["finite"], ("non-finite gradient", what, st)
+    assert st["bound_use"] <= 1.0, ("elementwise gradient bound", what, st)
+    assert st["rel_rms"] <= GRAD_REL_RMS, ("relative RMS gradient error", what, st)

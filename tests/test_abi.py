@@ -148,3 +148,49 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.attention(q, q, q)
+
+
+def bwd_call(**kw):
+    """fa_bwd with valid arguments except those overridden."""
+    a = dict(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, dk=A, dv=A, delta=A, B=1, H=8, H_kv=2,
+             S=64, D=128, scale=0.1, causal=1, cu=None)
+    a.update(kw)
+    return fa.load().fa_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"],
+                            a["dk"], a["dv"], a["delta"], a["B"], a["H"], a["H_kv"], a["S"],
+                            a["D"], a["scale"], a["causal"], a["cu"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dout=None), fa.FA_ERR_INVALID_ARG),
+    (dict(delta=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=A + 8), fa.FA_ERR_INVALID_ARG),        # not 16-byte aligned
+    (dict(lse=A + 2), fa.FA_ERR_INVALID_ARG),       # not 4-byte aligned
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(S=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(H_kv=3), fa.FA_ERR_INVALID_ARG),          # does not divide H
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(D=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(D=192), fa.FA_ERR_UNSUPPORTED),
+    (dict(S=1 << 30, H=8), fa.FA_ERR_UNSUPPORTED),  # beyond 32-bit row indexing
+])
+def test_backward_validation_rejects(kw, expect):
+    assert bwd_call(**kw) == expect
+
+
+def test_backward_valid_call_without_gpu_reports_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert bwd_call() == fa.FA_ERR_NO_DEVICE
+    assert bwd_call(D=64, H_kv=8, causal=0) == fa.FA_ERR_NO_DEVICE
+
+
+def test_backward_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError):
+        fa.attention_backward(q, q, q, q, lse, q)

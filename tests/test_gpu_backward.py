@@ -1,0 +1,168 @@
+"""GPU parity of the backward pass: fa_bwd (through the C ABI) against the
+fp64 oracle's gradients.
+
+The forward runs on the GPU first (its o and lse are fa_bwd's inputs, as in
+training); dO is drawn from its own seeded stream.  Small shapes are
+compared element by element on every gradient (several row and key tiles,
+ragged tails, both masks, D = 64 and 128, grouped K/V heads, packed
+variable-length batches); the 8k causal shape is compared on sampled query
+and key rows.  The gate, derived from the arithmetic, is in parity.py.
+Run-to-run reproducibility is checked bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_forward_04_amd as fa
+import oracle
+from attn_inputs import WORKLOADS, cu_seqlens_of, draw_dout, draw_qkv
+from parity import assert_grad_close, compare_grad, tensor_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def note(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_grads(q, k, v, g, causal, scale, cu=None, S=None):
+    """Forward then backward on the GPU; returns CPU (dq, dk, dv) tensors."""
+    dq_, dk_, dv_, dg = (t.cuda() for t in (q, k, v, g))
+    dcu = None if cu is None else torch.from_numpy(np.asarray(cu, np.int32)).cuda()
+    o, lse = fa.attention(dq_, dk_, dv_, causal=causal, scale=scale, cu_seqlens=dcu,
+                          max_seqlen=S)
+    grads = fa.attention_backward(dq_, dk_, dv_, o, lse, dg, causal=causal, scale=scale,
+                                  cu_seqlens=dcu, max_seqlen=S)
+    torch.cuda.synchronize()
+    return tuple(t.cpu() for t in grads)
+
+
+def full_bwd_check(q, k, v, g, causal, scale, cu=None, S=None, what=""):
+    note(what, "q", tuple(q.shape), "k", tuple(k.shape), "causal", causal)
+    got = gpu_grads(q, k, v, g, causal, scale, cu, S)
+    ref = oracle.attention_backward(q, k, v, g, scale, causal, cu, magnitudes=True)
+    for name, gg, rr, mm in zip(("dq", "dk", "dv"), got, ref[:3], ref[3:]):
+        st = compare_grad(tensor_to_f64(gg), rr, mm)
+        note(what, name, st)
+        assert_grad_close(st, (what, name))
+    return got
+
+
+# ---- full element-by-element parity on shapes the oracle finishes quickly
+# S = 333: one and a half 256-row query tiles, two or three key tiles, five
+# 64-row blocks and a ragged tail of 13 rows.
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_small(D, causal):
+    B, S, H = 2, 333, 3
+    q, k, v = draw_qkv((B, S, H, D), seed=101 + D)
+    g = draw_dout((B, S, H, D), seed=101 + D)
+    full_bwd_check(q, k, v, g, causal, D ** -0.5, what="bwd-small D%d" % D)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_short_sequences(D):
+    """S below one block (and a single row): tails only."""
+    for S in (1, 37):
+        q, k, v = draw_qkv((1, S, 2, D), seed=103 + S)
+        g = draw_dout((1, S, 2, D), seed=103 + S)
+        full_bwd_check(q, k, v, g, True, D ** -0.5, what="bwd-short S%d" % S)
+
+
+@pytest.mark.parametrize("H_kv", [1, 2])
+def test_backward_grouped_kv_heads(H_kv):
+    """GQA / MQA: dK and dV sum the contributions of every query head of the group."""
+    B, S, H, D = 2, 300, 4, 128
+    q, k, v = draw_qkv((B, S, H, D), seed=105, kv_heads=H_kv)
+    g = draw_dout((B, S, H, D), seed=105)
+    full_bwd_check(q, k, v, g, True, D ** -0.5, what="bwd-gqa Hkv%d" % H_kv)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_varlen(D):
+    lengths = [1, 64, 200, 333, 65, 129]
+    cu = cu_seqlens_of(lengths)
+    T, H = int(cu[-1]), 2
+    q, k, v = draw_qkv((T, H, D), seed=107)
+    g = draw_dout((T, H, D), seed=107)
+    full_bwd_check(q, k, v, g, True, D ** -0.5, cu=cu, S=max(lengths), what="bwd-varlen D%d" % D)
+
+
+def test_backward_spread_logits():
+    """Q with std 3: peaked rows (few keys carry the weight), non-causal."""
+    B, S, H, D = 1, 260, 2, 128
+    q, k, v = draw_qkv((B, S, H, D), seed=109, q_std=3.0)
+    g = draw_dout((B, S, H, D), seed=109)
+    full_bwd_check(q, k, v, g, False, D ** -0.5, what="bwd-spread")
+
+
+def test_backward_is_reproducible():
+    """Every gradient row is reduced by one workgroup in a fixed order: two
+    runs give identical bits."""
+    B, S, H, D = 1, 700, 4, 128
+    q, k, v = draw_qkv((B, S, H, D), seed=111, kv_heads=2)
+    g = draw_dout((B, S, H, D), seed=111)
+    a = gpu_grads(q, k, v, g, True, D ** -0.5)
+    b = gpu_grads(q, k, v, g, True, D ** -0.5)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_autograd_function_matches_backward_entry():
+    """attention_fn(...).backward(dO) runs the same kernels as attention_backward."""
+    B, S, H, D = 1, 200, 2, 64
+    q, k, v = draw_qkv((B, S, H, D), seed=113)
+    g = draw_dout((B, S, H, D), seed=113)
+    ref = gpu_grads(q, k, v, g, True, None)
+    tq, tk, tv = (t.cuda().requires_grad_(True) for t in (q, k, v))
+    o = fa.attention_fn(tq, tk, tv, causal=True)
+    o.backward(g.cuda())
+    torch.cuda.synchronize()
+    for x, y in zip((tq.grad, tk.grad, tv.grad), ref):
+        assert torch.equal(x.cpu().view(torch.int16), y.view(torch.int16))
+
+
+def test_backward_8k_causal_sampled():
+    """B=2, H=16, S=8192, D=128, causal (the 8k causal forward workload):
+    query rows and key rows sampled from one (sequence, head) slice and the
+    edges of others, compared with the oracle row by row."""
+    w = WORKLOADS["causal_b2h16s8192d128"]
+    B, S, H, D = w.B, w.S, w.H, w.D
+    q, k, v = draw_qkv((B, S, H, D), seed=w.seed)
+    g = draw_dout((B, S, H, D), seed=w.seed)
+    note("bwd-8k gpu run")
+    dq, dk, dv = gpu_grads(q, k, v, g, True, w.scale)
+    rng = np.random.default_rng(115)
+    # key rows of slice (b=1, h=5): first, last, block edges and random
+    b, h = 1, 5
+    js = sorted(set([0, 1, 63, 64, 127, 128, 255, 256, S - 1, S - 64]
+                    + list(rng.integers(0, S, 24))))
+    k_rows = [(b * H + h) * S + j for j in js]
+    # query rows of the same slice plus a few in other slices
+    is_ = sorted(set([0, 1, 255, 256, S - 1] + list(rng.integers(0, S, 24))))
+    q_rows = [(b * H + h) * S + i for i in is_] + [(0 * H + 0) * S + 0, (0 * H + 15) * S + S - 1]
+    note("bwd-8k oracle rows", len(q_rows), len(k_rows))
+    rdq, rdqm, rdk, rdv, rdkm, rdvm = oracle.attention_backward_rows_bf16(
+        q, k, v, g, q_rows, k_rows, w.scale, True)
+    gdq = tensor_to_f64(dq)
+    gdk, gdv = tensor_to_f64(dk), tensor_to_f64(dv)
+    sel_q = np.stack([gdq[r // (H * S), r % S, (r // S) % H] for r in q_rows])
+    sel_k = np.stack([gdk[b, j, h] for j in js])
+    sel_v = np.stack([gdv[b, j, h] for j in js])
+    for name, gg, rr, mm in (("dq", sel_q, rdq, rdqm), ("dk", sel_k, rdk, rdkm),
+                             ("dv", sel_v, rdv, rdvm)):
+        st = compare_grad(gg, rr, mm)
+        note("bwd-8k", name, st)
+        assert_grad_close(st, ("bwd-8k", name))

@@ -1,5 +1,6 @@
 """The parity gate's own arithmetic (CPU only)."""
 import numpy as np
+import pytest
 
 from parity import bf16_neighbours, bf16_round, cell_distance, compare
 
@@ -32,3 +33,21 @@ def test_compare_flags_errors():
     bad = good.copy()
     bad[7] += 0.05
     assert compare(bad, None, ref, None)["o_max"] > 0.03
+
+
+def test_gradient_gate_flags_planted_errors():
+    """The backward gate passes an exact result, and fails a gradient off by
+    more than the derived bound in one element or by a small bias everywhere."""
+    from parity import assert_grad_close, compare_grad
+    rng = np.random.default_rng(5)
+    g = rng.standard_normal(1000)
+    mag = np.abs(g) * 4 + 0.5
+    assert_grad_close(compare_grad(bf16_round(g), g, mag))
+    bad = bf16_round(g).copy()
+    bad[17] += 2.0 ** -8 * abs(g[17]) + 2.0 ** -7 * mag[17] + 1e-3
+    with pytest.raises(AssertionError):
+        assert_grad_close(compare_grad(bad, g, mag))
+    with pytest.raises(AssertionError):
+        assert_grad_close(compare_grad(g * 1.02, g, mag * 10))
+    with pytest.raises(AssertionError):
+        assert_grad_close(compare_grad(np.where(np.arange(1000) == 3, np.nan, g), g, mag))

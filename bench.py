@@ -19,6 +19,7 @@ The cpu_baseline leg times the fp64 oracle (test infrastructure) on a
 bounded sample of query rows of the same workload on the host cores.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --backward [--table]     # the backward pass (fa_bwd)
 """
 from __future__ import annotations
 
@@ -117,6 +118,57 @@ def time_workload(fa, torch, w, steps, warmup, tuning=None):
     }
 
 
+BACKWARD_WORKLOADS = ["causal_b2h16s8192d128", "long_b1h16s32768d128_causal",
+                      "dense_b2h16s2048d128", "dense_b2h16s2048d128_causal",
+                      "gqa_b2h32kv8s8192d128_causal", "varlen_16x512to8192_h32d128_causal",
+                      "smoke_b1h8s512d64_causal"]
+
+
+def time_backward(fa, torch, w, steps, warmup):
+    """Time fa_bwd (its dQ kernel and its dK/dV kernel) on a workload, after
+    one forward launch that provides o and lse.  Flops follow the usual
+    backward convention: 2.5x the forward's (five products of the forward's
+    size per block: S, dP, dV, dQ, dK)."""
+    from attn_inputs import draw_dout, flops, make
+    dev = torch.device("cuda:0")
+    q, k, v, cu, S = make(w)
+    dq_, dk_, dv_ = q.to(dev), k.to(dev), v.to(dev)
+    dcu = None if cu is None else torch.from_numpy(cu).to(dev)
+    ms = S if cu is not None else None
+    o, lse = fa.attention(dq_, dk_, dv_, causal=w.causal, scale=w.scale, cu_seqlens=dcu,
+                          max_seqlen=ms)
+    g = draw_dout(tuple(q.shape), w.seed).to(dev)
+    gq, gk, gv = torch.empty_like(dq_), torch.empty_like(dk_), torch.empty_like(dv_)
+    delta = torch.empty_like(lse)
+
+    def step():
+        fa.attention_backward(dq_, dk_, dv_, o, lse, g, causal=w.causal, scale=w.scale,
+                              cu_seqlens=dcu, max_seqlen=ms, dq=gq, dk=gk, dv=gv, delta=delta)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    fl = 2.5 * flops(w, cu)
+    return {"workload": w.name, "pass": "backward", "flops": fl,
+            "ms_per_step": round(wall * 1e3 / steps, 4),
+            "kernel_ms_mean": round(float(np.mean(kernel_ms)), 4),
+            "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
+            "TFLOP/s": round(fl / (float(np.mean(kernel_ms)) * 1e-3) / 1e12, 1),
+            "pct_of_peak": round(100 * fl / (float(np.mean(kernel_ms)) * 1e-3) / 1e12
+                                 / PEAK_BF16_TFLOPS, 2)}
+
+
 def cpu_baseline(w, inputs, target_s=15.0):
     """Time the fp64 oracle on a bounded, seeded sample of query rows."""
     import oracle
@@ -175,6 +227,9 @@ def main():
     ap.add_argument("--gemm-reference", action="store_true",
                     help="only time torch's bf16 matmul (hipBLASLt) on large shapes, as context "
                          "for the MFMA fraction the attention kernel reaches")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (fa_bwd) on --workload, or with --table on "
+                         "every workload it supports (one JSON line each)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times); used to "
                          "scale the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
@@ -231,6 +286,13 @@ def main():
             tuning.exp2_emu = args.exp2_emu
         if args.schedule is not None:
             tuning.schedule = args.schedule
+
+    if args.backward:
+        names = BACKWARD_WORKLOADS if args.table else [args.workload]
+        for name in names:
+            print(json.dumps(time_backward(fa, torch, WORKLOADS[name], args.steps, args.warmup)),
+                  flush=True)
+        return
 
     if args.table:
         for name, wl in WORKLOADS.items():

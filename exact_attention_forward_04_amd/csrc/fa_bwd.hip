@@ -44,6 +44,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "fa.h"
 #include "fa_host.h"
@@ -56,18 +57,22 @@ template <int D>
 struct BwdCfg {
   // dQ: eight waves (two per SIMD), 32 query rows each.
   static constexpr int NW_DQ = 8;
-  // dK/dV: the two D-wide fp32 accumulators of a wave take 2*D/32*16 VGPRs
-  // (128 at D = 128), so D = 128 runs one wave per SIMD.
-  static constexpr int NW_KV = (D == 128) ? 4 : 8;
+  // dK/dV: one wave per SIMD, 32 keys each.  The two D-wide fp32
+  // accumulators take 2*D/32*16 registers (128 at D = 128) and the software
+  // pipeline of the block body holds two sub-blocks' S and dP at once, which
+  // needs more than the 256 registers of two waves per SIMD.
+  static constexpr int NW_KV = 4;
   static constexpr int BM = 32 * NW_DQ;  // query rows per dQ tile
   static constexpr int BN = 32 * NW_KV;  // keys per dK/dV tile
   static constexpr int BLK = kBN * D * 2;  // bytes of one 64-row block in LDS
   static constexpr int STATS = 2 * kBN * 4;  // LSE and Delta of one block
-  // LDS: two stages of [K | V] blocks (dQ), or of [Q | dO] blocks followed
-  // by two stages of statistics (dK/dV).  Blocks sit at multiples of BLK, as
-  // the operand addressing needs.
-  static constexpr int LDS_DQ = 4 * BLK;
-  static constexpr int LDS_KV = 4 * BLK + 2 * STATS;
+  // LDS: a ring of four [K | V] slots (dQ), or of four [Q | dO] slots
+  // followed by four statistics slots (dK/dV); blocks are copied two ahead
+  // of their use.  Blocks sit at multiples of BLK, as the operand addressing
+  // needs.
+  static constexpr int SLOTS = 4;
+  static constexpr int LDS_DQ = SLOTS * 2 * BLK;
+  static constexpr int LDS_KV = SLOTS * 2 * BLK + SLOTS * STATS;
 };
 
 struct BwdArgs {
@@ -117,6 +122,66 @@ __device__ __forceinline__ void dma4(const float *gaddr, unsigned lds_addr) {
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The same product with the register files chosen explicitly (the dK/dV
+// kernel needs more than 256 registers per lane; left to itself the
+// compiler shuttles S and dP between AGPRs and VGPRs on every block):
+//   mfma_v0 / mfma_v: accumulator in VGPRs (read by the softmax VALU code),
+//                     B operand in AGPRs; mfma_v0 starts from zero;
+//   mfma_a:           accumulator in AGPRs (only MFMAs touch it).
+// The compiler does not look inside these statements for hazards, so the
+// caller keeps dependent products of one accumulator apart (two chains
+// alternate, as the compiler itself schedules them) and waits with
+// mfma_result_wait() before VALU code reads a result.
+__device__ __forceinline__ void mfma_v0(f32x16 &c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16 &c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_a(f32x16 &c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// 32 wait states: more than an XDL product's result latency before VALU
+// code (or v_accvgpr_read) may read its destination.
+__device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); }
+
+// The products of the dK/dV kernel: the explicit-register forms above when
+// ASM (only safe while the compiler never copies their accumulators between
+// register files inside the loop, which a test checks on the generated
+// code), else the intrinsic, whose hazards the compiler tracks itself.
+template <bool ASM>
+__device__ __forceinline__ void prod_first(f32x16 &c, bf16x8 a, bf16x8 b) {
+  if constexpr (ASM) {
+    mfma_v0(c, a, b);
+  } else {
+    f32x16 z;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = 0.0f;
+    c = mfma(a, b, z);
+  }
+}
+template <bool ASM>
+__device__ __forceinline__ void prod_next(f32x16 &c, bf16x8 a, bf16x8 b) {
+  if constexpr (ASM) mfma_v(c, a, b);
+  else c = mfma(a, b, c);
+}
+template <bool ASM>
+__device__ __forceinline__ void prod_acc(f32x16 &c, bf16x8 a, bf16x8 b) {
+  if constexpr (ASM) mfma_a(c, a, b);
+  else c = mfma(a, b, c);
+}
+// Waits tied to the data they protect: every read of x (and y) comes after
+// the wait because the wait is a use and a new definition of them, which no
+// earlier code motion can reorder.
+template <bool ASM>
+__device__ __forceinline__ void result_wait_v(f32x16 &x, f32x16 &y) {
+  if constexpr (ASM) asm volatile("s_nop 15\n\ts_nop 15" : "+v"(x), "+v"(y));
+}
+template <bool ASM>
+__device__ __forceinline__ void result_wait_a(f32x16 &x, f32x16 &y) {
+  if constexpr (ASM) asm volatile("s_nop 15\n\ts_nop 15" : "+a"(x), "+a"(y));
 }
 
 // Store the transposed accumulators acc[dt] (row d = 32dt + 8i + 4(l/32) + j,
@@ -209,8 +274,8 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_DQ * kWave, BwdCfg<D>::NW_DQ / 4) voi
   constexpr int LOADS_BLOCK = 2 * BlockLoader<D, NW>::LOADS;
   LdsAddr<D> la;
   la.init(lane);
-  auto kbuf = [&](int j) { return lds + (j & 1) * 2 * C::BLK; };
-  auto vbuf = [&](int j) { return lds + (j & 1) * 2 * C::BLK + C::BLK; };
+  auto kbuf = [&](int j) { return lds + (j % C::SLOTS) * 2 * C::BLK; };
+  auto vbuf = [&](int j) { return lds + (j % C::SLOTS) * 2 * C::BLK + C::BLK; };
   auto issue = [&](int j) {
     ld.issue(a.k, sp.tok0, a.Hkv, hk, j * kBN, L, kbuf(j));
     ld.issue(a.v, sp.tok0, a.Hkv, hk, j * kBN, L, vbuf(j));
@@ -222,10 +287,16 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_DQ * kWave, BwdCfg<D>::NW_DQ / 4) voi
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[dt][e] = 0.0f;
 
+  // Ring of four slots, copies two blocks ahead: block j+2 goes to the slot
+  // of block j-2, whose reads every wave finished before the barrier that
+  // opened block j-1.  One barrier per block.
   if (nblocks > 0) issue(0);
+  if (nblocks > 1) issue(1);
   for (int j = 0; j < nblocks; ++j) {
-    if (j + 1 < nblocks) {
-      issue(j + 1);
+    if (j + 2 < nblocks) {
+      issue(j + 2);
+      wait_vmcnt<2 * LOADS_BLOCK>();
+    } else if (j + 1 < nblocks) {
       wait_vmcnt<LOADS_BLOCK>();
     } else {
       wait_vmcnt<0>();
@@ -266,15 +337,21 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_DQ * kWave, BwdCfg<D>::NW_DQ / 4) voi
       const bool need_mask = (n0 + kBN > L) || (CAUSAL && n0 + kBN - 1 > wrow0);
       const int lim = (CAUSAL ? (row + 1 < L ? row + 1 : L) : L) - n0 - 4 * hh;
       bf16x8 ds8[4];
+      // (two instances: blocks off the diagonal and inside the sequence,
+      // the common case, skip the per-entry select)
+      auto p_ds = [&](auto masked) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int off = 32 * i + 8 * (e >> 2) + (e & 3);
-          float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -lse2));
-          if (need_mask) p = off < lim ? p : 0.0f;
-          ds8[2 * i + (e >> 3)][e & 7] = (__bf16)(p * (dp[i][e] - delta));
-        }
+          for (int e = 0; e < 16; ++e) {
+            const int off = 32 * i + 8 * (e >> 2) + (e & 3);
+            float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -lse2));
+            if constexpr (decltype(masked)::value) p = off < lim ? p : 0.0f;
+            ds8[2 * i + (e >> 3)][e & 7] = (__bf16)(p * (dp[i][e] - delta));
+          }
+      };
+      if (need_mask) p_ds(std::true_type{});
+      else p_ds(std::false_type{});
       // ---- dQ^T += K^T dS^T (K^T by transposed reads of the K block)
       const unsigned kt0 = la.vw0 + lds_u32(kbuf(j)), kt1 = la.vw1 + lds_u32(kbuf(j));
 #pragma unroll
@@ -282,7 +359,6 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_DQ * kWave, BwdCfg<D>::NW_DQ / 4) voi
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma(read_vt<D>(kt0, kt1, t, dt), ds8[t], acc[dt]);
     }
-    barrier_after_reads();  // every wave is done with this stage
   }
 
   if (active && row < L)
@@ -298,6 +374,9 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
   using C = BwdCfg<D>;
   constexpr int NW = C::NW_KV;
   constexpr int NS = D / 16;
+  // D = 128 needs more than 256 registers per lane and places them itself
+  // (K, V and the dK/dV accumulators in AGPRs); D = 64 fits in VGPRs.
+  constexpr bool ASM = (D == 128);
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   char LDS_AS *lds = (char LDS_AS *)lds_raw;
 
@@ -333,8 +412,13 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
       kf[s] = kp[2 * s];
       vf[s] = vp[2 * s];
     }
+    // K and V stay in registers for the whole tile (D = 128: in AGPRs, as
+    // B operands of mfma_v).
 #pragma unroll
-    for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(kf[s]), "+v"(vf[s]));
+    for (int s = 0; s < NS; ++s) {
+      if constexpr (ASM) asm volatile("" : "+a"(kf[s]), "+a"(vf[s]));
+      else asm volatile("" : "+v"(kf[s]), "+v"(vf[s]));
+    }
   }
 
   // Query blocks: for each query head of the group, the 64-row blocks from
@@ -349,9 +433,9 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
   constexpr int LOADS_BLOCK = 2 * BlockLoader<D, NW>::LOADS;
   LdsAddr<D> la;
   la.init(lane);
-  auto qbuf = [&](int t) { return lds + (t & 1) * 2 * C::BLK; };
-  auto gbuf = [&](int t) { return lds + (t & 1) * 2 * C::BLK + C::BLK; };
-  auto sbuf = [&](int t) { return lds + 4 * C::BLK + (t & 1) * C::STATS; };
+  auto qbuf = [&](int t) { return lds + (t % C::SLOTS) * 2 * C::BLK; };
+  auto gbuf = [&](int t) { return lds + (t % C::SLOTS) * 2 * C::BLK + C::BLK; };
+  auto sbuf = [&](int t) { return lds + C::SLOTS * 2 * C::BLK + (t % C::SLOTS) * C::STATS; };
   // Block t: Q and dO rows (every wave), LSE (wave 0) and Delta (wave 1) of
   // its 64 rows, one row per lane, rows past L reading row L-1.
   auto issue = [&](int t) {
@@ -365,12 +449,19 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
       dma4(src, lds_u32(sbuf(t)) + (unsigned)wave * (kBN * 4));
     }
   };
-  // Wait for block t while block t+1 may still be in flight (waves 0 and 1
-  // issue one statistics copy per block on top of the row copies).
-  auto wait_block = [&](bool next_in_flight) {
-    if (!next_in_flight) wait_vmcnt<0>();
-    else if (wave < 2) wait_vmcnt<LOADS_BLOCK + 1>();
-    else wait_vmcnt<LOADS_BLOCK>();
+  // Wait for block t while the n_after later blocks (0, 1 or 2) may still be
+  // in flight (waves 0 and 1 issue one statistics copy per block on top of
+  // the row copies).
+  auto wait_block = [&](int n_after) {
+    if (wave < 2) {
+      if (n_after >= 2) wait_vmcnt<2 * (LOADS_BLOCK + 1)>();
+      else if (n_after == 1) wait_vmcnt<LOADS_BLOCK + 1>();
+      else wait_vmcnt<0>();
+    } else {
+      if (n_after >= 2) wait_vmcnt<2 * LOADS_BLOCK>();
+      else if (n_after == 1) wait_vmcnt<LOADS_BLOCK>();
+      else wait_vmcnt<0>();
+    }
   };
 
   f32x16 dk[D / 32], dv[D / 32];
@@ -381,78 +472,144 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
       dk[dt][e] = 0.0f;
       dv[dt][e] = 0.0f;
     }
+  if constexpr (ASM) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
+    mfma_result_wait();  // the AGPR writes above land before the first product reads them
+  }
 
+  // Ring of four slots, copies two blocks ahead (as in fa_bwd_dq).
   if (nblocks > 0) issue(0);
+  if (nblocks > 1) issue(1);
   for (int t = 0; t < nblocks; ++t) {
-    if (t + 1 < nblocks) issue(t + 1);
-    wait_block(t + 1 < nblocks);
+    if (t + 2 < nblocks) issue(t + 2);
+    wait_block(t + 2 < nblocks ? 2 : (t + 1 < nblocks ? 1 : 0));
     barrier_nofence();
     const int m0 = (qb0 + t % per) * kBN;
     if (active && (!CAUSAL || m0 + kBN - 1 >= key0)) {
-      // ---- S = Q K^T and dP = dO V^T (query rows on the M side)
       const unsigned qa = la.ky + lds_u32(qbuf(t));
       const unsigned ga = la.ky + lds_u32(gbuf(t));
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          s[i][e] = 0.0f;
-          dp[i][e] = 0.0f;
-        }
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const bf16x8 q0 = read_k<D>(qa, 0, st), q1 = read_k<D>(qa, 1, st);
-        const bf16x8 g0 = read_k<D>(ga, 0, st), g1 = read_k<D>(ga, 1, st);
-        s[0] = mfma(q0, kf[st], s[0]);
-        s[1] = mfma(q1, kf[st], s[1]);
-        dp[0] = mfma(g0, vf[st], dp[0]);
-        dp[1] = mfma(g1, vf[st], dp[1]);
-      }
-      // ---- P and dS.  Entry e of sub-block i is query row m0 + 32i +
-      // 8(e>>2) + 4h + (e&3) against the lane's key; it is kept iff its
-      // in-block offset off satisfies lo <= off < hi (row < L, and row >=
-      // key when causal).  LSE and Delta of the four rows 4h + (0..3) of a
-      // group come from LDS as one 16-byte read each.
+      const unsigned gt0 = la.vw0 + lds_u32(gbuf(t)), gt1 = la.vw1 + lds_u32(gbuf(t));
+      const unsigned qt0 = la.vw0 + lds_u32(qbuf(t)), qt1 = la.vw1 + lds_u32(qbuf(t));
       const float LDS_AS *lse_l = (const float LDS_AS *)sbuf(t);
       const float LDS_AS *del_l = lse_l + kBN;
+      // Blocks off the diagonal and inside the sequence (the common case)
+      // get bounds that keep every entry: one select per entry, no branch
+      // (a branch would duplicate the body, and the two copies would hold
+      // the dK/dV accumulators in different registers).
       const bool need_mask = (m0 + kBN > L) || (CAUSAL && m0 < key0 + 31);
-      const int hi = L - m0 - 4 * hh;
-      const int lo = CAUSAL ? key - m0 - 4 * hh : INT_MIN;
+      const int hi = need_mask ? L - m0 - 4 * hh : INT_MAX;
+      const int lo = (need_mask && CAUSAL) ? key - m0 - 4 * hh : INT_MIN;
       typedef float f32x4 __attribute__((ext_vector_type(4)));
+      f32x16 s[2], dp[2];
       bf16x8 p8[4], ds8[4];
+      // The block is done in four phases of NST steps, two matrix products
+      // per step, with the operand reads of step k+2 issued before the
+      // products of step k, across phase boundaries too (LDS latency hides
+      // behind the matrix unit):
+      //   A: S_0 = Q_0 K^T, dP_0 = dO_0 V^T         (query rows 0-31)
+      //   B: S_1, dP_1                    + VALU: P_0, dS_0
+      //   C: dV^T, dK^T over rows 0-31    + VALU: P_1, dS_1
+      //   D: dV^T, dK^T over rows 32-63
+      // One wave per SIMD: the VALU work of one sub-block runs between the
+      // matrix products of the other, so the matrix unit keeps running
+      // (software pipelining inside the wave).
+      constexpr int NST = NS;  // steps per phase
+      constexpr int NT = D / 32;
+      static_assert(NST == 2 * NT, "phases C and D have 2*D/32 steps");
+      // Entry e of S_i/dP_i is query row m0 + 32i + 8(e>>2) + 4h + (e&3)
+      // against the lane's key; it is kept iff its in-block offset off
+      // satisfies lo <= off < hi (row < L, and row >= key when causal).
+      f32x4 l4[2][4], d4[2][4];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int r0 = 32 * i + 8 * g4 + 4 * hh;
-          const f32x4 l4 = *(const f32x4 LDS_AS *)(lse_l + r0);
-          const f32x4 d4 = *(const f32x4 LDS_AS *)(del_l + r0);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int e = 4 * g4 + jj;
-            const int off = 32 * i + 8 * g4 + jj;
-            float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -l4[jj] * kLog2e));
-            if (need_mask) p = (off < hi && off >= lo) ? p : 0.0f;
-            const int tt = 2 * i + (e >> 3);
-            p8[tt][e & 7] = (__bf16)p;
-            ds8[tt][e & 7] = (__bf16)(p * (dp[i][e] - d4[jj]));
-          }
+          l4[i][g4] = *(const f32x4 LDS_AS *)(lse_l + r0);
+          d4[i][g4] = *(const f32x4 LDS_AS *)(del_l + r0);
         }
-      // ---- dV^T += dO^T P and dK^T += Q^T dS (transposed reads of the blocks)
-      const unsigned gt0 = la.vw0 + lds_u32(gbuf(t)), gt1 = la.vw1 + lds_u32(gbuf(t));
-      const unsigned qt0 = la.vw0 + lds_u32(qbuf(t)), qt1 = la.vw1 + lds_u32(qbuf(t));
+      // P and dS of the n entries e0 .. e0+n-1 of sub-block i (the 16
+      // entries of a sub-block spread over the NST steps of a phase, EPS
+      // per step).
+      constexpr int EPS = 16 / NST;
+      static_assert(EPS * NST == 16, "entries split evenly over the steps");
+      auto softmax_grad_part = [&](int i, int e0, int n) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          dv[dt] = mfma(read_vt<D>(gt0, gt1, tt, dt), p8[tt], dv[dt]);
-          dk[dt] = mfma(read_vt<D>(qt0, qt1, tt, dt), ds8[tt], dk[dt]);
+        for (int e = e0; e < e0 + n; ++e) {
+          const int g4 = e >> 2, jj = e & 3;
+          const int off = 32 * i + 8 * g4 + jj;
+          float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -(l4[i][g4][jj] * kLog2e)));
+          p = (off < hi && off >= lo) ? p : 0.0f;
+          const int tt = 2 * i + (e >> 3);
+          p8[tt][e & 7] = (__bf16)p;
+          ds8[tt][e & 7] = (__bf16)(p * (dp[i][e] - d4[i][g4][jj]));
+          // An operand is complete here: pin it, so no part of its
+          // arithmetic can be moved down to the product that reads it
+          // (which comes at least one step later).
+          if ((e & 7) == 7) asm volatile("" : "+v"(p8[tt]), "+v"(ds8[tt]));
         }
+      };
+      // Operands of step k: rows of Q and dO (phases A, B) or transposed
+      // reads of dO and Q (phases C, D: 16-row step tt, d tile dt).
+      auto read_step = [&](int k, bf16x8 &x, bf16x8 &y) {
+        const int ph = k / NST, st = k % NST;
+        if (ph < 2) {
+          x = read_k<D>(qa, ph, st);
+          y = read_k<D>(ga, ph, st);
+        } else {
+          const int tt = 2 * (ph - 2) + st / NT, dt = st % NT;
+          x = read_vt<D>(gt0, gt1, tt, dt);
+          y = read_vt<D>(qt0, qt1, tt, dt);
+        }
+      };
+      constexpr int NK = 4 * NST;
+      bf16x8 ox[NK], oy[NK];
+      read_step(0, ox[0], oy[0]);
+      read_step(1, ox[1], oy[1]);
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        if (k + 2 < NK) read_step(k + 2, ox[k + 2], oy[k + 2]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int ph = k / NST, st = k % NST;
+        const bool valu = (ph == 1 || ph == 2);
+        // The first product of the step, then half of the step's VALU share
+        // while it runs, the second product, the other half: with one wave
+        // per SIMD the second product would otherwise hold the wave until
+        // the matrix unit is free, and the VALU work would start only then.
+        if (ph < 2) {
+          if (st == 0) prod_first<ASM>(s[ph], ox[k], kf[st]);
+          else prod_next<ASM>(s[ph], ox[k], kf[st]);
+        } else {
+          const int tt = 2 * (ph - 2) + st / NT, dt = st % NT;
+          prod_acc<ASM>(dv[dt], ox[k], p8[tt]);
+        }
+        if (valu) {
+          // S/dP of sub-block ph-1 were produced by the products just before
+          if (st == 0) result_wait_v<ASM>(s[ph - 1], dp[ph - 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          softmax_grad_part(ph - 1, EPS * st, EPS / 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (ph < 2) {
+          if (st == 0) prod_first<ASM>(dp[ph], oy[k], vf[st]);
+          else prod_next<ASM>(dp[ph], oy[k], vf[st]);
+        } else {
+          const int tt = 2 * (ph - 2) + st / NT, dt = st % NT;
+          prod_acc<ASM>(dk[dt], oy[k], ds8[tt]);
+        }
+        if (valu) {
+          __builtin_amdgcn_sched_barrier(0);
+          softmax_grad_part(ph - 1, EPS * st + EPS / 2, EPS / 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    barrier_after_reads();  // every wave is done with this stage
   }
 
+  // the last products into dK/dV have landed
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) result_wait_a<ASM>(dk[dt], dv[dt]);
   if (active && key < L) {
     const long long rowoff = ((sp.tok0 + key) * a.Hkv + hk) * (long long)D;
     store_rows<D>(a.dk + rowoff, dk, a.scale, hh);

@@ -95,6 +95,19 @@ def draw_dout(shape, seed: int, std: float = 1.0):
     return x.to(torch.bfloat16)
 
 
+def io_bytes(w: Workload, cu=None) -> float:
+    """Bytes the method must move: read Q, K, V, write O (bf16) and LSE (fp32)."""
+    Dv = w.head_dim_v
+    if w.q_range:
+        lq, lk = qk_lengths(w)
+        tq, tk = float(np.sum(lq)), float(np.sum(lk))
+    elif cu is not None:
+        tq = tk = float(cu[-1])
+    else:
+        tq = tk = float(w.B * w.S)
+    return tq * w.H * (2 * w.D + 2 * Dv + 4) + tk * w.kv_heads * 2 * (w.D + Dv)
+
+
 def qk_lengths(w: Workload):
     """(query lengths, key lengths) of a workload whose queries have lengths of
     their own: key lengths as for varlen, query lengths uniform on q_range
@@ -190,4 +203,10 @@ WORKLOADS = {
     "mixed_16x_q1to2048_k512to8192_h16d128_causal": Workload(
         "mixed_16x_q1to2048_k512to8192_h16d128_causal", 16, 8192, 16, 128, True, seed=10,
         varlen=(16, 512, 8192), q_range=(1, 2048)),
+    # A long-context decode step: one sequence, one query row against 32768
+    # cached keys, 32 query heads over 8 K/V heads.  It has far fewer query
+    # tiles than the GPU has CUs: the shape split-KV is for.
+    "decode_1x_q1_k32768_h32kv8d128": Workload(
+        "decode_1x_q1_k32768_h32kv8d128", 1, 32768, 32, 128, True, seed=11,
+        varlen=(1, 32768, 32768), q_range=(1, 1), Hkv=8),
 }

@@ -39,16 +39,18 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
+FORWARD_SOURCES = ("fa_fwd.hip", "fa_tile.h", "fa_sched.h", "exp2_poly.h", "fa_host.h")
+
+
 def kernel_sources_sha256() -> str:
-    """Hash of the kernel sources (csrc/*.hip, csrc/*.h), to tell whether a
+    """Hash of the sources the forward kernel is built from, to tell whether a
     stored counter measurement still describes the current kernel."""
-    import glob
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_forward_04_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for name in FORWARD_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
@@ -71,7 +73,7 @@ DEFAULT_WORKLOAD = "long_b1h16s32768d128_causal"
 SECONDARY_WORKLOAD = "causal_b2h16s8192d128"
 
 
-def time_workload(fa, torch, w, steps, warmup, tuning=None):
+def time_workload(fa, torch, w, steps, warmup, tuning=None, num_splits=None):
     from attn_inputs import make, make_qk, flops
     dev = torch.device("cuda:0")
     extra = {}
@@ -87,6 +89,19 @@ def time_workload(fa, torch, w, steps, warmup, tuning=None):
     lse = torch.empty((w.H, T) if cu is not None else (w.B, w.H, w.S), dtype=torch.float32,
                       device=dev)
     fl = flops(w, None if w.q_range else cu)
+
+    if num_splits is not None:   # split-KV: one workspace for every step
+        n_sp = num_splits
+        if n_sp == 0:
+            import ctypes
+            c = ctypes.c_int(1)
+            fa.load().fa_splitkv_auto_splits(w.B, w.H, S, extra.get("max_seqlen_k", S), w.D,
+                                             ctypes.byref(c))
+            n_sp = c.value
+        nbytes = fa.splitkv_workspace_size(w.B, w.H, S, extra.get("max_seqlen_k", S),
+                                           w.head_dim_v, n_sp)
+        extra = dict(extra, num_splits=n_sp,
+                     workspace=torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev))
 
     def step():
         fa.attention(dq, dk, dv, causal=w.causal, scale=w.scale, cu_seqlens=dcu,
@@ -108,8 +123,11 @@ def time_workload(fa, torch, w, steps, warmup, tuning=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    from attn_inputs import io_bytes
     return {
         "flops": fl,
+        "bytes": io_bytes(w, None if w.q_range else cu),
+        "num_splits": extra.get("num_splits", 1),
         "ms_per_step": wall * 1e3 / steps,
         "kernel_ms_mean": float(np.mean(kernel_ms)),
         "kernel_ms_median": float(np.median(kernel_ms)),
@@ -296,13 +314,17 @@ def main():
 
     if args.table:
         for name, wl in WORKLOADS.items():
-            rr = time_workload(fa, torch, wl, args.steps, args.warmup, tuning)
-            v = rr["flops"] / (rr["kernel_ms_mean"] * 1e-3) / 1e12
-            print(json.dumps({"workload": name, "kernel_ms_mean": round(rr["kernel_ms_mean"], 4),
-                              "kernel_ms_median": round(rr["kernel_ms_median"], 4),
-                              "TFLOP/s": round(v, 1),
-                              "pct_of_peak": round(100 * v / PEAK_BF16_TFLOPS, 2),
-                              "flops": rr["flops"]}), flush=True)
+            # workloads with few query rows per sequence also run split-KV
+            for sp in ([None, 0] if wl.q_range else [None]):
+                rr = time_workload(fa, torch, wl, args.steps, args.warmup, tuning, num_splits=sp)
+                v = rr["flops"] / (rr["kernel_ms_mean"] * 1e-3) / 1e12
+                print(json.dumps({"workload": name, "num_splits": rr["num_splits"],
+                                  "kernel_ms_mean": round(rr["kernel_ms_mean"], 4),
+                                  "kernel_ms_median": round(rr["kernel_ms_median"], 4),
+                                  "TFLOP/s": round(v, 1),
+                                  "pct_of_peak": round(100 * v / PEAK_BF16_TFLOPS, 2),
+                                  "GB/s": round(rr["bytes"] / (rr["kernel_ms_mean"] * 1e-3) / 1e9, 1),
+                                  "flops": rr["flops"]}), flush=True)
         return
 
     w = WORKLOADS[args.workload]

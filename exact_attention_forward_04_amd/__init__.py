@@ -65,6 +65,13 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd_general.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, P, P,
                                    ctypes.POINTER(Tuning)]
     lib.fa_fwd_general.restype = I
+    lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, P, I, P,
+                                   ctypes.c_size_t, P]
+    lib.fa_fwd_splitkv.restype = I
+    lib.fa_splitkv_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.fa_splitkv_workspace_size.restype = ctypes.c_size_t
+    lib.fa_splitkv_auto_splits.argtypes = [I, I, I, I, I, ctypes.POINTER(I)]
+    lib.fa_splitkv_auto_splits.restype = I
     lib.fa_bwd.argtypes = [P] * 10 + [I, I, I, I, I, F, I, P, P]
     lib.fa_bwd.restype = I
     lib.fa_tuning_default.argtypes = []
@@ -108,7 +115,8 @@ def _stream_ptr(stream) -> Optional[int]:
 def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
               cu_seqlens=None, max_seqlen: Optional[int] = None, return_lse: bool = True,
               out=None, lse_out=None, tuning: Optional[Tuning] = None, stream=None,
-              cu_seqlens_k=None, max_seqlen_k: Optional[int] = None):
+              cu_seqlens_k=None, max_seqlen_k: Optional[int] = None,
+              num_splits: Optional[int] = None, workspace=None):
     """Exact attention forward on the GPU.
 
     q, k, v: contiguous bf16 CUDA tensors.  Dense: q [B,Sq,H,D], k [B,Sk,H_kv,D],
@@ -119,6 +127,10 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
     H_kv divides H (query head h reads K/V head h // (H // H_kv)); D_v may
     differ from D for the (192, 128) pair.  With causal=True and query and key
     lengths that differ the mask is aligned to the bottom-right corner.
+    num_splits > 1 splits every key range over that many workgroups
+    (fa_fwd_splitkv, for decode-like batches with few query rows), 0 picks a
+    count for the device; workspace (a CUDA uint8 tensor of at least
+    splitkv_workspace_size(...) bytes) is allocated when not given.
     Returns (o, lse): o like q with D_v columns (bf16), lse fp32 [B,H,Sq] or
     [H,Tq] (None if return_lse is False).
     """
@@ -177,6 +189,23 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
     tref = ctypes.byref(tuning) if tuning is not None else None
     lse_ptr = lse.data_ptr() if lse is not None else None
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_ptr)
+    if num_splits is not None and tuning is None:
+        splits = int(num_splits)
+        if splits == 0:
+            n = ctypes.c_int(1)
+            _check("fa_splitkv_auto_splits",
+                   lib.fa_splitkv_auto_splits(B, H, S, S_k, D, ctypes.byref(n)))
+            splits = n.value
+        need = lib.fa_splitkv_workspace_size(B, H, S, S_k, D_v, splits)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        if workspace.numel() < need:
+            raise ValueError("workspace must hold %d bytes" % need)
+        rc = lib.fa_fwd_splitkv(*ptrs, B, H, H_kv, S, S_k, D, D_v, float(scale),
+                                int(bool(causal)), cu_ptr, cu_k_ptr, splits,
+                                workspace.data_ptr(), workspace.numel(), sp)
+        _check("fa_fwd_splitkv", rc)
+        return o, lse
     if S_k != S or cu_k_ptr != cu_ptr:
         rc = lib.fa_fwd_general(*ptrs, B, H, H_kv, S, S_k, D, D_v, float(scale),
                                 int(bool(causal)), cu_ptr, cu_k_ptr, sp, tref)
@@ -298,6 +327,11 @@ def attention_fn(q, k, v, causal: bool = False, scale: Optional[float] = None,
     if _attention_fn is None:
         _attention_fn = _autograd_function()
     return _attention_fn.apply(q, k, v, causal, scale, cu_seqlens, max_seqlen)
+
+
+def splitkv_workspace_size(B: int, H: int, S_q: int, S_k: int, D_v: int, num_splits: int) -> int:
+    """Bytes of workspace fa_fwd_splitkv needs (0 when one split is used)."""
+    return load().fa_splitkv_workspace_size(B, H, S_q, S_k, D_v, num_splits)
 
 
 def exp2_emu(x, stream=None):

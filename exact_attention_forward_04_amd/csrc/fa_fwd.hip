@@ -109,6 +109,11 @@ struct Args {
   float tau;
   unsigned long long *counters;
   int workers;              // persistent: number of workgroups
+  // split-KV: each workgroup covers key blocks [split*kbps, (split+1)*kbps)
+  // and writes a partial O (fp32) and LSE into the workspace, which a
+  // combine kernel merges
+  float *ws_o, *ws_lse;
+  int kbps;
 };
 
 // Per-wave state of one tile.
@@ -315,8 +320,9 @@ struct KvLayout {
   }
 };
 
-template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>
-__device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, char LDS_AS *lds) {
+template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT, bool SPLIT = false>
+__device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, char LDS_AS *lds,
+                                         int split = 0) {
   using C = Cfg<D>;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
@@ -335,7 +341,16 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     ktok0 = (long long)b * a.Sk;
     Lk = a.Sk;
   }
-  const int koff = Lk - L;  // bottom-right causal alignment
+  int koff = Lk - L;  // bottom-right causal alignment
+  if constexpr (SPLIT) {
+    // Keys [lo, hi) only: the tile sees a key sequence that starts at key
+    // lo, with the causal alignment shifted to match.
+    const int lo = split * a.kbps * kBN;
+    const int hi = (Lk - lo > a.kbps * kBN) ? lo + a.kbps * kBN : Lk;
+    ktok0 += lo;
+    koff -= lo;
+    Lk = hi > lo ? hi - lo : 0;
+  }
   const int m0 = mb * C::BM;
   if (m0 >= L) return;  // workgroup-uniform
   const int H = a.H;
@@ -506,6 +521,32 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   if (!wr.active) return;
   // ---- epilogue: combine the two half-wave partial sums of each row
   const float l32 = sum_halves(st.l32);
+  if constexpr (SPLIT) {
+    // partial O (normalised over this split's keys) and LSE, fp32, into the
+    // workspace slice of this split (rows of B*S query slots)
+    if (row < L) {
+      const float inv = l32 > 0.0f ? 1.0f / l32 : 0.0f;
+      const int hh = lane >> 5;
+      const long long slots = (long long)a.B * a.S * H;
+      float *op = a.ws_o + (split * slots + (tok0 + row) * H + h) * (long long)DV + 4 * hh;
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int dt = 0; dt < DV / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 out = {st.o[dt][4 * i + 0] * inv, st.o[dt][4 * i + 1] * inv,
+                       st.o[dt][4 * i + 2] * inv, st.o[dt][4 * i + 3] * inv};
+          *(f32x4 *)(op + 32 * dt + 8 * i) = out;
+        }
+      if (hh == 0) {
+        const float lse = (st.m_ref + log2f(l32)) * kLn2;
+        float *lp = a.ws_lse + split * slots;
+        if constexpr (VARLEN) lp[(long long)h * a.cu[a.B] + tok0 + row] = lse;
+        else lp[((long long)b * H + h) * a.S + row] = lse;
+      }
+    }
+    return;
+  }
   if (row < L) {
     const float inv = l32 > 0.0f ? 1.0f / l32 : 0.0f;  // a row without keys: O = 0, LSE = -inf
     const int hh = lane >> 5;
@@ -581,6 +622,77 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fw
   run_tile<D, CAUSAL, VARLEN, EMU, COUNT>(a, b, h, mb, lds);
 }
 
+// Split-KV: one workgroup per (tile, key split), natural order.
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fwd_split(Args a,
+                                                                                        int splits) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  char LDS_AS *lds = (char LDS_AS *)lds_raw;
+  using C = Cfg<D>;
+  const int nmb = fa::ceil_div(a.S, C::BM);
+  const int id = blockIdx.x;
+  const int split = id % splits;
+  const int rest = id / splits;
+  const int mb = rest % nmb;
+  const int h = (rest / nmb) % a.H;
+  const int b = rest / (nmb * a.H);
+  run_tile<D, CAUSAL, VARLEN, 0, false, true>(a, b, h, mb, lds, split);
+}
+
+// Merge the split partials of each (query row, head): with the splits'
+// LSE_s and normalised O_s, LSE = ln sum_s e^{LSE_s} and
+// O = sum_s e^{LSE_s - LSE} O_s (the merge of partial softmax results by
+// their log-sum-exp).  One wavefront per row; a row whose every split was
+// empty gets O = 0, LSE = -inf.
+template <int DV, bool VARLEN>
+__global__ __launch_bounds__(256) void fa_split_combine(Args a, int splits) {
+  const long long rows = VARLEN ? (long long)a.cu[a.B] * a.H : (long long)a.B * a.S * a.H;
+  const long long r = (long long)blockIdx.x * 4 + threadIdx.x / kWave;  // token*H + h
+  const int lane = threadIdx.x % kWave;
+  if (r >= rows) return;
+  const int H = a.H;
+  const long long t = r / H;  // query token
+  const int h = (int)(r % H);
+  long long li;               // index in the lse layout
+  if constexpr (VARLEN) {
+    li = (long long)h * a.cu[a.B] + t;
+  } else {
+    const long long b = t / a.S, i = t % a.S;
+    li = (b * H + h) * a.S + i;
+  }
+  const long long slots = (long long)a.B * a.S * H;
+  float m = -INFINITY;
+  for (int s = 0; s < splits; ++s) m = fmaxf(m, a.ws_lse[s * slots + li]);
+  constexpr int PER = (DV + kWave - 1) / kWave;
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
+  float lse = -INFINITY;
+  if (m != -INFINITY) {
+    float wsum = 0.0f;
+    for (int s = 0; s < splits; ++s) {
+      const float w = exp2_hw((a.ws_lse[s * slots + li] - m) * kLog2e);
+      wsum += w;
+      const float *op = a.ws_o + (s * slots + r) * (long long)DV;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int d = lane + k * kWave;
+        if (d < DV) acc[k] = __builtin_fmaf(w, op[d], acc[k]);
+      }
+    }
+    const float inv = 1.0f / wsum;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] *= inv;
+    lse = m + log2f(wsum) * kLn2;
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int d = lane + k * kWave;
+    if (d < DV) a.o[r * DV + d] = (__bf16)acc[k];
+  }
+  if (a.lse != nullptr && lane == 0) a.lse[li] = lse;
+}
+
 __global__ void exp2_emu_kernel(const float *x, float *y, long long n) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) y[i] = exp2_poly(x[i]);
@@ -640,6 +752,54 @@ int launch_variant(const Args &a0, int schedule, int cus, hipStream_t stream) {
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), lds, stream, a);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int bm_for(int D);
+
+template <int D, bool CAUSAL, bool VARLEN>
+int launch_split(const Args &a, int splits, hipStream_t stream) {
+  using C = Cfg<D>;
+  const long long grid = (long long)a.B * a.H * fa::ceil_div(a.S, C::BM) * splits;
+  const long long rows = (long long)a.B * a.S * a.H;  // combine: 4 rows per workgroup
+  if (grid > 0x7fffffffLL || (rows + 3) / 4 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  auto kern = fa_fwd_split<D, CAUSAL, VARLEN>;
+  const size_t lds = lds_bytes<D>();
+  if (!allow_lds(kern, lds)) return FA_ERR_HIP;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), lds, stream, a, splits);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  hipLaunchKernelGGL((fa_split_combine<C::DV, VARLEN>), dim3((unsigned)((rows + 3) / 4)), dim3(256),
+                     0, stream, a, splits);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+template <int D>
+int dispatch_split(const Args &a, bool causal, bool varlen, int splits, hipStream_t st) {
+  if (causal) return varlen ? launch_split<D, true, true>(a, splits, st) : launch_split<D, true, false>(a, splits, st);
+  return varlen ? launch_split<D, false, true>(a, splits, st) : launch_split<D, false, false>(a, splits, st);
+}
+
+// Split count for a key range: enough (tile, split) pairs for one per CU
+// (one workgroup fills a CU; measured on a one-row decode step over 32768
+// keys, 32 query tiles: 8 splits run 7x faster than none, 16 or more lose
+// again to the partial writes and the merge), at least two 64-key blocks per
+// split, at most kMaxSplits.  Batches that already have a tile per CU get 1.
+constexpr int kMaxSplits = 64;
+int auto_splits(int B, int H, int S_q, int S_k, int D, int cus) {
+  const long long tiles = (long long)B * H * fa::ceil_div(S_q, bm_for(D));
+  const int kblocks = fa::ceil_div(S_k, kBN);
+  long long want = ((long long)cus + tiles - 1) / tiles;
+  if (want > kblocks / 2) want = kblocks / 2;
+  if (want > kMaxSplits) want = kMaxSplits;
+  return want < 1 ? 1 : (int)want;
+}
+
+// (splits, key blocks per split) actually used for a requested count.
+void split_plan(int S_k, int requested, int *splits, int *kbps) {
+  const int kblocks = fa::ceil_div(S_k, kBN);
+  int n = requested < 1 ? 1 : (requested > kblocks ? kblocks : requested);
+  const int per = fa::ceil_div(kblocks, n);
+  *kbps = per;
+  *splits = fa::ceil_div(kblocks, per);
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
@@ -714,6 +874,8 @@ int fa_fwd_general(const void *q, const void *k, const void *v, void *o, float *
   a.tau = t.tau;
   a.counters = t.counters;
   a.workers = 0;
+  a.ws_o = a.ws_lse = nullptr;
+  a.kbps = 0;
   hipStream_t st = (hipStream_t)stream;
   const bool varlen = cu_seqlens_q != nullptr;
   switch (D) {
@@ -721,6 +883,75 @@ int fa_fwd_general(const void *q, const void *k, const void *v, void *o, float *
     case 128: return dispatch_d<128>(a, causal, varlen, t, dev->cus, st);
     case 192: return dispatch_d<192>(a, causal, varlen, t, dev->cus, st);
     default: return dispatch_d<256>(a, causal, varlen, t, dev->cus, st);
+  }
+}
+
+size_t fa_splitkv_workspace_size(int B, int H, int S_q, int S_k, int D_v, int num_splits) {
+  if (B <= 0 || H <= 0 || S_q <= 0 || S_k <= 0 || D_v <= 0 || num_splits < 0) return 0;
+  int splits, kbps;
+  split_plan(S_k, num_splits, &splits, &kbps);
+  if (splits <= 1) return 0;
+  return (size_t)splits * (size_t)B * (size_t)S_q * (size_t)H * ((size_t)D_v + 1) * sizeof(float);
+}
+
+int fa_splitkv_auto_splits(int B, int H, int S_q, int S_k, int D, int *splits_out) {
+  if (!splits_out || B <= 0 || H <= 0 || S_q <= 0 || S_k <= 0) return FA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128 && D != 192 && D != 256) return FA_ERR_UNSUPPORTED;
+  DeviceInfo *dev = nullptr;
+  const int rc = current_device(&dev);
+  if (rc != FA_OK) return rc;
+  int splits, kbps;
+  split_plan(S_k, auto_splits(B, H, S_q, S_k, D, dev->cus), &splits, &kbps);
+  *splits_out = splits;
+  return FA_OK;
+}
+
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                   int H, int H_kv, int S_q, int S_k, int D, int D_v, float scale, int causal,
+                   const int *cu_seqlens_q, const int *cu_seqlens_k, int num_splits,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+  int rc = validate(q, k, v, o, lse, B, H, H_kv, S_q, S_k, D, D_v, scale, causal, cu_seqlens_q,
+                    cu_seqlens_k, nullptr);
+  if (rc != FA_OK) return rc;
+  int splits, kbps;
+  split_plan(S_k, num_splits, &splits, &kbps);
+  if (splits <= 1)  // one split: the plain path, no workspace
+    return fa_fwd_general(q, k, v, o, lse, B, H, H_kv, S_q, S_k, D, D_v, scale, causal,
+                          cu_seqlens_q, cu_seqlens_k, stream, nullptr);
+  const size_t need = fa_splitkv_workspace_size(B, H, S_q, S_k, D_v, num_splits);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  DeviceInfo *dev = nullptr;
+  rc = current_device(&dev);
+  if (rc != FA_OK) return rc;
+  Args a;
+  a.q = (const __bf16 *)q;
+  a.k = (const __bf16 *)k;
+  a.v = (const __bf16 *)v;
+  a.o = (__bf16 *)o;
+  a.lse = lse;
+  a.cu = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.B = B;
+  a.H = H;
+  a.Hkv = H_kv;
+  a.S = S_q;
+  a.Sk = S_k;
+  a.c = scale * kLog2e;
+  a.tau = fa_tuning_default().tau;
+  a.counters = nullptr;
+  a.workers = 0;
+  const size_t slots = (size_t)B * S_q * H;
+  a.ws_o = (float *)workspace;
+  a.ws_lse = a.ws_o + (size_t)splits * slots * D_v;
+  a.kbps = kbps;
+  hipStream_t st = (hipStream_t)stream;
+  const bool varlen = cu_seqlens_q != nullptr;
+  switch (D) {
+    case 64: return dispatch_split<64>(a, causal, varlen, splits, st);
+    case 128: return dispatch_split<128>(a, causal, varlen, splits, st);
+    case 192: return dispatch_split<192>(a, causal, varlen, splits, st);
+    default: return dispatch_split<256>(a, causal, varlen, splits, st);
   }
 }
 
@@ -832,6 +1063,6 @@ const char *fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 104; }
+int fa_version(void) { return 105; }
 
 }  // extern "C"

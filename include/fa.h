@@ -178,6 +178,49 @@ int fa_fwd_general(const void *q, const void *k, const void *v, void *o, float *
                    const fa_tuning *tuning);
 
 /*
+ * fa_fwd_splitkv -- fa_fwd_general with each key range split over
+ * num_splits workgroups ("split-KV"), for batches with few query rows per
+ * (sequence, head), such as decode steps, where one workgroup per query tile
+ * would leave most of the GPU idle while it streams a long K/V range (the
+ * FlashAttention-4 paper motivates its varlen scheduling with such mixed
+ * prefill/decode batches, section 3.3).
+ *
+ * Each (query tile, split) covers consecutive blocks of 64 keys and writes
+ * the softmax over its own keys, O_s (normalised) and LSE_s, into the
+ * workspace; a second kernel merges them per row:
+ *   LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+ * The result is the same attention as fa_fwd_general (up to rounding).
+ *
+ * Arguments are those of fa_fwd_general, plus:
+ *   num_splits       1 .. 64; fewer are used when the longest key range has
+ *                    fewer 64-key blocks (1 = fa_fwd_general, no workspace);
+ *                    fa_splitkv_auto_splits suggests a count.
+ *   workspace        caller-owned device scratch, 16-byte aligned, of at
+ *                    least fa_splitkv_workspace_size(...) bytes; its
+ *                    contents on entry do not matter, and it must not be
+ *                    used by another call until this one has completed on
+ *                    the stream.
+ * Errors: as fa_fwd_general, plus FA_ERR_INVALID_ARG for num_splits out of
+ * range or a missing, misaligned or too small workspace.
+ */
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int H, int H_kv, int S_q, int S_k, int D, int D_v, float scale,
+                   int causal, const int *cu_seqlens_q, const int *cu_seqlens_k,
+                   int num_splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes fa_fwd_splitkv needs for these sizes (B, H, the longest
+ * query and key lengths S_q and S_k, D_v) and num_splits: partial O and LSE,
+ * fp32, for splits x B x S_q x H rows.  0 when no workspace is needed (one
+ * split) or for invalid sizes. */
+size_t fa_splitkv_workspace_size(int B, int H, int S_q, int S_k, int D_v, int num_splits);
+
+/* A split count for these sizes on the current device: enough (tile,
+ * split) pairs for one per CU (1 when the batch already has a query tile per
+ * CU), at least two 64-key blocks per split.
+ * Writes it to *splits_out; returns an fa_status. */
+int fa_splitkv_auto_splits(int B, int H, int S_q, int S_k, int D, int *splits_out);
+
+/*
  * fa_bwd -- exact attention backward (FlashAttention-4 paper, section 3.2,
  * "attention backward pass": S is recomputed block by block from Q and K,
  * then dP, dV, dQ and dK follow from it).
@@ -262,7 +305,7 @@ int fa_num_workers(int D, int *workers_out);
 const char *fa_status_string(int status);
 
 /* Library ABI version: 100 * major + minor (101: fa_fwd_gqa; 102: fa_fwd_hd;
- * 103: fa_fwd_general; 104: fa_bwd). */
+ * 103: fa_fwd_general; 104: fa_bwd; 105: fa_fwd_splitkv). */
 int fa_version(void);
 
 #ifdef __cplusplus

@@ -194,3 +194,47 @@ def test_backward_binding_refuses_cpu_tensors():
     lse = torch.zeros(1, 1, 8)
     with pytest.raises(ValueError):
         fa.attention_backward(q, q, q, q, lse, q)
+
+
+def test_splitkv_workspace_size():
+    lib = fa.load()
+    # splits x B x S_q x H x (D_v + 1) x 4 bytes; one split (or fewer key
+    # blocks than two) needs none
+    assert lib.fa_splitkv_workspace_size(2, 4, 1, 1000, 128, 4) == 4 * 2 * 1 * 4 * 129 * 4
+    assert lib.fa_splitkv_workspace_size(2, 4, 1, 1000, 128, 1) == 0
+    assert lib.fa_splitkv_workspace_size(1, 1, 1, 64, 128, 8) == 0       # one key block
+    # 1000 keys = 16 blocks: 5 requested -> 4 blocks per split -> 4 splits
+    assert lib.fa_splitkv_workspace_size(1, 1, 1, 1000, 64, 5) == 4 * 1 * 1 * 1 * 65 * 4
+    assert lib.fa_splitkv_workspace_size(0, 4, 1, 1000, 128, 4) == 0
+    assert lib.fa_splitkv_workspace_size(1, 4, 1, 1000, 128, -1) == 0
+
+
+def splitkv_call(**kw):
+    a = dict(B=1, H=8, H_kv=2, S_q=1, S_k=4096, D=128, D_v=128, scale=0.1, causal=1,
+             splits=4, ws=A, ws_bytes=1 << 30)
+    a.update(kw)
+    return fa.load().fa_fwd_splitkv(A, A, A, A, A, a["B"], a["H"], a["H_kv"], a["S_q"], a["S_k"],
+                                    a["D"], a["D_v"], a["scale"], a["causal"], None, None,
+                                    a["splits"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(splits=0), fa.FA_ERR_INVALID_ARG),
+    (dict(splits=65), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=None), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=A + 4), fa.FA_ERR_INVALID_ARG),        # misaligned workspace
+    (dict(ws_bytes=100), fa.FA_ERR_INVALID_ARG),     # too small
+    (dict(H_kv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(D=96, D_v=96), fa.FA_ERR_UNSUPPORTED),
+])
+def test_splitkv_validation_rejects(kw, expect):
+    assert splitkv_call(**kw) == expect
+
+
+def test_splitkv_valid_call_without_gpu_reports_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert splitkv_call() == fa.FA_ERR_NO_DEVICE
+    n = ctypes.c_int(0)
+    assert fa.load().fa_splitkv_auto_splits(1, 8, 1, 4096, 128, ctypes.byref(n)) == fa.FA_ERR_NO_DEVICE

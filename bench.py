@@ -245,6 +245,9 @@ def main():
     ap.add_argument("--gemm-reference", action="store_true",
                     help="only time torch's bf16 matmul (hipBLASLt) on large shapes, as context "
                          "for the MFMA fraction the attention kernel reaches")
+    ap.add_argument("--num-splits", type=int, default=None,
+                    help="run the workload through split-KV (fa_fwd_splitkv) with this many "
+                         "key splits (0: the library's choice for the device)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fa_bwd) on --workload, or with --table on "
                          "every workload it supports (one JSON line each)")
@@ -328,7 +331,7 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
-    r = time_workload(fa, torch, w, args.steps, args.warmup, tuning)
+    r = time_workload(fa, torch, w, args.steps, args.warmup, tuning, num_splits=args.num_splits)
     value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
     achieved = r["flops"] / (r["kernel_ms_mean"] * 1e-3) / 1e12
     out = {
@@ -346,7 +349,9 @@ def main():
         "data": "synthetic",
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
-                   "causal": w.causal, "seed": w.seed, "flops_per_step": r["flops"]},
+                   "causal": w.causal, "seed": w.seed, "flops_per_step": r["flops"],
+                   "num_splits": r["num_splits"],
+                   "io_GB_per_s": round(r["bytes"] / (r["kernel_ms_mean"] * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -133,3 +133,11 @@ def test_splitkv_mixed_workload_sampled():
     st = compare(o_g[t, h], l_g[h, t], o_ref, lse_ref)
     note("split-mixed", st)
     assert_close(st, "split-mixed")
+
+
+def test_splitkv_long_context_decode_auto():
+    """The long-context decode workload (one row per head against 32768
+    keys) through the automatic split count, every output against the oracle."""
+    w = WORKLOADS["decode_1x_q1_k32768_h32kv8d128"]
+    q, k, v, cu_q, cu_k, Sq, Sk = make_qk(w)
+    split_check(q, k, v, True, w.scale, 0, cu_q, cu_k, Sq, Sk, what="split-decode-32k")

@@ -10,7 +10,8 @@ The S=8192 causal workload (B=2, H=16, D=128) the metric also names is timed
 the same way and reported under "secondary".
 
 Timing follows the FlashAttention-4 paper's protocol (appendix A.1: warm up,
-then time repeated runs and report the mean): W untimed warm-up steps, then K
+then time repeated runs and report the mean): about a second of untimed
+back-to-back steps so the clock settles (--settle-s), W untimed warm-up steps, then K
 timed steps bracketed by torch.cuda.synchronize(); each launch is also
 bracketed by HIP events on the launch stream for the per-launch kernel time
 used by the roofline figure.
@@ -73,7 +74,29 @@ DEFAULT_WORKLOAD = "long_b1h16s32768d128_causal"
 SECONDARY_WORKLOAD = "causal_b2h16s8192d128"
 
 
-def time_workload(fa, torch, w, steps, warmup, tuning=None, num_splits=None):
+def settle(torch, step, seconds):
+    """Run the step back to back, untimed, for about `seconds` of wall time.
+
+    Under sustained matrix-core load the GPU's clock and power state take a
+    fraction of a second to settle; a handful of warm-up launches of a
+    sub-millisecond kernel end before that, and the timed steps then run
+    partly at the idle clock (the 8k causal workload reads about 20% low).
+    Returns the number of launches made."""
+    if seconds <= 0:
+        return 0
+    torch.cuda.synchronize()
+    n = 0
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        step()
+        n += 1
+        if n % 4 == 0:   # keep the launch queue short so the loop tracks GPU time
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def time_workload(fa, torch, w, steps, warmup, tuning=None, num_splits=None, settle_s=0.0):
     from attn_inputs import make, make_qk, flops
     dev = torch.device("cuda:0")
     extra = {}
@@ -108,6 +131,7 @@ def time_workload(fa, torch, w, steps, warmup, tuning=None, num_splits=None):
                      max_seqlen=S if cu is not None else None, out=o, lse_out=lse,
                      tuning=tuning, **extra)
 
+    n_settle = settle(torch, step, settle_s)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -132,6 +156,7 @@ def time_workload(fa, torch, w, steps, warmup, tuning=None, num_splits=None):
         "kernel_ms_mean": float(np.mean(kernel_ms)),
         "kernel_ms_median": float(np.median(kernel_ms)),
         "kernel_ms_min": float(np.min(kernel_ms)),
+        "settle_launches": n_settle,
         "inputs": (q, k, v, cu),
     }
 
@@ -142,7 +167,7 @@ BACKWARD_WORKLOADS = ["causal_b2h16s8192d128", "long_b1h16s32768d128_causal",
                       "smoke_b1h8s512d64_causal"]
 
 
-def time_backward(fa, torch, w, steps, warmup):
+def time_backward(fa, torch, w, steps, warmup, settle_s=0.0):
     """Time fa_bwd (its dQ kernel and its dK/dV kernel) on a workload, after
     one forward launch that provides o and lse.  Flops follow the usual
     backward convention: 2.5x the forward's (five products of the forward's
@@ -163,6 +188,7 @@ def time_backward(fa, torch, w, steps, warmup):
         fa.attention_backward(dq_, dk_, dv_, o, lse, g, causal=w.causal, scale=w.scale,
                               cu_seqlens=dcu, max_seqlen=ms, dq=gq, dk=gk, dv=gv, delta=delta)
 
+    settle(torch, step, settle_s)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -234,6 +260,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="untimed back-to-back steps for this many seconds before the warm-up "
+                         "steps, so that the timed steps run at the settled clock (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--tau", type=float, default=None)
@@ -311,7 +340,8 @@ def main():
     if args.backward:
         names = BACKWARD_WORKLOADS if args.table else [args.workload]
         for name in names:
-            print(json.dumps(time_backward(fa, torch, WORKLOADS[name], args.steps, args.warmup)),
+            print(json.dumps(time_backward(fa, torch, WORKLOADS[name], args.steps, args.warmup,
+                                            args.settle_s)),
                   flush=True)
         return
 
@@ -319,7 +349,8 @@ def main():
         for name, wl in WORKLOADS.items():
             # workloads with few query rows per sequence also run split-KV
             for sp in ([None, 0] if wl.q_range else [None]):
-                rr = time_workload(fa, torch, wl, args.steps, args.warmup, tuning, num_splits=sp)
+                rr = time_workload(fa, torch, wl, args.steps, args.warmup, tuning, num_splits=sp,
+                                   settle_s=args.settle_s)
                 v = rr["flops"] / (rr["kernel_ms_mean"] * 1e-3) / 1e12
                 print(json.dumps({"workload": name, "num_splits": rr["num_splits"],
                                   "kernel_ms_mean": round(rr["kernel_ms_mean"], 4),
@@ -331,7 +362,8 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
-    r = time_workload(fa, torch, w, args.steps, args.warmup, tuning, num_splits=args.num_splits)
+    r = time_workload(fa, torch, w, args.steps, args.warmup, tuning, num_splits=args.num_splits,
+                      settle_s=args.settle_s)
     value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
     achieved = r["flops"] / (r["kernel_ms_mean"] * 1e-3) / 1e12
     out = {
@@ -341,6 +373,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"seconds": args.settle_s, "launches": r["settle_launches"]},
         "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -362,7 +395,7 @@ def main():
     }
     if not args.no_secondary and args.workload == DEFAULT_WORKLOAD:
         w2 = WORKLOADS[SECONDARY_WORKLOAD]
-        r2 = time_workload(fa, torch, w2, args.steps, args.warmup, tuning)
+        r2 = time_workload(fa, torch, w2, args.steps, args.warmup, tuning, settle_s=args.settle_s)
         v2 = r2["flops"] / (r2["ms_per_step"] * 1e-3) / 1e12
         out["secondary"] = {"workload": w2.name, "value": round(v2, 2), "unit": "TFLOP/s",
                             "pct_of_peak": round(100 * v2 / PEAK_BF16_TFLOPS, 2),

@@ -432,11 +432,13 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     // after the barrier would queue 32 KB on the CU's vector-memory path at
     // once and hold the waves that start matrix products behind it.
     // Part 0: this wave's K copies of block it+2; part 1: its V copies.
+    const char *kseq = ldk.seq_base(a.k, ktok0, Hk, hk);
+    const char *vseq = ldv.seq_base(a.v, ktok0, Hk, hk);
     auto copies = [&](int it) {
       return [&, it](int part) {
         if (it + 2 < nblocks) {
-          if (part == 0) ldk.issue(a.k, ktok0, Hk, hk, (it + 2) * kBN, Lk, kbuf(it + 2), kbuf2(it + 2));
-          else ldv.issue(a.v, ktok0, Hk, hk, (it + 2) * kBN, Lk, vbuf(it + 2));
+          if (part == 0) ldk.issue_at(kseq, (it + 2) * kBN, Lk, kbuf(it + 2), kbuf2(it + 2));
+          else ldv.issue_at(vseq, (it + 2) * kBN, Lk, vbuf(it + 2));
         }
       };
     };
@@ -452,12 +454,12 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       }
     };
     if (nblocks > 0) {
-      ldk.issue(a.k, ktok0, Hk, hk, 0, Lk, kbuf(0), kbuf2(0));
-      ldv.issue(a.v, ktok0, Hk, hk, 0, Lk, vbuf(0));
+      ldk.issue_at(kseq, 0, Lk, kbuf(0), kbuf2(0));
+      ldv.issue_at(vseq, 0, Lk, vbuf(0));
     }
     if (nblocks > 1) {
-      ldk.issue(a.k, ktok0, Hk, hk, kBN, Lk, kbuf(1), kbuf2(1));
-      ldv.issue(a.v, ktok0, Hk, hk, kBN, Lk, vbuf(1));
+      ldk.issue_at(kseq, kBN, Lk, kbuf(1), kbuf2(1));
+      ldv.issue_at(vseq, kBN, Lk, vbuf(1));
     }
     // The two halves run separate loops that meet at the same barriers.
     if (half == 0) {

@@ -149,38 +149,55 @@ struct BlockLoader {
         : "memory", "m0");
   }
 
-  // Copy this wave's chunk i of rows n0 .. n0+BN-1 of one (sequence, K/V
-  // head) of K or V into the LDS block dst (dst2: its second part, W = 192).
-  // Rows at or past L read row L-1 instead (in bounds; masked later).  The
-  // full-block test is on scalars only: one scalar branch.
+  // LDS byte address of this wave's copy I in the block at dst (dst2: the
+  // second part of a W = 192 block).
   template <int I>
-  __device__ __forceinline__ void issue_one(const __bf16 *base, long long tok0, int Hk, int hk,
-                                            int n0, int L, char LDS_AS *dst,
-                                            char LDS_AS *dst2) const {
-    const char *blk = (const char *)(base + ((tok0 + n0) * Hk + hk) * (long long)W);
-    const unsigned lds_addr =
-        second_part(I) ? (unsigned)(uintptr_t)dst2 + (unsigned)(slot0(I) - 1024) * 16u
-                       : (unsigned)(uintptr_t)dst + (unsigned)slot0(I) * 16u;
+  __device__ __forceinline__ unsigned lds_slot(unsigned dst, unsigned dst2) const {
+    return second_part(I) ? dst2 + (unsigned)(slot0(I) - 1024) * 16u
+                          : dst + (unsigned)slot0(I) * 16u;
+  }
+
+  // Row 0 of one (sequence, K/V head): the per-tile base of issue_at.
+  static __device__ __forceinline__ const char *seq_base(const __bf16 *base, long long tok0,
+                                                         int Hk, int hk) {
+    return (const char *)(base + (tok0 * Hk + hk) * (long long)W);
+  }
+
+  // Copy this wave's chunks of rows n0 .. n0+BN-1 of the (sequence, head)
+  // whose row 0 is at seq into the LDS block dst (dst2: its second part,
+  // W = 192).  Rows at or past L read row L-1 instead (in bounds; masked
+  // later).  The block address and the full-block test are computed once per
+  // block on scalars, so a copy costs one m0 write and the load: the scalar
+  // unit is shared by every wave of the CU, and per-copy address arithmetic
+  // and branches used to hold the issuing wave for hundreds of cycles.
+  __device__ __forceinline__ void issue_at(const char *seq, int n0, int L, char LDS_AS *dst,
+                                           char LDS_AS *dst2 = nullptr) const {
+    const char *blk = seq + (long long)n0 * row_bytes;
+    const unsigned d0 = (unsigned)(uintptr_t)dst, d1 = (unsigned)(uintptr_t)dst2;
     if (n0 + kBN <= L) {
-      dma16(blk, voff[I], lds_addr);
+      issue_full(blk, d0, d1, std::make_integer_sequence<int, LOADS>{});
     } else {
-      const int last = L - 1 - n0;  // >= 0: blocks start below L
-      const int row = row_of(I);
-      const int r = row < last ? row : last;
-      dma16(blk, voff[I] - (unsigned)(row - r) * row_bytes, lds_addr);
+      issue_tail(blk, d0, d1, L - 1 - n0, std::make_integer_sequence<int, LOADS>{});
     }
   }
-  // All of this wave's chunks of one block.
+  template <int... I>
+  __device__ __forceinline__ void issue_full(const char *blk, unsigned d0, unsigned d1,
+                                             std::integer_sequence<int, I...>) const {
+    (dma16(blk, voff[I], lds_slot<I>(d0, d1)), ...);
+  }
+  // last = L-1-n0 >= 0 (blocks start below L): rows past it read row last.
+  template <int... I>
+  __device__ __forceinline__ void issue_tail(const char *blk, unsigned d0, unsigned d1, int last,
+                                             std::integer_sequence<int, I...>) const {
+    (dma16(blk, voff[I] - (unsigned)(row_of(I) - (row_of(I) < last ? row_of(I) : last)) * row_bytes,
+           lds_slot<I>(d0, d1)),
+     ...);
+  }
+  // All of this wave's chunks of rows n0 .. n0+BN-1 of one (sequence, head).
   __device__ __forceinline__ void issue(const __bf16 *base, long long tok0, int Hk, int hk, int n0,
                                         int L, char LDS_AS *dst,
                                         char LDS_AS *dst2 = nullptr) const {
-    issue_all(base, tok0, Hk, hk, n0, L, dst, dst2, std::make_integer_sequence<int, LOADS>{});
-  }
-  template <int... I>
-  __device__ __forceinline__ void issue_all(const __bf16 *base, long long tok0, int Hk, int hk,
-                                            int n0, int L, char LDS_AS *dst, char LDS_AS *dst2,
-                                            std::integer_sequence<int, I...>) const {
-    (issue_one<I>(base, tok0, Hk, hk, n0, L, dst, dst2), ...);
+    issue_at(seq_base(base, tok0, Hk, hk), n0, L, dst, dst2);
   }
 };
 

@@ -581,7 +581,8 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fw
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   char LDS_AS *lds = (char LDS_AS *)lds_raw;
   using C = Cfg<D>;
-  fa::Sched s = fa::make_sched(a.B, a.H, a.Hkv, a.S, C::BM, CAUSAL, VARLEN, a.workers);
+  fa::Sched s = fa::make_sched(a.B, a.H, a.Hkv, a.S, C::BM, CAUSAL, VARLEN, a.workers,
+                               a.cu_k == a.cu);
   fa::SchedTables t{nullptr, nullptr, nullptr};
   if constexpr (VARLEN) {
     int *tab = (int *)(lds_raw + lds_bytes<D>());
@@ -606,6 +607,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fw
     const int p = fa::snake_position(r, w, W);
     if (p >= npos) break;
     const fa::Tile tl = fa::decode_position(s, t, x, p);
+    if (tl.b < 0) continue;  // a level this sequence does not reach
     run_tile<D, CAUSAL, VARLEN, EMU, COUNT>(a, tl.b, tl.h, tl.mb, lds);
   }
 }
@@ -1026,18 +1028,18 @@ int fa_schedule_gqa(int B, int H, int H_kv, int S, int D, int causal, const int 
   for (int wk = 0; wk < workers; ++wk) {
     int x, w, W;
     fa::worker_slot(s, wk, workers, &x, &w, &W);
-    for (int r = 0; r < max_rounds; ++r) {
+    // the worker's tiles in the order it runs them (idle positions skipped)
+    int n = 0;
+    for (int r = 0;; ++r) {
       const int p = fa::snake_position(r, w, W);
-      int code = -1;
-      if (p < npos) {
-        const fa::Tile tl = fa::decode_position(s, t, x, p);
-        code = (tl.b * H + tl.h) * s.nmb_max + tl.mb;
-        if (r + 1 > rounds) rounds = r + 1;
-      }
-      tiles[(long long)wk * max_rounds + r] = code;
+      if (p >= npos) break;
+      const fa::Tile tl = fa::decode_position(s, t, x, p);
+      if (tl.b < 0) continue;
+      if (n == max_rounds) return FA_ERR_INVALID_ARG;  // the list must fit max_rounds
+      tiles[(long long)wk * max_rounds + n++] = (tl.b * H + tl.h) * s.nmb_max + tl.mb;
     }
-    // the worker must have finished within max_rounds
-    if (fa::snake_position(max_rounds, w, W) < npos) return FA_ERR_INVALID_ARG;
+    if (n > rounds) rounds = n;
+    for (int r = n; r < max_rounds; ++r) tiles[(long long)wk * max_rounds + r] = -1;
   }
   if (rounds_out) *rounds_out = rounds;
   if (bm_out) *bm_out = BM;

@@ -274,14 +274,16 @@ int fa_exp2_emu(const float *x, float *y, long long n, void *stream);
 /*
  * fa_schedule -- host-only view of the persistent tile order (no GPU use).
  *
- * Fills tiles[w * max_rounds + r] with the tile that persistent workgroup w
- * processes in its round r, or -1 when it has no more work, for a launch of
- * `workers` workgroups.  A tile is encoded as
+ * Fills tiles[w * max_rounds + r] with the r-th tile that persistent
+ * workgroup w processes, or -1 when it has no more work, for a launch of
+ * `workers` workgroups (positions of the order that hold no tile, such as a
+ * level a short sequence does not reach, are skipped as the kernel skips
+ * them).  A tile is encoded as
  *   ((seq * H + head) * n_mblocks_max + mblock)
  * with n_mblocks_max = ceil(S / BM) and BM the row-tile height chosen for D
  * (the q/k head dimension: 64, 128, 192 or 256).
  * cu_seqlens, if not NULL, is a HOST int32 array of B+1 entries.  *rounds_out
- * receives the number of rounds used and *bm_out the BM used.  Returns
+ * receives the length of the longest list and *bm_out the BM used.  Returns
  * FA_ERR_INVALID_ARG when max_rounds is too small or an argument is invalid.
  */
 int fa_schedule(int B, int H, int S, int D, int causal, const int *cu_seqlens,

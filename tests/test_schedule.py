@@ -71,8 +71,19 @@ def test_every_tile_exactly_once(case):
         idle = np.flatnonzero(row < 0)
         if idle.size:
             assert np.all(row[idle[0]:] < 0)
-    # LPT (causal): within each worker the costs never increase
-    if causal:
+    # LPT (causal): within each worker the costs never increase.  Varlen
+    # causal batches are ordered by chunks of `sub` levels (the m-blocks of
+    # one sequence run together for K/V reuse in L2): there the chunk of a
+    # worker's tiles never goes back, and inside a chunk costs differ by at
+    # most sub-1 m-blocks.
+    if causal and lens is not None:
+        nmb = math.ceil(S / bm)
+        groups = 8 if H % 8 == 0 and workers % 8 == 0 else 1
+        sub = min(max((workers // groups) // (H // groups), 1), 8)
+        for row in tiles:
+            ch = [(nmb - 1 - t % nmb) // sub for t in row if t >= 0]
+            assert all(ch[i] <= ch[i + 1] for i in range(len(ch) - 1)), ch
+    elif causal:
         for row in tiles:
             c = [tile_cost(t, H, S, bm, causal, L) for t in row if t >= 0]
             assert all(c[i] >= c[i + 1] for i in range(len(c) - 1)), c

@@ -160,6 +160,99 @@ __device__ __forceinline__ void qk_step(WaveState<D> &st, const LdsAddr<D> &la,
   }
 }
 
+// Softmax of one block, in pieces the pipelined D = 256 body interleaves with
+// matrix products.  Scores are S^T accumulators s[kb] (kb: 32-key sub-block);
+// the key index of s[kb][4i+j] is n0 + 32kb + 8i + 4h + j, h = lane / 32.
+//
+// mask_slice: mask scores e0 .. e0+7 of sub-block kb.  A key is kept iff
+// key < L and (non-causal or key <= row), i.e. iff its in-block offset
+// 32kb + 8(e>>2) + (e&3), a constant, is below the per-lane limit lim: one
+// compare and one select per score.  max_slice folds the same scores into
+// the running maximum mx.
+template <bool CAUSAL>
+__device__ __forceinline__ int mask_limit(int lane, int n0, int row, int L) {
+  return (CAUSAL ? (row + 1 < L ? row + 1 : L) : L) - n0 - 4 * (lane >> 5);
+}
+__device__ __forceinline__ void mask_slice(f32x16 (&s)[2], int kb, int e0, int lim) {
+#pragma unroll
+  for (int e = e0; e < e0 + 8; ++e) {
+    const int off = 32 * kb + 8 * (e >> 2) + (e & 3);
+    s[kb][e] = off < lim ? s[kb][e] : -INFINITY;
+  }
+}
+__device__ __forceinline__ void max_slice(const f32x16 (&s)[2], int kb, int e0, float &mx) {
+#pragma unroll
+  for (int e = e0; e < e0 + 8; ++e) mx = fmaxf(mx, s[kb][e]);
+}
+
+// Conditional rescale (paper section 3.1.4), decided for the whole wave, from
+// the block's raw row maximum (both half-waves combined).  rescale_decide
+// moves m_ref and the row sum; the caller scales O by alpha when `any` (at
+// once, or after products still in flight that use the old scale).
+struct Rescale {
+  bool any;
+  float alpha;
+};
+template <int D, bool COUNT>
+__device__ __forceinline__ Rescale rescale_decide(WaveState<D> &st, float mx, int lane,
+                                                  const Args &a) {
+  mx = max_halves(mx);
+  const float m_blk = mx * a.c;  // -inf when the whole row of the block is masked
+  const bool need = m_blk > st.m_ref + a.tau;
+  Rescale r{__builtin_amdgcn_ballot_w64(need) != 0, 1.0f};
+  if (r.any) {
+    const float m_new = fmaxf(st.m_ref, m_blk);
+    r.alpha = (st.m_ref == -INFINITY) ? 0.0f : exp2_hw(st.m_ref - m_new);
+    st.m_ref = m_new;
+    st.l32 *= r.alpha;
+    if constexpr (COUNT) {
+      if (lane == 0) atomicAdd(&a.counters[0], 1ull);
+    }
+  }
+  if constexpr (COUNT) {
+    if (lane == 0) atomicAdd(&a.counters[1], 1ull);
+  }
+  return r;
+}
+template <int D>
+__device__ __forceinline__ void scale_o(WaveState<D> &st, float alpha) {
+#pragma unroll
+  for (int dt = 0; dt < head_dim_v<D>() / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st.o[dt][e] *= alpha;
+}
+// The reference maximum the block's exponentials use.
+template <int D>
+__device__ __forceinline__ float m_use_of(const WaveState<D> &st) {
+  return (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
+}
+template <int D, bool COUNT>
+__device__ __forceinline__ float rescale_step(WaveState<D> &st, float mx, int lane, const Args &a) {
+  const Rescale r = rescale_decide<D, COUNT>(st, mx, lane, a);
+  if (r.any) scale_o<D>(st, r.alpha);
+  return m_use_of<D>(st);
+}
+
+// p = exp2(c*s - m) for scores e, e+1 of sub-block kb: row sum (one partial
+// sum per sub-block, to halve the dependent chain) and bf16 pack into the PV
+// operand layout.
+template <int EMU>
+__device__ __forceinline__ void exp_pair(bf16x8 (&p)[4], const f32x16 (&s)[2], int kb, int e,
+                                         float m_use, bool last_block, const Args &a,
+                                         float (&lsum)[2]) {
+  const float x0 = __builtin_fmaf(s[kb][e], a.c, -m_use);
+  const float x1 = __builtin_fmaf(s[kb][e + 1], a.c, -m_use);
+  float p0, p1;
+  if (EMU > 0 && !last_block && (e % EMU) == 0) p0 = exp2_poly(x0);
+  else p0 = exp2_hw(x0);
+  p1 = exp2_hw(x1);
+  lsum[kb] += p0 + p1;
+  const bf16x2 pb = {(__bf16)p0, (__bf16)p1};
+  const int t = 2 * kb + (e >> 3);
+  p[t][e & 7] = pb[0];
+  p[t][(e & 7) + 1] = pb[1];
+}
+
 // Mask, row statistics, conditional rescale, exp2, row sums and bf16 packing
 // of one block (scores in st.s, probabilities out to st.p).  side(0) runs
 // before the row max and side(1) before the exp loop: the caller hangs its
@@ -169,69 +262,26 @@ __device__ __forceinline__ void softmax_step(WaveState<D> &st, int lane, int n0,
                                              bool need_mask, bool last_block, const Args &a,
                                              Side &&side) {
   side(0);
-  // ---- mask: key index of s[kb][4i+j] is n0 + 32kb + 8i + 4h + j
-  const int h = lane >> 5;
-  // A key is kept iff key < L and (non-causal or key <= row), i.e. iff its
-  // in-block offset 32kb + 8(e>>2) + (e&3), a constant, is below the per-lane
-  // limit lim: one compare and one select per score.
   if (need_mask) {
-    const int lim = (CAUSAL ? (row + 1 < L ? row + 1 : L) : L) - n0 - 4 * h;
+    const int lim = mask_limit<CAUSAL>(lane, n0, row, L);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int off = 32 * kb + 8 * (e >> 2) + (e & 3);
-        st.s[kb][e] = off < lim ? st.s[kb][e] : -INFINITY;
-      }
+      for (int e0 = 0; e0 < 16; e0 += 8) mask_slice(st.s, kb, e0, lim);
   }
-  // ---- block row max (raw scores; c > 0 so it commutes with scaling)
-  float mx = st.s[0][0];
+  // block row max (raw scores; c > 0 so it commutes with scaling)
+  float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st.s[kb][e]);
-  mx = max_halves(mx);
-  const float m_blk = mx * a.c;  // -inf when the whole row of the block is masked
-  // ---- conditional rescale, decided for the whole wave
-  const bool need = m_blk > st.m_ref + a.tau;
-  if (__builtin_amdgcn_ballot_w64(need) != 0) {
-    const float m_new = fmaxf(st.m_ref, m_blk);
-    const float alpha = (st.m_ref == -INFINITY) ? 0.0f : exp2_hw(st.m_ref - m_new);
-    st.m_ref = m_new;
-    st.l32 *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < head_dim_v<D>() / 32; ++dt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) st.o[dt][e] *= alpha;
-    if constexpr (COUNT) {
-      if (lane == 0) atomicAdd(&a.counters[0], 1ull);
-    }
-  }
-  if constexpr (COUNT) {
-    if (lane == 0) atomicAdd(&a.counters[1], 1ull);
-  }
-  const float m_use = (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
+    for (int e0 = 0; e0 < 16; e0 += 8) max_slice(st.s, kb, e0, mx);
+  const float m_use = rescale_step<D, COUNT>(st, mx, lane, a);
   side(1);
-  // ---- p = exp2(c*s - m), row sum (one partial sum per key sub-block, to
-  // halve the dependent chain), bf16 pack into the PV operand layout
   float lsum[2] = {0.0f, 0.0f};
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const float x0 = __builtin_fmaf(st.s[kb][e], a.c, -m_use);
-      const float x1 = __builtin_fmaf(st.s[kb][e + 1], a.c, -m_use);
-      float p0, p1;
-      if (EMU > 0 && !last_block && (e % EMU) == 0) p0 = exp2_poly(x0);
-      else p0 = exp2_hw(x0);
-      p1 = exp2_hw(x1);
-      lsum[kb] += p0 + p1;
-      const bf16x2 pb = {(__bf16)p0, (__bf16)p1};
-      const int t = 2 * kb + (e >> 3);
-      st.p[t][e & 7] = pb[0];
-      st.p[t][(e & 7) + 1] = pb[1];
-    }
-  }
+    for (int e = 0; e < 16; e += 2) exp_pair<EMU>(st.p, st.s, kb, e, m_use, last_block, a, lsum);
   st.l32 += lsum[0] + lsum[1];
 }
 
@@ -258,6 +308,70 @@ __device__ __forceinline__ void pv_step(WaveState<D> &st, const LdsAddr<D> &la,
       st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t][dt], st.p[t], st.o[dt], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// ---------------------------------------------------------------------------
+// The pipelined single-wave body (D = 256; run_tile) runs the softmax of
+// block j between the PV products of block j-1.  MFMAs run asynchronously to
+// the instructions of their own wave, so VALU work placed between them runs
+// in the matrix unit's shadow; the scheduling barriers keep that order.
+// ---------------------------------------------------------------------------
+// O^T += V^T P_prev^T (the previous block), with the exp pairs of the current
+// block (scores s, probabilities out to p_cur) spread over its products.
+// V^T of key step t+1, d tile dt, is read right after the product that
+// consumed the step-t operand of the same tile.  (Placing the mask, row max
+// and rescale decision beside the first products as well measured slower:
+// the decision waits on the whole row maximum in the middle of the stream.)
+template <int D, int EMU>
+__device__ __forceinline__ void pv_with_exp(WaveState<D> &st, const LdsAddr<D> &la,
+                                            const char LDS_AS *vbuf, const bf16x8 (&p_prev)[4],
+                                            const f32x16 (&s)[2], bf16x8 (&p_cur)[4],
+                                            float m_use, bool last_block, const Args &a,
+                                            float (&lsum)[2]) {
+  constexpr int DV = head_dim_v<D>();
+  constexpr int NT = DV / 32;
+  constexpr int PAIRS = 16;  // score pairs per lane and block
+  static_assert((4 * NT) % PAIRS == 0, "exp pairs spread evenly over the products");
+  const unsigned va0 = la.vw0 + lds_u32(vbuf), va1 = la.vw1 + lds_u32(vbuf);
+  bf16x8 vf[4][NT];
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) vf[0][dt] = read_vt<DV>(va0, va1, 0, dt);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+      __builtin_amdgcn_sched_barrier(0);
+      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t][dt], p_prev[t], st.o[dt], 0, 0, 0);
+      if (t + 1 < 4) vf[t + 1][dt] = read_vt<DV>(va0, va1, t + 1, dt);
+      if ((t * NT + dt) % (4 * NT / PAIRS) == 0) {
+        const int i = (t * NT + dt) / (4 * NT / PAIRS);
+        exp_pair<EMU>(p_cur, s, i / 8, 2 * (i % 8), m_use, last_block, a, lsum);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// O^T += V^T P^T for a given P set (the pipelined body's last block).
+template <int D>
+__device__ __forceinline__ void pv_of(WaveState<D> &st, const LdsAddr<D> &la,
+                                      const char LDS_AS *vbuf, const bf16x8 (&p)[4]) {
+  constexpr int DV = head_dim_v<D>();
+  constexpr int NT = DV / 32;
+  const unsigned va0 = la.vw0 + lds_u32(vbuf), va1 = la.vw1 + lds_u32(vbuf);
+  bf16x8 vf[4][NT];
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) vf[0][dt] = read_vt<DV>(va0, va1, 0, dt);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+      __builtin_amdgcn_sched_barrier(0);
+      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t][dt], p[t], st.o[dt], 0, 0, 0);
+      if (t + 1 < 4) vf[t + 1][dt] = read_vt<DV>(va0, va1, t + 1, dt);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Which KV blocks a wave (32 rows from wrow0) needs, and which need masking.
@@ -485,6 +599,91 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
         __builtin_amdgcn_s_setprio(0);
       }
     }
+  } else if constexpr (!VARLEN && !CAUSAL) {
+    // One wave per SIMD (D = 256: O alone is 128 registers per lane), so
+    // the matrix/softmax overlap comes from within the wave.  The iteration
+    // of block j runs S_j = K_j Q^T, the mask, row max and rescale decision
+    // of block j and its exp loop between the PV products of block j-1 (two
+    // P register sets).  O is scaled after those products, which still use
+    // the old scale.  Without a causal mask every wave runs
+    // every block, so the loop has one path: a wave whose rows lie past the
+    // sequence end works on clamped rows and stores nothing.  V_{j-1} is
+    // read in the iteration of block j, so K sits in a ring of two 32 KiB
+    // slots and V in a ring of three (160 KiB in all).  After the barrier
+    // that opens iteration j, slot ((j+1)&1) of K (K_{j-1}) and slot
+    // ((j+1)%3) of V (V_{j-2}) are free, and block j+1 is copied into them:
+    // K one iteration ahead of its use, V two.
+    static_assert(D == DV, "the pipelined single-wave body keeps K and V blocks of one size");
+    constexpr int BLK = C::K_BYTES;
+    auto kslot = [&](int j) { return lds + (j & 1) * BLK; };
+    auto vslot = [&](int j) { return lds + 2 * BLK + (j % 3) * BLK; };
+    constexpr int LK = BlockLoader<D, C::NW>::LOADS;
+    const char *kseq = ldk.seq_base(a.k, ktok0, Hk, hk);
+    const char *vseq = ldk.seq_base(a.v, ktok0, Hk, hk);
+    auto issue_block = [&](int j) {
+      if (j < nblocks) {
+        ldk.issue_at(kseq, j * kBN, Lk, kslot(j));
+        ldk.issue_at(vseq, j * kBN, Lk, vslot(j));
+      }
+    };
+    // Opens iteration j: K_j and V_{j-1} have landed (V_j may still be in
+    // flight), the barrier makes them visible and frees the slots of block j+1.
+    auto open = [&](int j) {
+      if (j < nblocks) wait_vmcnt<LK>();
+      else wait_vmcnt<0>();
+      barrier_after_reads();
+      issue_block(j + 1);
+    };
+    // S_j, its mask and row max, and the rescale decision.
+    auto scores = [&](int j, float &m_use) {
+      qk_step<D>(st, la, kslot(j), kslot(j));
+      if (wr.need_mask(j, Lk, false)) {
+        const int lim = mask_limit<false>(lane, j * kBN, row + koff, Lk);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e0 = 0; e0 < 16; e0 += 8) mask_slice(st.s, kb, e0, lim);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e0 = 0; e0 < 16; e0 += 8) max_slice(st.s, kb, e0, mx);
+      const Rescale r = rescale_decide<D, COUNT>(st, mx, lane, a);
+      m_use = m_use_of<D>(st);
+      return r;
+    };
+    bf16x8 p_prev[4];
+    if (nblocks > 0) {
+      issue_block(0);
+      open(0);
+      float m_use;
+      const Rescale r = scores(0, m_use);  // O is still zero: nothing to scale
+      (void)r;
+      float lsum[2] = {0.0f, 0.0f};
+      const bool last = nblocks == 1;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) exp_pair<EMU>(st.p, st.s, kb, e, m_use, last, a, lsum);
+      st.l32 += lsum[0] + lsum[1];
+    }
+    for (int j = 1; j < nblocks; ++j) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) p_prev[t] = st.p[t];
+      open(j);
+      float m_use;
+      const Rescale r = scores(j, m_use);
+      float lsum[2] = {0.0f, 0.0f};
+      pv_with_exp<D, EMU>(st, la, vslot(j - 1), p_prev, st.s, st.p, m_use, j == nblocks - 1, a,
+                          lsum);
+      st.l32 += lsum[0] + lsum[1];
+      if (r.any) scale_o<D>(st, r.alpha);
+    }
+    if (nblocks > 0) {
+      open(nblocks);
+      pv_of<D>(st, la, vslot(nblocks - 1), st.p);
+    }
   } else {
     static_assert(D == DV, "the serial path keeps K and V blocks of one size");
     char LDS_AS *kb0 = lds;
@@ -570,9 +769,12 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   }
 }
 
-template <int D>
+// Dynamic LDS of a kernel instance: the ping-pong K/V ring; for the
+// single-wave body, rings of two K and three V blocks (the pipelined dense
+// non-causal body) or the double buffer.
+template <int D, bool VARLEN, bool CAUSAL>
 constexpr int lds_bytes() {
-  return Cfg<D>::PINGPONG ? KvLayout<D>::BYTES : 4 * Cfg<D>::K_BYTES;
+  return Cfg<D>::PINGPONG ? KvLayout<D>::BYTES : (VARLEN || CAUSAL ? 4 : 5) * Cfg<D>::K_BYTES;
 }
 
 // Persistent kernel: each workgroup walks its static LPT list.
@@ -585,7 +787,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fw
                                a.cu_k == a.cu);
   fa::SchedTables t{nullptr, nullptr, nullptr};
   if constexpr (VARLEN) {
-    int *tab = (int *)(lds_raw + lds_bytes<D>());
+    int *tab = (int *)(lds_raw + lds_bytes<D, VARLEN, CAUSAL>());
     t.len = tab;
     t.sorted = tab + fa::kMaxVarlenSeqs;
     t.off = tab + 2 * fa::kMaxVarlenSeqs;
@@ -738,7 +940,7 @@ template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>
 int launch_variant(const Args &a0, int schedule, int cus, hipStream_t stream) {
   using C = Cfg<D>;
   Args a = a0;
-  size_t lds = lds_bytes<D>();
+  size_t lds = lds_bytes<D, VARLEN, CAUSAL>();
   const int nmb = fa::ceil_div(a.S, C::BM);
   bool persistent = (schedule == 0);
   if (VARLEN && (a.B > fa::kMaxVarlenSeqs || nmb > fa::kMaxVarlenLevels)) persistent = false;
@@ -767,7 +969,7 @@ int launch_split(const Args &a, int splits, hipStream_t stream) {
   const long long rows = (long long)a.B * a.S * a.H;  // combine: 4 rows per workgroup
   if (grid > 0x7fffffffLL || (rows + 3) / 4 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   auto kern = fa_fwd_split<D, CAUSAL, VARLEN>;
-  const size_t lds = lds_bytes<D>();
+  const size_t lds = lds_bytes<D, VARLEN, CAUSAL>();
   if (!allow_lds(kern, lds)) return FA_ERR_HIP;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), lds, stream, a, splits);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;

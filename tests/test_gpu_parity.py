@@ -68,6 +68,12 @@ SMALL = [
     (1, 63, 2, 128),
     (2, 257, 1, 64),
     (1, 513, 2, 256),
+    # D = 256 sequences of one block (ragged and full) and of a few blocks:
+    # the first and last blocks of the pipelined single-wave body, and waves
+    # whose rows lie past the sequence end
+    (1, 40, 2, 256),
+    (1, 64, 1, 256),
+    (2, 130, 1, 256),
 ]
 
 
@@ -450,9 +456,10 @@ def test_tau_invariance():
     assert excess <= 1e-2, excess
 
 
+@pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("emu", [8, 4])
-def test_exp2_split_variants(emu):
-    q, k, v = draw_qkv((2, 900, 2, 128), seed=71)
+def test_exp2_split_variants(emu, D):
+    q, k, v = draw_qkv((2, 900, 2, 128) if D == 128 else (1, 700, 2, 256), seed=71)
     t = fa.default_tuning()
     t.exp2_emu = emu
     note("exp2 emu", emu)

@@ -83,6 +83,9 @@ def load(path: str = LIB_PATH):
     lib.fa_schedule_gqa.argtypes = [I, I, I, I, I, I, P, I, P, I, ctypes.POINTER(I),
                                     ctypes.POINTER(I)]
     lib.fa_schedule_gqa.restype = I
+    lib.fa_schedule_general.argtypes = [I, I, I, I, I, I, P, P, I, P, I, ctypes.POINTER(I),
+                                        ctypes.POINTER(I)]
+    lib.fa_schedule_general.restype = I
     lib.fa_num_workers.argtypes = [I, ctypes.POINTER(I)]
     lib.fa_num_workers.restype = I
     lib.fa_status_string.argtypes = [I]
@@ -346,12 +349,15 @@ def exp2_emu(x, stream=None):
 
 
 def schedule(B: int, H: int, S: int, D: int, causal: bool, workers: int,
-             cu_seqlens=None, max_rounds: int = 4096, H_kv: Optional[int] = None):
+             cu_seqlens=None, max_rounds: int = 4096, H_kv: Optional[int] = None,
+             cu_seqlens_k=None):
     """Host-side persistent tile order: (tiles [workers, rounds] int32, BM).
 
     Tile code = (seq * H + head) * ceil(S / BM) + mblock, -1 = idle.
     cu_seqlens (optional) is a host sequence of B+1 offsets; H_kv (optional)
-    the number of K/V heads for grouped-query attention.
+    the number of K/V heads for grouped-query attention; cu_seqlens_k
+    (optional, with cu_seqlens) key offsets of their own, S then being the
+    longest query length.
     """
     import numpy as np
     lib = load()
@@ -361,6 +367,15 @@ def schedule(B: int, H: int, S: int, D: int, causal: bool, workers: int,
         cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
     rounds, bm = ctypes.c_int(0), ctypes.c_int(0)
     cu_ptr = None if cu is None else cu.ctypes.data
+    if cu_seqlens_k is not None:
+        if cu is None:
+            raise ValueError("cu_seqlens_k needs cu_seqlens")
+        cuk = np.ascontiguousarray(np.asarray(cu_seqlens_k, dtype=np.int32))
+        rc = lib.fa_schedule_general(B, H, H if H_kv is None else H_kv, S, D, int(bool(causal)),
+                                     cu_ptr, cuk.ctypes.data, workers, tiles.ctypes.data,
+                                     max_rounds, ctypes.byref(rounds), ctypes.byref(bm))
+        _check("fa_schedule_general", rc)
+        return tiles[:, :rounds.value].copy(), bm.value
     if H_kv is None:
         rc = lib.fa_schedule(B, H, S, D, int(bool(causal)), cu_ptr, workers, tiles.ctypes.data,
                              max_rounds, ctypes.byref(rounds), ctypes.byref(bm))

@@ -785,13 +785,14 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fw
   using C = Cfg<D>;
   fa::Sched s = fa::make_sched(a.B, a.H, a.Hkv, a.S, C::BM, CAUSAL, VARLEN, a.workers,
                                a.cu_k == a.cu);
-  fa::SchedTables t{nullptr, nullptr, nullptr};
+  fa::SchedTables t{nullptr, nullptr, nullptr, nullptr};
   if constexpr (VARLEN) {
     int *tab = (int *)(lds_raw + lds_bytes<D, VARLEN, CAUSAL>());
     t.len = tab;
     t.sorted = tab + fa::kMaxVarlenSeqs;
     t.off = tab + 2 * fa::kMaxVarlenSeqs;
-    fa::tables_phase1(s, a.cu, t, threadIdx.x, blockDim.x);
+    t.key = t.off + fa::kMaxVarlenLevels + 2;  // after the item count below
+    fa::tables_phase1(s, a.cu, a.cu_k, t, threadIdx.x, blockDim.x);
     __syncthreads();
     fa::tables_phase2(s, t, threadIdx.x, blockDim.x);
     __syncthreads();
@@ -946,7 +947,7 @@ int launch_variant(const Args &a0, int schedule, int cus, hipStream_t stream) {
   if (VARLEN && (a.B > fa::kMaxVarlenSeqs || nmb > fa::kMaxVarlenLevels)) persistent = false;
   if (persistent) {
     a.workers = cus * C::OCC;
-    if (VARLEN) lds += sizeof(int) * (2 * fa::kMaxVarlenSeqs + fa::kMaxVarlenLevels + 2);
+    if (VARLEN) lds += sizeof(int) * (3 * fa::kMaxVarlenSeqs + fa::kMaxVarlenLevels + 2);
     auto kern = fa_fwd_persistent<D, CAUSAL, VARLEN, EMU, COUNT>;
     if (!allow_lds(kern, lds)) return FA_ERR_HIP;
     hipLaunchKernelGGL(kern, dim3(a.workers), dim3(C::THREADS), lds, stream, a);
@@ -1208,19 +1209,28 @@ int fa_schedule(int B, int H, int S, int D, int causal, const int *cu_seqlens, i
 
 int fa_schedule_gqa(int B, int H, int H_kv, int S, int D, int causal, const int *cu_seqlens,
                     int workers, int *tiles, int max_rounds, int *rounds_out, int *bm_out) {
+  return fa_schedule_general(B, H, H_kv, S, D, causal, cu_seqlens, cu_seqlens, workers, tiles,
+                             max_rounds, rounds_out, bm_out);
+}
+
+int fa_schedule_general(int B, int H, int H_kv, int S, int D, int causal, const int *cu_seqlens,
+                        const int *cu_seqlens_k, int workers, int *tiles, int max_rounds,
+                        int *rounds_out, int *bm_out) {
   if (B <= 0 || H <= 0 || S <= 0 || workers <= 0 || !tiles || max_rounds <= 0) return FA_ERR_INVALID_ARG;
   if (H_kv <= 0 || H % H_kv != 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if ((cu_seqlens == nullptr) != (cu_seqlens_k == nullptr)) return FA_ERR_INVALID_ARG;
   if (D != 64 && D != 128 && D != 192 && D != 256) return FA_ERR_UNSUPPORTED;
   const int BM = bm_for(D);
   const bool varlen = cu_seqlens != nullptr;
-  fa::Sched s = fa::make_sched(B, H, H_kv, S, BM, causal, varlen, workers);
+  fa::Sched s = fa::make_sched(B, H, H_kv, S, BM, causal, varlen, workers,
+                               cu_seqlens_k == cu_seqlens);
   if (varlen && (B > fa::kMaxVarlenSeqs || s.nmb_max > fa::kMaxVarlenLevels)) return FA_ERR_UNSUPPORTED;
   static thread_local int len[fa::kMaxVarlenSeqs], sorted[fa::kMaxVarlenSeqs],
-      off[fa::kMaxVarlenLevels + fa::kMaxVarlenSeqs + 1];
-  fa::SchedTables t{len, sorted, off};
+      off[fa::kMaxVarlenLevels + fa::kMaxVarlenSeqs + 1], key[fa::kMaxVarlenSeqs];
+  fa::SchedTables t{len, sorted, off, key};
   if (varlen) {
-    fa::tables_phase1(s, cu_seqlens, t, 0, 1);
+    fa::tables_phase1(s, cu_seqlens, cu_seqlens_k, t, 0, 1);
     fa::tables_phase2(s, t, 0, 1);
     fa::tables_phase3(s, t, 0, 1);
     s.n_items = fa::tables_phase4(s, t);

@@ -300,6 +300,19 @@ int fa_schedule(int B, int H, int S, int D, int causal, const int *cu_seqlens,
 int fa_schedule_gqa(int B, int H, int H_kv, int S, int D, int causal, const int *cu_seqlens,
                     int workers, int *tiles, int max_rounds, int *rounds_out, int *bm_out);
 
+/*
+ * fa_schedule_general -- fa_schedule_gqa for query and key lengths of their
+ * own, as fa_fwd_general takes them: cu_seqlens_q and cu_seqlens_k are both
+ * NULL (dense) or both HOST int32 arrays of B+1 entries; S_q is the longest
+ * query length.  For causal batches whose key lengths differ from their query
+ * lengths, the order ranks the sequences by key length (a query tile's cost
+ * follows its key length under bottom-right alignment).  Tile codes use
+ * n_mblocks_max = ceil(S_q / BM).
+ */
+int fa_schedule_general(int B, int H, int H_kv, int S_q, int D, int causal,
+                        const int *cu_seqlens_q, const int *cu_seqlens_k, int workers, int *tiles,
+                        int max_rounds, int *rounds_out, int *bm_out);
+
 /* Number of persistent workgroups fa_fwd launches on the current device. */
 int fa_num_workers(int D, int *workers_out);
 

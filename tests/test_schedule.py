@@ -173,3 +173,40 @@ def test_gqa_schedule_rejects_bad_kv_heads():
 def test_schedule_rejects_small_round_budget():
     with pytest.raises(fa.FaError):
         fa.schedule(1, 16, 32768, 128, True, 256, max_rounds=2)
+
+
+def test_qk_lengths_order_ranks_by_key_length():
+    """Causal batches with key lengths of their own (bottom-right aligned):
+    a query tile sees nearly all of its sequence's keys, so the order ranks
+    sequences by key length; every tile still runs exactly once and the
+    makespan under the key-length cost stays near the ideal."""
+    from attn_inputs import qk_lengths
+    w = WORKLOADS["mixed_16x_q1to2048_k512to8192_h16d128_causal"]
+    lq, lk = qk_lengths(w)
+    B, H, S = len(lq), w.H, max(lq)
+    tiles, bm = fa.schedule(B, H, S, w.D, True, 256, cu_seqlens=cu_seqlens_of(lq),
+                            cu_seqlens_k=cu_seqlens_of(lk))
+    seen = tiles[tiles >= 0].tolist()
+    assert len(seen) == len(set(seen))
+    assert set(seen) == all_tiles(B, H, S, bm, list(lq))
+    nmb = math.ceil(S / bm)
+
+    def cost(t):
+        b, mb = t // (nmb * H), t % nmb
+        last_key = lk[b] - lq[b] + min((mb + 1) * bm, lq[b])   # bottom-right causal
+        return math.ceil(min(lk[b], max(0, last_key)) / BN) + 2
+
+    per_worker = [sum(cost(t) for t in row if t >= 0) for row in tiles]
+    ideal = max(sum(per_worker) / len(per_worker), max(cost(t) for t in seen))
+    assert max(per_worker) / ideal <= 1.15, max(per_worker) / ideal
+
+
+def test_schedule_general_rejects_one_sided_key_offsets():
+    with pytest.raises(fa.FaError):
+        import ctypes
+        cu = np.array([0, 10], dtype=np.int32)
+        tiles = np.zeros((8, 16), dtype=np.int32)
+        r, b = ctypes.c_int(0), ctypes.c_int(0)
+        fa._check("fa_schedule_general", fa.load().fa_schedule_general(
+            1, 8, 8, 10, 128, 1, cu.ctypes.data, None, 8, tiles.ctypes.data, 16,
+            ctypes.byref(r), ctypes.byref(b)))

@@ -203,6 +203,32 @@ __device__ __forceinline__ void store_rows(__bf16 *row_ptr, const f32x16 *acc, f
 // ---------------------------------------------------------------------------
 // dQ (and Delta): one tile of BM query rows of head h.
 // ---------------------------------------------------------------------------
+// Launch slot -> (head slot hs of n_hs, level r; level 0 is the longest tile
+// for causal masking).  Dense batches: tiles of one head are n_hs slots
+// apart (the same XCD when n_hs is a multiple of 8).  Varlen batches have
+// many more (sequence, head) pairs than CUs, and that order ran every
+// concurrent tile on a pair of its own, each streaming its own operands past
+// the L2.  There, XCD x = slot % 8 owns the head slots x, x+8, ... and its
+// stream runs kBwdChunk consecutive levels of one head slot together, so
+// those tiles share their K/V (or Q/dO) in the XCD's L2; chunks go longest
+// first.  The grid is padded to whole chunks; slots past the last level exit.
+constexpr int kBwdChunk = 8;
+__device__ __forceinline__ void bwd_slot(int id, int n_hs, bool chunked, int *hs, int *r) {
+  if (!chunked) {
+    *hs = id % n_hs;
+    *r = id / n_hs;
+    return;
+  }
+  const int x = id % 8, q = id / 8;
+  const int per = n_hs / 8;  // head slots per XCD
+  const int chunk = q / (per * kBwdChunk);
+  const int rem = q - chunk * per * kBwdChunk;
+  const int k = rem / kBwdChunk, j = rem - k * kBwdChunk;
+  *hs = x + 8 * k;
+  *r = chunk * kBwdChunk + j;
+}
+__host__ __device__ inline bool bwd_chunked(bool varlen, int n_hs) { return varlen && n_hs % 8 == 0; }
+
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(BwdCfg<D>::NW_DQ * kWave, BwdCfg<D>::NW_DQ / 4) void fa_bwd_dq(
     BwdArgs a) {
@@ -212,13 +238,12 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_DQ * kWave, BwdCfg<D>::NW_DQ / 4) voi
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   char LDS_AS *lds = (char LDS_AS *)lds_raw;
 
-  // Tiles of one (b, h) are B*H launch slots apart, so with B*H a multiple
-  // of 8 they share an XCD (and its L2 copy of K and V).  Causal: the last
-  // (longest) m-blocks start first.
+  // Launch order (bwd_slot): causal, the last (longest) m-blocks start first.
   const int nmb = fa::ceil_div(a.S, C::BM);
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int r = blockIdx.x / BH;
+  int bh, r;
+  bwd_slot(blockIdx.x, BH, bwd_chunked(VARLEN, BH), &bh, &r);
+  if (r >= nmb) return;  // grid padding
   const int mb = CAUSAL ? nmb - 1 - r : r;
   const int b = bh / a.H, h = bh % a.H;
   const Span sp = seq_of<VARLEN>(a, b);
@@ -380,12 +405,12 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   char LDS_AS *lds = (char LDS_AS *)lds_raw;
 
-  // Tiles of one (b, hk) are B*Hkv slots apart (same XCD when B*Hkv is a
-  // multiple of 8).  Causal: the first key tiles, which every later query
-  // row reads, are the longest and start first.
+  // Launch order (bwd_slot): causal, the first key tiles, which every later
+  // query row reads, are the longest and start first.
   const int BK = a.B * a.Hkv;
-  const int bhk = blockIdx.x % BK;
-  const int nb = blockIdx.x / BK;
+  int bhk, nb;
+  bwd_slot(blockIdx.x, BK, bwd_chunked(VARLEN, BK), &bhk, &nb);
+  if (nb >= fa::ceil_div(a.S, C::BN)) return;  // grid padding
   const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
   const Span sp = seq_of<VARLEN>(a, b);
   const int L = sp.L;
@@ -642,8 +667,14 @@ int validate_bwd(const void *q, const void *k, const void *v, const void *o, con
 template <int D, bool CAUSAL, bool VARLEN>
 int launch_bwd(const BwdArgs &a, hipStream_t st) {
   using C = BwdCfg<D>;
-  const long long g1 = (long long)a.B * a.H * fa::ceil_div(a.S, C::BM);
-  const long long g2 = (long long)a.B * a.Hkv * fa::ceil_div(a.S, C::BN);
+  // levels per head slot, padded to whole chunks where bwd_slot chunks them
+  auto levels = [](int n, bool chunked) {
+    return chunked ? fa::ceil_div(n, kBwdChunk) * kBwdChunk : n;
+  };
+  const long long g1 = (long long)a.B * a.H *
+                       levels(fa::ceil_div(a.S, C::BM), bwd_chunked(VARLEN, a.B * a.H));
+  const long long g2 = (long long)a.B * a.Hkv *
+                       levels(fa::ceil_div(a.S, C::BN), bwd_chunked(VARLEN, a.B * a.Hkv));
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   auto k1 = fa_bwd_dq<D, CAUSAL, VARLEN>;
   auto k2 = fa_bwd_dkdv<D, CAUSAL, VARLEN>;

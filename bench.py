@@ -118,8 +118,9 @@ def time_workload(fa, torch, w, steps, warmup, tuning=None, num_splits=None, set
         if n_sp == 0:
             import ctypes
             c = ctypes.c_int(1)
-            fa.load().fa_splitkv_auto_splits(w.B, w.H, S, extra.get("max_seqlen_k", S), w.D,
-                                             ctypes.byref(c))
+            fa.load().fa_splitkv_auto_splits_gqa(w.B, w.H, w.kv_heads, S,
+                                                 extra.get("max_seqlen_k", S), w.D,
+                                                 ctypes.byref(c))
             n_sp = c.value
         nbytes = fa.splitkv_workspace_size(w.B, w.H, S, extra.get("max_seqlen_k", S),
                                            w.head_dim_v, n_sp)

@@ -72,6 +72,8 @@ def load(path: str = LIB_PATH):
     lib.fa_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fa_splitkv_auto_splits.argtypes = [I, I, I, I, I, ctypes.POINTER(I)]
     lib.fa_splitkv_auto_splits.restype = I
+    lib.fa_splitkv_auto_splits_gqa.argtypes = [I, I, I, I, I, I, ctypes.POINTER(I)]
+    lib.fa_splitkv_auto_splits_gqa.restype = I
     lib.fa_bwd.argtypes = [P] * 10 + [I, I, I, I, I, F, I, P, P]
     lib.fa_bwd.restype = I
     lib.fa_tuning_default.argtypes = []
@@ -196,8 +198,8 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
         splits = int(num_splits)
         if splits == 0:
             n = ctypes.c_int(1)
-            _check("fa_splitkv_auto_splits",
-                   lib.fa_splitkv_auto_splits(B, H, S, S_k, D, ctypes.byref(n)))
+            _check("fa_splitkv_auto_splits_gqa",
+                   lib.fa_splitkv_auto_splits_gqa(B, H, H_kv, S, S_k, D, ctypes.byref(n)))
             splits = n.value
         need = lib.fa_splitkv_workspace_size(B, H, S, S_k, D_v, splits)
         if workspace is None:

@@ -434,7 +434,13 @@ struct KvLayout {
   }
 };
 
-template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT, bool SPLIT = false>
+// PACK: h is a K/V head and the tile's rows are the (query index i, query
+// head g of the group) pairs of that K/V head, row r = i*G + g, in one tile
+// (the caller guarantees L*G <= BM): the group's K/V are streamed once for
+// all G query heads instead of once per head (decode with grouped-query
+// attention).  Otherwise row r is query index m0 + r of query head h.
+template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT, bool SPLIT = false,
+          bool PACK = false>
 __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, char LDS_AS *lds,
                                          int split = 0) {
   using C = Cfg<D>;
@@ -469,19 +475,23 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   if (m0 >= L) return;  // workgroup-uniform
   const int H = a.H;
   const int Hk = a.Hkv;              // K/V row layout: [.., Hk, D]
-  const int hk = h / (H / Hk);       // the K/V head this query head reads
+  const int G = PACK ? H / Hk : 1;   // query heads per row index (packed)
+  const int R = PACK ? L * G : L;    // rows of the tile's row space
+  const int hk = PACK ? h : h / (H / Hk);  // the K/V head the rows read
   WaveRows wr;
   wr.wrow0 = m0 + wave * 32;
-  wr.active = wr.wrow0 < L;
-  wr.wrow_last = (wr.wrow0 + 31 < L - 1) ? wr.wrow0 + 31 : L - 1;
-  wr.krow0 = wr.wrow0 + koff;
-  wr.krow_last = wr.wrow_last + koff;
+  wr.active = wr.wrow0 < R;
+  wr.wrow_last = (wr.wrow0 + 31 < R - 1) ? wr.wrow0 + 31 : R - 1;
+  wr.krow0 = (PACK ? wr.wrow0 / G : wr.wrow0) + koff;
+  wr.krow_last = (PACK ? wr.wrow_last / G : wr.wrow_last) + koff;
   const int row = wr.wrow0 + (lane & 31);
+  const int qi = PACK ? row / G : row;          // query index of the lane's row
+  const int hq = PACK ? hk * G + row % G : h;   // query head of the lane's row
 
   // KV range shared by the workgroup (0 blocks: no row of the tile has a key)
   int n_end = Lk;
   if (CAUSAL) {
-    const int e = m0 + C::BM + koff;
+    const int e = (PACK ? L : m0 + C::BM) + koff;
     n_end = e < 0 ? 0 : (e < Lk ? e : Lk);
   }
   const int nblocks = fa::ceil_div(n_end, kBN);
@@ -495,8 +505,11 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   // Q fragments: lane l holds row (l%32), d = 16s + 8(l/32) .. +7
   WaveState<D> st;
   {
-    const int qrow = row < L ? row : L - 1;
-    const bf16x8 *qp = (const bf16x8 *)(a.q + ((tok0 + qrow) * H + h) * (long long)D + 8 * (lane >> 5));
+    const int rc = row < R ? row : R - 1;  // rows past the end read the last row (never stored)
+    const int qrow = PACK ? rc / G : rc;
+    const int qhead = PACK ? hk * G + rc % G : h;
+    const bf16x8 *qp =
+        (const bf16x8 *)(a.q + ((tok0 + qrow) * H + qhead) * (long long)D + 8 * (lane >> 5));
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) st.qf[s] = qp[2 * s];
     // Opaque to the compiler: Q stays in registers for the whole tile instead
@@ -559,7 +572,7 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     auto softmax_phase = [&](bool run, int j, int it) {
       auto side = copies(it);
       if (run) {
-        softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, j * kBN, row + koff, Lk,
+        softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, j * kBN, qi + koff, Lk,
                                             wr.need_mask(j, Lk, CAUSAL), j == wr.last_block, a,
                                             side);
       } else {
@@ -638,7 +651,7 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     auto scores = [&](int j, float &m_use) {
       qk_step<D>(st, la, kslot(j), kslot(j));
       if (wr.need_mask(j, Lk, false)) {
-        const int lim = mask_limit<false>(lane, j * kBN, row + koff, Lk);
+        const int lim = mask_limit<false>(lane, j * kBN, qi + koff, Lk);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -710,7 +723,7 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       barrier_nofence();
       if (wr.useful(j, CAUSAL)) {
         qk_step<D>(st, la, kcur, kcur);
-        softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, n0, row + koff, Lk,
+        softmax_step<D, CAUSAL, EMU, COUNT>(st, lane, n0, qi + koff, Lk,
                                             wr.need_mask(j, Lk, CAUSAL), j == wr.last_block, a,
                                             [](int) {});
         pv_step<D>(st, la, vcur);
@@ -725,11 +738,11 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
   if constexpr (SPLIT) {
     // partial O (normalised over this split's keys) and LSE, fp32, into the
     // workspace slice of this split (rows of B*S query slots)
-    if (row < L) {
+    if (row < R) {
       const float inv = l32 > 0.0f ? 1.0f / l32 : 0.0f;
       const int hh = lane >> 5;
       const long long slots = (long long)a.B * a.S * H;
-      float *op = a.ws_o + (split * slots + (tok0 + row) * H + h) * (long long)DV + 4 * hh;
+      float *op = a.ws_o + (split * slots + (tok0 + qi) * H + hq) * (long long)DV + 4 * hh;
       typedef float f32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
       for (int dt = 0; dt < DV / 32; ++dt)
@@ -742,16 +755,16 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       if (hh == 0) {
         const float lse = (st.m_ref + log2f(l32)) * kLn2;
         float *lp = a.ws_lse + split * slots;
-        if constexpr (VARLEN) lp[(long long)h * a.cu[a.B] + tok0 + row] = lse;
-        else lp[((long long)b * H + h) * a.S + row] = lse;
+        if constexpr (VARLEN) lp[(long long)hq * a.cu[a.B] + tok0 + qi] = lse;
+        else lp[((long long)b * H + hq) * a.S + qi] = lse;
       }
     }
     return;
   }
-  if (row < L) {
+  if (row < R) {
     const float inv = l32 > 0.0f ? 1.0f / l32 : 0.0f;  // a row without keys: O = 0, LSE = -inf
     const int hh = lane >> 5;
-    __bf16 *op = a.o + ((tok0 + row) * H + h) * (long long)DV + 4 * hh;
+    __bf16 *op = a.o + ((tok0 + qi) * H + hq) * (long long)DV + 4 * hh;
 #pragma unroll
     for (int dt = 0; dt < DV / 32; ++dt)
 #pragma unroll
@@ -763,8 +776,8 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       }
     if (a.lse != nullptr && hh == 0) {
       const float lse = (st.m_ref + log2f(l32)) * kLn2;
-      if constexpr (VARLEN) a.lse[(long long)h * a.cu[a.B] + tok0 + row] = lse;
-      else a.lse[((long long)b * H + h) * a.S + row] = lse;
+      if constexpr (VARLEN) a.lse[(long long)hq * a.cu[a.B] + tok0 + qi] = lse;
+      else a.lse[((long long)b * H + hq) * a.S + qi] = lse;
     }
   }
 }
@@ -829,21 +842,23 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fw
   run_tile<D, CAUSAL, VARLEN, EMU, COUNT>(a, b, h, mb, lds);
 }
 
-// Split-KV: one workgroup per (tile, key split), natural order.
-template <int D, bool CAUSAL, bool VARLEN>
+// Split-KV: one workgroup per (tile, key split), natural order.  PACK: one
+// tile per (sequence, K/V head) holding the rows of all its query heads.
+template <int D, bool CAUSAL, bool VARLEN, bool PACK>
 __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fwd_split(Args a,
                                                                                         int splits) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   char LDS_AS *lds = (char LDS_AS *)lds_raw;
   using C = Cfg<D>;
-  const int nmb = fa::ceil_div(a.S, C::BM);
+  const int nmb = PACK ? 1 : fa::ceil_div(a.S, C::BM);
+  const int nh = PACK ? a.Hkv : a.H;
   const int id = blockIdx.x;
   const int split = id % splits;
   const int rest = id / splits;
   const int mb = rest % nmb;
-  const int h = (rest / nmb) % a.H;
-  const int b = rest / (nmb * a.H);
-  run_tile<D, CAUSAL, VARLEN, 0, false, true>(a, b, h, mb, lds, split);
+  const int h = (rest / nmb) % nh;
+  const int b = rest / (nmb * nh);
+  run_tile<D, CAUSAL, VARLEN, 0, false, true, PACK>(a, b, h, mb, lds, split);
 }
 
 // Merge the split partials of each (query row, head): with the splits'
@@ -962,14 +977,18 @@ int launch_variant(const Args &a0, int schedule, int cus, hipStream_t stream) {
 }
 
 int bm_for(int D);
+bool split_packs(int H, int Hkv, int S_q, int BM);
 
 template <int D, bool CAUSAL, bool VARLEN>
 int launch_split(const Args &a, int splits, hipStream_t stream) {
   using C = Cfg<D>;
-  const long long grid = (long long)a.B * a.H * fa::ceil_div(a.S, C::BM) * splits;
+  const bool pack = split_packs(a.H, a.Hkv, a.S, C::BM);
+  const long long tiles =
+      pack ? (long long)a.B * a.Hkv : (long long)a.B * a.H * fa::ceil_div(a.S, C::BM);
+  const long long grid = tiles * splits;
   const long long rows = (long long)a.B * a.S * a.H;  // combine: 4 rows per workgroup
   if (grid > 0x7fffffffLL || (rows + 3) / 4 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
-  auto kern = fa_fwd_split<D, CAUSAL, VARLEN>;
+  auto kern = pack ? fa_fwd_split<D, CAUSAL, VARLEN, true> : fa_fwd_split<D, CAUSAL, VARLEN, false>;
   const size_t lds = lds_bytes<D, VARLEN, CAUSAL>();
   if (!allow_lds(kern, lds)) return FA_ERR_HIP;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), lds, stream, a, splits);
@@ -991,8 +1010,16 @@ int dispatch_split(const Args &a, bool causal, bool varlen, int splits, hipStrea
 // again to the partial writes and the merge), at least two 64-key blocks per
 // split, at most kMaxSplits.  Batches that already have a tile per CU get 1.
 constexpr int kMaxSplits = 64;
-int auto_splits(int B, int H, int S_q, int S_k, int D, int cus) {
-  const long long tiles = (long long)B * H * fa::ceil_div(S_q, bm_for(D));
+// Split-KV packs the query heads of a K/V group into one tile when all their
+// rows (S_q per head) fit one tile.
+bool split_packs(int H, int Hkv, int S_q, int BM) {
+  return H > Hkv && (long long)S_q * (H / Hkv) <= BM;
+}
+
+int auto_splits(int B, int H, int Hkv, int S_q, int S_k, int D, int cus) {
+  const int BM = bm_for(D);
+  const long long tiles = split_packs(H, Hkv, S_q, BM) ? (long long)B * Hkv
+                                                       : (long long)B * H * fa::ceil_div(S_q, BM);
   const int kblocks = fa::ceil_div(S_k, kBN);
   long long want = ((long long)cus + tiles - 1) / tiles;
   if (want > kblocks / 2) want = kblocks / 2;
@@ -1102,13 +1129,18 @@ size_t fa_splitkv_workspace_size(int B, int H, int S_q, int S_k, int D_v, int nu
 }
 
 int fa_splitkv_auto_splits(int B, int H, int S_q, int S_k, int D, int *splits_out) {
+  return fa_splitkv_auto_splits_gqa(B, H, H, S_q, S_k, D, splits_out);
+}
+
+int fa_splitkv_auto_splits_gqa(int B, int H, int H_kv, int S_q, int S_k, int D, int *splits_out) {
   if (!splits_out || B <= 0 || H <= 0 || S_q <= 0 || S_k <= 0) return FA_ERR_INVALID_ARG;
+  if (H_kv <= 0 || H % H_kv != 0) return FA_ERR_INVALID_ARG;
   if (D != 64 && D != 128 && D != 192 && D != 256) return FA_ERR_UNSUPPORTED;
   DeviceInfo *dev = nullptr;
   const int rc = current_device(&dev);
   if (rc != FA_OK) return rc;
   int splits, kbps;
-  split_plan(S_k, auto_splits(B, H, S_q, S_k, D, dev->cus), &splits, &kbps);
+  split_plan(S_k, auto_splits(B, H, H_kv, S_q, S_k, D, dev->cus), &splits, &kbps);
   *splits_out = splits;
   return FA_OK;
 }

@@ -220,6 +220,13 @@ size_t fa_splitkv_workspace_size(int B, int H, int S_q, int S_k, int D_v, int nu
  * Writes it to *splits_out; returns an fa_status. */
 int fa_splitkv_auto_splits(int B, int H, int S_q, int S_k, int D, int *splits_out);
 
+/* fa_splitkv_auto_splits for H_kv K/V heads (H_kv divides H).  When the rows
+ * of a K/V group's query heads fit one tile (S_q * H/H_kv <= the row-tile
+ * height), fa_fwd_splitkv packs them into one tile per (sequence, K/V head),
+ * so the group's K/V are streamed once per split, and the count is sized for
+ * those B*H_kv tiles. */
+int fa_splitkv_auto_splits_gqa(int B, int H, int H_kv, int S_q, int S_k, int D, int *splits_out);
+
 /*
  * fa_bwd -- exact attention backward (FlashAttention-4 paper, section 3.2,
  * "attention backward pass": S is recomputed block by block from Q and K,

@@ -68,6 +68,11 @@ SPLIT_DENSE = [
     (1, 700, 300, 2, 2, 128, 128, 2),     # more queries than keys: rows without keys
     (1, 2, 1500, 2, 2, 192, 128, 5),
     (1, 1, 640, 2, 2, 256, 256, 64),      # more splits requested than key blocks
+    # query heads of a K/V group packed into one tile (S_q * H/H_kv <= 256):
+    (1, 60, 900, 8, 2, 128, 128, 3),      # 240 packed rows over 8 waves, per-row causal limits
+    (2, 7, 530, 8, 1, 64, 64, 5),         # MQA, D = 64
+    (1, 3, 800, 4, 2, 192, 128, 4),       # (192, 128) head dimensions
+    (1, 1, 700, 4, 2, 256, 256, 3),       # D = 256
 ]
 
 

@@ -883,18 +883,26 @@ __global__ __launch_bounds__(256) void fa_split_combine(Args a, int splits) {
     li = (b * H + h) * a.S + i;
   }
   const long long slots = (long long)a.B * a.S * H;
-  float m = -INFINITY;
-  for (int s = 0; s < splits; ++s) m = fmaxf(m, a.ws_lse[s * slots + li]);
+  // Lane s holds the LSE of split s (splits <= 64): the row's maximum and
+  // the split weights are wave reductions, not a serial walk over splits.
+  const float ls = lane < splits ? a.ws_lse[lane * slots + li] : -INFINITY;
+  float m = ls;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   constexpr int PER = (DV + kWave - 1) / kWave;
   float acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
   float lse = -INFINITY;
   if (m != -INFINITY) {
-    float wsum = 0.0f;
+    const float wl = (ls == -INFINITY) ? 0.0f : exp2_hw((ls - m) * kLog2e);
+    float wsum = wl;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+    // the loads of several splits in flight at once
+#pragma unroll 16
     for (int s = 0; s < splits; ++s) {
-      const float w = exp2_hw((a.ws_lse[s * slots + li] - m) * kLog2e);
-      wsum += w;
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
       const float *op = a.ws_o + (s * slots + r) * (long long)DV;
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
@@ -1009,7 +1017,8 @@ int dispatch_split(const Args &a, bool causal, bool varlen, int splits, hipStrea
 // keys, 32 query tiles: 8 splits run 7x faster than none, 16 or more lose
 // again to the partial writes and the merge), at least two 64-key blocks per
 // split, at most kMaxSplits.  Batches that already have a tile per CU get 1.
-constexpr int kMaxSplits = 64;
+constexpr int kMaxSplits = 64;  // fa_split_combine holds one split per lane
+static_assert(kMaxSplits <= kWave, "one split per lane in the merge");
 // Split-KV packs the query heads of a K/V group into one tile when all their
 // rows (S_q per head) fit one tile.
 bool split_packs(int H, int Hkv, int S_q, int BM) {

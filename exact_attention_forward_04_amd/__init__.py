@@ -76,6 +76,8 @@ def load(path: str = LIB_PATH):
     lib.fa_splitkv_auto_splits_gqa.restype = I
     lib.fa_bwd.argtypes = [P] * 10 + [I, I, I, I, I, F, I, P, P]
     lib.fa_bwd.restype = I
+    lib.fa_bwd_general.argtypes = [P] * 10 + [I, I, I, I, I, I, F, I, P, P, P]
+    lib.fa_bwd_general.restype = I
     lib.fa_tuning_default.argtypes = []
     lib.fa_tuning_default.restype = Tuning
     lib.fa_exp2_emu.argtypes = [P, P, LL, P]
@@ -235,11 +237,13 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
 def attention_backward(q, k, v, o, lse, dout, causal: bool = False,
                        scale: Optional[float] = None, cu_seqlens=None,
                        max_seqlen: Optional[int] = None, dq=None, dk=None, dv=None, delta=None,
-                       stream=None):
-    """Exact attention backward on the GPU (the fa_bwd entry point).
+                       stream=None, cu_seqlens_k=None, max_seqlen_k: Optional[int] = None):
+    """Exact attention backward on the GPU (the fa_bwd_general entry point).
 
-    q, k, v, causal, scale, cu_seqlens and max_seqlen as given to attention()
-    (query and key lengths equal, D_v = D); o and lse its outputs; dout the
+    q, k, v, causal, scale, cu_seqlens, max_seqlen, cu_seqlens_k and
+    max_seqlen_k as given to attention() (D_v = D; query and key lengths may
+    differ, causal masks aligned to the bottom-right corner); o and lse its
+    outputs; dout the
     gradient with respect to o (o's shape, contiguous bf16).  Returns
     (dq, dk, dv) shaped like q, k, v (bf16).  dq/dk/dv/delta may be passed
     in to reuse buffers (delta: fp32 scratch of lse's shape).
@@ -255,26 +259,37 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False,
     nd = 4 if dense else 3
     if any(t.dim() != nd for t in (q, k, v, o, dout)):
         raise ValueError("dense inputs are [B, S, H, D]" if dense else "varlen inputs are [T, H, D]")
-    if tuple(k.shape) != tuple(v.shape) or k.shape[:-2] != q.shape[:-2] or \
+    if tuple(k.shape) != tuple(v.shape) or k.shape[:-3] != q.shape[:-3] or \
             k.shape[-1] != q.shape[-1] or tuple(o.shape) != tuple(q.shape) or \
             tuple(dout.shape) != tuple(q.shape):
-        raise ValueError("q, o, dout must share a shape; k, v another with the same tokens and D")
+        raise ValueError("q, o, dout must share a shape; k, v another with the same batch and D")
     H, D, H_kv = q.shape[-2], q.shape[-1], k.shape[-2]
     if H_kv < 1 or H % H_kv != 0:
         raise ValueError("the K/V head count must divide the query head count")
     if dense:
-        B, S = q.shape[0], q.shape[1]
+        if cu_seqlens_k is not None:
+            raise ValueError("cu_seqlens_k needs cu_seqlens")
+        B, S, S_k = q.shape[0], q.shape[1], k.shape[1]
         lse_shape = (B, H, S)
-        cu_ptr = None
+        cu_ptr = cu_k_ptr = None
     else:
-        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or \
-                not cu_seqlens.is_contiguous():
-            raise ValueError("cu_seqlens must be a contiguous int32 CUDA tensor")
+        for name, c in (("cu_seqlens", cu_seqlens), ("cu_seqlens_k", cu_seqlens_k)):
+            if c is not None and (c.dtype != torch.int32 or not c.is_cuda or not c.is_contiguous()):
+                raise ValueError("%s must be a contiguous int32 CUDA tensor" % name)
         if max_seqlen is None:
             raise ValueError("varlen needs max_seqlen")
-        B, S = cu_seqlens.numel() - 1, int(max_seqlen)
+        if cu_seqlens_k is None:
+            if k.shape[0] != q.shape[0]:
+                raise ValueError("different query and key token counts need cu_seqlens_k")
+            cu_seqlens_k, max_seqlen_k = cu_seqlens, max_seqlen
+        elif max_seqlen_k is None:
+            raise ValueError("cu_seqlens_k needs max_seqlen_k")
+        B = cu_seqlens.numel() - 1
+        if cu_seqlens_k.numel() != B + 1:
+            raise ValueError("cu_seqlens and cu_seqlens_k must have the same length")
+        S, S_k = int(max_seqlen), int(max_seqlen_k)
         lse_shape = (H, q.shape[0])
-        cu_ptr = cu_seqlens.data_ptr()
+        cu_ptr, cu_k_ptr = cu_seqlens.data_ptr(), cu_seqlens_k.data_ptr()
     if tuple(lse.shape) != lse_shape:
         raise ValueError("lse must have shape %s" % (lse_shape,))
     if scale is None:
@@ -289,11 +304,11 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False,
             raise ValueError("%s must be bf16 of shape %s" % (name, tuple(ref.shape)))
     if tuple(delta.shape) != lse_shape or delta.dtype != torch.float32:
         raise ValueError("delta must be fp32 of shape %s" % (lse_shape,))
-    rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                    delta.data_ptr(), B, H, H_kv, S, D, float(scale), int(bool(causal)), cu_ptr,
-                    _stream_ptr(stream))
-    _check("fa_bwd", rc)
+    rc = lib.fa_bwd_general(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(), delta.data_ptr(), B, H, H_kv, S, S_k, D, float(scale),
+                            int(bool(causal)), cu_ptr, cu_k_ptr, _stream_ptr(stream))
+    _check("fa_bwd_general", rc)
     return dq, dk, dv
 
 

@@ -80,8 +80,9 @@ struct BwdArgs {
   const float *lse;
   __bf16 *dq, *dk, *dv;
   float *delta;
-  const int *cu;  // varlen offsets (queries and keys alike) or nullptr
-  int B, H, Hkv, S;
+  const int *cu;    // varlen query offsets or nullptr
+  const int *cu_k;  // varlen key offsets (nullptr with cu)
+  int B, H, Hkv, S, Sk;  // S: longest query length, Sk: longest key length
   float c;      // scale * log2(e)
   float scale;
 };
@@ -98,6 +99,18 @@ __device__ __forceinline__ Span seq_of(const BwdArgs &a, int b) {
     return {(long long)a.cu[b], Lr < 0 ? 0 : (Lr > a.S ? a.S : Lr)};
   } else {
     return {(long long)b * a.S, a.S};
+  }
+}
+
+// Key span of sequence b (its own offsets and length when they differ from
+// the queries').
+template <bool VARLEN>
+__device__ __forceinline__ Span kseq_of(const BwdArgs &a, int b) {
+  if constexpr (VARLEN) {
+    const int Lr = a.cu_k[b + 1] - a.cu_k[b];
+    return {(long long)a.cu_k[b], Lr < 0 ? 0 : (Lr > a.Sk ? a.Sk : Lr)};
+  } else {
+    return {(long long)b * a.Sk, a.Sk};
   }
 }
 
@@ -250,6 +263,11 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_DQ * kWave, BwdCfg<D>::NW_DQ / 4) voi
   const int L = sp.L;
   const int m0 = mb * C::BM;
   if (m0 >= L) return;  // workgroup-uniform
+  // Keys of the sequence; causal masks align to the bottom-right corner:
+  // row i may use key j when j <= i + koff.
+  const Span spk = kseq_of<VARLEN>(a, b);
+  const int Lk = spk.L;
+  const int koff = Lk - L;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
@@ -290,8 +308,9 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_DQ * kWave, BwdCfg<D>::NW_DQ / 4) voi
     asm volatile("" : "+v"(lse2), "+v"(delta));
   }
 
-  int n_end = L;
-  if (CAUSAL) n_end = (m0 + C::BM < L) ? m0 + C::BM : L;
+  int n_end = Lk;
+  if (CAUSAL) n_end = (m0 + C::BM + koff < Lk) ? m0 + C::BM + koff : Lk;
+  if (n_end < 0) n_end = 0;  // no row of the tile may use a key
   const int nblocks = fa::ceil_div(n_end, kBN);
 
   BlockLoader<D, NW> ld;
@@ -302,8 +321,8 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_DQ * kWave, BwdCfg<D>::NW_DQ / 4) voi
   auto kbuf = [&](int j) { return lds + (j % C::SLOTS) * 2 * C::BLK; };
   auto vbuf = [&](int j) { return lds + (j % C::SLOTS) * 2 * C::BLK + C::BLK; };
   auto issue = [&](int j) {
-    ld.issue(a.k, sp.tok0, a.Hkv, hk, j * kBN, L, kbuf(j));
-    ld.issue(a.v, sp.tok0, a.Hkv, hk, j * kBN, L, vbuf(j));
+    ld.issue(a.k, spk.tok0, a.Hkv, hk, j * kBN, Lk, kbuf(j));
+    ld.issue(a.v, spk.tok0, a.Hkv, hk, j * kBN, Lk, vbuf(j));
   };
 
   f32x16 acc[D / 32];
@@ -328,7 +347,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_DQ * kWave, BwdCfg<D>::NW_DQ / 4) voi
     }
     barrier_nofence();
     const int n0 = j * kBN;
-    if (active && (!CAUSAL || n0 <= wrow_last)) {
+    if (active && (!CAUSAL || n0 <= wrow_last + koff)) {
       // ---- S^T = K Q^T and dP^T = V dO^T (keys on the M side)
       const unsigned ka = la.ky + lds_u32(kbuf(j));
       const unsigned va = la.ky + lds_u32(vbuf(j));
@@ -358,9 +377,9 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_DQ * kWave, BwdCfg<D>::NW_DQ / 4) voi
       }
       // ---- P and dS.  Entry e of sub-block i is key n0 + 32i + 8(e>>2) +
       // 4h + (e&3) of the lane's row; it is kept iff its in-block offset is
-      // below lim (key < L, and key <= row when causal).
-      const bool need_mask = (n0 + kBN > L) || (CAUSAL && n0 + kBN - 1 > wrow0);
-      const int lim = (CAUSAL ? (row + 1 < L ? row + 1 : L) : L) - n0 - 4 * hh;
+      // below lim (key < Lk, and key <= row + koff when causal).
+      const bool need_mask = (n0 + kBN > Lk) || (CAUSAL && n0 + kBN - 1 > wrow0 + koff);
+      const int lim = (CAUSAL ? (row + koff + 1 < Lk ? row + koff + 1 : Lk) : Lk) - n0 - 4 * hh;
       bf16x8 ds8[4];
       // (two instances: blocks off the diagonal and inside the sequence,
       // the common case, skip the per-entry select)
@@ -410,26 +429,31 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
   const int BK = a.B * a.Hkv;
   int bhk, nb;
   bwd_slot(blockIdx.x, BK, bwd_chunked(VARLEN, BK), &bhk, &nb);
-  if (nb >= fa::ceil_div(a.S, C::BN)) return;  // grid padding
+  if (nb >= fa::ceil_div(a.Sk, C::BN)) return;  // grid padding
   const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const Span spk = kseq_of<VARLEN>(a, b);  // keys of the sequence
+  const int Lk = spk.L;
+  const int n0t = nb * C::BN;
+  if (n0t >= Lk) return;  // workgroup-uniform
+  // Query rows of the sequence; causal: row i may use key j when
+  // j <= i + koff (bottom-right alignment), i.e. i >= j - koff.
   const Span sp = seq_of<VARLEN>(a, b);
   const int L = sp.L;
-  const int n0t = nb * C::BN;
-  if (n0t >= L) return;  // workgroup-uniform
+  const int koff = Lk - L;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int hh = lane >> 5;
   const int G = a.H / a.Hkv;
   const int key0 = n0t + 32 * wave;  // first key of this wave
-  const bool active = key0 < L;
+  const bool active = key0 < Lk;
   const int key = key0 + (lane & 31);
-  const int keyc = key < L ? key : L - 1;  // keys past L read key L-1 (never stored)
+  const int keyc = key < Lk ? key : Lk - 1;  // keys past Lk read key Lk-1 (never stored)
 
   // K and V rows as B operands (lane: key l%32, d = 16s + 8(l/32) + 0..7).
   bf16x8 kf[NS], vf[NS];
   {
-    const long long base = ((sp.tok0 + keyc) * a.Hkv + hk) * (long long)D + 8 * hh;
+    const long long base = ((spk.tok0 + keyc) * a.Hkv + hk) * (long long)D + 8 * hh;
     const bf16x8 *kp = (const bf16x8 *)(a.k + base);
     const bf16x8 *vp = (const bf16x8 *)(a.v + base);
 #pragma unroll
@@ -447,10 +471,11 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
   }
 
   // Query blocks: for each query head of the group, the 64-row blocks from
-  // the one holding the tile's first key (causal) to the end.
+  // the one holding the first row that may use the tile's first key (causal)
+  // to the end.
   const int nqb = fa::ceil_div(L, kBN);
-  const int qb0 = CAUSAL ? n0t / kBN : 0;
-  const int per = nqb - qb0;
+  const int qb0 = CAUSAL ? (n0t - koff > 0 ? n0t - koff : 0) / kBN : 0;
+  const int per = nqb > qb0 ? nqb - qb0 : 0;
   const int nblocks = G * per;
 
   BlockLoader<D, NW> ld;
@@ -511,7 +536,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
     wait_block(t + 2 < nblocks ? 2 : (t + 1 < nblocks ? 1 : 0));
     barrier_nofence();
     const int m0 = (qb0 + t % per) * kBN;
-    if (active && (!CAUSAL || m0 + kBN - 1 >= key0)) {
+    if (active && (!CAUSAL || m0 + kBN - 1 >= key0 - koff)) {
       const unsigned qa = la.ky + lds_u32(qbuf(t));
       const unsigned ga = la.ky + lds_u32(gbuf(t));
       const unsigned gt0 = la.vw0 + lds_u32(gbuf(t)), gt1 = la.vw1 + lds_u32(gbuf(t));
@@ -522,9 +547,9 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
       // get bounds that keep every entry: one select per entry, no branch
       // (a branch would duplicate the body, and the two copies would hold
       // the dK/dV accumulators in different registers).
-      const bool need_mask = (m0 + kBN > L) || (CAUSAL && m0 < key0 + 31);
+      const bool need_mask = (m0 + kBN > L) || (CAUSAL && m0 < key0 - koff + 31);
       const int hi = need_mask ? L - m0 - 4 * hh : INT_MAX;
-      const int lo = (need_mask && CAUSAL) ? key - m0 - 4 * hh : INT_MIN;
+      const int lo = (need_mask && CAUSAL) ? key - koff - m0 - 4 * hh : INT_MIN;
       typedef float f32x4 __attribute__((ext_vector_type(4)));
       f32x16 s[2], dp[2];
       bf16x8 p8[4], ds8[4];
@@ -544,7 +569,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
       static_assert(NST == 2 * NT, "phases C and D have 2*D/32 steps");
       // Entry e of S_i/dP_i is query row m0 + 32i + 8(e>>2) + 4h + (e&3)
       // against the lane's key; it is kept iff its in-block offset off
-      // satisfies lo <= off < hi (row < L, and row >= key when causal).
+      // satisfies lo <= off < hi (row < L, and row >= key - koff when causal).
       f32x4 l4[2][4], d4[2][4];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -635,8 +660,8 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
   // the last products into dK/dV have landed
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) result_wait_a<ASM>(dk[dt], dv[dt]);
-  if (active && key < L) {
-    const long long rowoff = ((sp.tok0 + key) * a.Hkv + hk) * (long long)D;
+  if (active && key < Lk) {
+    const long long rowoff = ((spk.tok0 + key) * a.Hkv + hk) * (long long)D;
     store_rows<D>(a.dk + rowoff, dk, a.scale, hh);
     store_rows<D>(a.dv + rowoff, dv, 1.0f, hh);
   }
@@ -647,19 +672,22 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
 // ---------------------------------------------------------------------------
 int validate_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
                  const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
-                 int Hkv, int S, int D, float scale, int causal) {
+                 int Hkv, int S, int Sk, int D, float scale, int causal, const int *cu_q,
+                 const int *cu_k) {
   const void *bufs[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void *p : bufs)
     if (!p || !aligned16(p)) return FA_ERR_INVALID_ARG;
   if (!lse || !delta) return FA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(lse) & 3) || (reinterpret_cast<uintptr_t>(delta) & 3))
     return FA_ERR_INVALID_ARG;
-  if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || S <= 0 || Sk <= 0 || D <= 0) return FA_ERR_INVALID_ARG;
+  if ((cu_q == nullptr) != (cu_k == nullptr)) return FA_ERR_INVALID_ARG;
   if (Hkv <= 0 || H % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  if ((long long)B * S > (1LL << 31) - 1 || (long long)S * H > (1LL << 31) - 1)
+  const long long Smax = S > Sk ? S : Sk;
+  if ((long long)B * Smax > (1LL << 31) - 1 || Smax * H > (1LL << 31) - 1)
     return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
@@ -674,7 +702,7 @@ int launch_bwd(const BwdArgs &a, hipStream_t st) {
   const long long g1 = (long long)a.B * a.H *
                        levels(fa::ceil_div(a.S, C::BM), bwd_chunked(VARLEN, a.B * a.H));
   const long long g2 = (long long)a.B * a.Hkv *
-                       levels(fa::ceil_div(a.S, C::BN), bwd_chunked(VARLEN, a.B * a.Hkv));
+                       levels(fa::ceil_div(a.Sk, C::BN), bwd_chunked(VARLEN, a.B * a.Hkv));
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   auto k1 = fa_bwd_dq<D, CAUSAL, VARLEN>;
   auto k2 = fa_bwd_dkdv<D, CAUSAL, VARLEN>;
@@ -696,10 +724,12 @@ int dispatch_bwd(const BwdArgs &a, bool causal, bool varlen, hipStream_t st) {
 
 extern "C" {
 
-int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
-           const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H, int H_kv,
-           int S, int D, float scale, int causal, const int *cu_seqlens, void *stream) {
-  int rc = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, S, D, scale, causal);
+int fa_bwd_general(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                   const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
+                   int H_kv, int S_q, int S_k, int D, float scale, int causal,
+                   const int *cu_seqlens_q, const int *cu_seqlens_k, void *stream) {
+  int rc = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, S_q, S_k, D, scale,
+                        causal, cu_seqlens_q, cu_seqlens_k);
   if (rc != FA_OK) return rc;
   DeviceInfo *dev = nullptr;
   rc = current_device(&dev);
@@ -715,17 +745,26 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
   a.dk = (__bf16 *)dk;
   a.dv = (__bf16 *)dv;
   a.delta = delta;
-  a.cu = cu_seqlens;
+  a.cu = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
   a.B = B;
   a.H = H;
   a.Hkv = H_kv;
-  a.S = S;
+  a.S = S_q;
+  a.Sk = S_k;
   a.c = scale * kLog2e;
   a.scale = scale;
   hipStream_t st = (hipStream_t)stream;
-  const bool varlen = cu_seqlens != nullptr;
+  const bool varlen = cu_seqlens_q != nullptr;
   if (D == 64) return dispatch_bwd<64>(a, causal, varlen, st);
   return dispatch_bwd<128>(a, causal, varlen, st);
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H, int H_kv,
+           int S, int D, float scale, int causal, const int *cu_seqlens, void *stream) {
+  return fa_bwd_general(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, S, S, D, scale,
+                        causal, cu_seqlens, cu_seqlens, stream);
 }
 
 }  // extern "C"

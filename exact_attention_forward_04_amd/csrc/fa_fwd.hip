@@ -1320,6 +1320,6 @@ const char *fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 105; }
+int fa_version(void) { return 106; }
 
 }  // extern "C"

@@ -267,6 +267,30 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            void *stream);
 
 /*
+ * fa_bwd_general -- fa_bwd for query and key lengths that may differ, the
+ * backward of fa_fwd_general (D_v = D).  The same gradients, over the keys
+ * each row may use under fa_fwd_general's rules: with causal = 1 the mask is
+ * aligned to the bottom-right corner, row i of a sequence with lengths L_q,
+ * L_k using key j when j <= i + L_k - L_q.
+ *
+ *   dense  (both offsets NULL): q, o, dout, dq [B, S_q, H, D];
+ *          k, v, dk, dv [B, S_k, H_kv, D]; lse, delta fp32 [B, H, S_q]
+ *   varlen (both non-NULL):     q, o, dout, dq [T_q, H, D];
+ *          k, v, dk, dv [T_k, H_kv, D]; lse, delta fp32 [H, T_q]; device
+ *          int32 offsets cu_seqlens_q, cu_seqlens_k of B+1 entries as in
+ *          fa_fwd_general, S_q and S_k the longest lengths.
+ * A row that may use no key (the forward gave it O = 0 and LSE = -inf) gets
+ * dq = 0; a key that no row may use gets dk = dv = 0.  One offset array NULL
+ * and the other not, or S_k <= 0, is FA_ERR_INVALID_ARG; otherwise the
+ * errors, alignment, ownership and determinism of fa_bwd apply.  fa_bwd is
+ * the S_q = S_k, cu_seqlens_q = cu_seqlens_k case.
+ */
+int fa_bwd_general(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                   const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
+                   int H_kv, int S_q, int S_k, int D, float scale, int causal,
+                   const int *cu_seqlens_q, const int *cu_seqlens_k, void *stream);
+
+/*
  * fa_exp2_emu -- test hook: y[i] = the device's polynomial 2^x[i] for n
  * floats (device pointers, 4-byte aligned).  The function is the one the
  * attention kernel uses for its emulated exponentials: Cody-Waite
@@ -327,7 +351,7 @@ int fa_num_workers(int D, int *workers_out);
 const char *fa_status_string(int status);
 
 /* Library ABI version: 100 * major + minor (101: fa_fwd_gqa; 102: fa_fwd_hd;
- * 103: fa_fwd_general; 104: fa_bwd; 105: fa_fwd_splitkv). */
+ * 103: fa_fwd_general; 104: fa_bwd; 105: fa_fwd_splitkv; 106: fa_bwd_general). */
 int fa_version(void);
 
 #ifdef __cplusplus

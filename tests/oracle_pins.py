@@ -318,6 +318,15 @@ def _bwd_cases(rng):
     q, g = rng.standard_normal((1, 3, 1, 3)), rng.standard_normal((1, 3, 1, 3))
     k, v = rng.standard_normal((1, 5, 1, 3)), rng.standard_normal((1, 5, 1, 3))
     cases.append(("qk_lengths", q, k, v, g, 0.7, True, None, None))
+    # varlen with key offsets of their own (every row keeps at least one key)
+    cu_q, cu_k = [0, 2, 5, 9], [0, 4, 8, 13]
+    q, g = rng.standard_normal((9, 2, 3)), rng.standard_normal((9, 2, 3))
+    k, v = rng.standard_normal((13, 1, 3)), rng.standard_normal((13, 1, 3))
+    cases.append(("qk_lengths_varlen", q, k, v, g, 0.55, True, cu_q, cu_k))
+    # more queries than keys, causal: the first two rows may use no key
+    q, g = rng.standard_normal((1, 5, 2, 3)), rng.standard_normal((1, 5, 2, 3))
+    k, v = rng.standard_normal((1, 3, 2, 3)), rng.standard_normal((1, 3, 2, 3))
+    cases.append(("nokey_rows", q, k, v, g, 0.65, True, None, None))
     return cases
 
 
@@ -348,14 +357,17 @@ def check_bwd_torch_autograd(o):
     import torch
     rng = np.random.default_rng(32)
     for name, q, k, v, g, scale, causal, cu, cu_k in _bwd_cases(rng):
+        if name.startswith("nokey"):
+            continue  # torch's softmax of an all-masked row is NaN; pinned below
         got = o.attention_backward(q, k, v, g, scale, causal, cu, cu_k)
         tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
         tg = torch.tensor(g, dtype=torch.float64)
         if cu is None:
             segs = [(tq, tk, tv, tg)]
         else:
-            segs = [(tq[None, a:b], tk[None, a:b], tv[None, a:b], tg[None, a:b])
-                    for a, b in zip(cu[:-1], cu[1:])]
+            ck = cu if cu_k is None else cu_k
+            segs = [(tq[None, a:b], tk[None, c:d], tv[None, c:d], tg[None, a:b])
+                    for a, b, c, d in zip(cu[:-1], cu[1:], ck[:-1], ck[1:])]
         total = 0
         for sq, sk, sv, sg in segs:
             G = sq.shape[2] // sk.shape[2]
@@ -373,6 +385,21 @@ def check_bwd_torch_autograd(o):
         total.backward()
         for got_x, ref_x, nm in zip(got, (tq.grad, tk.grad, tv.grad), ("dq", "dk", "dv")):
             assert np.max(np.abs(got_x - ref_x.numpy())) <= 1e-12, (name, nm)
+
+
+def check_bwd_rows_without_keys(o):
+    """Rows that may use no key (causal, more queries than keys) get a zero
+    query gradient and add nothing to dK and dV: the backward of the same
+    batch without those rows gives the same key gradients."""
+    rng = np.random.default_rng(33)
+    q, g = rng.standard_normal((1, 6, 2, 4)), rng.standard_normal((1, 6, 2, 4))
+    k, v = rng.standard_normal((1, 4, 2, 4)), rng.standard_normal((1, 4, 2, 4))
+    dq, dk, dv = o.attention_backward(q, k, v, g, 0.5, True)
+    assert np.all(dq[0, :2] == 0.0)
+    assert np.any(dq[0, 2:] != 0.0)
+    dq2, dk2, dv2 = o.attention_backward(q[:, 2:], k, v, g[:, 2:], 0.5, True)
+    assert np.max(np.abs(dq[0, 2:] - dq2[0])) <= 1e-12
+    assert np.max(np.abs(dk - dk2)) <= 1e-12 and np.max(np.abs(dv - dv2)) <= 1e-12
 
 
 def check_bwd_single_key(o):
@@ -472,6 +499,7 @@ ALL_CHECKS = [
     check_rows_without_keys,
     check_bwd_finite_differences,
     check_bwd_torch_autograd,
+    check_bwd_rows_without_keys,
     check_bwd_single_key,
     check_bwd_uniform_probabilities,
     check_bwd_rows_match_full,

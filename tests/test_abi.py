@@ -238,3 +238,46 @@ def test_splitkv_valid_call_without_gpu_reports_no_device():
     assert splitkv_call() == fa.FA_ERR_NO_DEVICE
     n = ctypes.c_int(0)
     assert fa.load().fa_splitkv_auto_splits(1, 8, 1, 4096, 128, ctypes.byref(n)) == fa.FA_ERR_NO_DEVICE
+
+
+def bwd_general_call(**kw):
+    """fa_bwd_general with valid arguments except those overridden."""
+    a = dict(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, dk=A, dv=A, delta=A, B=1, H=8, H_kv=2,
+             S_q=5, S_k=300, D=128, scale=0.1, causal=1, cu=None, cu_k=None)
+    a.update(kw)
+    return fa.load().fa_bwd_general(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"],
+                                    a["dq"], a["dk"], a["dv"], a["delta"], a["B"], a["H"],
+                                    a["H_kv"], a["S_q"], a["S_k"], a["D"], a["scale"],
+                                    a["causal"], a["cu"], a["cu_k"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(S_k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(S_q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(cu=A), fa.FA_ERR_INVALID_ARG),            # one offset array without the other
+    (dict(cu_k=A), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=None), fa.FA_ERR_INVALID_ARG),
+    (dict(H_kv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(D=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(S_k=1 << 30), fa.FA_ERR_UNSUPPORTED),     # the longer length sets the index bound
+])
+def test_backward_general_validation_rejects(kw, expect):
+    assert bwd_general_call(**kw) == expect
+
+
+def test_backward_general_valid_call_without_gpu_reports_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert bwd_general_call() == fa.FA_ERR_NO_DEVICE
+    assert bwd_general_call(cu=A, cu_k=A, causal=0) == fa.FA_ERR_NO_DEVICE
+
+
+def test_backward_binding_checks_key_offsets():
+    import torch
+    q = torch.zeros(8, 1, 64, dtype=torch.bfloat16)
+    k = torch.zeros(5, 1, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 8)
+    with pytest.raises(ValueError):
+        fa.attention_backward(q, k, k, q, lse, q, cu_seqlens=torch.zeros(2, dtype=torch.int32),
+                              max_seqlen=8)

@@ -166,3 +166,99 @@ def test_backward_8k_causal_sampled():
         st = compare_grad(gg, rr, mm)
         note("bwd-8k", name, st)
         assert_grad_close(st, ("bwd-8k", name))
+
+
+# ---- query and key lengths that differ (fa_bwd_general; bottom-right causal)
+def gpu_grads_general(q, k, v, g, causal, scale, cu=None, cu_k=None, S=None, S_k=None):
+    dq_, dk_, dv_, dg = (t.cuda() for t in (q, k, v, g))
+    dcu = dcu_k = None
+    if cu is not None:
+        dcu = torch.from_numpy(np.asarray(cu, np.int32)).cuda()
+        dcu_k = torch.from_numpy(np.asarray(cu_k, np.int32)).cuda()
+    o, lse = fa.attention(dq_, dk_, dv_, causal=causal, scale=scale, cu_seqlens=dcu,
+                          max_seqlen=S, cu_seqlens_k=dcu_k, max_seqlen_k=S_k)
+    grads = fa.attention_backward(dq_, dk_, dv_, o, lse, dg, causal=causal, scale=scale,
+                                  cu_seqlens=dcu, max_seqlen=S, cu_seqlens_k=dcu_k,
+                                  max_seqlen_k=S_k)
+    torch.cuda.synchronize()
+    return tuple(t.cpu() for t in grads)
+
+
+def full_bwd_check_general(q, k, v, g, causal, scale, cu=None, cu_k=None, S=None, S_k=None,
+                           what=""):
+    note(what, "q", tuple(q.shape), "k", tuple(k.shape), "causal", causal, "cu", cu, "cu_k", cu_k)
+    got = gpu_grads_general(q, k, v, g, causal, scale, cu, cu_k, S, S_k)
+    ref = oracle.attention_backward(q, k, v, g, scale, causal, cu, cu_k, magnitudes=True)
+    for name, gg, rr, mm in zip(("dq", "dk", "dv"), got, ref[:3], ref[3:]):
+        st = compare_grad(tensor_to_f64(gg), rr, mm)
+        note(what, name, st)
+        assert_grad_close(st, (what, name))
+    return got
+
+
+# (S_q, S_k): fewer queries than keys (chunked prefill), one query (decode),
+# more queries than keys (causal rows without keys), and tails of each
+QK_BWD = [(100, 333), (1, 300), (333, 130), (64, 64 + 257)]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lens", QK_BWD, ids=lambda s: "q%dk%d" % s)
+def test_backward_qk_lengths_dense(lens, causal, D):
+    S_q, S_k = lens
+    B, H, H_kv = 2, 4, 2
+    q, _, _ = draw_qkv((B, S_q, H, D), seed=111 + S_q + D)
+    _, k, v = draw_qkv((B, S_k, H, D), seed=112 + S_k + D, kv_heads=H_kv)
+    g = draw_dout((B, S_q, H, D), seed=113 + S_q)
+    got = full_bwd_check_general(q, k, v, g, causal, D ** -0.5,
+                                 what="bwd-qk q%d k%d D%d" % (S_q, S_k, D))
+    if causal and S_q > S_k:
+        assert torch.all(got[0][:, :S_q - S_k].float() == 0)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_qk_lengths_varlen(causal, D):
+    """Packed sequences with key lengths of their own, including a sequence
+    without queries, one without keys and one-query (decode) rows."""
+    lq = [5, 0, 130, 1, 70, 9]
+    lk = [40, 17, 66, 300, 0, 9]
+    cu, cu_k = cu_seqlens_of(lq), cu_seqlens_of(lk)
+    H, H_kv = 4, 1
+    q, _, _ = draw_qkv((int(cu[-1]), H, D), seed=121 + D)
+    _, k, v = draw_qkv((int(cu_k[-1]), H, D), seed=122 + D, kv_heads=H_kv)
+    g = draw_dout((int(cu[-1]), H, D), seed=123 + D)
+    got = full_bwd_check_general(q, k, v, g, causal, D ** -0.5, cu=cu, cu_k=cu_k, S=max(lq),
+                                 S_k=max(lk), what="bwd-qk-varlen D%d" % D)
+    # the sequence without keys: zero query gradient
+    a = int(cu[4])
+    assert torch.all(got[0][a:a + lq[4]].float() == 0)
+    # keys of the sequence without queries: zero key and value gradients
+    c = int(cu_k[1])
+    assert torch.all(got[1][c:c + lk[1]].float() == 0)
+    assert torch.all(got[2][c:c + lk[1]].float() == 0)
+
+
+def test_backward_general_equal_lengths_is_fa_bwd():
+    """fa_bwd_general with S_q = S_k and the same offsets is fa_bwd, bit for bit."""
+    D, S, H = 128, 333, 2
+    q, k, v = draw_qkv((1, S, H, D), seed=131)
+    g = draw_dout((1, S, H, D), seed=131)
+    dq_, dk_, dv_, dg = (t.cuda() for t in (q, k, v, g))
+    o, lse = fa.attention(dq_, dk_, dv_, causal=True)
+    lib = fa.load()
+    outs = []
+    for general in (False, True):
+        dq, dk, dv = (torch.empty_like(t) for t in (dq_, dk_, dv_))
+        delta = torch.empty_like(lse)
+        ptrs = [t.data_ptr() for t in (dq_, dk_, dv_, o, dg, lse, dq, dk, dv, delta)]
+        stream = torch.cuda.current_stream().cuda_stream
+        if general:
+            rc = lib.fa_bwd_general(*ptrs, 1, H, H, S, S, D, D ** -0.5, 1, None, None, stream)
+        else:
+            rc = lib.fa_bwd(*ptrs, 1, H, H, S, D, D ** -0.5, 1, None, stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        outs.append((dq.cpu(), dk.cpu(), dv.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

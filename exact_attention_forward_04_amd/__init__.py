@@ -317,21 +317,24 @@ def _autograd_function():
 
     class _Attention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, causal, scale, cu_seqlens, max_seqlen):
+        def forward(ctx, q, k, v, causal, scale, cu_seqlens, max_seqlen, cu_seqlens_k,
+                    max_seqlen_k):
             o, lse = attention(q, k, v, causal=causal, scale=scale, cu_seqlens=cu_seqlens,
-                               max_seqlen=max_seqlen)
+                               max_seqlen=max_seqlen, cu_seqlens_k=cu_seqlens_k,
+                               max_seqlen_k=max_seqlen_k)
             ctx.save_for_backward(q, k, v, o, lse)
-            ctx.cfg = (causal, scale, cu_seqlens, max_seqlen)
+            ctx.cfg = (causal, scale, cu_seqlens, max_seqlen, cu_seqlens_k, max_seqlen_k)
             return o
 
         @staticmethod
         def backward(ctx, do):
             q, k, v, o, lse = ctx.saved_tensors
-            causal, scale, cu_seqlens, max_seqlen = ctx.cfg
+            causal, scale, cu_seqlens, max_seqlen, cu_seqlens_k, max_seqlen_k = ctx.cfg
             dq, dk, dv = attention_backward(q, k, v, o, lse, do.contiguous(), causal=causal,
                                             scale=scale, cu_seqlens=cu_seqlens,
-                                            max_seqlen=max_seqlen)
-            return dq, dk, dv, None, None, None, None
+                                            max_seqlen=max_seqlen, cu_seqlens_k=cu_seqlens_k,
+                                            max_seqlen_k=max_seqlen_k)
+            return dq, dk, dv, None, None, None, None, None, None
 
     return _Attention
 
@@ -340,13 +343,16 @@ _attention_fn = None
 
 
 def attention_fn(q, k, v, causal: bool = False, scale: Optional[float] = None,
-                 cu_seqlens=None, max_seqlen: Optional[int] = None):
-    """attention() as a differentiable torch op: returns o, and o.backward()
-    computes the input gradients with fa_bwd."""
+                 cu_seqlens=None, max_seqlen: Optional[int] = None, cu_seqlens_k=None,
+                 max_seqlen_k: Optional[int] = None):
+    """attention() as a differentiable torch op (D_v = D): returns o, and
+    o.backward() computes the input gradients with fa_bwd_general.  Query and
+    key lengths may differ as in attention()."""
     global _attention_fn
     if _attention_fn is None:
         _attention_fn = _autograd_function()
-    return _attention_fn.apply(q, k, v, causal, scale, cu_seqlens, max_seqlen)
+    return _attention_fn.apply(q, k, v, causal, scale, cu_seqlens, max_seqlen, cu_seqlens_k,
+                               max_seqlen_k)
 
 
 def splitkv_workspace_size(B: int, H: int, S_q: int, S_k: int, D_v: int, num_splits: int) -> int:

@@ -262,3 +262,24 @@ def test_backward_general_equal_lengths_is_fa_bwd():
         outs.append((dq.cpu(), dk.cpu(), dv.cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_autograd_function_with_key_offsets():
+    """attention_fn with key offsets of their own runs fa_bwd_general: the
+    same bits as attention_backward on the same call."""
+    D, H = 64, 2
+    lq, lk = [3, 90, 1], [50, 40, 129]
+    cu, cu_k = cu_seqlens_of(lq), cu_seqlens_of(lk)
+    q, _, _ = draw_qkv((int(cu[-1]), H, D), seed=141)
+    _, k, v = draw_qkv((int(cu_k[-1]), H, D), seed=142)
+    g = draw_dout((int(cu[-1]), H, D), seed=143)
+    ref = gpu_grads_general(q, k, v, g, True, None, cu, cu_k, max(lq), max(lk))
+    dcu = torch.from_numpy(cu).cuda()
+    dcu_k = torch.from_numpy(cu_k).cuda()
+    tq, tk, tv = (t.cuda().requires_grad_(True) for t in (q, k, v))
+    o = fa.attention_fn(tq, tk, tv, causal=True, cu_seqlens=dcu, max_seqlen=max(lq),
+                        cu_seqlens_k=dcu_k, max_seqlen_k=max(lk))
+    o.backward(g.cuda())
+    torch.cuda.synchronize()
+    for x, y in zip((tq.grad, tk.grad, tv.grad), ref):
+        assert torch.equal(x.cpu().view(torch.int16), y.view(torch.int16))

@@ -283,3 +283,41 @@ def test_autograd_function_with_key_offsets():
     torch.cuda.synchronize()
     for x, y in zip((tq.grad, tk.grad, tv.grad), ref):
         assert torch.equal(x.cpu().view(torch.int16), y.view(torch.int16))
+
+
+def test_backward_chunked_prefill_sampled():
+    """A chunked-prefill batch at full size: B=2, H=16 query heads over 4 K/V
+    heads, 1024 queries against 8192 keys, D=128, causal (bottom-right: the
+    chunk's queries follow 7168 earlier keys).  Query rows and key rows
+    around the diagonal's start, block edges and random ones, compared with
+    the oracle row by row."""
+    B, H, H_kv, S_q, S_k, D = 2, 16, 4, 1024, 8192, 128
+    scale = D ** -0.5
+    q, _, _ = draw_qkv((B, S_q, H, D), seed=151)
+    _, k, v = draw_qkv((B, S_k, H, D), seed=152, kv_heads=H_kv)
+    g = draw_dout((B, S_q, H, D), seed=153)
+    note("bwd-chunk gpu run")
+    dq, dk, dv = gpu_grads_general(q, k, v, g, True, scale)
+    rng = np.random.default_rng(155)
+    off = S_k - S_q
+    b, hk = 1, 2
+    js = sorted(set([0, 63, 64, off - 1, off, off + 1, off + 255, off + 256, S_k - 64, S_k - 1]
+                    + list(rng.integers(0, S_k, 20))))
+    k_rows = [(b * H_kv + hk) * S_k + j for j in js]
+    h = hk * (H // H_kv) + 1
+    is_ = sorted(set([0, 1, 255, 256, S_q - 1] + list(rng.integers(0, S_q, 20))))
+    q_rows = [(b * H + h) * S_q + i for i in is_] + [(0 * H + 0) * S_q + 0,
+                                                      (0 * H + 15) * S_q + S_q - 1]
+    note("bwd-chunk oracle rows", len(q_rows), len(k_rows))
+    rdq, rdqm, rdk, rdv, rdkm, rdvm = oracle.attention_backward_rows_bf16(
+        q, k, v, g, q_rows, k_rows, scale, True)
+    gdq = tensor_to_f64(dq)
+    gdk, gdv = tensor_to_f64(dk), tensor_to_f64(dv)
+    sel_q = np.stack([gdq[r // (H * S_q), r % S_q, (r // S_q) % H] for r in q_rows])
+    sel_k = np.stack([gdk[b, j, hk] for j in js])
+    sel_v = np.stack([gdv[b, j, hk] for j in js])
+    for name, gg, rr, mm in (("dq", sel_q, rdq, rdqm), ("dk", sel_k, rdk, rdkm),
+                             ("dv", sel_v, rdv, rdvm)):
+        st = compare_grad(gg, rr, mm)
+        note("bwd-chunk", name, st)
+        assert_grad_close(st, ("bwd-chunk", name))

@@ -62,6 +62,8 @@ MUTANTS = [
      "acc += at(dout, obase + d) * at(k, vbase + d);"),
     ("bwd_key_rows_start_late", "i0 = j - (spk.len - spq.len);", "i0 = j - (spk.len - spq.len) + 1;"),
     ("bwd_key_rows_top_left", "i0 = j - (spk.len - spq.len);", "i0 = j;"),
+    ("bwd_key_span_from_query_offsets", "const seq_span spk = span_of(b, sh->Sk, sh->cu_k);",
+     "const seq_span spk = span_of(b, sh->Sq, sh->cu_q);"),
     ("bwd_group_first_head_only", "const int h = hk * G + g;", "const int h = hk * G;"),
     ("bwd_probs_unnormalised", "p[j] = exp(p[j] - *lse);", "p[j] = exp(p[j] - m);"),
     ("bwd_lse_sign", "const double p = exp(scale * s - st->lse);",

@@ -20,7 +20,7 @@ The cpu_baseline leg times the fp64 oracle (test infrastructure) on a
 bounded sample of query rows of the same workload on the host cores.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-  python bench.py --backward [--table]     # the backward pass (fa_bwd)
+  python bench.py --backward [--table]     # the backward pass (fa_bwd_general)
 """
 from __future__ import annotations
 
@@ -165,29 +165,35 @@ def time_workload(fa, torch, w, steps, warmup, tuning=None, num_splits=None, set
 BACKWARD_WORKLOADS = ["causal_b2h16s8192d128", "long_b1h16s32768d128_causal",
                       "dense_b2h16s2048d128", "dense_b2h16s2048d128_causal",
                       "gqa_b2h32kv8s8192d128_causal", "varlen_16x512to8192_h32d128_causal",
-                      "smoke_b1h8s512d64_causal"]
+                      "smoke_b1h8s512d64_causal", "mixed_16x_q1to2048_k512to8192_h16d128_causal"]
 
 
 def time_backward(fa, torch, w, steps, warmup, settle_s=0.0):
-    """Time fa_bwd (its dQ kernel and its dK/dV kernel) on a workload, after
-    one forward launch that provides o and lse.  Flops follow the usual
+    """Time fa_bwd_general (its dQ kernel and its dK/dV kernel) on a workload,
+    after one forward launch that provides o and lse.  Flops follow the usual
     backward convention: 2.5x the forward's (five products of the forward's
     size per block: S, dP, dV, dQ, dK)."""
-    from attn_inputs import draw_dout, flops, make
+    from attn_inputs import draw_dout, flops, make, make_qk
     dev = torch.device("cuda:0")
-    q, k, v, cu, S = make(w)
+    dcu_k, ms_k = None, None
+    if w.q_range:   # queries with lengths of their own
+        q, k, v, cu, cu_k, S, S_k = make_qk(w)
+        dcu_k, ms_k = torch.from_numpy(cu_k).to(dev), S_k
+    else:
+        q, k, v, cu, S = make(w)
     dq_, dk_, dv_ = q.to(dev), k.to(dev), v.to(dev)
     dcu = None if cu is None else torch.from_numpy(cu).to(dev)
     ms = S if cu is not None else None
     o, lse = fa.attention(dq_, dk_, dv_, causal=w.causal, scale=w.scale, cu_seqlens=dcu,
-                          max_seqlen=ms)
+                          max_seqlen=ms, cu_seqlens_k=dcu_k, max_seqlen_k=ms_k)
     g = draw_dout(tuple(q.shape), w.seed).to(dev)
     gq, gk, gv = torch.empty_like(dq_), torch.empty_like(dk_), torch.empty_like(dv_)
     delta = torch.empty_like(lse)
 
     def step():
         fa.attention_backward(dq_, dk_, dv_, o, lse, g, causal=w.causal, scale=w.scale,
-                              cu_seqlens=dcu, max_seqlen=ms, dq=gq, dk=gk, dv=gv, delta=delta)
+                              cu_seqlens=dcu, max_seqlen=ms, dq=gq, dk=gk, dv=gv, delta=delta,
+                              cu_seqlens_k=dcu_k, max_seqlen_k=ms_k)
 
     settle(torch, step, settle_s)
     for _ in range(warmup):
@@ -204,7 +210,7 @@ def time_backward(fa, torch, w, steps, warmup, settle_s=0.0):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
-    fl = 2.5 * flops(w, cu)
+    fl = 2.5 * flops(w, None if w.q_range else cu)
     return {"workload": w.name, "pass": "backward", "flops": fl,
             "ms_per_step": round(wall * 1e3 / steps, 4),
             "kernel_ms_mean": round(float(np.mean(kernel_ms)), 4),

@@ -113,6 +113,19 @@ def default_tuning() -> Tuning:
     return load().fa_tuning_default()
 
 
+def _require_buffer(t, name: str, shape, dtype, device) -> None:
+    """A caller-supplied output or scratch buffer must be exactly what the
+    kernels write through a raw pointer: the expected shape and dtype,
+    contiguous, on the inputs' device.  Anything else raises ValueError
+    before a launch (a smaller buffer would take out-of-bounds writes)."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError("%s must be %s of shape %s" % (name, dtype, tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device != device:
+        raise ValueError("%s must be on %s" % (name, device))
+
+
 def _stream_ptr(stream) -> Optional[int]:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -184,19 +197,26 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
         cu_ptr, cu_k_ptr = cu_seqlens.data_ptr(), cu_seqlens_k.data_ptr()
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if num_splits is not None and tuning is not None:
+        raise ValueError("num_splits (split-KV) takes no tuning: pass one or the other")
     o_shape = tuple(q.shape[:-1]) + (D_v,)
+    for name, t in (("k", k), ("v", v)):
+        if t.device != q.device:
+            raise ValueError("%s must be on %s" % (name, q.device))
+    if out is not None:
+        _require_buffer(out, "out", o_shape, torch.bfloat16, q.device)
     o = out if out is not None else torch.empty(o_shape, dtype=q.dtype, device=q.device)
-    if tuple(o.shape) != o_shape:
-        raise ValueError("out must have shape %s" % (o_shape,))
     lse = None
     if return_lse:
+        if lse_out is not None:
+            _require_buffer(lse_out, "lse_out", lse_shape, torch.float32, q.device)
         lse = lse_out if lse_out is not None else torch.empty(lse_shape, dtype=torch.float32,
                                                               device=q.device)
     sp = _stream_ptr(stream)
     tref = ctypes.byref(tuning) if tuning is not None else None
     lse_ptr = lse.data_ptr() if lse is not None else None
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_ptr)
-    if num_splits is not None and tuning is None:
+    if num_splits is not None:
         splits = int(num_splits)
         if splits == 0:
             n = ctypes.c_int(1)
@@ -206,11 +226,14 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
         need = lib.fa_splitkv_workspace_size(B, H, S, S_k, D_v, splits)
         if workspace is None:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-        if workspace.numel() < need:
-            raise ValueError("workspace must hold %d bytes" % need)
+        if workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous() \
+                or workspace.device != q.device:
+            raise ValueError("workspace must be a contiguous buffer of at least %d bytes on %s"
+                             % (need, q.device))
         rc = lib.fa_fwd_splitkv(*ptrs, B, H, H_kv, S, S_k, D, D_v, float(scale),
                                 int(bool(causal)), cu_ptr, cu_k_ptr, splits,
-                                workspace.data_ptr(), workspace.numel(), sp)
+                                workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), sp)
         _check("fa_fwd_splitkv", rc)
         return o, lse
     if S_k != S or cu_k_ptr != cu_ptr:
@@ -299,11 +322,12 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False,
     dv = dv if dv is not None else torch.empty_like(v)
     delta = delta if delta is not None else torch.empty(lse_shape, dtype=torch.float32,
                                                         device=q.device)
+    for name, t in (("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
+        if t.device != q.device:
+            raise ValueError("%s must be on %s" % (name, q.device))
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        if tuple(t.shape) != tuple(ref.shape) or t.dtype != torch.bfloat16:
-            raise ValueError("%s must be bf16 of shape %s" % (name, tuple(ref.shape)))
-    if tuple(delta.shape) != lse_shape or delta.dtype != torch.float32:
-        raise ValueError("delta must be fp32 of shape %s" % (lse_shape,))
+        _require_buffer(t, name, ref.shape, torch.bfloat16, q.device)
+    _require_buffer(delta, "delta", lse_shape, torch.float32, q.device)
     rc = lib.fa_bwd_general(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                             dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                             dv.data_ptr(), delta.data_ptr(), B, H, H_kv, S, S_k, D, float(scale),

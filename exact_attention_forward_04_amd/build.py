@@ -21,24 +21,53 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 
+COMPILE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+                 "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                 "-Wno-inline-asm"]
+
+
 def hipcc_command(out: str = LIB_PATH):
-    return [HIPCC, "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-inline-asm",
-            "-o", out] + SOURCES
+    """One hipcc line that compiles and links every source (for reference;
+    build() runs the same flags per source in parallel, then links)."""
+    return [HIPCC] + COMPILE_FLAGS + ["-shared", "-o", out] + SOURCES
 
 
-def build(out: str = LIB_PATH, verbose: bool = False) -> str:
-    """Compile the library (always recompiles) and return its path."""
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = hipcc_command(tmp)
-    if verbose:
-        print(" ".join(cmd))
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + r.stderr[-4000:])
-    os.replace(tmp, out)
+def build(out: str = LIB_PATH, verbose: bool = False, defines=()) -> str:
+    """Compile the library (always recompiles) and return its path.  Each
+    source is compiled to an object by its own hipcc process, in parallel;
+    defines (e.g. "FA_SYNC_DEBUG") are passed as -D flags."""
+    tag = ".tmp%d" % os.getpid()
+    extra = ["-D" + d for d in defines]
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = out + "." + os.path.splitext(os.path.basename(src))[0] + tag + ".o"
+        cmd = [HIPCC] + COMPILE_FLAGS + extra + ["-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd))
+        objs.append(obj)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                      text=True))
+    errs = []
+    for p in procs:
+        _, err = p.communicate()
+        if p.returncode != 0:
+            errs.append(err[-4000:])
+    try:
+        if errs:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
+        tmp = out + tag
+        cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+        if verbose:
+            print(" ".join(cmd))
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + r.stderr[-4000:])
+        os.replace(tmp, out)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return out
 
 

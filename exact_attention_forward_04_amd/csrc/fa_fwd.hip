@@ -58,6 +58,7 @@
 namespace {
 
 constexpr int kMatrixPrio = 2;    // wave priority (s_setprio) of a ping-pong matrix phase
+constexpr float kMaxTau = 64.0f;  // largest accepted rescale threshold (log2 units)
 
 // ---------------------------------------------------------------------------
 // Polynomial exp2 (Cody-Waite split + degree-3 Horner, three FMAs).
@@ -949,7 +950,9 @@ int validate(const void *q, const void *k, const void *v, void *o, float *lse, i
   if (!(scale > 0.0f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (t) {
-    if (!(t->tau >= 0.0f) || !std::isfinite(t->tau)) return FA_ERR_INVALID_ARG;
+    // p = exp2(c*s - m_ref) reaches 2^tau before a rescale: bounded so that
+    // the fp32 row sums and O accumulators stay far from overflow.
+    if (!(t->tau >= 0.0f && t->tau <= kMaxTau)) return FA_ERR_INVALID_ARG;
     if (t->exp2_emu != 0 && t->exp2_emu != 4 && t->exp2_emu != 8) return FA_ERR_INVALID_ARG;
     if (t->schedule != 0 && t->schedule != 1) return FA_ERR_INVALID_ARG;
   }

@@ -83,7 +83,11 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 /*
  * Experiment knobs for fa_fwd_ex.  fa_fwd uses fa_tuning_default().
  *
- *   tau        Rescale threshold in log2 units (>= 0).  The running row
+ *   tau        Rescale threshold in log2 units, 0 <= tau <= 64 (other
+ *              values, NaN included, are FA_ERR_INVALID_ARG: an
+ *              exponential may reach 2^tau before the rescale, and above
+ *              2^64 per entry the fp32 row sums and O accumulators of long
+ *              rows would come near overflow).  The running row
  *              maximum used for the exponentials is moved, and the output
  *              and row sums rescaled, only when some row of a wavefront sees
  *              a block maximum more than tau above it; otherwise the stale

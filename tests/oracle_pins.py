@@ -445,6 +445,79 @@ def check_bwd_uniform_probabilities(o):
             assert np.all(np.abs(got) <= mag + 1e-15), "a gradient exceeds its magnitude"
 
 
+def check_bwd_magnitudes_single_key(o):
+    """The magnitude A that bounds each gradient element is the sum of the
+    absolute values of its terms, where the term of key j in dQ_i (and of row
+    i in dK_j) is scale * (|dS_ij| + P_ij * E_i) * |k_jd| (|q_id|), E_i being
+    the bound sum_d |dO_id| |O_id| of |Delta_i|.  With one key P = 1 and
+    dS = 0, and O_i = v_0, so in closed form
+    |dQ|_id = scale * E_i * |k_0d| and |dK|_0d = scale * sum_i E_i |q_id|,
+    with E_i = sum_d |dO_id| |v_0d|."""
+    rng = np.random.default_rng(36)
+    B, S, H, D = 2, 1, 3, 4
+    q, k, v, g = (rng.standard_normal((B, S, H, D)) for _ in range(4))
+    scale = 0.6
+    for causal in (False, True):
+        res = o.attention_backward(q, k, v, g, scale, causal, magnitudes=True)
+        dqm, dkm = res[3], res[4]
+        for b in range(B):
+            for h in range(H):
+                e = np.sum(np.abs(g[b, 0, h]) * np.abs(v[b, 0, h]))
+                ref_q = scale * e * np.abs(k[b, 0, h])
+                ref_k = scale * e * np.abs(q[b, 0, h])
+                assert np.allclose(dqm[b, 0, h], ref_q, rtol=1e-13, atol=0), ("|dq|", causal, b, h)
+                assert np.allclose(dkm[b, 0, h], ref_k, rtol=1e-13, atol=0), ("|dk|", causal, b, h)
+    # grouped K/V: the one key of a K/V head collects every query head of its group
+    q, g = rng.standard_normal((1, 1, 4, 3)), rng.standard_normal((1, 1, 4, 3))
+    k, v = rng.standard_normal((1, 1, 2, 3)), rng.standard_normal((1, 1, 2, 3))
+    res = o.attention_backward(q, k, v, g, scale, True, magnitudes=True)
+    for hk in range(2):
+        ref = 0.0
+        for h in (2 * hk, 2 * hk + 1):
+            e = np.sum(np.abs(g[0, 0, h]) * np.abs(v[0, 0, hk]))
+            ref = ref + scale * e * np.abs(q[0, 0, h])
+        assert np.allclose(res[4][0, 0, hk], ref, rtol=1e-13, atol=0), ("gqa |dk|", hk)
+
+
+def check_bwd_magnitudes_equal_logits(o):
+    """Equal logits make P_ij = 1/n_i exactly (n_i: the keys row i may use),
+    which fixes every term of the magnitudes in closed form.  Q = 0 gives
+    |dQ|_id = scale/n_i * sum_j (|dp_ij - Delta_i| + E_i) |k_jd|; K = 0
+    gives |dK|_jd = scale * sum_(i uses j) (|dp_ij - Delta_i| + E_i)/n_i |q_id|,
+    with dp_ij = <dO_i, v_j>, Delta_i = mean_j dp_ij, O_i = mean_j v_j and
+    E_i = sum_d |dO_id| |O_id|."""
+    rng = np.random.default_rng(37)
+    S, D = 6, 3
+    scale = 0.7
+    for causal in (False, True):
+        v, g, kq = (rng.standard_normal((1, S, 1, D)) for _ in range(3))
+        zero = np.zeros((1, S, 1, D))
+
+        def row_terms(i):
+            n = i + 1 if causal else S
+            dp = v[0, :n, 0] @ g[0, i, 0]
+            delta = dp.mean()
+            e = np.sum(np.abs(g[0, i, 0]) * np.abs(v[0, :n, 0].mean(0)))
+            return n, np.abs(dp - delta), e
+
+        # Q = 0, keys kq: dQ magnitudes
+        res = o.attention_backward(zero, kq, v, g, scale, causal, magnitudes=True)
+        for i in range(S):
+            n, adp, e = row_terms(i)
+            ref = scale / n * ((adp + e)[:, None] * np.abs(kq[0, :n, 0])).sum(0)
+            assert np.allclose(res[3][0, i, 0], ref, rtol=1e-12, atol=0), ("|dq|", causal, i)
+        # K = 0, queries kq: dK magnitudes
+        res = o.attention_backward(kq, zero, v, g, scale, causal, magnitudes=True)
+        for j in range(S):
+            ref = np.zeros(D)
+            for i in range(S):
+                if causal and j > i:
+                    continue
+                n, adp, e = row_terms(i)
+                ref += scale * (adp[j] + e) / n * np.abs(kq[0, i, 0])
+            assert np.allclose(res[4][0, j, 0], ref, rtol=1e-12, atol=0), ("|dk|", causal, j)
+
+
 def check_bwd_rows_match_full(o):
     """The row-list entry point returns the rows of the full backward, for
     dense and varlen inputs with grouped K/V heads."""
@@ -502,5 +575,7 @@ ALL_CHECKS = [
     check_bwd_rows_without_keys,
     check_bwd_single_key,
     check_bwd_uniform_probabilities,
+    check_bwd_magnitudes_single_key,
+    check_bwd_magnitudes_equal_logits,
     check_bwd_rows_match_full,
 ]

@@ -74,11 +74,17 @@ def test_validation_rejects(kw, expect):
 
 def test_tuning_validation():
     lib = fa.load()
-    for field, val in (("tau", -1.0), ("tau", float("nan")), ("exp2_emu", 3), ("schedule", 2)):
+    for field, val in (("tau", -1.0), ("tau", float("nan")), ("tau", 64.5), ("tau", float("inf")),
+                       ("exp2_emu", 3), ("schedule", 2)):
         t = fa.default_tuning()
         setattr(t, field, val)
         rc = lib.fa_fwd_ex(A, A, A, A, A, 1, 1, 8, 128, 0.1, 0, None, None, ctypes.byref(t))
         assert rc == fa.FA_ERR_INVALID_ARG, (field, val)
+    # the largest accepted threshold passes validation (then finds no device here)
+    t = fa.default_tuning()
+    t.tau = 64.0
+    rc = lib.fa_fwd_ex(A, A, A, A, A, 1, 1, 8, 128, 0.1, 0, None, None, ctypes.byref(t))
+    assert rc != fa.FA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("H,H_kv,expect", [
@@ -281,3 +287,22 @@ def test_backward_binding_checks_key_offsets():
     with pytest.raises(ValueError):
         fa.attention_backward(q, k, k, q, lse, q, cu_seqlens=torch.zeros(2, dtype=torch.int32),
                               max_seqlen=8)
+
+
+def test_output_buffer_checks():
+    """Caller-supplied outputs and scratch (out, lse_out, dq/dk/dv, delta) are
+    written through raw pointers: a wrong shape, dtype, layout or device is
+    rejected before any launch."""
+    import torch
+    cpu = torch.device("cpu")
+    fa._require_buffer(torch.empty((2, 3, 4)), "lse_out", (2, 3, 4), torch.float32, cpu)
+    bad = [
+        torch.empty((2, 3, 3)),                              # too small
+        torch.empty((2, 3, 5)),                              # too large
+        torch.empty((2, 3, 4), dtype=torch.bfloat16),        # wrong dtype
+        torch.empty((2, 4, 3)).transpose(1, 2),              # right shape, not contiguous
+        torch.empty((2, 3, 4), device="meta"),               # another device
+    ]
+    for t in bad:
+        with pytest.raises(ValueError):
+            fa._require_buffer(t, "lse_out", (2, 3, 4), torch.float32, cpu)

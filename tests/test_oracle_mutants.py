@@ -68,6 +68,21 @@ MUTANTS = [
     ("bwd_probs_unnormalised", "p[j] = exp(p[j] - *lse);", "p[j] = exp(p[j] - m);"),
     ("bwd_lse_sign", "const double p = exp(scale * s - st->lse);",
      "const double p = exp(scale * s + st->lse);"),
+    ("bwd_dq_magnitude_x4", "dq_mag[d] = scale * mag;", "dq_mag[d] = 4 * scale * mag;"),
+    ("bwd_dk_magnitude_x4", "dk_mag[d] += scale * (fabs(ds) + p * st->e) * fabs(qd);",
+     "dk_mag[d] += 4 * scale * (fabs(ds) + p * st->e) * fabs(qd);"),
+    ("bwd_dq_delta_bound_x8", "mag += (fabs(ds) + p[j] * e) * fabs(kd);",
+     "mag += (fabs(ds) + 8 * p[j] * e) * fabs(kd);"),
+    ("bwd_dk_delta_bound_x8", "dk_mag[d] += scale * (fabs(ds) + p * st->e) * fabs(qd);",
+     "dk_mag[d] += scale * (fabs(ds) + 8 * p * st->e) * fabs(qd);"),
+    ("bwd_dq_magnitude_drops_ds", "mag += (fabs(ds) + p[j] * e) * fabs(kd);",
+     "mag += (p[j] * e) * fabs(kd);"),
+    ("bwd_dk_magnitude_drops_ds", "dk_mag[d] += scale * (fabs(ds) + p * st->e) * fabs(qd);",
+     "dk_mag[d] += scale * (p * st->e) * fabs(qd);"),
+    ("bwd_delta_bound_unsigned_o", "e += fabs(at(dout, obase + d)) * fabs(od);",
+     "e += fabs(at(dout, obase + d)) * od;"),
+    ("bwd_dq_magnitude_key_index", "mag += (fabs(ds) + p[j] * e) * fabs(kd);",
+     "mag += (fabs(ds) + p[j] * e) * fabs(at(k, ((spk.tok0 + j) * Hkv + hk) * (int64_t)D));"),
     ("bwd_key_row_decode_swaps", "*j = (int)(row % S);\n        *hk = (int)((row / S) % Hkv);",
      "*hk = (int)(row % Hkv);\n        *j = (int)((row / Hkv) % S);"),
 ]

@@ -19,14 +19,16 @@
 //              then holds 16 keys of ONE query row per 32-key sub-block, so a
 //              row maximum is an in-lane max plus one v_permlane32_swap with
 //              the other half-wave, and the row statistics are per lane.
-//   softmax    running row max m_ref in log2 units; a block whose maximum
-//              exceeds m_ref by more than tau in ANY row of the wave triggers
-//              a rescale of O and the row sums for the whole wave (paper
-//              section 3.1.4); otherwise m_ref is kept and the final
-//              normalisation absorbs the difference.  p = exp2(c*s - m_ref)
-//              with c = scale*log2(e), by v_exp_f32 or, for a fixed share of
-//              column slots, by the Cody-Waite degree-3 polynomial (paper
-//              section 3.1.3).  The row sum l = sum p is kept in fp32 from
+//   softmax    reference row max m_ref in log2 units.  p = exp2(c*s - m_ref)
+//              with c = scale*log2(e) is computed against the stale m_ref,
+//              by v_exp_f32 or, for a fixed share of column slots, by the
+//              Cody-Waite degree-3 polynomial (paper section 3.1.3).  Only
+//              when some lane's share of the block's row sum exceeds 2^tau
+//              (or a row has no reference yet) does the whole wave take the
+//              block maximum, move m_ref and rescale O and the row sums
+//              (paper section 3.1.4: rescale only when the growth of the
+//              maximum threatens the range); otherwise the final
+//              normalisation absorbs the stale reference.  The row sum l = sum p is kept in fp32 from
 //              the unrounded p (paper section 3.1.2 sums after the exp);
 //              P is rounded to bf16 only as the operand of the PV product.
 //   O^T += V^T P^T  on MFMA: the S accumulator registers, rounded to bf16,
@@ -107,7 +109,8 @@ struct Args {
   int Sk;                   // (longest) key length
   int Hkv;                  // K/V heads (divides H); query head h reads K/V head h / (H / Hkv)
   float c;                  // scale * log2(e)
-  float tau;
+  float tau;                // rescale threshold (log2 units) of the max-first test
+  float bound;              // 2^tau: largest lane share of a block's row sum kept without rescale
   unsigned long long *counters;
   int workers;              // persistent: number of workgroups
   // split-KV: each workgroup covers key blocks [split*kbps, (split+1)*kbps)
@@ -186,10 +189,12 @@ __device__ __forceinline__ void max_slice(const f32x16 (&s)[2], int kb, int e0, 
   for (int e = e0; e < e0 + 8; ++e) mx = fmaxf(mx, s[kb][e]);
 }
 
-// Conditional rescale (paper section 3.1.4), decided for the whole wave, from
-// the block's raw row maximum (both half-waves combined).  rescale_decide
-// moves m_ref and the row sum; the caller scales O by alpha when `any` (at
-// once, or after products still in flight that use the old scale).
+// Conditional rescale decided from the block's raw row maximum (both
+// half-waves combined), for the pipelined single-wave body: the wave moves
+// to max(m_ref, m_blk) when any row's block maximum exceeds m_ref by more
+// than tau (paper section 3.1.4).  rescale_decide moves m_ref and the row
+// sum; the caller scales O by alpha when `any`, after the products still in
+// flight that use the old scale.
 struct Rescale {
   bool any;
   float alpha;
@@ -227,12 +232,6 @@ template <int D>
 __device__ __forceinline__ float m_use_of(const WaveState<D> &st) {
   return (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
 }
-template <int D, bool COUNT>
-__device__ __forceinline__ float rescale_step(WaveState<D> &st, float mx, int lane, const Args &a) {
-  const Rescale r = rescale_decide<D, COUNT>(st, mx, lane, a);
-  if (r.any) scale_o<D>(st, r.alpha);
-  return m_use_of<D>(st);
-}
 
 // p = exp2(c*s - m) for scores e, e+1 of sub-block kb: row sum (one partial
 // sum per sub-block, to halve the dependent chain) and bf16 pack into the PV
@@ -254,10 +253,58 @@ __device__ __forceinline__ void exp_pair(bf16x8 (&p)[4], const f32x16 (&s)[2], i
   p[t][(e & 7) + 1] = pb[1];
 }
 
-// Mask, row statistics, conditional rescale, exp2, row sums and bf16 packing
-// of one block (scores in st.s, probabilities out to st.p).  side(0) runs
-// before the row max and side(1) before the exp loop: the caller hangs its
-// K/V copies there, off the path of the other half's matrix products.
+// Exponentials of one block against the reference m_use: p = exp2(c*s - m_use),
+// this lane's share of the row sum, and the bf16 P operand.
+template <int EMU>
+__device__ __forceinline__ float exp_block(bf16x8 (&p)[4], const f32x16 (&s)[2], float m_use,
+                                           bool last_block, const Args &a) {
+  float lsum[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) exp_pair<EMU>(p, s, kb, e, m_use, last_block, a, lsum);
+  return lsum[0] + lsum[1];
+}
+
+// The rescale path of a block: row maximum of the block's scores (raw; c > 0
+// so it commutes with scaling), new reference m_new = max(m_ref, m_blk) for
+// every row of the wave, O and the row sum scaled by exp2(m_ref - m_new), and
+// the block's exponentials against m_new.  Returns the lane's row-sum share.
+template <int D, int EMU, bool COUNT>
+__device__ __forceinline__ float rescale_block(WaveState<D> &st, int lane, bool last_block,
+                                               const Args &a) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e0 = 0; e0 < 16; e0 += 8) max_slice(st.s, kb, e0, mx);
+  const float m_blk = max_halves(mx) * a.c;  // -inf when the row's block is fully masked
+  const float m_new = fmaxf(st.m_ref, m_blk);
+  const float alpha = (st.m_ref == -INFINITY) ? 0.0f : exp2_hw(st.m_ref - m_new);
+  st.m_ref = m_new;
+  st.l32 *= alpha;
+  scale_o<D>(st, alpha);
+  if constexpr (COUNT) {
+    if (lane == 0) atomicAdd(&a.counters[0], 1ull);
+  }
+  return exp_block<EMU>(st.p, st.s, m_use_of<D>(st), last_block, a);
+}
+
+// Mask, conditional rescale, exp2, row sums and bf16 packing of one block
+// (scores in st.s, probabilities out to st.p).
+//
+// The rescale condition (paper section 3.1.4: correct O and the row sum only
+// when the running maximum has grown enough to threaten the range of the
+// exponentials) is tested on the exponentials themselves.  They are first
+// computed against the stale reference m_ref; if every lane's share of the
+// block's row sum stays within 2^tau, so does every p (all p >= 0), and the
+// block is done without any row-maximum reduction.  Otherwise, and when some
+// row of the wave has no reference yet (its first keys), the whole wave takes
+// the rescale path: block row maximum, new reference max(m_ref, m_blk) for
+// every row, O and the row sum scaled by exp2(m_ref - m_new), exponentials
+// again.  The decision is a wave-wide ballot, so the wave never diverges.
+// side(0) runs first and side(1) after the mask: the caller hangs its K/V
+// copies and operand prefetches there.
 template <int D, bool CAUSAL, int EMU, bool COUNT, typename Side>
 __device__ __forceinline__ void softmax_step(WaveState<D> &st, int lane, int n0, int row, int L,
                                              bool need_mask, bool last_block, const Args &a,
@@ -270,20 +317,18 @@ __device__ __forceinline__ void softmax_step(WaveState<D> &st, int lane, int n0,
 #pragma unroll
       for (int e0 = 0; e0 < 16; e0 += 8) mask_slice(st.s, kb, e0, lim);
   }
-  // block row max (raw scores; c > 0 so it commutes with scaling)
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int e0 = 0; e0 < 16; e0 += 8) max_slice(st.s, kb, e0, mx);
-  const float m_use = rescale_step<D, COUNT>(st, mx, lane, a);
   side(1);
-  float lsum[2] = {0.0f, 0.0f};
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) exp_pair<EMU>(st.p, st.s, kb, e, m_use, last_block, a, lsum);
-  st.l32 += lsum[0] + lsum[1];
+  bool redo = __builtin_amdgcn_ballot_w64(st.m_ref == -INFINITY) != 0;
+  float lsum = 0.0f;
+  if (!redo) {
+    lsum = exp_block<EMU>(st.p, st.s, st.m_ref, last_block, a);
+    redo = __builtin_amdgcn_ballot_w64(!(lsum <= a.bound)) != 0;
+  }
+  if (redo) lsum = rescale_block<D, EMU, COUNT>(st, lane, last_block, a);
+  if constexpr (COUNT) {
+    if (lane == 0) atomicAdd(&a.counters[1], 1ull);
+  }
+  st.l32 += lsum;
 }
 
 // O^T += V^T P^T for one block: D/32 d-tiles, 4 steps of 16 keys.  The V^T
@@ -648,7 +693,10 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       barrier_after_reads();
       issue_block(j + 1);
     };
-    // S_j, its mask and row max, and the rescale decision.
+    // S_j, its mask and row max, and the rescale decision.  This body keeps
+    // the max-first form of the rescale test: its exponentials run between
+    // the PV products, and holding the scores until a decision taken after
+    // them (softmax_step's form) would take 32 registers it does not have.
     auto scores = [&](int j, float &m_use) {
       qk_step<D>(st, la, kslot(j), kslot(j));
       if (wr.need_mask(j, Lk, false)) {
@@ -1118,6 +1166,7 @@ int fa_fwd_general(const void *q, const void *k, const void *v, void *o, float *
   a.Sk = S_k;
   a.c = scale * kLog2e;
   a.tau = t.tau;
+  a.bound = exp2f(t.tau);
   a.counters = t.counters;
   a.workers = 0;
   a.ws_o = a.ws_lse = nullptr;
@@ -1190,6 +1239,7 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
   a.Sk = S_k;
   a.c = scale * kLog2e;
   a.tau = fa_tuning_default().tau;
+  a.bound = exp2f(a.tau);
   a.counters = nullptr;
   a.workers = 0;
   const size_t slots = (size_t)B * S_q * H;

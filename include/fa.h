@@ -84,18 +84,19 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  * Experiment knobs for fa_fwd_ex.  fa_fwd uses fa_tuning_default().
  *
  *   tau        Rescale threshold in log2 units, 0 <= tau <= 64 (other
- *              values, NaN included, are FA_ERR_INVALID_ARG: an
- *              exponential may reach 2^tau before the rescale, and above
- *              2^64 per entry the fp32 row sums and O accumulators of long
- *              rows would come near overflow).  The running row
- *              maximum used for the exponentials is moved, and the output
- *              and row sums rescaled, only when some row of a wavefront sees
- *              a block maximum more than tau above it; otherwise the stale
- *              maximum is kept (FlashAttention-4 paper, section 3.1.4,
- *              skipping online-softmax rescaling: the final normalisation
- *              corrects the skipped steps; the decision is taken for the
- *              whole wavefront so it never diverges).  tau = 0 is the
- *              textbook online softmax.  Default 8 (factor 256).
+ *              values, NaN included, are FA_ERR_INVALID_ARG).  Each block's
+ *              exponentials are computed against the running reference
+ *              maximum as it stands; the reference is moved to the block
+ *              maximum, and the output and row sums rescaled, only when
+ *              some lane's share of the block's row sum exceeds 2^tau (so
+ *              every exponential stays within 2^tau) or a row has no
+ *              reference yet.  The decision is taken for the whole
+ *              wavefront, so it never diverges (FlashAttention-4 paper,
+ *              section 3.1.4, skipping online-softmax rescaling: the final
+ *              normalisation corrects the skipped steps).  The result does
+ *              not depend on tau; tau = 0 rescales whenever an exponential
+ *              could exceed 1, i.e. on every growth of the maximum, as the
+ *              textbook online softmax does.  Default 8 (factor 256).
  *   exp2_emu   Share of exponentials evaluated by the degree-3 polynomial
  *              instead of v_exp_f32 (paper section 3.1.3, partial emulation):
  *              0 = none, 8 = one column slot in 8 (12.5 %), 4 = one in 4

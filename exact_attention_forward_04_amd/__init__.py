@@ -26,6 +26,8 @@ FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 FA_ERR_NO_DEVICE = -4
+FA_ERR_TOO_LARGE = -5
+SPLITKV_SCRATCH_BYTES = 16 << 20   # FA_SPLITKV_SCRATCH_BYTES
 
 LIB_PATH = _build.LIB_PATH
 _lib = None
@@ -68,6 +70,8 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, P, I, P,
                                    ctypes.c_size_t, P]
     lib.fa_fwd_splitkv.restype = I
+    lib.fa_fwd_splitkv_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, P, I, P]
+    lib.fa_fwd_splitkv_noalloc.restype = I
     lib.fa_splitkv_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.fa_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fa_splitkv_auto_splits.argtypes = [I, I, I, I, I, ctypes.POINTER(I)]
@@ -150,12 +154,17 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
     num_splits > 1 splits every key range over that many workgroups
     (fa_fwd_splitkv, for decode-like batches with few query rows), 0 picks a
     count for the device; workspace (a CUDA uint8 tensor of at least
-    splitkv_workspace_size(...) bytes) is allocated when not given.
+    splitkv_workspace_size(...) bytes) is allocated when not given, and
+    workspace="static" uses the library's fixed device scratch instead
+    (fa_fwd_splitkv_noalloc: with out and lse_out given nothing is allocated;
+    calls that overlap on one device race).
     Returns (o, lse): o like q with D_v columns (bf16), lse fp32 [B,H,Sq] or
     [H,Tq] (None if return_lse is False).
     """
     import torch
     lib = load()
+    if workspace is not None and num_splits is None:
+        raise ValueError("workspace is used only with num_splits (split-KV)")
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("%s must be a contiguous bf16 CUDA tensor" % name)
@@ -223,6 +232,13 @@ def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
             _check("fa_splitkv_auto_splits_gqa",
                    lib.fa_splitkv_auto_splits_gqa(B, H, H_kv, S, S_k, D, ctypes.byref(n)))
             splits = n.value
+        if isinstance(workspace, str):
+            if workspace != "static":
+                raise ValueError('workspace must be a tensor, None or "static"')
+            rc = lib.fa_fwd_splitkv_noalloc(*ptrs, B, H, H_kv, S, S_k, D, D_v, float(scale),
+                                            int(bool(causal)), cu_ptr, cu_k_ptr, splits, sp)
+            _check("fa_fwd_splitkv_noalloc", rc)
+            return o, lse
         need = lib.fa_splitkv_workspace_size(B, H, S, S_k, D_v, splits)
         if workspace is None:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

@@ -1127,6 +1127,39 @@ int bm_for(int D) {
   }
 }
 
+// The partial results of fa_fwd_splitkv_noalloc: a fixed array in each
+// device's memory, so that the call allocates nothing.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in
+// symbol); it uses the device address scratch_address() looks up once per
+// device.
+__device__ __align__(256) float scratch[FA_SPLITKV_SCRATCH_BYTES / sizeof(float)];
+
+struct ScratchSlot {
+  std::once_flag once;
+  void *ptr = nullptr;
+};
+ScratchSlot g_scratch[64];
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with it current) and kept per device.
+int scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FA_ERR_NO_DEVICE;
+  ScratchSlot &slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) slot.ptr = p;
+  });
+  if (!slot.ptr) return FA_ERR_HIP;
+  *out = slot.ptr;
+  return FA_OK;
+}
+
+int splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+            int H_kv, int S_q, int S_k, int D, int D_v, float scale, int causal,
+            const int *cu_seqlens_q, const int *cu_seqlens_k, int num_splits, void *workspace,
+            size_t workspace_bytes, void *stream, bool fixed_scratch);
+
 }  // namespace
 
 extern "C" {
@@ -1210,6 +1243,26 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
                    int H, int H_kv, int S_q, int S_k, int D, int D_v, float scale, int causal,
                    const int *cu_seqlens_q, const int *cu_seqlens_k, int num_splits,
                    void *workspace, size_t workspace_bytes, void *stream) {
+  return splitkv(q, k, v, o, lse, B, H, H_kv, S_q, S_k, D, D_v, scale, causal, cu_seqlens_q,
+                 cu_seqlens_k, num_splits, workspace, workspace_bytes, stream, false);
+}
+
+int fa_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int B, int H, int H_kv, int S_q, int S_k, int D, int D_v,
+                           float scale, int causal, const int *cu_seqlens_q,
+                           const int *cu_seqlens_k, int num_splits, void *stream) {
+  return splitkv(q, k, v, o, lse, B, H, H_kv, S_q, S_k, D, D_v, scale, causal, cu_seqlens_q,
+                 cu_seqlens_k, num_splits, nullptr, 0, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+int splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+            int H_kv, int S_q, int S_k, int D, int D_v, float scale, int causal,
+            const int *cu_seqlens_q, const int *cu_seqlens_k, int num_splits, void *workspace,
+            size_t workspace_bytes, void *stream, bool fixed_scratch) {
   if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
   int rc = validate(q, k, v, o, lse, B, H, H_kv, S_q, S_k, D, D_v, scale, causal, cu_seqlens_q,
                     cu_seqlens_k, nullptr);
@@ -1220,10 +1273,19 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
     return fa_fwd_general(q, k, v, o, lse, B, H, H_kv, S_q, S_k, D, D_v, scale, causal,
                           cu_seqlens_q, cu_seqlens_k, stream, nullptr);
   const size_t need = fa_splitkv_workspace_size(B, H, S_q, S_k, D_v, num_splits);
-  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_INVALID_ARG;
   DeviceInfo *dev = nullptr;
-  rc = current_device(&dev);
-  if (rc != FA_OK) return rc;
+  if (fixed_scratch) {
+    if (need > FA_SPLITKV_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
+    rc = current_device(&dev);
+    if (rc != FA_OK) return rc;
+    rc = scratch_address(&workspace);
+    if (rc != FA_OK) return rc;
+    workspace_bytes = FA_SPLITKV_SCRATCH_BYTES;
+  } else {
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_INVALID_ARG;
+    rc = current_device(&dev);
+    if (rc != FA_OK) return rc;
+  }
   Args a;
   a.q = (const __bf16 *)q;
   a.k = (const __bf16 *)k;
@@ -1255,6 +1317,10 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
     default: return dispatch_split<256>(a, causal, varlen, splits, st);
   }
 }
+
+}  // namespace
+
+extern "C" {
 
 int fa_fwd_hd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
               int H_kv, int S, int D, int D_v, float scale, int causal, const int *cu_seqlens,
@@ -1369,10 +1435,11 @@ const char *fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported configuration";
     case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
     case FA_ERR_NO_DEVICE: return "FA_ERR_NO_DEVICE: no gfx950 device is current";
+    case FA_ERR_TOO_LARGE: return "FA_ERR_TOO_LARGE: sizes exceed the fixed scratch buffer";
     default: return "unknown fa_status";
   }
 }
 
-int fa_version(void) { return 106; }
+int fa_version(void) { return 107; }
 
 }  // extern "C"

@@ -37,7 +37,8 @@ typedef enum fa_status {
     FA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size, bad scale, ... */
     FA_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement (e.g. D) */
     FA_ERR_HIP = -3,           /* a HIP runtime call or kernel launch failed */
-    FA_ERR_NO_DEVICE = -4      /* no gfx950 device is current */
+    FA_ERR_NO_DEVICE = -4,     /* no gfx950 device is current */
+    FA_ERR_TOO_LARGE = -5      /* the sizes need more than a fixed scratch buffer holds */
 } fa_status;
 
 /*
@@ -213,6 +214,32 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
                    int causal, const int *cu_seqlens_q, const int *cu_seqlens_k,
                    int num_splits, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc): the partial results live in a fixed scratch array
+ * that the library holds in each device's memory (FA_SPLITKV_SCRATCH_BYTES,
+ * from the first call on a device until the process ends) instead of a
+ * workspace argument.  The call allocates nothing; the caller passes inputs
+ * and outputs as for fa_fwd_splitkv.
+ *
+ * Arguments and results are those of fa_fwd_splitkv without workspace and
+ * workspace_bytes.  Errors: as fa_fwd_splitkv, plus FA_ERR_TOO_LARGE when
+ * fa_splitkv_workspace_size(B, H, S_q, S_k, D_v, num_splits) exceeds
+ * FA_SPLITKV_SCRATCH_BYTES (nothing is enqueued then), and FA_ERR_HIP when
+ * the scratch address cannot be obtained.
+ *
+ * All calls on one device share its scratch array: calls whose work can
+ * overlap on that device (different streams, or host threads without
+ * ordering) race and give wrong results.  Calls on one stream are ordered
+ * and safe.  The scratch contents on entry do not matter.
+ */
+#define FA_SPLITKV_SCRATCH_BYTES ((size_t)16 << 20)
+int fa_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int B, int H, int H_kv, int S_q, int S_k, int D, int D_v,
+                           float scale, int causal, const int *cu_seqlens_q,
+                           const int *cu_seqlens_k, int num_splits, void *stream);
+
 /* Workspace bytes fa_fwd_splitkv needs for these sizes (B, H, the longest
  * query and key lengths S_q and S_k, D_v) and num_splits: partial O and LSE,
  * fp32, for splits x B x S_q x H rows.  0 when no workspace is needed (one
@@ -356,7 +383,8 @@ int fa_num_workers(int D, int *workers_out);
 const char *fa_status_string(int status);
 
 /* Library ABI version: 100 * major + minor (101: fa_fwd_gqa; 102: fa_fwd_hd;
- * 103: fa_fwd_general; 104: fa_bwd; 105: fa_fwd_splitkv; 106: fa_bwd_general). */
+ * 103: fa_fwd_general; 104: fa_bwd; 105: fa_fwd_splitkv; 106: fa_bwd_general;
+ * 107: fa_fwd_splitkv_noalloc). */
 int fa_version(void);
 
 #ifdef __cplusplus

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert fa.status_string(st).startswith(("FA_OK", "FA_ERR"))
     assert fa.status_string(12345) == "unknown fa_status"
     assert fa.version() >= 100
@@ -244,6 +244,50 @@ def test_splitkv_valid_call_without_gpu_reports_no_device():
     assert splitkv_call() == fa.FA_ERR_NO_DEVICE
     n = ctypes.c_int(0)
     assert fa.load().fa_splitkv_auto_splits(1, 8, 1, 4096, 128, ctypes.byref(n)) == fa.FA_ERR_NO_DEVICE
+
+
+def splitkv_noalloc_call(**kw):
+    a = dict(B=1, H=8, H_kv=2, S_q=1, S_k=4096, D=128, D_v=128, scale=0.1, causal=1, splits=4)
+    a.update(kw)
+    return fa.load().fa_fwd_splitkv_noalloc(A, A, A, A, A, a["B"], a["H"], a["H_kv"], a["S_q"],
+                                            a["S_k"], a["D"], a["D_v"], a["scale"], a["causal"],
+                                            None, None, a["splits"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(splits=0), fa.FA_ERR_INVALID_ARG),
+    (dict(splits=65), fa.FA_ERR_INVALID_ARG),
+    (dict(H_kv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(D=96, D_v=96), fa.FA_ERR_UNSUPPORTED),
+    # 64 splits x 32 x 1 x 32 rows x 129 floats = 33.8 MB > the 16 MiB scratch
+    (dict(B=32, H=32, H_kv=8, S_k=8192, splits=64), fa.FA_ERR_TOO_LARGE),
+])
+def test_splitkv_noalloc_validation_rejects(kw, expect):
+    assert splitkv_noalloc_call(**kw) == expect
+
+
+def test_splitkv_noalloc_limit_matches_workspace_size():
+    """The scratch limit is checked against the same byte count the
+    workspace variant asks for: the largest batch that fits is accepted (it
+    reaches the device check), one more sequence is refused."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lib = fa.load()
+    per_seq = lib.fa_splitkv_workspace_size(1, 32, 1, 8192, 128, 64)
+    fit = fa.SPLITKV_SCRATCH_BYTES // per_seq
+    assert lib.fa_splitkv_workspace_size(fit, 32, 1, 8192, 128, 64) <= fa.SPLITKV_SCRATCH_BYTES
+    assert splitkv_noalloc_call(B=fit, H=32, H_kv=8, S_k=8192, splits=64) == fa.FA_ERR_NO_DEVICE
+    assert splitkv_noalloc_call(B=fit + 1, H=32, H_kv=8, S_k=8192, splits=64) == fa.FA_ERR_TOO_LARGE
+    # one split needs no scratch at any size
+    assert splitkv_noalloc_call(B=4096, H=32, H_kv=8, S_k=8192, splits=1) == fa.FA_ERR_NO_DEVICE
+
+
+def test_binding_static_workspace_needs_splits():
+    import torch
+    q = torch.zeros(1, 1, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="only with num_splits"):
+        fa.attention(q, q, q, workspace="static")
 
 
 def bwd_general_call(**kw):

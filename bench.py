@@ -21,6 +21,13 @@ bounded sample of query rows of the same workload on the host cores.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --backward [--table]     # the backward pass (fa_bwd_general)
+  python bench.py --mfma-ceiling           # the matrix-unit ceiling alone
+
+After the timed steps the bench line also carries the measured ceiling
+(roofline.attainable, fa_mfma_ceiling): the forward's own product sequence
+alone on every CU, operands in registers, and its clock; frac_of_attainable
+is the kernel's rate against it (the lds_fed figures read the operands from
+LDS as the forward does).
 """
 from __future__ import annotations
 
@@ -261,6 +268,26 @@ def cpu_baseline(w, inputs, target_s=15.0):
     }
 
 
+CEILING_BLOCKS = 8192   # 64-key blocks per wave: about 10 ms per ceiling launch
+
+
+def settle_ceiling(fa, seconds):
+    """Untimed ceiling launches for about this many seconds (clock settle)."""
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        fa.mfma_ceiling(0, CEILING_BLOCKS, 5)
+
+
+def ceiling_record(mode, c):
+    return {"mfma_ceiling": "registers" if mode == 0 else "lds_fed",
+            "TFLOP/s": round(c["tflops"], 2), "best_TFLOP/s": round(c["best_tflops"], 2),
+            "ms": round(c["ms"], 4), "cus": c["workers"], "products": c["products"],
+            "clock_mhz": round(c["clock_mhz"], 1),
+            "cycles_per_product": round(c["cycles_per_product"], 2),
+            "frac_of_nominal_peak": round(c["tflops"] / PEAK_BF16_TFLOPS, 4),
+            "peak_at_measured_clock": round(4096 * c["workers"] * c["clock_mhz"] * 1e-6, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,6 +314,11 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fa_bwd) on --workload, or with --table on "
                          "every workload it supports (one JSON line each)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only run the matrix-unit ceiling microbenchmark (the D = 128 "
+                         "forward's product sequence alone, operands in registers and from LDS)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="leave the measured ceiling (roofline.attainable) out of the bench line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times); used to "
                          "scale the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
@@ -313,6 +345,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
+        return
+
+    if args.mfma_ceiling:
+        settle_ceiling(fa, 1.0)
+        for mode in (0, 1):
+            c = fa.mfma_ceiling(mode, CEILING_BLOCKS, 7)
+            print(json.dumps(ceiling_record(mode, c)), flush=True)
         return
 
     if args.gemm_reference:
@@ -400,6 +439,24 @@ def main():
                      "kernel_ms_median": round(r["kernel_ms_median"], 4),
                      "kernel_ms_min": round(r["kernel_ms_min"], 4)},
     }
+    if not args.no_ceiling:
+        # right after the timed steps, at the clock the GPU has settled to
+        c0 = fa.mfma_ceiling(0, CEILING_BLOCKS, 7)
+        c1 = fa.mfma_ceiling(1, CEILING_BLOCKS, 7)
+        rf = out["roofline"]
+        rf["attainable"] = round(c0["tflops"], 2)
+        rf["frac_of_attainable"] = round(achieved / c0["tflops"], 4)
+        rf["attainable_lds_fed"] = round(c1["tflops"], 2)
+        rf["frac_of_attainable_lds_fed"] = round(achieved / c1["tflops"], 4)
+        rf["ceiling"] = {"what": "fa_mfma_ceiling: the forward's 32 products per 64-key block "
+                                 "alone, one 8-wave workgroup per CU",
+                         "cus": c0["workers"],
+                         "clock_mhz": round(c0["clock_mhz"], 1),
+                         "clock_mhz_lds_fed": round(c1["clock_mhz"], 1),
+                         "cycles_per_product": round(c0["cycles_per_product"], 2),
+                         "cycles_per_product_lds_fed": round(c1["cycles_per_product"], 2),
+                         "peak_at_measured_clock": round(
+                             4096 * c0["workers"] * c0["clock_mhz"] * 1e-6, 1)}
     if not args.no_secondary and args.workload == DEFAULT_WORKLOAD:
         w2 = WORKLOADS[SECONDARY_WORKLOAD]
         r2 = time_workload(fa, torch, w2, args.steps, args.warmup, tuning, settle_s=args.settle_s)

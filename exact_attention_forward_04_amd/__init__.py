@@ -41,6 +41,14 @@ class FaError(RuntimeError):
         self.status = status
 
 
+class MfmaRate(ctypes.Structure):
+    """Mirror of struct fa_mfma_rate (include/fa.h)."""
+    _fields_ = [("workers", ctypes.c_int), ("products", ctypes.c_longlong),
+                ("ms", ctypes.c_double), ("tflops", ctypes.c_double),
+                ("best_tflops", ctypes.c_double), ("clock_mhz", ctypes.c_double),
+                ("cycles_per_product", ctypes.c_double)]
+
+
 class Tuning(ctypes.Structure):
     """Mirror of struct fa_tuning (include/fa.h)."""
     _fields_ = [("tau", ctypes.c_float), ("exp2_emu", ctypes.c_int),
@@ -54,7 +62,23 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         _build.build(path)
-    lib = ctypes.CDLL(path)
+    lib = _declare(ctypes.CDLL(path))
+    _lib = lib
+    return lib
+
+
+def load_sync_debug(path: str = _build.SYNC_DEBUG_LIB_PATH):
+    """The race-check build of the forward (FA_SYNC_DEBUG: every wait drains
+    every counter, barriers between the pipeline phases), for tests that
+    compare it bit for bit with load()'s library.  Holds the forward entry
+    points only."""
+    if not os.path.exists(path):
+        _build.build(path, defines=("FA_SYNC_DEBUG",), sources=_build.SYNC_DEBUG_SOURCES)
+    return _declare(ctypes.CDLL(path), backward=False)
+
+
+def _declare(lib, backward: bool = True):
+    """Argument and result types of the library's entry points."""
     P, I, F, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_longlong
     lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P]
     lib.fa_fwd.restype = I
@@ -78,10 +102,11 @@ def load(path: str = LIB_PATH):
     lib.fa_splitkv_auto_splits.restype = I
     lib.fa_splitkv_auto_splits_gqa.argtypes = [I, I, I, I, I, I, ctypes.POINTER(I)]
     lib.fa_splitkv_auto_splits_gqa.restype = I
-    lib.fa_bwd.argtypes = [P] * 10 + [I, I, I, I, I, F, I, P, P]
-    lib.fa_bwd.restype = I
-    lib.fa_bwd_general.argtypes = [P] * 10 + [I, I, I, I, I, I, F, I, P, P, P]
-    lib.fa_bwd_general.restype = I
+    if backward:
+        lib.fa_bwd.argtypes = [P] * 10 + [I, I, I, I, I, F, I, P, P]
+        lib.fa_bwd.restype = I
+        lib.fa_bwd_general.argtypes = [P] * 10 + [I, I, I, I, I, I, F, I, P, P, P]
+        lib.fa_bwd_general.restype = I
     lib.fa_tuning_default.argtypes = []
     lib.fa_tuning_default.restype = Tuning
     lib.fa_exp2_emu.argtypes = [P, P, LL, P]
@@ -96,11 +121,12 @@ def load(path: str = LIB_PATH):
     lib.fa_schedule_general.restype = I
     lib.fa_num_workers.argtypes = [I, ctypes.POINTER(I)]
     lib.fa_num_workers.restype = I
+    lib.fa_mfma_ceiling.argtypes = [I, I, I, ctypes.POINTER(MfmaRate)]
+    lib.fa_mfma_ceiling.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
     lib.fa_version.restype = I
-    _lib = lib
     return lib
 
 
@@ -456,6 +482,17 @@ def num_workers(D: int = 128) -> int:
     n = ctypes.c_int(0)
     _check("fa_num_workers", load().fa_num_workers(D, ctypes.byref(n)))
     return n.value
+
+
+def mfma_ceiling(mode: int = 0, blocks: int = 8192, reps: int = 5) -> dict:
+    """The matrix-unit rate on the D = 128 forward's product sequence alone
+    (fa_mfma_ceiling): mode 0 with operands in registers, mode 1 with K and
+    V^T read from LDS as the forward reads them.  Synchronous; returns the
+    median launch's figures as a dict."""
+    r = MfmaRate()
+    _check("fa_mfma_ceiling", load().fa_mfma_ceiling(int(mode), int(blocks), int(reps),
+                                                     ctypes.byref(r)))
+    return {name: getattr(r, name) for name, _ in MfmaRate._fields_}
 
 
 def version() -> int:

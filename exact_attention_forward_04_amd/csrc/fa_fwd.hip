@@ -50,6 +50,8 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
+#include <algorithm>
 
 #include "fa.h"
 #include "exp2_poly.h"
@@ -644,6 +646,7 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
         __builtin_amdgcn_sched_barrier(0);
         if (it > 0 && wr.useful(it - 1, CAUSAL)) pv_step<D>(st, la, vbuf(it - 1));
         __builtin_amdgcn_s_setprio(0);
+        debug_phase_barrier();
         softmax_phase(cur, it, it);
       }
     } else {
@@ -651,6 +654,7 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
         interval_start(it);
         const bool prev = it > 0 && wr.useful(it - 1, CAUSAL);
         softmax_phase(prev, it - 1, it);
+        debug_phase_barrier();
         __builtin_amdgcn_s_setprio(kMatrixPrio);
         if (it < nblocks && wr.useful(it, CAUSAL)) qk_step<D>(st, la, kbuf(it), kbuf2(it));
         __builtin_amdgcn_sched_barrier(0);
@@ -975,6 +979,109 @@ __global__ __launch_bounds__(256) void fa_split_combine(Args a, int splits) {
 __global__ void exp2_emu_kernel(const float *x, float *y, long long n) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) y[i] = exp2_poly(x[i]);
+}
+
+// ---------------------------------------------------------------------------
+// The matrix-product ceiling of the D = 128 tile body (a measurement, not
+// part of attention).  Every wave of a forward-shaped launch (one
+// workgroup of 8 waves per CU) runs, per 64-key block, the forward's own QK
+// and PV phases (qk_step, pv_step: 32 products of 32x32x16, with operands
+// read from LDS exactly as the forward reads them), or the same product
+// sequence with operands held in registers (REG), and nothing else: no
+// softmax, copies or barriers.  The operands are pseudo-random (K, V and Q
+// uniform on [-2, 2), P on [0, 1)) because the matrix unit's power, and so
+// the clock the chip holds, depends on the data: constant operands run
+// faster than attention's inputs ever could.  Lane 0 of each wave stamps the
+// shader clock (s_memtime) and the constant-rate clock (s_memrealtime)
+// around its loop.
+// ---------------------------------------------------------------------------
+constexpr int kCeilLds = 2 * 64 * 128 * 2;  // one K and one V block of 64 x 128 bf16
+
+// A pseudo-random value in [0, 1) from an integer (a 32-bit integer hash).
+__device__ __forceinline__ float hash_unit(unsigned x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return (float)(x >> 8) * (1.0f / 16777216.0f);
+}
+
+template <bool REG>
+__global__ __launch_bounds__(512, 1) void mfma_ceiling_kernel(int blocks, long long *stamps,
+                                                             float *sink) {
+  __shared__ __attribute__((aligned(16))) char lds_raw[kCeilLds];
+  char LDS_AS *lds = (char LDS_AS *)lds_raw;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const unsigned seed = (unsigned)blockIdx.x * 0x9e3779b9u;
+  for (int i = tid; i < kCeilLds / 2; i += blockDim.x)
+    ((__bf16 LDS_AS *)lds)[i] = (__bf16)(4.0f * hash_unit(seed + (unsigned)i) - 2.0f);
+  LdsAddr<128> la;
+  la.init(lane);
+  WaveState<128> st;
+  bf16x8 kops[8], vops[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const unsigned base = seed + 0x10000u + (unsigned)(tid * 64 + e);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      kops[r][e] = (__bf16)(4.0f * hash_unit(base + 8u * r) - 2.0f);
+      vops[r][e] = (__bf16)(4.0f * hash_unit(base + 8u * r + 4096u) - 2.0f);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) st.p[t][e] = (__bf16)hash_unit(base + 8u * t + 8192u);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) st.qf[s][e] = (__bf16)(4.0f * hash_unit(base + 8u * s + 12288u) - 2.0f);
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st.o[dt][e] = 0.0f;
+  __syncthreads();
+  const long long t0 = (long long)__builtin_amdgcn_s_memtime();
+  const long long r0 = (long long)__builtin_amdgcn_s_memrealtime();
+  for (int j = 0; j < blocks; ++j) {
+    if constexpr (REG) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st.s[kb][e] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        st.s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kops[s], st.qf[s], st.s[0], 0, 0, 0);
+        st.s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kops[7 - s], st.qf[s], st.s[1], 0, 0, 0);
+      }
+    } else {
+      qk_step<128>(st, la, lds, lds);
+    }
+    // the scores are consumed (kept live) without any arithmetic
+    asm volatile("" ::"v"(st.s[0]), "v"(st.s[1]));
+    if constexpr (REG) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vops[(2 * t + dt) & 7], st.p[t],
+                                                             st.o[dt], 0, 0, 0);
+    } else {
+      pv_step<128>(st, la, lds + kCeilLds / 2);
+    }
+  }
+  const long long t1 = (long long)__builtin_amdgcn_s_memtime();
+  const long long r1 = (long long)__builtin_amdgcn_s_memrealtime();
+  float acc = 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc += st.o[dt][e];
+  sink[(size_t)blockIdx.x * blockDim.x + tid] = acc;
+  if (lane == 0) {
+    long long *w = stamps + ((size_t)blockIdx.x * (blockDim.x / kWave) + wave) * 4;
+    w[0] = t0;
+    w[1] = t1;
+    w[2] = r0;
+    w[3] = r1;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1361,6 +1468,82 @@ int fa_exp2_emu(const float *x, float *y, long long n, void *stream) {
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_mfma_ceiling(int mode, int blocks, int reps, fa_mfma_rate *out) {
+  if ((mode != 0 && mode != 1) || blocks < 1 || blocks > (1 << 20) || reps < 1 || reps > 1000 ||
+      !out)
+    return FA_ERR_INVALID_ARG;
+  DeviceInfo *dev = nullptr;
+  int rc = current_device(&dev);
+  if (rc != FA_OK) return rc;
+  int dev_id = 0, wall_khz = 0;
+  if (hipGetDevice(&dev_id) != hipSuccess ||
+      hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev_id) != hipSuccess ||
+      wall_khz <= 0)
+    return FA_ERR_HIP;
+  const int workers = dev->cus;
+  const int waves = workers * 8;
+  long long *stamps = nullptr;
+  float *sink = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  std::vector<double> ms(reps), mhz(reps), cyc(reps);
+  std::vector<long long> host((size_t)waves * 4);
+  rc = FA_ERR_HIP;
+  if (hipMalloc((void **)&stamps, host.size() * sizeof(long long)) != hipSuccess) goto done;
+  if (hipMalloc((void **)&sink, (size_t)workers * 512 * sizeof(float)) != hipSuccess) goto done;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) goto done;
+  for (int r = 0; r < reps; ++r) {
+    hipEventRecord(e0, nullptr);
+    if (mode == 0)
+      hipLaunchKernelGGL(mfma_ceiling_kernel<true>, dim3(workers), dim3(512), 0, nullptr, blocks,
+                         stamps, sink);
+    else
+      hipLaunchKernelGGL(mfma_ceiling_kernel<false>, dim3(workers), dim3(512), 0, nullptr, blocks,
+                         stamps, sink);
+    if (hipGetLastError() != hipSuccess) goto done;
+    hipEventRecord(e1, nullptr);
+    if (hipEventSynchronize(e1) != hipSuccess) goto done;
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, e0, e1) != hipSuccess) goto done;
+    if (hipMemcpy(host.data(), stamps, host.size() * sizeof(long long), hipMemcpyDeviceToHost) !=
+        hipSuccess)
+      goto done;
+    double sclk = 0.0, real = 0.0;
+    for (int w = 0; w < waves; ++w) {
+      sclk += (double)(host[(size_t)w * 4 + 1] - host[(size_t)w * 4 + 0]);
+      real += (double)(host[(size_t)w * 4 + 3] - host[(size_t)w * 4 + 2]);
+    }
+    ms[r] = t;
+    // the shader clock over the waves' loops (s_memtime ticks per second of
+    // the constant-rate clock), and the launch's cycles per product on one
+    // SIMD's matrix unit at that clock (the two waves of a SIMD need not
+    // overlap for their whole loops, so per-wave spans would undercount)
+    mhz[r] = real > 0.0 ? sclk / (real / (wall_khz * 1e3)) / 1e6 : 0.0;
+    cyc[r] = (double)t * 1e-3 * mhz[r] * 1e6 / ((double)waves * blocks * 32.0 / (workers * 4.0));
+  }
+  {
+    // the median launch (by time) and its clock
+    std::vector<int> order(reps);
+    for (int r = 0; r < reps; ++r) order[r] = r;
+    std::sort(order.begin(), order.end(), [&](int x, int y) { return ms[x] < ms[y]; });
+    const int m = order[reps / 2];
+    const double flops = (double)waves * blocks * 32.0 * (2.0 * 32 * 32 * 16);
+    out->workers = workers;
+    out->products = (long long)waves * blocks * 32;
+    out->ms = ms[m];
+    out->tflops = flops / (ms[m] * 1e-3) / 1e12;
+    out->best_tflops = flops / (ms[order[0]] * 1e-3) / 1e12;
+    out->clock_mhz = mhz[m];
+    out->cycles_per_product = cyc[m];
+  }
+  rc = FA_OK;
+done:
+  if (e0) hipEventDestroy(e0);
+  if (e1) hipEventDestroy(e1);
+  if (stamps) hipFree(stamps);
+  if (sink) hipFree(sink);
+  return rc;
+}
+
 int fa_schedule(int B, int H, int S, int D, int causal, const int *cu_seqlens, int workers,
                 int *tiles, int max_rounds, int *rounds_out, int *bm_out) {
   return fa_schedule_gqa(B, H, H, S, D, causal, cu_seqlens, workers, tiles, max_rounds,
@@ -1440,6 +1623,6 @@ const char *fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 107; }
+int fa_version(void) { return 108; }
 
 }  // extern "C"

@@ -39,11 +39,33 @@ __device__ __forceinline__ float sum_halves(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Race-check builds (compiled with FA_SYNC_DEBUG; a second library used only
+// to test this one): every wait below drains every counter, every barrier
+// drains them first, each wave waits for its global->LDS copies right after
+// issuing them, and the ping-pong body adds a barrier between its two
+// phases.  Such a build computes the same values in the same order, so its
+// results must equal the pipelined build's bit for bit; a copy that is read
+// before it lands or overwritten while still being read would show as a
+// difference.
+#ifdef FA_SYNC_DEBUG
+constexpr bool kSyncDebug = true;
+#else
+constexpr bool kSyncDebug = false;
+#endif
+
+__device__ __forceinline__ void drain_all() {
+  asm volatile("s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)" ::: "memory");
+}
+
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  if constexpr (kSyncDebug) {
+    drain_all();
+  } else {
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  }
 }
 
 // Workgroup barrier without a memory fence.  __syncthreads() would also wait
@@ -51,12 +73,25 @@ __device__ __forceinline__ void wait_vmcnt() {
 // block's prefetch; the copies this barrier must cover are waited for
 // explicitly with wait_vmcnt<>() first.  The "memory" clobber keeps the
 // compiler from moving LDS accesses across it.
-__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void barrier_nofence() {
+  if constexpr (kSyncDebug) drain_all();
+  asm volatile("s_barrier" ::: "memory");
+}
 
 // Barrier after this wave's LDS reads of a buffer have all returned, so no
 // read is still queued when another wave's copy starts overwriting it.
 __device__ __forceinline__ void barrier_after_reads() {
+  if constexpr (kSyncDebug) drain_all();
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// A barrier that only race-check builds have (between the ping-pong phases;
+// every wave passes the same number of them).
+__device__ __forceinline__ void debug_phase_barrier() {
+  if constexpr (kSyncDebug) {
+    drain_all();
+    asm volatile("s_barrier" ::: "memory");
+  }
 }
 
 // 16-byte chunk swizzle of an LDS row: chunk c of row r lives at c ^ swz(r).
@@ -179,6 +214,7 @@ struct BlockLoader {
     } else {
       issue_tail(blk, d0, d1, L - 1 - n0, std::make_integer_sequence<int, LOADS>{});
     }
+    if constexpr (kSyncDebug) drain_all();
   }
   template <int... I>
   __device__ __forceinline__ void issue_full(const char *blk, unsigned d0, unsigned d1,

@@ -379,12 +379,52 @@ int fa_schedule_general(int B, int H, int H_kv, int S_q, int D, int causal,
 /* Number of persistent workgroups fa_fwd launches on the current device. */
 int fa_num_workers(int D, int *workers_out);
 
+/*
+ * fa_mfma_ceiling -- a measurement, not attention: the rate the matrix unit
+ * sustains on the forward's own product sequence, against which the
+ * forward's rate is judged (the FlashAttention-4 paper's rate analysis,
+ * section 3.1.1, compares a tile's matrix time with its other work; this
+ * measures the matrix time's floor on the device).
+ *
+ * Launches the D = 128 forward's shape (one workgroup of 8 waves per CU);
+ * every wave runs `blocks` 64-key blocks of its matrix phases only: 32
+ * products of v_mfma_f32_32x32x16_bf16 per block (QK for two 32-key
+ * sub-blocks over 8 k-steps, PV over 4 key steps and 4 d-tiles), with no
+ * softmax, copies or barriers.
+ *   mode 0: operands held in registers (the matrix unit alone);
+ *   mode 1: K and V^T operands read from LDS exactly as the forward reads
+ *           them (the matrix phases as the forward runs them).
+ * Operands are pseudo-random (K, V, Q uniform on [-2, 2), P on [0, 1)): the
+ * matrix unit's power, and so the clock the device sustains, depends on the
+ * data, and constant operands would overstate the ceiling.
+ * Runs `reps` launches on the null stream and waits for them (it allocates
+ * and frees small device buffers; not for use inside a captured stream).
+ * *out receives the median launch (by time): its duration, TFLOP/s
+ * (2*32*32*16 flop per product), the fastest launch's TFLOP/s, the shader
+ * clock over the loop (s_memtime ticks per s_memrealtime second, averaged
+ * over waves) and the cycles per product on one SIMD's matrix unit (launch
+ * duration times that clock over the products per SIMD; 32 is the unit's
+ * issue rate for this instruction).
+ * Returns FA_ERR_INVALID_ARG for mode not 0/1, blocks outside 1..2^20,
+ * reps outside 1..1000 or out == NULL; FA_ERR_NO_DEVICE or FA_ERR_HIP.
+ */
+typedef struct fa_mfma_rate {
+    int workers;                  /* workgroups launched (one per CU) */
+    long long products;           /* matrix products per launch */
+    double ms;                    /* median launch duration */
+    double tflops;                /* rate of the median launch */
+    double best_tflops;           /* rate of the fastest launch */
+    double clock_mhz;             /* shader clock during the median launch */
+    double cycles_per_product;    /* per SIMD, median launch */
+} fa_mfma_rate;
+int fa_mfma_ceiling(int mode, int blocks, int reps, fa_mfma_rate *out);
+
 /* Human-readable name of an fa_status value (static string, never NULL). */
 const char *fa_status_string(int status);
 
 /* Library ABI version: 100 * major + minor (101: fa_fwd_gqa; 102: fa_fwd_hd;
  * 103: fa_fwd_general; 104: fa_bwd; 105: fa_fwd_splitkv; 106: fa_bwd_general;
- * 107: fa_fwd_splitkv_noalloc). */
+ * 107: fa_fwd_splitkv_noalloc; 108: fa_mfma_ceiling). */
 int fa_version(void);
 
 #ifdef __cplusplus

@@ -14,6 +14,8 @@ the reported "o_max_fp64" / "o_mean_fp64" use the literal |O_gpu - O_exact|.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 O_MAX = 1e-2
@@ -89,7 +91,19 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref):
     return st
 
 
+# Figures of every parity check run in this process, in order:
+# (test id, case, kind, statistics).  conftest.py prints them at the end of
+# the pytest session, so a run's log carries each configuration's errors.
+FIGURES = []
+
+
+def record(kind: str, what: str, st: dict) -> None:
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    FIGURES.append((test, str(what), kind, dict(st)))
+
+
 def assert_close(st, what=""):
+    record("forward", what, st)
     assert st["finite"], ("non-finite output", what, st)
     assert st["o_max"] <= O_MAX, ("max |dO|", what, st)
     assert st["o_mean"] <= O_MEAN, ("mean |dO|", what, st)
@@ -127,6 +141,7 @@ def compare_grad(g_gpu, g_ref, mag):
 
 
 def assert_grad_close(st, what=""):
+    record("gradient", what, st)
     assert st["finite"], ("non-finite gradient", what, st)
     assert st["bound_use"] <= 1.0, ("elementwise gradient bound", what, st)
     assert st["rel_rms"] <= GRAD_REL_RMS, ("relative RMS gradient error", what, st)

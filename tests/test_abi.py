@@ -350,3 +350,15 @@ def test_output_buffer_checks():
     for t in bad:
         with pytest.raises(ValueError):
             fa._require_buffer(t, "lse_out", (2, 3, 4), torch.float32, cpu)
+
+
+def test_mfma_ceiling_argument_checks():
+    lib = fa.load()
+    r = fa.MfmaRate()
+    for mode, blocks, reps in ((2, 10, 1), (-1, 10, 1), (0, 0, 1), (0, (1 << 20) + 1, 1),
+                               (0, 10, 0), (1, 10, 1001)):
+        assert lib.fa_mfma_ceiling(mode, blocks, reps, ctypes.byref(r)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_mfma_ceiling(0, 10, 1, None) == fa.FA_ERR_INVALID_ARG
+    import torch
+    if not torch.cuda.is_available():
+        assert lib.fa_mfma_ceiling(0, 10, 1, ctypes.byref(r)) == fa.FA_ERR_NO_DEVICE

@@ -19,7 +19,7 @@ import torch
 import exact_attention_forward_04_amd as fa
 import oracle
 from attn_inputs import WORKLOADS, Workload, make, make_qk, draw_qkv, cu_seqlens_of
-from parity import assert_close, compare, tensor_to_f64
+from parity import assert_close, compare, record, tensor_to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -157,10 +157,13 @@ def test_named_sampled(name, n):
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
 
 
-# ---- every output of the full-size dense workloads against an fp32 reference
+# ---- every output of the full-size workloads against an fp32 reference
 # computed on the GPU with torch (its error, ~1e-6, is far below the gate).  This
 # complements the sampled oracle rows above: the bf16 rounding of P makes the
-# worst output, not a typical one, decide the 1e-2 gate.
+# worst output, not a typical one, decide the 1e-2 gate.  Dense and
+# variable-length batches alike (queries shorter than their keys too): each
+# (sequence, head) in chunks of query rows, the causal mask aligned to the
+# bottom-right corner as the kernel aligns it.
 
 def _cell_distance_t(o_bf16, ref):
     o = o_bf16.float()
@@ -168,39 +171,77 @@ def _cell_distance_t(o_bf16, ref):
     return torch.clamp(torch.maximum(o - ulp / 2 - ref, ref - o - ulp / 2), min=0)
 
 
-@pytest.mark.parametrize("name", ["wide_b2h16s8192d256_spread3", "causal_b2h16s8192d128",
-                                  "dense_b2h16s2048d128", "dense_b2h16s2048d128_causal",
-                                  "gqa_b2h32kv8s8192d128_causal", "hd192v128_b2h16s8192_causal"])
+ALL_OUTPUTS = ["wide_b2h16s8192d256_spread3", "causal_b2h16s8192d128", "dense_b2h16s2048d128",
+               "dense_b2h16s2048d128_causal", "gqa_b2h32kv8s8192d128_causal",
+               "hd192v128_b2h16s8192_causal", "long_b1h16s32768d128_causal",
+               "varlen_16x512to8192_h32d128_causal",
+               "mixed_16x_q1to2048_k512to8192_h16d128_causal"]
+
+
+@pytest.mark.parametrize("name", ALL_OUTPUTS)
 def test_all_outputs_vs_fp32_reference(name):
     w = WORKLOADS[name]
-    q, k, v, cu, S = make(w)
-    note(name, "all outputs vs fp32 reference")
-    o, lse = run_gpu(q, k, v, w.causal, w.scale)
+    note(name, "generating inputs")
+    if w.q_range:
+        q, k, v, cu_q, cu_k, Sq, Sk = make_qk(w)
+    else:
+        q, k, v, cu_q, Sq = make(w)
+        cu_k, Sk = cu_q, Sq
+    H, D, Dv, group = w.H, w.D, w.head_dim_v, w.H // w.kv_heads
     dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
-    worst, total, count, lse_worst = 0.0, 0.0, 0, 0.0
-    group = w.H // w.kv_heads
-    for b in range(w.B):
-        for h in range(w.H):
-            K = dk[b, :, h // group].float().contiguous()
-            Kt = K.t().contiguous()
-            V = dv[b, :, h // group].float().contiguous()
-            for r0 in range(0, w.S, 4096):
-                r1 = min(w.S, r0 + 4096)
-                s = (dq[b, r0:r1, h].float() @ Kt) * w.scale
+    note(name, "gpu run")
+    if cu_q is None:
+        o, lse = fa.attention(dq, dk, dv, causal=w.causal, scale=w.scale)
+        seqs = [(b * Sq, Sq, b * Sk, Sk) for b in range(w.B)]
+        dq, dk, dv = dq.view(-1, H, D), dk.view(-1, w.kv_heads, D), dv.view(-1, w.kv_heads, Dv)
+        o2 = o.view(-1, H, Dv)
+        lse_at = lambda b, h, i0, i1: lse[b, h, i0:i1]                     # noqa: E731
+    else:
+        dcq = torch.from_numpy(np.asarray(cu_q, np.int32)).cuda()
+        dck = torch.from_numpy(np.asarray(cu_k, np.int32)).cuda()
+        o, lse = fa.attention(dq, dk, dv, causal=w.causal, scale=w.scale, cu_seqlens=dcq,
+                              max_seqlen=Sq, cu_seqlens_k=dck, max_seqlen_k=Sk)
+        seqs = [(int(cu_q[b]), int(cu_q[b + 1] - cu_q[b]), int(cu_k[b]), int(cu_k[b + 1] - cu_k[b]))
+                for b in range(len(cu_q) - 1)]
+        o2 = o
+        lse_at = lambda b, h, i0, i1: lse[h, seqs[b][0] + i0:seqs[b][0] + i1]  # noqa: E731
+    torch.cuda.synchronize()
+    worst = worst_bf16 = lse_worst = 0.0
+    total, count = 0.0, 0
+    note(name, "fp32 reference over", len(seqs), "sequences x", H, "heads")
+    for b, (q0, Lq, k0, Lk) in enumerate(seqs):
+        if Lq == 0:
+            continue
+        assert not w.causal or Lk >= Lq, "every query row of these workloads has a key"
+        chunk = max(1, min(4096, (1 << 27) // max(Lk, 1)))
+        for h in range(H):
+            hk = h // group
+            Kt = dk[k0:k0 + Lk, hk].float().t().contiguous()
+            V = dv[k0:k0 + Lk, hk].float().contiguous()
+            for r0 in range(0, Lq, chunk):
+                r1 = min(Lq, r0 + chunk)
+                s = (dq[q0 + r0:q0 + r1, h].float() @ Kt) * w.scale
                 if w.causal:
-                    rows = torch.arange(r0, r1, device="cuda")[:, None]
-                    keys = torch.arange(w.S, device="cuda")[None, :]
+                    rows = torch.arange(r0, r1, device="cuda")[:, None] + (Lk - Lq)
+                    keys = torch.arange(Lk, device="cuda")[None, :]
                     s = s.masked_fill(keys > rows, float("-inf"))
                 m = s.max(dim=1, keepdim=True).values
                 p = torch.exp(s - m)
                 l = p.sum(dim=1, keepdim=True)
                 ref = (p @ V) / l
-                worst = max(worst, _cell_distance_t(o[b, r0:r1, h], ref).max().item())
-                total += (o[b, r0:r1, h].float() - ref).abs().sum().item()
+                og = o2[q0 + r0:q0 + r1, h]
+                worst = max(worst, _cell_distance_t(og, ref).max().item())
+                worst_bf16 = max(worst_bf16, (og.float() - ref.bfloat16().float()).abs().max().item())
+                total += (og.float() - ref).abs().sum().item()
                 count += ref.numel()
                 lse_ref = (m + torch.log(l)).squeeze(1)
-                lse_worst = max(lse_worst, (lse[b, h, r0:r1] - lse_ref).abs().max().item())
-    note(name, "max cell distance %.3e, mean |dO| %.3e, max |dLSE| %.3e" % (worst, total / count, lse_worst))
+                lse_worst = max(lse_worst, (lse_at(b, h, r0, r1) - lse_ref).abs().max().item())
+    st = {"o_max": worst, "o_max_vs_bf16_ref": worst_bf16, "o_mean": total / count,
+          "lse_max": lse_worst, "outputs": count}
+    record("all-outputs", name, st)
+    note(name, "max cell distance %.3e, max vs bf16(ref) %.3e, mean |dO| %.3e, max |dLSE| %.3e "
+         "over %d outputs" % (worst, worst_bf16, total / count, lse_worst, count))
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
     assert worst <= 1e-2 and total / count <= 1e-3 and lse_worst <= 1e-3
 
 

@@ -1,0 +1,128 @@
+"""Race check of the forward's hand-synchronised pipeline.
+
+The forward overlaps global->LDS copies of later key blocks with the matrix
+products and softmax of the current one: copies are issued from inline asm
+that the compiler does not track, waited for with hand-counted
+`s_waitcnt vmcnt(N)`, and published with fenceless barriers.  The
+race-check build (libfa_mi355x_syncdebug.so, compiled with FA_SYNC_DEBUG)
+runs the same kernels with every wait draining every counter, each copy
+waited for as soon as it is issued, and a barrier between the ping-pong
+phases.  Both builds compute the same values in the same order, so a block
+read before its copy landed, or overwritten while another wave still read
+it, would make their outputs differ.  Every case below must be bitwise
+equal, through the C ABI of each library.
+"""
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_forward_04_amd as fa
+from attn_inputs import WORKLOADS, cu_seqlens_of, draw_qkv, make, make_qk
+
+pytestmark = pytest.mark.gpu
+
+
+def note(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def libs():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield fa.load(), fa.load_sync_debug()
+    torch.cuda.synchronize()
+
+
+def run_general(lib, q, k, v, B, H, Hkv, Sq, Sk, D, Dv, causal, cu_q=None, cu_k=None,
+                splits=None):
+    o = torch.full(tuple(q.shape[:-1]) + (Dv,), float("nan"), dtype=torch.bfloat16,
+                   device="cuda")
+    T = q.shape[0]
+    lse_shape = (B, H, Sq) if cu_q is None else (H, T)
+    lse = torch.full(lse_shape, float("nan"), dtype=torch.float32, device="cuda")
+    cq = cu_q.data_ptr() if cu_q is not None else None
+    ck = cu_k.data_ptr() if cu_k is not None else None
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Hkv,
+            Sq, Sk, D, Dv, D ** -0.5, int(causal), cq, ck)
+    if splits is None:
+        rc = lib.fa_fwd_general(*args, stream, None)
+    else:
+        need = lib.fa_splitkv_workspace_size(B, H, Sq, Sk, Dv, splits)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        rc = lib.fa_fwd_splitkv(*args, splits, ws.data_ptr(), ws.numel(), stream)
+        torch.cuda.synchronize()
+    assert rc == fa.FA_OK, fa.status_string(rc)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def assert_same(libs, what, *args, **kw):
+    fast, debug = libs
+    o1, l1 = run_general(fast, *args, **kw)
+    o2, l2 = run_general(debug, *args, **kw)
+    diff = int((o1.view(torch.int16) != o2.view(torch.int16)).sum().item())
+    ldiff = int((l1.view(torch.int32) != l2.view(torch.int32)).sum().item())
+    note(what, "O elements differing", diff, "LSE rows differing", ldiff, "of", o1.numel(),
+         l1.numel())
+    assert diff == 0 and ldiff == 0, what
+
+
+def dense_case(B, S, H, D, Dv, causal, seed, Hkv=None, q_std=1.0):
+    q, k, v = draw_qkv((B, S, H, D), seed, q_std=q_std, kv_heads=Hkv, v_dim=Dv)
+    return [t.cuda() for t in (q, k, v)]
+
+
+@pytest.mark.parametrize("name", ["dense_b2h16s2048d128_causal", "causal_b2h16s8192d128",
+                                  "dense_b2h16s2048d128", "gqa_b2h32kv8s8192d128_causal"])
+def test_race_check_dense_workloads(libs, name):
+    w = WORKLOADS[name]
+    note("race-check", name)
+    q, k, v, _, S = make(w)
+    q, k, v = (t.cuda() for t in (q, k, v))
+    assert_same(libs, name, q, k, v, w.B, w.H, w.kv_heads, S, S, w.D, w.head_dim_v, w.causal)
+
+
+@pytest.mark.parametrize("D,Dv,causal,S", [
+    (192, 128, True, 2000),     # two-part K layout, 3-slot K ring
+    (192, 128, False, 1100),
+    (256, 256, False, 2000),    # the pipelined single-wave body
+    (256, 256, True, 1500),     # the serial body
+    (64, 64, True, 1500),
+])
+def test_race_check_head_dims(libs, D, Dv, causal, S):
+    note("race-check D", D, "Dv", Dv, "causal", causal, "S", S)
+    q, k, v = dense_case(1, S, 4, D, Dv, causal, seed=400 + D + S)
+    assert_same(libs, "D%d/%d causal=%s S=%d" % (D, Dv, causal, S), q, k, v, 1, 4, 4, S, S, D,
+                Dv, causal)
+
+
+def test_race_check_small_varlen(libs):
+    lens = [1, 63, 64, 65, 300, 1000, 2049, 0, 130]
+    cu = cu_seqlens_of(lens)
+    H, D = 4, 128
+    note("race-check varlen", lens)
+    q, k, v = draw_qkv((int(cu[-1]), H, D), seed=410)
+    dcu = torch.from_numpy(np.asarray(cu, np.int32)).cuda()
+    q, k, v = (t.cuda() for t in (q, k, v))
+    assert_same(libs, "varlen", q, k, v, len(lens), H, H, max(lens), max(lens), D, D, True,
+                cu_q=dcu, cu_k=dcu)
+
+
+def test_race_check_mixed_and_splitkv(libs):
+    w = WORKLOADS["mixed_16x_q1to2048_k512to8192_h16d128_causal"]
+    note("race-check mixed")
+    q, k, v, cu_q, cu_k, Sq, Sk = make_qk(w)
+    dq, dk, dv = (t.cuda() for t in (q, k, v))
+    dcq = torch.from_numpy(cu_q).cuda()
+    dck = torch.from_numpy(cu_k).cuda()
+    B = len(cu_q) - 1
+    assert_same(libs, "mixed", dq, dk, dv, B, w.H, w.kv_heads, Sq, Sk, w.D, w.D, True,
+                cu_q=dcq, cu_k=dck)
+    assert_same(libs, "mixed split-KV x4", dq, dk, dv, B, w.H, w.kv_heads, Sq, Sk, w.D, w.D,
+                True, cu_q=dcq, cu_k=dck, splits=4)

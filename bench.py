@@ -172,14 +172,16 @@ def time_workload(fa, torch, w, steps, warmup, tuning=None, num_splits=None, set
 BACKWARD_WORKLOADS = ["causal_b2h16s8192d128", "long_b1h16s32768d128_causal",
                       "dense_b2h16s2048d128", "dense_b2h16s2048d128_causal",
                       "gqa_b2h32kv8s8192d128_causal", "varlen_16x512to8192_h32d128_causal",
-                      "smoke_b1h8s512d64_causal", "mixed_16x_q1to2048_k512to8192_h16d128_causal"]
+                      "smoke_b1h8s512d64_causal", "mixed_16x_q1to2048_k512to8192_h16d128_causal",
+                      "wide_b2h16s8192d256_spread3", "hd192v128_b2h16s8192_causal"]
 
 
 def time_backward(fa, torch, w, steps, warmup, settle_s=0.0):
-    """Time fa_bwd_general (its dQ kernel and its dK/dV kernel) on a workload,
-    after one forward launch that provides o and lse.  Flops follow the usual
-    backward convention: 2.5x the forward's (five products of the forward's
-    size per block: S, dP, dV, dQ, dK)."""
+    """Time the backward (fa_bwd_general, or fa_bwd_hd for the (192, 128) head
+    dimensions: its dQ kernel and its dK/dV kernel) on a workload, after one
+    forward launch that provides o and lse.  Flops follow the usual backward
+    convention: five products per block (S, dP, dV, dQ, dK), 2.5x the
+    forward's when D_v = D."""
     from attn_inputs import draw_dout, flops, make, make_qk
     dev = torch.device("cuda:0")
     dcu_k, ms_k = None, None
@@ -193,7 +195,7 @@ def time_backward(fa, torch, w, steps, warmup, settle_s=0.0):
     ms = S if cu is not None else None
     o, lse = fa.attention(dq_, dk_, dv_, causal=w.causal, scale=w.scale, cu_seqlens=dcu,
                           max_seqlen=ms, cu_seqlens_k=dcu_k, max_seqlen_k=ms_k)
-    g = draw_dout(tuple(q.shape), w.seed).to(dev)
+    g = draw_dout(tuple(o.shape), w.seed).to(dev)
     gq, gk, gv = torch.empty_like(dq_), torch.empty_like(dk_), torch.empty_like(dv_)
     delta = torch.empty_like(lse)
 
@@ -217,7 +219,10 @@ def time_backward(fa, torch, w, steps, warmup, settle_s=0.0):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
-    fl = 2.5 * flops(w, None if w.q_range else cu)
+    # five products per block: S and dQ, dK contract or produce D-wide rows,
+    # dP and dV D_v-wide ones (2.5x the forward when D_v = D)
+    D, Dv = w.D, w.head_dim_v
+    fl = flops(w, None if w.q_range else cu) * (3 * D + 2 * Dv) / (D + Dv)
     return {"workload": w.name, "pass": "backward", "flops": fl,
             "ms_per_step": round(wall * 1e3 / steps, 4),
             "kernel_ms_mean": round(float(np.mean(kernel_ms)), 4),

@@ -107,6 +107,8 @@ def _declare(lib, backward: bool = True):
         lib.fa_bwd.restype = I
         lib.fa_bwd_general.argtypes = [P] * 10 + [I, I, I, I, I, I, F, I, P, P, P]
         lib.fa_bwd_general.restype = I
+        lib.fa_bwd_hd.argtypes = [P] * 10 + [I, I, I, I, I, I, I, F, I, P, P, P]
+        lib.fa_bwd_hd.restype = I
     lib.fa_tuning_default.argtypes = []
     lib.fa_tuning_default.restype = Tuning
     lib.fa_exp2_emu.argtypes = [P, P, LL, P]
@@ -303,12 +305,13 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False,
                        scale: Optional[float] = None, cu_seqlens=None,
                        max_seqlen: Optional[int] = None, dq=None, dk=None, dv=None, delta=None,
                        stream=None, cu_seqlens_k=None, max_seqlen_k: Optional[int] = None):
-    """Exact attention backward on the GPU (the fa_bwd_general entry point).
+    """Exact attention backward on the GPU (the fa_bwd_general entry point, or
+    fa_bwd_hd when v's head dimension D_v differs from q's D).
 
     q, k, v, causal, scale, cu_seqlens, max_seqlen, cu_seqlens_k and
-    max_seqlen_k as given to attention() (D_v = D; query and key lengths may
-    differ, causal masks aligned to the bottom-right corner); o and lse its
-    outputs; dout the
+    max_seqlen_k as given to attention() (query and key lengths may differ,
+    causal masks aligned to the bottom-right corner; (D, D_v) one of (64, 64),
+    (128, 128), (256, 256), (192, 128)); o and lse its outputs; dout the
     gradient with respect to o (o's shape, contiguous bf16).  Returns
     (dq, dk, dv) shaped like q, k, v (bf16).  dq/dk/dv/delta may be passed
     in to reuse buffers (delta: fp32 scratch of lse's shape).
@@ -324,11 +327,14 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False,
     nd = 4 if dense else 3
     if any(t.dim() != nd for t in (q, k, v, o, dout)):
         raise ValueError("dense inputs are [B, S, H, D]" if dense else "varlen inputs are [T, H, D]")
-    if tuple(k.shape) != tuple(v.shape) or k.shape[:-3] != q.shape[:-3] or \
-            k.shape[-1] != q.shape[-1] or tuple(o.shape) != tuple(q.shape) or \
-            tuple(dout.shape) != tuple(q.shape):
-        raise ValueError("q, o, dout must share a shape; k, v another with the same batch and D")
+    o_shape = tuple(q.shape[:-1]) + (v.shape[-1],)
+    if tuple(k.shape[:-1]) != tuple(v.shape[:-1]) or k.shape[:-3] != q.shape[:-3] or \
+            k.shape[-1] != q.shape[-1] or tuple(o.shape) != o_shape or \
+            tuple(dout.shape) != o_shape:
+        raise ValueError("o and dout must be q's shape with v's head dimension; k, v must share "
+                         "their leading shape, and k q's batch and head dimension")
     H, D, H_kv = q.shape[-2], q.shape[-1], k.shape[-2]
+    D_v = v.shape[-1]
     if H_kv < 1 or H % H_kv != 0:
         raise ValueError("the K/V head count must divide the query head count")
     if dense:
@@ -370,11 +376,16 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False,
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         _require_buffer(t, name, ref.shape, torch.bfloat16, q.device)
     _require_buffer(delta, "delta", lse_shape, torch.float32, q.device)
-    rc = lib.fa_bwd_general(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                            dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                            dv.data_ptr(), delta.data_ptr(), B, H, H_kv, S, S_k, D, float(scale),
-                            int(bool(causal)), cu_ptr, cu_k_ptr, _stream_ptr(stream))
-    _check("fa_bwd_general", rc)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr())
+    if D_v == D:
+        rc = lib.fa_bwd_general(*ptrs, B, H, H_kv, S, S_k, D, float(scale), int(bool(causal)),
+                                cu_ptr, cu_k_ptr, _stream_ptr(stream))
+        _check("fa_bwd_general", rc)
+    else:
+        rc = lib.fa_bwd_hd(*ptrs, B, H, H_kv, S, S_k, D, D_v, float(scale), int(bool(causal)),
+                           cu_ptr, cu_k_ptr, _stream_ptr(stream))
+        _check("fa_bwd_hd", rc)
     return dq, dk, dv
 
 
@@ -411,9 +422,10 @@ _attention_fn = None
 def attention_fn(q, k, v, causal: bool = False, scale: Optional[float] = None,
                  cu_seqlens=None, max_seqlen: Optional[int] = None, cu_seqlens_k=None,
                  max_seqlen_k: Optional[int] = None):
-    """attention() as a differentiable torch op (D_v = D): returns o, and
-    o.backward() computes the input gradients with fa_bwd_general.  Query and
-    key lengths may differ as in attention()."""
+    """attention() as a differentiable torch op: returns o, and o.backward()
+    computes the input gradients with fa_bwd_general (fa_bwd_hd for the
+    (192, 128) head dimensions).  Query and key lengths may differ as in
+    attention()."""
     global _attention_fn
     if _attention_fn is None:
         _attention_fn = _autograd_function()

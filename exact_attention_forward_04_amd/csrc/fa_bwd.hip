@@ -668,11 +668,407 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
 }
 
 // ---------------------------------------------------------------------------
+// Wide heads: D = 256, and D = 192 with D_v = 128 (the pair of DeepSeek V3
+// the FlashAttention-4 paper benchmarks, section 5.1).  A wave's operands
+// and accumulators need more than the 256 registers of two waves per SIMD,
+// so both kernels run one wave per SIMD (4 waves, 128-row tiles) and the
+// compiler places what does not fit in VGPRs in AGPRs.  The streamed blocks
+// use a two-slot LDS ring copied one block ahead: the copy of block j+1
+// starts right after the barrier that opens block j, into the slot of block
+// j-1, which every wave finished reading before that barrier.  The dK/dV
+// kernel for D = 256 splits dK's and dV's columns over two workgroups per
+// key tile (each recomputes S and dP); that keeps its accumulators in the
+// register file.
+// ---------------------------------------------------------------------------
+template <int D>
+struct WideCfg {
+  static constexpr int DV = head_dim_v<D>();
+  static constexpr int NW = 4;
+  static constexpr int BM = 32 * NW;  // query rows per dQ tile
+  static constexpr int BN = 32 * NW;  // keys per dK/dV tile
+  static constexpr int DSPLIT = (D == 256) ? 2 : 1;  // dK/dV column parts per key tile
+  // One slot holds a D-wide block (K or Q; D = 192 in two parts, 128 and 64
+  // wide) and a DV-wide block (V or dO).  Every part starts at a multiple of
+  // its own size, as the operand addressing needs.
+  static constexpr int W1 = (D == 192) ? 128 : D;
+  static constexpr int P1 = W1 * kBN * 2;
+  static constexpr int P2 = (D == 192) ? 64 * kBN * 2 : 0;
+  static constexpr int PV = DV * kBN * 2;
+  static constexpr int OFF2 = P1;
+  static constexpr int OFFV = ((P1 + P2 + PV - 1) / PV) * PV;
+  static constexpr int SLOT = ((OFFV + PV + P1 - 1) / P1) * P1;
+  static constexpr int STATS = 2 * kBN * 4;  // LSE and Delta of one block
+  static constexpr int LDS_DQ = 2 * SLOT;
+  static constexpr int LDS_KV = 2 * SLOT + 2 * STATS;
+  static_assert(SLOT % P1 == 0 && SLOT % PV == 0 && OFFV % PV == 0, "part alignment");
+  static_assert(LDS_KV <= 160 * 1024, "LDS");
+};
+
+// Operand reads of one slot: rows (A operands over a 32-row sub-block kb
+// and a 16-wide k-step s) and transposed reads (A operands over a 16-row
+// step t and a 32-wide d tile dt) of its D-wide and DV-wide blocks.
+template <int D>
+struct WideOps {
+  static constexpr int DV = head_dim_v<D>();
+  static constexpr int W1 = WideCfg<D>::W1;
+  unsigned r1, r2, rv, t1a, t1b, t2a, t2b, tva, tvb;
+  __device__ __forceinline__ void init(int lane) {
+    r1 = k_lane_const<W1>(lane);
+    r2 = (D == 192) ? k_lane_const<64>(lane) : 0u;
+    rv = k_lane_const<DV>(lane);
+    LdsAddr<W1> l1;
+    l1.init(lane);
+    t1a = l1.vw0;
+    t1b = l1.vw1;
+    LdsAddr<64> l2;
+    l2.init(lane);
+    t2a = l2.vw0;
+    t2b = l2.vw1;
+    LdsAddr<DV> lv;
+    lv.init(lane);
+    tva = lv.vw0;
+    tvb = lv.vw1;
+  }
+  // b1, b2: the D-wide block's parts; bv: the DV-wide block (LDS byte addresses)
+  __device__ __forceinline__ bf16x8 row_d(unsigned b1, unsigned b2, int kb, int s) const {
+    if constexpr (D == 192) {
+      if (s >= 8) return read_k<64>(r2 + b2, kb, s - 8);
+    }
+    return read_k<W1>(r1 + b1, kb, s);
+  }
+  __device__ __forceinline__ bf16x8 row_v(unsigned bv, int kb, int s) const {
+    return read_k<DV>(rv + bv, kb, s);
+  }
+  __device__ __forceinline__ bf16x8 tr_d(unsigned b1, unsigned b2, int t, int dt) const {
+    if constexpr (D == 192) {
+      if (dt >= 4) return read_vt<64>(t2a + b2, t2b + b2, t, dt - 4);
+    }
+    return read_vt<W1>(t1a + b1, t1b + b1, t, dt);
+  }
+  __device__ __forceinline__ bf16x8 tr_v(unsigned bv, int t, int dt) const {
+    return read_vt<DV>(tva + bv, tvb + bv, t, dt);
+  }
+};
+
+// Store NT transposed accumulator tiles (as store_rows) times f as bf16
+// into the lane's output row from column 0 of row_ptr.
+template <int NT>
+__device__ __forceinline__ void store_tiles(__bf16 *row_ptr, const f32x16 *acc, float f, int hh) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  __bf16 *op = row_ptr + 4 * hh;
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x4 out = {(__bf16)(acc[dt][4 * i + 0] * f), (__bf16)(acc[dt][4 * i + 1] * f),
+                    (__bf16)(acc[dt][4 * i + 2] * f), (__bf16)(acc[dt][4 * i + 3] * f)};
+      *(bf16x4 *)(op + 32 * dt + 8 * i) = out;
+    }
+}
+
+// dQ (and Delta) for wide heads: as fa_bwd_dq, one wave per SIMD.
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(WideCfg<D>::NW * kWave, 1) void fa_bwd_dq_wide(BwdArgs a) {
+  using C = WideCfg<D>;
+  constexpr int DV = C::DV;
+  constexpr int NW = C::NW;
+  constexpr int NS = D / 16, NSV = DV / 16, NT = D / 32;
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  char LDS_AS *lds = (char LDS_AS *)lds_raw;
+
+  const int nmb = fa::ceil_div(a.S, C::BM);
+  const int BH = a.B * a.H;
+  int bh, r;
+  bwd_slot(blockIdx.x, BH, bwd_chunked(VARLEN, BH), &bh, &r);
+  if (r >= nmb) return;  // grid padding
+  const int mb = CAUSAL ? nmb - 1 - r : r;
+  const int b = bh / a.H, h = bh % a.H;
+  const Span sp = seq_of<VARLEN>(a, b);
+  const int L = sp.L;
+  const int m0 = mb * C::BM;
+  if (m0 >= L) return;  // workgroup-uniform
+  const Span spk = kseq_of<VARLEN>(a, b);
+  const int Lk = spk.L;
+  const int koff = Lk - L;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int hh = lane >> 5;
+  const int hk = h / (a.H / a.Hkv);
+  const int wrow0 = m0 + 32 * wave;
+  const bool active = wrow0 < L;
+  const int wrow_last = (wrow0 + 31 < L - 1) ? wrow0 + 31 : L - 1;
+  const int row = wrow0 + (lane & 31);
+  const int rowc = row < L ? row : L - 1;
+
+  // Q (D wide) and dO (DV wide) rows as B operands; Delta = <dO, O>.
+  bf16x8 qf[NS], gf[NSV];
+  float delta, lse2;
+  {
+    const long long si = stat_index<VARLEN>(a, b, h, sp.tok0, rowc);
+    lse2 = a.lse[si] * kLog2e;
+    const long long tok = (sp.tok0 + rowc) * a.H + h;
+    const bf16x8 *qp = (const bf16x8 *)(a.q + tok * D + 8 * hh);
+    const bf16x8 *gp = (const bf16x8 *)(a.dout + tok * DV + 8 * hh);
+    const bf16x8 *op = (const bf16x8 *)(a.o + tok * DV + 8 * hh);
+    float dsum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = qp[2 * s];
+#pragma unroll
+    for (int s = 0; s < NSV; ++s) {
+      gf[s] = gp[2 * s];
+      const bf16x8 of = op[2 * s];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)gf[s][e], (float)of[e], dsum);
+    }
+    delta = sum_halves(dsum);
+    if (hh == 0 && row < L) a.delta[si] = delta;
+  }
+
+  int n_end = Lk;
+  if (CAUSAL) n_end = (m0 + C::BM + koff < Lk) ? m0 + C::BM + koff : Lk;
+  if (n_end < 0) n_end = 0;
+  const int nblocks = fa::ceil_div(n_end, kBN);
+
+  BlockLoader<D, NW> ldk;
+  ldk.init(a.Hkv, wave, lane);
+  BlockLoader<DV, NW> ldv;
+  ldv.init(a.Hkv, wave, lane);
+  WideOps<D> ops;
+  ops.init(lane);
+  auto slot = [&](int j) { return lds + (j & 1) * C::SLOT; };
+  auto issue = [&](int j) {
+    ldk.issue(a.k, spk.tok0, a.Hkv, hk, j * kBN, Lk, slot(j), slot(j) + C::OFF2);
+    ldv.issue(a.v, spk.tok0, a.Hkv, hk, j * kBN, Lk, slot(j) + C::OFFV);
+  };
+
+  f32x16 acc[NT];
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.0f;
+
+  if (nblocks > 0) issue(0);
+  for (int j = 0; j < nblocks; ++j) {
+    wait_vmcnt<0>();        // this wave's copies of block j have landed
+    barrier_after_reads();  // everyone's have, and block j-1 is read
+    if (j + 1 < nblocks) issue(j + 1);
+    const int n0 = j * kBN;
+    if (active && (!CAUSAL || n0 <= wrow_last + koff)) {
+      const unsigned b1 = lds_u32(slot(j)), b2 = b1 + C::OFF2, bv = b1 + C::OFFV;
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s[i][e] = 0.0f;
+          dp[i][e] = 0.0f;
+        }
+      // S^T = K Q^T, dP^T = V dO^T
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        s[0] = mfma(ops.row_d(b1, b2, 0, st), qf[st], s[0]);
+        s[1] = mfma(ops.row_d(b1, b2, 1, st), qf[st], s[1]);
+      }
+#pragma unroll
+      for (int st = 0; st < NSV; ++st) {
+        dp[0] = mfma(ops.row_v(bv, 0, st), gf[st], dp[0]);
+        dp[1] = mfma(ops.row_v(bv, 1, st), gf[st], dp[1]);
+      }
+      // P and dS (entry layout and mask as in fa_bwd_dq)
+      const bool need_mask = (n0 + kBN > Lk) || (CAUSAL && n0 + kBN - 1 > wrow0 + koff);
+      const int lim = (CAUSAL ? (row + koff + 1 < Lk ? row + koff + 1 : Lk) : Lk) - n0 - 4 * hh;
+      bf16x8 ds8[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int off = 32 * i + 8 * (e >> 2) + (e & 3);
+          float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -lse2));
+          if (need_mask) p = off < lim ? p : 0.0f;
+          ds8[2 * i + (e >> 3)][e & 7] = (__bf16)(p * (dp[i][e] - delta));
+        }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) acc[dt] = mfma(ops.tr_d(b1, b2, t, dt), ds8[t], acc[dt]);
+    }
+  }
+
+  if (active && row < L)
+    store_tiles<NT>(a.dq + ((sp.tok0 + row) * a.H + h) * (long long)D, acc, a.scale, hh);
+}
+
+// dK and dV for wide heads: as fa_bwd_dkdv, with column part `part` of
+// DSPLIT of dK and dV per workgroup.
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(WideCfg<D>::NW * kWave, 1) void fa_bwd_dkdv_wide(BwdArgs a) {
+  using C = WideCfg<D>;
+  constexpr int DV = C::DV;
+  constexpr int NW = C::NW;
+  constexpr int DS = C::DSPLIT;
+  constexpr int NS = D / 16, NSV = DV / 16;
+  constexpr int NTK = D / 32 / DS, NTV = DV / 32 / DS;
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  char LDS_AS *lds = (char LDS_AS *)lds_raw;
+
+  // Launch slot -> (tile slot, column part): the DS parts of one key tile
+  // are 8 slots apart, on the same XCD, so they share their Q/dO in its L2.
+  int part = 0, tslot = blockIdx.x;
+  if constexpr (DS > 1) {
+    const int x = blockIdx.x % 8, q = blockIdx.x / 8;
+    part = q % DS;
+    tslot = (q / DS) * 8 + x;
+  }
+  const int BK = a.B * a.Hkv;
+  int bhk, nb;
+  bwd_slot(tslot, BK, bwd_chunked(VARLEN, BK), &bhk, &nb);
+  if (bhk >= BK || nb >= fa::ceil_div(a.Sk, C::BN)) return;  // grid padding
+  const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const Span spk = kseq_of<VARLEN>(a, b);
+  const int Lk = spk.L;
+  const int n0t = nb * C::BN;
+  if (n0t >= Lk) return;
+  const Span sp = seq_of<VARLEN>(a, b);
+  const int L = sp.L;
+  const int koff = Lk - L;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int hh = lane >> 5;
+  const int G = a.H / a.Hkv;
+  const int key0 = n0t + 32 * wave;
+  const bool active = key0 < Lk;
+  const int key = key0 + (lane & 31);
+  const int keyc = key < Lk ? key : Lk - 1;
+
+  // K (D wide) and V (DV wide) rows of the lane's key as B operands.
+  bf16x8 kf[NS], vf[NSV];
+  {
+    const long long tok = (spk.tok0 + keyc) * a.Hkv + hk;
+    const bf16x8 *kp = (const bf16x8 *)(a.k + tok * D + 8 * hh);
+    const bf16x8 *vp = (const bf16x8 *)(a.v + tok * DV + 8 * hh);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf[s] = kp[2 * s];
+#pragma unroll
+    for (int s = 0; s < NSV; ++s) vf[s] = vp[2 * s];
+  }
+
+  const int nqb = fa::ceil_div(L, kBN);
+  const int qb0 = CAUSAL ? (n0t - koff > 0 ? n0t - koff : 0) / kBN : 0;
+  const int per = nqb > qb0 ? nqb - qb0 : 0;
+  const int nblocks = G * per;
+
+  BlockLoader<D, NW> ldq;
+  ldq.init(a.H, wave, lane);
+  BlockLoader<DV, NW> ldg;
+  ldg.init(a.H, wave, lane);
+  WideOps<D> ops;
+  ops.init(lane);
+  auto slot = [&](int t) { return lds + (t & 1) * C::SLOT; };
+  auto sbuf = [&](int t) { return lds + 2 * C::SLOT + (t & 1) * C::STATS; };
+  auto issue = [&](int t) {
+    const int h = hk * G + t / per;
+    const int m0 = (qb0 + t % per) * kBN;
+    ldq.issue(a.q, sp.tok0, a.H, h, m0, L, slot(t), slot(t) + C::OFF2);
+    ldg.issue(a.dout, sp.tok0, a.H, h, m0, L, slot(t) + C::OFFV);
+    if (wave < 2) {
+      const int rr = m0 + lane < L ? m0 + lane : L - 1;
+      const float *src = (wave == 0 ? a.lse : a.delta) + stat_index<VARLEN>(a, b, h, sp.tok0, rr);
+      dma4(src, lds_u32(sbuf(t)) + (unsigned)wave * (kBN * 4));
+    }
+  };
+
+  f32x16 dk[NTK], dv[NTV];
+#pragma unroll
+  for (int dt = 0; dt < NTK; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dk[dt][e] = 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < NTV; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dv[dt][e] = 0.0f;
+
+  if (nblocks > 0) issue(0);
+  for (int t = 0; t < nblocks; ++t) {
+    wait_vmcnt<0>();
+    barrier_after_reads();
+    if (t + 1 < nblocks) issue(t + 1);
+    const int m0 = (qb0 + t % per) * kBN;
+    if (active && (!CAUSAL || m0 + kBN - 1 >= key0 - koff)) {
+      const unsigned b1 = lds_u32(slot(t)), b2 = b1 + C::OFF2, bv = b1 + C::OFFV;
+      const float LDS_AS *lse_l = (const float LDS_AS *)sbuf(t);
+      const float LDS_AS *del_l = lse_l + kBN;
+      const bool need_mask = (m0 + kBN > L) || (CAUSAL && m0 < key0 - koff + 31);
+      const int hi = need_mask ? L - m0 - 4 * hh : INT_MAX;
+      const int lo = (need_mask && CAUSAL) ? key - koff - m0 - 4 * hh : INT_MIN;
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s[i][e] = 0.0f;
+          dp[i][e] = 0.0f;
+        }
+      // S = Q K^T, dP = dO V^T for query sub-blocks 0 and 1
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        s[0] = mfma(ops.row_d(b1, b2, 0, st), kf[st], s[0]);
+        s[1] = mfma(ops.row_d(b1, b2, 1, st), kf[st], s[1]);
+      }
+#pragma unroll
+      for (int st = 0; st < NSV; ++st) {
+        dp[0] = mfma(ops.row_v(bv, 0, st), vf[st], dp[0]);
+        dp[1] = mfma(ops.row_v(bv, 1, st), vf[st], dp[1]);
+      }
+      // P and dS (entry layout and mask as in fa_bwd_dkdv)
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      bf16x8 p8[4], ds8[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int r0 = 32 * i + 8 * g4 + 4 * hh;
+          const f32x4 l4 = *(const f32x4 LDS_AS *)(lse_l + r0);
+          const f32x4 d4 = *(const f32x4 LDS_AS *)(del_l + r0);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int e = 4 * g4 + jj;
+            const int off = 32 * i + 8 * g4 + jj;
+            float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -(l4[jj] * kLog2e)));
+            p = (off < hi && off >= lo) ? p : 0.0f;
+            const int tt = 2 * i + (e >> 3);
+            p8[tt][e & 7] = (__bf16)p;
+            ds8[tt][e & 7] = (__bf16)(p * (dp[i][e] - d4[jj]));
+          }
+        }
+      // dV^T += dO^T P and dK^T += Q^T dS over this part's d tiles
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int dt = 0; dt < NTV; ++dt)
+          dv[dt] = mfma(ops.tr_v(bv, tt, part * NTV + dt), p8[tt], dv[dt]);
+#pragma unroll
+        for (int dt = 0; dt < NTK; ++dt)
+          dk[dt] = mfma(ops.tr_d(b1, b2, tt, part * NTK + dt), ds8[tt], dk[dt]);
+      }
+    }
+  }
+
+  if (active && key < Lk) {
+    const long long tok = (spk.tok0 + key) * a.Hkv + hk;
+    store_tiles<NTK>(a.dk + tok * D + 32 * NTK * part, dk, a.scale, hh);
+    store_tiles<NTV>(a.dv + tok * DV + 32 * NTV * part, dv, 1.0f, hh);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 int validate_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
                  const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
-                 int Hkv, int S, int Sk, int D, float scale, int causal, const int *cu_q,
+                 int Hkv, int S, int Sk, int D, int Dv, float scale, int causal, const int *cu_q,
                  const int *cu_k) {
   const void *bufs[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void *p : bufs)
@@ -680,12 +1076,13 @@ int validate_bwd(const void *q, const void *k, const void *v, const void *o, con
   if (!lse || !delta) return FA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(lse) & 3) || (reinterpret_cast<uintptr_t>(delta) & 3))
     return FA_ERR_INVALID_ARG;
-  if (B <= 0 || H <= 0 || S <= 0 || Sk <= 0 || D <= 0) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || S <= 0 || Sk <= 0 || D <= 0 || Dv <= 0) return FA_ERR_INVALID_ARG;
   if ((cu_q == nullptr) != (cu_k == nullptr)) return FA_ERR_INVALID_ARG;
   if (Hkv <= 0 || H % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  const bool pair_ok = (D == Dv && (D == 64 || D == 128 || D == 256)) || (D == 192 && Dv == 128);
+  if (!pair_ok) return FA_ERR_UNSUPPORTED;
   const long long Smax = S > Sk ? S : Sk;
   if ((long long)B * Smax > (1LL << 31) - 1 || Smax * H > (1LL << 31) - 1)
     return FA_ERR_UNSUPPORTED;
@@ -714,6 +1111,34 @@ int launch_bwd(const BwdArgs &a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+template <int D, bool CAUSAL, bool VARLEN>
+int launch_bwd_wide(const BwdArgs &a, hipStream_t st) {
+  using C = WideCfg<D>;
+  auto levels = [](int n, bool chunked) {
+    return chunked ? fa::ceil_div(n, kBwdChunk) * kBwdChunk : n;
+  };
+  const long long g1 = (long long)a.B * a.H *
+                       levels(fa::ceil_div(a.S, C::BM), bwd_chunked(VARLEN, a.B * a.H));
+  long long g2 = (long long)a.B * a.Hkv *
+                 levels(fa::ceil_div(a.Sk, C::BN), bwd_chunked(VARLEN, a.B * a.Hkv));
+  if (C::DSPLIT > 1) g2 = ((g2 + 7) / 8) * 8 * C::DSPLIT;  // whole groups of 8 tile slots
+  if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  auto k1 = fa_bwd_dq_wide<D, CAUSAL, VARLEN>;
+  auto k2 = fa_bwd_dkdv_wide<D, CAUSAL, VARLEN>;
+  if (!allow_lds(k1, C::LDS_DQ) || !allow_lds(k2, C::LDS_KV)) return FA_ERR_HIP;
+  hipLaunchKernelGGL(k1, dim3((unsigned)g1), dim3(C::NW * kWave), C::LDS_DQ, st, a);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  hipLaunchKernelGGL(k2, dim3((unsigned)g2), dim3(C::NW * kWave), C::LDS_KV, st, a);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+template <int D>
+int dispatch_bwd_wide(const BwdArgs &a, bool causal, bool varlen, hipStream_t st) {
+  if (causal)
+    return varlen ? launch_bwd_wide<D, true, true>(a, st) : launch_bwd_wide<D, true, false>(a, st);
+  return varlen ? launch_bwd_wide<D, false, true>(a, st) : launch_bwd_wide<D, false, false>(a, st);
+}
+
 template <int D>
 int dispatch_bwd(const BwdArgs &a, bool causal, bool varlen, hipStream_t st) {
   if (causal) return varlen ? launch_bwd<D, true, true>(a, st) : launch_bwd<D, true, false>(a, st);
@@ -724,12 +1149,12 @@ int dispatch_bwd(const BwdArgs &a, bool causal, bool varlen, hipStream_t st) {
 
 extern "C" {
 
-int fa_bwd_general(const void *q, const void *k, const void *v, const void *o, const void *dout,
-                   const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
-                   int H_kv, int S_q, int S_k, int D, float scale, int causal,
-                   const int *cu_seqlens_q, const int *cu_seqlens_k, void *stream) {
-  int rc = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, S_q, S_k, D, scale,
-                        causal, cu_seqlens_q, cu_seqlens_k);
+int fa_bwd_hd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+              const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
+              int H_kv, int S_q, int S_k, int D, int D_v, float scale, int causal,
+              const int *cu_seqlens_q, const int *cu_seqlens_k, void *stream) {
+  int rc = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, S_q, S_k, D, D_v,
+                        scale, causal, cu_seqlens_q, cu_seqlens_k);
   if (rc != FA_OK) return rc;
   DeviceInfo *dev = nullptr;
   rc = current_device(&dev);
@@ -756,8 +1181,20 @@ int fa_bwd_general(const void *q, const void *k, const void *v, const void *o, c
   a.scale = scale;
   hipStream_t st = (hipStream_t)stream;
   const bool varlen = cu_seqlens_q != nullptr;
-  if (D == 64) return dispatch_bwd<64>(a, causal, varlen, st);
-  return dispatch_bwd<128>(a, causal, varlen, st);
+  switch (D) {
+    case 64: return dispatch_bwd<64>(a, causal, varlen, st);
+    case 128: return dispatch_bwd<128>(a, causal, varlen, st);
+    case 192: return dispatch_bwd_wide<192>(a, causal, varlen, st);
+    default: return dispatch_bwd_wide<256>(a, causal, varlen, st);
+  }
+}
+
+int fa_bwd_general(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                   const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
+                   int H_kv, int S_q, int S_k, int D, float scale, int causal,
+                   const int *cu_seqlens_q, const int *cu_seqlens_k, void *stream) {
+  return fa_bwd_hd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, S_q, S_k, D, D, scale,
+                   causal, cu_seqlens_q, cu_seqlens_k, stream);
 }
 
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,

@@ -1623,6 +1623,6 @@ const char *fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 108; }
+int fa_version(void) { return 109; }
 
 }  // extern "C"

@@ -285,7 +285,8 @@ int fa_splitkv_auto_splits_gqa(int B, int H, int H_kv, int S_q, int S_k, int D, 
  * delta is caller-owned scratch that this call fills; dq, dk, dv and delta
  * must not alias any input.  Every gradient row is accumulated by one
  * workgroup in a fixed order, so results are bitwise reproducible, without
- * atomics.  Supported D: 64 and 128.
+ * atomics.  Supported D: 64, 128 and 256 (fa_bwd_hd adds the (192, 128)
+ * pair).
  *
  * Errors (nothing is launched): FA_ERR_INVALID_ARG for a null or misaligned
  * pointer, a size <= 0, H not a multiple of H_kv, a non-finite or
@@ -321,6 +322,20 @@ int fa_bwd_general(const void *q, const void *k, const void *v, const void *o, c
                    const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
                    int H_kv, int S_q, int S_k, int D, float scale, int causal,
                    const int *cu_seqlens_q, const int *cu_seqlens_k, void *stream);
+
+/*
+ * fa_bwd_hd -- fa_bwd_general with a value head dimension D_v of its own,
+ * the backward of fa_fwd_general for every head-dimension pair it serves:
+ * (D, D_v) in {(64, 64), (128, 128), (256, 256), (192, 128)} (the last is
+ * the DeepSeek V3 pair the FlashAttention-4 paper benchmarks, section 5.1).
+ * q, dq [.., H, D]; k, dk [.., H_kv, D]; v, dv [.., H_kv, D_v];
+ * o, dout [.., H, D_v]; otherwise as fa_bwd_general, which is the D_v = D
+ * case.  Another pair is FA_ERR_UNSUPPORTED.
+ */
+int fa_bwd_hd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+              const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
+              int H_kv, int S_q, int S_k, int D, int D_v, float scale, int causal,
+              const int *cu_seqlens_q, const int *cu_seqlens_k, void *stream);
 
 /*
  * fa_exp2_emu -- test hook: y[i] = the device's polynomial 2^x[i] for n
@@ -424,7 +439,7 @@ const char *fa_status_string(int status);
 
 /* Library ABI version: 100 * major + minor (101: fa_fwd_gqa; 102: fa_fwd_hd;
  * 103: fa_fwd_general; 104: fa_bwd; 105: fa_fwd_splitkv; 106: fa_bwd_general;
- * 107: fa_fwd_splitkv_noalloc; 108: fa_mfma_ceiling). */
+ * 107: fa_fwd_splitkv_noalloc; 108: fa_mfma_ceiling; 109: fa_bwd_hd). */
 int fa_version(void);
 
 #ifdef __cplusplus

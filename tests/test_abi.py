@@ -178,8 +178,8 @@ def bwd_call(**kw):
     (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
     (dict(causal=2), fa.FA_ERR_INVALID_ARG),
-    (dict(D=256), fa.FA_ERR_UNSUPPORTED),
-    (dict(D=192), fa.FA_ERR_UNSUPPORTED),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(D=192), fa.FA_ERR_UNSUPPORTED),           # (192, 192): only fa_bwd_hd's (192, 128)
     (dict(S=1 << 30, H=8), fa.FA_ERR_UNSUPPORTED),  # beyond 32-bit row indexing
 ])
 def test_backward_validation_rejects(kw, expect):
@@ -192,6 +192,7 @@ def test_backward_valid_call_without_gpu_reports_no_device():
         pytest.skip("a GPU is present")
     assert bwd_call() == fa.FA_ERR_NO_DEVICE
     assert bwd_call(D=64, H_kv=8, causal=0) == fa.FA_ERR_NO_DEVICE
+    assert bwd_call(D=256) == fa.FA_ERR_NO_DEVICE
 
 
 def test_backward_binding_refuses_cpu_tensors():
@@ -308,11 +309,30 @@ def bwd_general_call(**kw):
     (dict(cu_k=A), fa.FA_ERR_INVALID_ARG),
     (dict(dv=None), fa.FA_ERR_INVALID_ARG),
     (dict(H_kv=3), fa.FA_ERR_INVALID_ARG),
-    (dict(D=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(D=320), fa.FA_ERR_UNSUPPORTED),
     (dict(S_k=1 << 30), fa.FA_ERR_UNSUPPORTED),     # the longer length sets the index bound
 ])
 def test_backward_general_validation_rejects(kw, expect):
     assert bwd_general_call(**kw) == expect
+
+
+def bwd_hd_call(D, Dv):
+    return fa.load().fa_bwd_hd(A, A, A, A, A, A, A, A, A, A, 1, 8, 2, 5, 300, D, Dv, 0.1, 1,
+                               None, None, None)
+
+
+@pytest.mark.parametrize("D,Dv,supported", [
+    (64, 64, True), (128, 128, True), (256, 256, True), (192, 128, True),
+    (192, 192, False), (128, 64, False), (256, 128, False), (96, 96, False),
+])
+def test_backward_head_dim_pairs(D, Dv, supported):
+    import torch
+    rc = bwd_hd_call(D, Dv)
+    if not supported:
+        assert rc == fa.FA_ERR_UNSUPPORTED
+    elif not torch.cuda.is_available():
+        assert rc == fa.FA_ERR_NO_DEVICE
+    assert bwd_hd_call(D, 0) == fa.FA_ERR_INVALID_ARG
 
 
 def test_backward_general_valid_call_without_gpu_reports_no_device():

@@ -4,7 +4,7 @@ fp64 oracle's gradients.
 The forward runs on the GPU first (its o and lse are fa_bwd's inputs, as in
 training); dO is drawn from its own seeded stream.  Small shapes are
 compared element by element on every gradient (several row and key tiles,
-ragged tails, both masks, D = 64 and 128, grouped K/V heads, packed
+ragged tails, both masks, D = 64, 128, 256 and (192, 128), grouped K/V heads, packed
 variable-length batches); the 8k causal shape is compared on sampled query
 and key rows.  The gate, derived from the arithmetic, is in parity.py.
 Run-to-run reproducibility is checked bit for bit.
@@ -321,3 +321,77 @@ def test_backward_chunked_prefill_sampled():
         st = compare_grad(gg, rr, mm)
         note("bwd-chunk", name, st)
         assert_grad_close(st, ("bwd-chunk", name))
+
+
+# ---- wide heads: D = 256 and the (192, 128) pair (one wave per SIMD, dK/dV
+# columns split over two workgroups at D = 256)
+WIDE = [(256, 256), (192, 128)]
+
+
+def _wide_id(d):
+    return "D%dDv%d" % d
+
+
+@pytest.mark.parametrize("dims", WIDE, ids=_wide_id)
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_wide_small(dims, causal):
+    """S = 333: three 128-row query and key tiles, six 64-row blocks, a
+    ragged tail of 13 rows."""
+    D, Dv = dims
+    B, S, H = 2, 333, 2
+    q, k, v = draw_qkv((B, S, H, D), seed=141 + D, v_dim=Dv)
+    g = draw_dout((B, S, H, Dv), seed=141 + D)
+    full_bwd_check(q, k, v, g, causal, D ** -0.5, what="bwd-wide D%d/%d" % dims)
+
+
+@pytest.mark.parametrize("dims", WIDE, ids=_wide_id)
+def test_backward_wide_short_and_grouped(dims):
+    """Sequences below one block, and grouped K/V heads (MQA)."""
+    D, Dv = dims
+    for S in (1, 37):
+        q, k, v = draw_qkv((1, S, 2, D), seed=143 + S, v_dim=Dv)
+        g = draw_dout((1, S, 2, Dv), seed=143 + S)
+        full_bwd_check(q, k, v, g, True, D ** -0.5, what="bwd-wide-short S%d" % S)
+    q, k, v = draw_qkv((1, 200, 4, D), seed=145, kv_heads=1, v_dim=Dv)
+    g = draw_dout((1, 200, 4, Dv), seed=145)
+    full_bwd_check(q, k, v, g, True, D ** -0.5, what="bwd-wide-mqa D%d" % D)
+
+
+@pytest.mark.parametrize("dims", WIDE, ids=_wide_id)
+def test_backward_wide_varlen_and_lengths(dims):
+    """A packed batch, then query and key lengths of their own (a sequence
+    without queries, one without keys, one-query rows)."""
+    D, Dv = dims
+    lengths = [1, 64, 200, 333, 65, 129]
+    cu = cu_seqlens_of(lengths)
+    q, k, v = draw_qkv((int(cu[-1]), 2, D), seed=147, v_dim=Dv)
+    g = draw_dout((int(cu[-1]), 2, Dv), seed=147)
+    full_bwd_check(q, k, v, g, True, D ** -0.5, cu=cu, S=max(lengths),
+                   what="bwd-wide-varlen D%d" % D)
+    lq = [5, 0, 130, 1, 70, 9]
+    lk = [40, 17, 66, 300, 0, 9]
+    cu_q, cu_k = cu_seqlens_of(lq), cu_seqlens_of(lk)
+    q, _, _ = draw_qkv((int(cu_q[-1]), 4, D), seed=149)
+    _, k, v = draw_qkv((int(cu_k[-1]), 4, D), seed=150, kv_heads=2, v_dim=Dv)
+    g = draw_dout((int(cu_q[-1]), 4, Dv), seed=151)
+    got = full_bwd_check_general(q, k, v, g, True, D ** -0.5, cu=cu_q, cu_k=cu_k, S=max(lq),
+                                 S_k=max(lk), what="bwd-wide-qk-varlen D%d" % D)
+    a = int(cu_q[4])
+    assert torch.all(got[0][a:a + lq[4]].float() == 0)
+    c = int(cu_k[1])
+    assert torch.all(got[1][c:c + lk[1]].float() == 0)
+    assert torch.all(got[2][c:c + lk[1]].float() == 0)
+
+
+@pytest.mark.parametrize("dims", WIDE, ids=_wide_id)
+def test_backward_wide_dense_lengths_and_reproducible(dims):
+    """Fewer queries than keys (chunked prefill), bottom-right causal; two
+    runs give identical bits."""
+    D, Dv = dims
+    q, _, _ = draw_qkv((2, 100, 4, D), seed=153)
+    _, k, v = draw_qkv((2, 333, 4, D), seed=154, kv_heads=2, v_dim=Dv)
+    g = draw_dout((2, 100, 4, Dv), seed=155)
+    a = full_bwd_check_general(q, k, v, g, True, D ** -0.5, what="bwd-wide-qk D%d" % D)
+    b = gpu_grads_general(q, k, v, g, True, D ** -0.5)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))

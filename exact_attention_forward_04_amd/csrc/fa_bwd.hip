@@ -1104,6 +1104,11 @@ int launch_bwd(const BwdArgs &a, hipStream_t st) {
   auto k1 = fa_bwd_dq<D, CAUSAL, VARLEN>;
   auto k2 = fa_bwd_dkdv<D, CAUSAL, VARLEN>;
   if (!allow_lds(k1, C::LDS_DQ) || !allow_lds(k2, C::LDS_KV)) return FA_ERR_HIP;
+  FA_LOG_LAUNCH("fa_bwd_dq<D=%d causal=%d varlen=%d>: %lld workgroups x %d threads, %d B LDS; "
+                "fa_bwd_dkdv: %lld workgroups x %d threads, %d B LDS; B=%d H=%d H_kv=%d S_q=%d "
+                "S_k=%d",
+                D, (int)CAUSAL, (int)VARLEN, g1, C::NW_DQ * kWave, C::LDS_DQ, g2,
+                C::NW_KV * kWave, C::LDS_KV, a.B, a.H, a.Hkv, a.S, a.Sk);
   // dQ first: it also writes Delta, which the dK/dV kernel reads.
   hipLaunchKernelGGL(k1, dim3((unsigned)g1), dim3(C::NW_DQ * kWave), C::LDS_DQ, st, a);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
@@ -1126,6 +1131,11 @@ int launch_bwd_wide(const BwdArgs &a, hipStream_t st) {
   auto k1 = fa_bwd_dq_wide<D, CAUSAL, VARLEN>;
   auto k2 = fa_bwd_dkdv_wide<D, CAUSAL, VARLEN>;
   if (!allow_lds(k1, C::LDS_DQ) || !allow_lds(k2, C::LDS_KV)) return FA_ERR_HIP;
+  FA_LOG_LAUNCH("fa_bwd_dq_wide<D=%d D_v=%d causal=%d varlen=%d>: %lld workgroups x %d threads, "
+                "%d B LDS; fa_bwd_dkdv_wide: %lld workgroups x %d threads, %d B LDS, %d column "
+                "parts; B=%d H=%d H_kv=%d S_q=%d S_k=%d",
+                D, C::DV, (int)CAUSAL, (int)VARLEN, g1, C::NW * kWave, C::LDS_DQ, g2,
+                C::NW * kWave, C::LDS_KV, C::DSPLIT, a.B, a.H, a.Hkv, a.S, a.Sk);
   hipLaunchKernelGGL(k1, dim3((unsigned)g1), dim3(C::NW * kWave), C::LDS_DQ, st, a);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   hipLaunchKernelGGL(k2, dim3((unsigned)g2), dim3(C::NW * kWave), C::LDS_KV, st, a);

@@ -1131,12 +1131,22 @@ int launch_variant(const Args &a0, int schedule, int cus, hipStream_t stream) {
     if (VARLEN) lds += sizeof(int) * (3 * fa::kMaxVarlenSeqs + fa::kMaxVarlenLevels + 2);
     auto kern = fa_fwd_persistent<D, CAUSAL, VARLEN, EMU, COUNT>;
     if (!allow_lds(kern, lds)) return FA_ERR_HIP;
+    FA_LOG_LAUNCH("fa_fwd_persistent<D=%d causal=%d varlen=%d exp2_emu=%d counters=%d>: %d "
+                  "workgroups x %d threads, %zu B LDS; B=%d H=%d H_kv=%d S_q=%d S_k=%d, "
+                  "%d-row tiles, up to %lld tiles, tau=%g",
+                  D, (int)CAUSAL, (int)VARLEN, EMU, (int)COUNT, a.workers, C::THREADS, lds, a.B,
+                  a.H, a.Hkv, a.S, a.Sk, C::BM, (long long)a.B * a.H * nmb, (double)a.tau);
     hipLaunchKernelGGL(kern, dim3(a.workers), dim3(C::THREADS), lds, stream, a);
   } else {
     const long long grid = (long long)a.B * a.H * nmb;
     if (grid > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
     auto kern = fa_fwd_grid<D, CAUSAL, VARLEN, EMU, COUNT>;
     if (!allow_lds(kern, lds)) return FA_ERR_HIP;
+    FA_LOG_LAUNCH("fa_fwd_grid<D=%d causal=%d varlen=%d exp2_emu=%d counters=%d>: %lld "
+                  "workgroups x %d threads, %zu B LDS; B=%d H=%d H_kv=%d S_q=%d S_k=%d, "
+                  "%d-row tiles, tau=%g",
+                  D, (int)CAUSAL, (int)VARLEN, EMU, (int)COUNT, grid, C::THREADS, lds, a.B, a.H,
+                  a.Hkv, a.S, a.Sk, C::BM, (double)a.tau);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), lds, stream, a);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -1157,6 +1167,11 @@ int launch_split(const Args &a, int splits, hipStream_t stream) {
   auto kern = pack ? fa_fwd_split<D, CAUSAL, VARLEN, true> : fa_fwd_split<D, CAUSAL, VARLEN, false>;
   const size_t lds = lds_bytes<D, VARLEN, CAUSAL>();
   if (!allow_lds(kern, lds)) return FA_ERR_HIP;
+  FA_LOG_LAUNCH("fa_fwd_split<D=%d causal=%d varlen=%d packed=%d>: %lld workgroups x %d threads, "
+                "%zu B LDS; %lld tiles x %d splits of %d key blocks; B=%d H=%d H_kv=%d S_q=%d "
+                "S_k=%d; then fa_split_combine: %lld workgroups x 256 threads",
+                D, (int)CAUSAL, (int)VARLEN, (int)pack, grid, C::THREADS, lds, tiles, splits,
+                a.kbps, a.B, a.H, a.Hkv, a.S, a.Sk, (rows + 3) / 4);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), lds, stream, a, splits);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   hipLaunchKernelGGL((fa_split_combine<C::DV, VARLEN>), dim3((unsigned)((rows + 3) / 4)), dim3(256),

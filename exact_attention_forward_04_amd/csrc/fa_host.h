@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -38,6 +40,24 @@ int current_device(DeviceInfo **out) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// FA_LOG set to anything but "" or "0" in the environment: one line on
+// stderr per kernel launch, naming the kernel variant, its grid, its LDS
+// bytes and what the launch covers.  Read once per process.
+bool log_on() {
+  static const bool on = [] {
+    const char *e = std::getenv("FA_LOG");
+    return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
+  }();
+  return on;
+}
+#define FA_LOG_LAUNCH(...)                        \
+  do {                                            \
+    if (log_on()) {                               \
+      std::fprintf(stderr, "[fa] " __VA_ARGS__);  \
+      std::fputc('\n', stderr);                   \
+    }                                             \
+  } while (0)
 
 // Allow a kernel the dynamic LDS it needs (above the 64 KB default).
 template <typename K>

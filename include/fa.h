@@ -32,6 +32,13 @@
 extern "C" {
 #endif
 
+/*
+ * Diagnostics: with the environment variable FA_LOG set to a value other
+ * than "" or "0" when the library first launches a kernel, every launch
+ * writes one line to stderr: "[fa] " followed by the kernel variant, its
+ * grid and LDS bytes, and the sizes it covers.
+ */
+
 typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size, bad scale, ... */

@@ -73,6 +73,8 @@ SPLIT_DENSE = [
     (2, 7, 530, 8, 1, 64, 64, 5),         # MQA, D = 64
     (1, 3, 800, 4, 2, 192, 128, 4),       # (192, 128) head dimensions
     (1, 1, 700, 4, 2, 256, 256, 3),       # D = 256
+    # a full 256-row tile and a ragged one over 8 splits
+    (1, 300, 2000, 2, 2, 128, 128, 8),
 ]
 
 
@@ -146,3 +148,28 @@ def test_splitkv_long_context_decode_auto():
     w = WORKLOADS["decode_1x_q1_k32768_h32kv8d128"]
     q, k, v, cu_q, cu_k, Sq, Sk = make_qk(w)
     split_check(q, k, v, True, w.scale, 0, cu_q, cu_k, Sq, Sk, what="split-decode-32k")
+
+
+def test_splitkv_workspace_needs_no_clearing():
+    """The workspace's contents on entry do not matter: a workspace full of
+    stale bytes (all ones, then what a previous call left) gives the same
+    result call after call."""
+    B, Sq, Sk, H, Hkv, D = 2, 1, 3000, 8, 2, 128
+    q, _, _ = draw_qkv((B, Sq, H, D), seed=211)
+    _, k, v = draw_qkv((B, Sk, H, D), seed=212, kv_heads=Hkv)
+    dq, dk, dv = (t.cuda() for t in (q, k, v))
+    splits = 6
+    need = fa.splitkv_workspace_size(B, H, Sq, Sk, D, splits)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        o, lse = fa.attention(dq, dk, dv, causal=True, num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((o.clone(), lse.clone()))
+    for o, lse in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(lse, outs[0][1])
+    o_ref, lse_ref = oracle.attention_bf16(q, k, v, D ** -0.5, True)
+    st = compare(tensor_to_f64(outs[0][0]), tensor_to_f64(outs[0][1]), o_ref, lse_ref)
+    note("split-stale-workspace", st)
+    assert_close(st, "split-stale-workspace")

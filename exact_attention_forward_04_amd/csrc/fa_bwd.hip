@@ -550,6 +550,14 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
       const bool need_mask = (m0 + kBN > L) || (CAUSAL && m0 < key0 - koff + 31);
       const int hi = need_mask ? L - m0 - 4 * hh : INT_MAX;
       const int lo = (need_mask && CAUSAL) ? key - koff - m0 - 4 * hh : INT_MIN;
+      // Entry offsets lie in [0, 64): kept iff lo <= off < hi, i.e. iff
+      // off - lo_c < span as unsigned, with lo and hi clamped to [0, 64]:
+      // one subtract, one compare and one select per entry.  (The two-sided
+      // test written out was compiled into a branch per entry, with its
+      // exec-mask bookkeeping.)
+      const int lo_c = lo < 0 ? 0 : (lo > 64 ? 64 : lo);
+      const int hi_c = hi < 0 ? 0 : (hi > 64 ? 64 : hi);
+      const unsigned span = hi_c > lo_c ? (unsigned)(hi_c - lo_c) : 0u;
       typedef float f32x4 __attribute__((ext_vector_type(4)));
       f32x16 s[2], dp[2];
       bf16x8 p8[4], ds8[4];
@@ -590,7 +598,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
           const int g4 = e >> 2, jj = e & 3;
           const int off = 32 * i + 8 * g4 + jj;
           float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -(l4[i][g4][jj] * kLog2e)));
-          p = (off < hi && off >= lo) ? p : 0.0f;
+          p = ((unsigned)(off - lo_c) < span) ? p : 0.0f;
           const int tt = 2 * i + (e >> 3);
           p8[tt][e & 7] = (__bf16)p;
           ds8[tt][e & 7] = (__bf16)(p * (dp[i][e] - d4[i][g4][jj]));
@@ -1003,6 +1011,14 @@ __global__ __launch_bounds__(WideCfg<D>::NW * kWave, 1) void fa_bwd_dkdv_wide(Bw
       const bool need_mask = (m0 + kBN > L) || (CAUSAL && m0 < key0 - koff + 31);
       const int hi = need_mask ? L - m0 - 4 * hh : INT_MAX;
       const int lo = (need_mask && CAUSAL) ? key - koff - m0 - 4 * hh : INT_MIN;
+      // Entry offsets lie in [0, 64): kept iff lo <= off < hi, i.e. iff
+      // off - lo_c < span as unsigned, with lo and hi clamped to [0, 64]:
+      // one subtract, one compare and one select per entry.  (The two-sided
+      // test written out was compiled into a branch per entry, with its
+      // exec-mask bookkeeping.)
+      const int lo_c = lo < 0 ? 0 : (lo > 64 ? 64 : lo);
+      const int hi_c = hi < 0 ? 0 : (hi > 64 ? 64 : hi);
+      const unsigned span = hi_c > lo_c ? (unsigned)(hi_c - lo_c) : 0u;
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -1037,7 +1053,7 @@ __global__ __launch_bounds__(WideCfg<D>::NW * kWave, 1) void fa_bwd_dkdv_wide(Bw
             const int e = 4 * g4 + jj;
             const int off = 32 * i + 8 * g4 + jj;
             float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -(l4[jj] * kLog2e)));
-            p = (off < hi && off >= lo) ? p : 0.0f;
+            p = ((unsigned)(off - lo_c) < span) ? p : 0.0f;
             const int tt = 2 * i + (e >> 3);
             p8[tt][e & 7] = (__bf16)p;
             ds8[tt][e & 7] = (__bf16)(p * (dp[i][e] - d4[jj]));

@@ -125,3 +125,15 @@ def test_dkdv_d128_operand_and_result_distances(device_asm):
                             assert ws >= 32, (name, "product result read too soon", line, t)
                             break
                     ws += _wait_states(t)
+
+
+def test_dkdv_entry_mask_is_branch_free(device_asm):
+    """The per-entry causal/length mask of P is a compare and a select: no
+    exec-mask branch inside the block body (a two-sided test written with
+    && was once compiled into one such branch per entry, a third of the
+    body's instructions)."""
+    for name, lines in kernels(device_asm, "fa_bwd_dkdvILi128E"):
+        mf = [i for i, l in enumerate(lines) if l.startswith("v_mfma")]
+        body = [l.split()[0] for l in lines[mf[0]:mf[-1] + 1]]
+        assert "s_and_saveexec_b64" not in body, name
+        assert not any(op.startswith("s_cbranch") for op in body), name

@@ -844,6 +844,33 @@ constexpr int lds_bytes() {
 }
 
 // Persistent kernel: each workgroup walks its static LPT list.
+// One round of the greedy assignment (fa::greedy_round), with lane i of
+// wave 0 standing for worker i of the group and for position r*W + i: the
+// ranks of the positions' costs and of the workers' loads come from W
+// broadcasts each; the position of each cost rank goes through LDS.  Writes
+// this worker's (w) position, or -1, to *mine and updates the loads.
+__device__ __forceinline__ void greedy_round_wave(const fa::Sched &s, const fa::SchedTables &t,
+                                                  int x, int r, int W, int npos, int w,
+                                                  int *gload, int *gpos, int *mine) {
+  const int i = threadIdx.x;
+  const int c = i < W ? fa::position_cost2(s, t, x, r * W + i, npos) : -2;
+  const int ld = i < W ? gload[i] : 0x7fffffff;
+  int rc = 0, rl = 0;
+  for (int k = 0; k < W; ++k) {
+    const int ck = __builtin_amdgcn_readlane(c, k);
+    const int lk = __builtin_amdgcn_readlane(ld, k);
+    rc += fa::cost_before(ck, k, c, i);
+    rl += fa::load_before(lk, k, ld, i);
+  }
+  if (i < W) gpos[rc] = i;
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  const int gi = i < W ? gpos[rl] : 0;
+  const int gc = __shfl(c, gi);
+  if (i < W && gc > 0) gload[i] = ld + gc;
+  if (i == w) *mine = gc > 0 ? r * W + gi : -1;
+}
+
 template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT>
 __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fwd_persistent(Args a) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
@@ -872,6 +899,28 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fw
   int x, w, W;
   fa::worker_slot(s, blockIdx.x, a.workers, &x, &w, &W);
   const int npos = fa::group_positions(s);
+  if constexpr (VARLEN && CAUSAL) {
+    if (fa::greedy_rounds(s, W)) {
+      // Greedy rounds: wave 0 works out each round's assignment for the
+      // whole group (every worker of the group computes the same one) and
+      // publishes this worker's position; two slots, so a round's slot is
+      // rewritten only after every wave has passed the next round's barrier.
+      int *gload = t.key + fa::kMaxVarlenSeqs;  // [W] accumulated costs
+      int *gpos = gload + fa::kGreedyMaxW;        // [W] position index by cost rank
+      int *gmine = gpos + fa::kGreedyMaxW;        // [2] this worker's position
+      if (threadIdx.x < W) gload[threadIdx.x] = 0;
+      __syncthreads();
+      for (int r = 0; r * W < npos; ++r) {
+        if (threadIdx.x < kWave) greedy_round_wave(s, t, x, r, W, npos, w, gload, gpos, gmine + (r & 1));
+        __syncthreads();
+        const int p = gmine[r & 1];
+        if (p < 0) continue;  // no tile for this worker in this round
+        const fa::Tile tl = fa::decode_position(s, t, x, p);
+        run_tile<D, CAUSAL, VARLEN, EMU, COUNT>(a, tl.b, tl.h, tl.mb, lds);
+      }
+      return;
+    }
+  }
   for (int r = 0;; ++r) {
     const int p = fa::snake_position(r, w, W);
     if (p >= npos) break;
@@ -1128,7 +1177,10 @@ int launch_variant(const Args &a0, int schedule, int cus, hipStream_t stream) {
   if (VARLEN && (a.B > fa::kMaxVarlenSeqs || nmb > fa::kMaxVarlenLevels)) persistent = false;
   if (persistent) {
     a.workers = cus * C::OCC;
-    if (VARLEN) lds += sizeof(int) * (3 * fa::kMaxVarlenSeqs + fa::kMaxVarlenLevels + 2);
+    // varlen tables, then the greedy rounds' loads, ranks and two slots
+    if (VARLEN)
+      lds += sizeof(int) * (3 * fa::kMaxVarlenSeqs + fa::kMaxVarlenLevels + 2 +
+                            2 * fa::kGreedyMaxW + 2);
     auto kern = fa_fwd_persistent<D, CAUSAL, VARLEN, EMU, COUNT>;
     if (!allow_lds(kern, lds)) return FA_ERR_HIP;
     FA_LOG_LAUNCH("fa_fwd_persistent<D=%d causal=%d varlen=%d exp2_emu=%d counters=%d>: %d "
@@ -1595,21 +1647,40 @@ int fa_schedule_general(int B, int H, int H_kv, int S, int D, int causal, const 
   }
   const int npos = fa::group_positions(s);
   int rounds = 0;
-  for (int wk = 0; wk < workers; ++wk) {
-    int x, w, W;
-    fa::worker_slot(s, wk, workers, &x, &w, &W);
-    // the worker's tiles in the order it runs them (idle positions skipped)
-    int n = 0;
-    for (int r = 0;; ++r) {
-      const int p = fa::snake_position(r, w, W);
-      if (p >= npos) break;
-      const fa::Tile tl = fa::decode_position(s, t, x, p);
-      if (tl.b < 0) continue;
-      if (n == max_rounds) return FA_ERR_INVALID_ARG;  // the list must fit max_rounds
-      tiles[(long long)wk * max_rounds + n++] = (tl.b * H + tl.h) * s.nmb_max + tl.mb;
+  int x0, w0, W;
+  fa::worker_slot(s, 0, workers, &x0, &w0, &W);
+  std::vector<int> count(workers, 0);
+  auto put = [&](int wk, int p, int x) {
+    const fa::Tile tl = fa::decode_position(s, t, x, p);
+    if (tl.b < 0) return true;  // an idle position
+    if (count[wk] == max_rounds) return false;  // the list must fit max_rounds
+    tiles[(long long)wk * max_rounds + count[wk]++] = (tl.b * H + tl.h) * s.nmb_max + tl.mb;
+    return true;
+  };
+  if (fa::greedy_rounds(s, W)) {
+    // every group's rounds, in the order each worker runs them
+    for (int x = 0; x < s.groups; ++x) {
+      int load[fa::kGreedyMaxW] = {}, take[fa::kGreedyMaxW];
+      for (int r = 0; r * W < npos; ++r) {
+        fa::greedy_round(s, t, x, r, W, npos, load, take);
+        for (int w = 0; w < W; ++w)
+          if (take[w] >= 0 && !put(w * s.groups + x, take[w], x)) return FA_ERR_INVALID_ARG;
+      }
     }
-    if (n > rounds) rounds = n;
-    for (int r = n; r < max_rounds; ++r) tiles[(long long)wk * max_rounds + r] = -1;
+  } else {
+    for (int wk = 0; wk < workers; ++wk) {
+      int x, w;
+      fa::worker_slot(s, wk, workers, &x, &w, &W);
+      for (int r = 0;; ++r) {
+        const int p = fa::snake_position(r, w, W);
+        if (p >= npos) break;
+        if (!put(wk, p, x)) return FA_ERR_INVALID_ARG;
+      }
+    }
+  }
+  for (int wk = 0; wk < workers; ++wk) {
+    if (count[wk] > rounds) rounds = count[wk];
+    for (int r = count[wk]; r < max_rounds; ++r) tiles[(long long)wk * max_rounds + r] = -1;
   }
   if (rounds_out) *rounds_out = rounds;
   if (bm_out) *bm_out = BM;

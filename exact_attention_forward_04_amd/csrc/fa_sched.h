@@ -18,8 +18,14 @@
 //     G query heads of each, visited one K/V head at a time (the survey of
 //     the paper's section 3.3: walk every query head of one K/V head before
 //     moving on), so a K/V head is read into one L2 only.
-// Within an XCD, workers take positions in "snake" order: round r gives
-// worker w position r*W + w on even rounds and r*W + W-1-w on odd rounds.
+// Within an XCD, workers take positions W at a time (one round).  Dense
+// batches, whose rounds hold tiles of equal cost, pair them in "snake"
+// order: round r gives worker w position r*W + w on even rounds and
+// r*W + W-1-w on odd rounds.  Varlen causal batches, whose rounds mix costs
+// (chunks of levels, idle positions), pair them greedily: the round's
+// costliest position goes to the worker with the least accumulated cost
+// (greedy_round; host model on the 16-sequence batch: the busiest worker
+// 1.064x the mean with the snake, 1.00x greedily).
 //
 // Item order (an item is (b, mb); heads are expanded innermost):
 //   causal   : level l = 0..nmb_max-1 is m-block nmb_max-1-l; a level holds
@@ -239,6 +245,60 @@ FA_HD inline void worker_slot(const Sched &s, int worker, int workers, int *x, i
 // Snake position of worker w (of W) in round r.
 FA_HD inline int snake_position(int r, int w, int W) {
   return r * W + ((r & 1) ? (W - 1 - w) : w);
+}
+
+// ---- greedy rounds (varlen causal batches) ----
+constexpr int kGreedyMaxW = 64;  // one lane per worker of a group on the device
+FA_HD inline bool greedy_rounds(const Sched &s, int W) {
+  return s.varlen && s.causal && W <= kGreedyMaxW;
+}
+
+// Doubled cost of a tile: two per 64-key block it reads, plus 5 for its
+// fixed part (about 2.5 blocks: the pipeline's fill and drain and the
+// epilogue).  The key range follows the kernel's causal bound.
+FA_HD inline int tile_cost2(const Sched &s, const SchedTables &t, const Tile &tl) {
+  const int L = t.len[tl.b];
+  const int Lk = s.by_klen ? t.key[tl.b] : L;
+  const int e = tl.mb * s.BM + s.BM + (Lk - L);
+  const int n_end = e < 0 ? 0 : (e < Lk ? e : Lk);
+  return 2 * ceil_div(n_end, 64) + 5;
+}
+
+// Cost of position p of group x: > 0 for a tile, 0 for an idle position,
+// -1 past the end of the list.
+FA_HD inline int position_cost2(const Sched &s, const SchedTables &t, int x, int p, int npos) {
+  if (p >= npos) return -1;
+  const Tile tl = decode_position(s, t, x, p);
+  return tl.b < 0 ? 0 : tile_cost2(s, t, tl);
+}
+
+// Whether position i of a round goes before position k (cost descending,
+// ties: lower index), and whether worker i's load ranks before worker k's
+// (ascending, ties: lower index).
+FA_HD inline bool cost_before(int ci, int i, int ck, int k) { return ci > ck || (ci == ck && i < k); }
+FA_HD inline bool load_before(int li, int i, int lk, int k) { return li < lk || (li == lk && i < k); }
+
+// One greedy round on the host: take[w] = the position worker w takes in
+// round r (-1: none), load[] updated.  The device computes the same
+// assignment with one lane per worker (fa_fwd_persistent).
+inline void greedy_round(const Sched &s, const SchedTables &t, int x, int r, int W, int npos,
+                         int *load, int *take) {
+  int cost[kGreedyMaxW], by_cost[kGreedyMaxW], by_load[kGreedyMaxW];
+  for (int i = 0; i < W; ++i) cost[i] = position_cost2(s, t, x, r * W + i, npos);
+  for (int i = 0; i < W; ++i) {
+    int rc = 0, rl = 0;
+    for (int k = 0; k < W; ++k) {
+      rc += cost_before(cost[k], k, cost[i], i);
+      rl += load_before(load[k], k, load[i], i);
+    }
+    by_cost[rc] = i;
+    by_load[rl] = i;
+  }
+  for (int q = 0; q < W; ++q) {
+    const int w = by_load[q], i = by_cost[q];
+    take[w] = cost[i] > 0 ? r * W + i : -1;
+    if (cost[i] > 0) load[w] += cost[i];
+  }
 }
 
 }  // namespace fa

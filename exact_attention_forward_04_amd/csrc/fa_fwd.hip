@@ -985,13 +985,25 @@ __global__ __launch_bounds__(256) void fa_split_combine(Args a, int splits) {
     li = (b * H + h) * a.S + i;
   }
   const long long slots = (long long)a.B * a.S * H;
+  constexpr int PER = (DV + kWave - 1) / kWave;
+  // The partial rows of the first PRE splits are loaded before the weights
+  // are known, in flight together with the LSE loads: the merge of a short
+  // batch (a decode step) is one memory round trip shorter.
+  constexpr int PRE = 16;
+  float pre[PRE][PER];
+#pragma unroll
+  for (int s = 0; s < PRE; ++s)
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int d = lane + k * kWave;
+      pre[s][k] = (s < splits && d < DV) ? a.ws_o[(s * slots + r) * (long long)DV + d] : 0.0f;
+    }
   // Lane s holds the LSE of split s (splits <= 64): the row's maximum and
   // the split weights are wave reductions, not a serial walk over splits.
   const float ls = lane < splits ? a.ws_lse[lane * slots + li] : -INFINITY;
   float m = ls;
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  constexpr int PER = (DV + kWave - 1) / kWave;
   float acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
@@ -1001,9 +1013,17 @@ __global__ __launch_bounds__(256) void fa_split_combine(Args a, int splits) {
     float wsum = wl;
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+#pragma unroll
+    for (int s = 0; s < PRE; ++s) {
+      if (s < splits) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] = __builtin_fmaf(w, pre[s][k], acc[k]);
+      }
+    }
     // the loads of several splits in flight at once
 #pragma unroll 16
-    for (int s = 0; s < splits; ++s) {
+    for (int s = PRE; s < splits; ++s) {
       const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
       const float *op = a.ws_o + (s * slots + r) * (long long)DV;
 #pragma unroll

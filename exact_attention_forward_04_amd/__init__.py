@@ -52,7 +52,8 @@ class MfmaRate(ctypes.Structure):
 class Tuning(ctypes.Structure):
     """Mirror of struct fa_tuning (include/fa.h)."""
     _fields_ = [("tau", ctypes.c_float), ("exp2_emu", ctypes.c_int),
-                ("schedule", ctypes.c_int), ("counters", ctypes.c_void_p)]
+                ("schedule", ctypes.c_int), ("counters", ctypes.c_void_p),
+                ("split_levels", ctypes.c_int)]
 
 
 def load(path: str = LIB_PATH):
@@ -123,6 +124,10 @@ def _declare(lib, backward: bool = True):
     lib.fa_schedule_general.restype = I
     lib.fa_num_workers.argtypes = [I, ctypes.POINTER(I)]
     lib.fa_num_workers.restype = I
+    lib.fa_split_plan.argtypes = [I, I, I, I, I, I, ctypes.POINTER(I)]
+    lib.fa_split_plan.restype = I
+    lib.fa_schedule_split.argtypes = [I, I, I, I, I, I, P, I, ctypes.POINTER(I), ctypes.POINTER(I)]
+    lib.fa_schedule_split.restype = I
     lib.fa_mfma_ceiling.argtypes = [I, I, I, ctypes.POINTER(MfmaRate)]
     lib.fa_mfma_ceiling.restype = I
     lib.fa_status_string.argtypes = [I]
@@ -486,6 +491,28 @@ def schedule(B: int, H: int, S: int, D: int, causal: bool, workers: int,
                                  tiles.ctypes.data, max_rounds, ctypes.byref(rounds),
                                  ctypes.byref(bm))
         _check("fa_schedule_gqa", rc)
+    return tiles[:, :rounds.value].copy(), bm.value
+
+
+def split_plan(B: int, H: int, S: int, D: int, workers: int, requested: int = -1) -> int:
+    """Split levels a dense causal self-attention launch uses (fa_split_plan;
+    requested -1: the library's makespan model decides)."""
+    n = ctypes.c_int(0)
+    _check("fa_split_plan", load().fa_split_plan(B, H, S, D, workers, requested, ctypes.byref(n)))
+    return n.value
+
+
+def schedule_split(B: int, H: int, S: int, D: int, nsplit: int, workers: int,
+                   max_rounds: int = 4096):
+    """Host-side persistent order of a dense causal batch with nsplit split
+    levels: (items [workers, rounds] int32, BM).  Item code =
+    ((seq * H + head) * ceil(S / BM) + mblock) * 3 + part, -1 = none."""
+    import numpy as np
+    tiles = np.full((workers, max_rounds), -2, dtype=np.int32)
+    rounds, bm = ctypes.c_int(0), ctypes.c_int(0)
+    _check("fa_schedule_split", load().fa_schedule_split(B, H, S, D, nsplit, workers,
+                                                         tiles.ctypes.data, max_rounds,
+                                                         ctypes.byref(rounds), ctypes.byref(bm)))
     return tiles[:, :rounds.value].copy(), bm.value
 
 

@@ -52,6 +52,7 @@
 #include <utility>
 #include <vector>
 #include <algorithm>
+#include <array>
 
 #include "fa.h"
 #include "exp2_poly.h"
@@ -120,6 +121,12 @@ struct Args {
   // combine kernel merges
   float *ws_o, *ws_lse;
   int kbps;
+  // persistent dense causal with split levels: the nsplit costliest m-blocks
+  // run as two parts (fa_sched.h); each part's partial rows go to ws_o /
+  // ws_lse, and hs_cnt holds one arrival counter per (split tile, wave),
+  // zero between launches
+  int nsplit;
+  int *hs_cnt;
 };
 
 // Per-wave state of one tile.
@@ -490,7 +497,7 @@ struct KvLayout {
 template <int D, bool CAUSAL, bool VARLEN, int EMU, bool COUNT, bool SPLIT = false,
           bool PACK = false>
 __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, char LDS_AS *lds,
-                                         int split = 0) {
+                                         int split = 0, int part = 0) {
   using C = Cfg<D>;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
@@ -518,6 +525,19 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     ktok0 += lo;
     koff -= lo;
     Lk = hi > lo ? hi - lo : 0;
+  }
+  if (part != 0) {
+    // One part of a split m-block (dense causal self-attention): of the
+    // tile's n key blocks, part 1 takes the first floor(n/2) and part 2 the
+    // rest, each as a key sequence of its own (as a split-KV slice).
+    const int e = mb * C::BM + C::BM + koff;
+    const int n_full = e < 0 ? 0 : (e < Lk ? e : Lk);
+    const int half = fa::ceil_div(n_full, kBN) / 2 * kBN;
+    const int lo = part == 1 ? 0 : half;
+    const int hi = part == 1 ? half : n_full;
+    ktok0 += lo;
+    koff -= lo;
+    Lk = hi - lo;
   }
   const int m0 = mb * C::BM;
   if (m0 >= L) return;  // workgroup-uniform
@@ -814,6 +834,97 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     }
     return;
   }
+  if (part != 0) {
+    // A part of a split m-block: the wave writes its partial rows (O
+    // normalised over the part's keys, fp32, and the LSE) to the part's
+    // slot and counts its arrival; the wave that arrives second for these
+    // rows reads the other part's slot and writes the merged rows.  No wave
+    // waits for another.
+    //
+    // The two parts may run on different XCDs, whose L2 caches are not
+    // coherent with each other.  The slots are written and read with
+    // device-coherent accesses (sc1: through to memory, and from it), so no
+    // cache-wide write-back or invalidation is needed: the writer waits for
+    // its stores to complete before it counts, and the reader reads after
+    // the count it saw.  (Agent-scope fences would write back and invalidate
+    // the whole L2 of the XCD, once per wave: measured 6x slower.)
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kCoherent = 16;  // cache policy sc1: coherent at device scope
+    const int nmb = fa::ceil_div(a.S, C::BM);
+    const int tix = (b * H + h) * a.nsplit + (mb - (nmb - a.nsplit));  // split tile
+    const long long own = 2LL * tix + (part - 1), other = 2LL * tix + (2 - part);
+    const int r = row - m0;  // row within the tile
+    const int hh = lane >> 5;
+    const float inv = l32 > 0.0f ? 1.0f / l32 : 0.0f;
+    const float lse_own = (st.m_ref + log2f(l32)) * kLn2;  // -inf for a row without keys
+    constexpr int SLOT = C::BM * DV * 4;                   // bytes of one part's rows
+    const __amdgpu_buffer_rsrc_t own_o =
+        __builtin_amdgcn_make_buffer_rsrc(a.ws_o + own * C::BM * DV, (short)0, SLOT, 0x00020000);
+    const __amdgpu_buffer_rsrc_t other_o =
+        __builtin_amdgcn_make_buffer_rsrc(a.ws_o + other * C::BM * DV, (short)0, SLOT, 0x00020000);
+    const int lane_off = (r * DV + 4 * hh) * 4;  // byte offset of the lane's first value
+    f32x4 mine[DV / 32][4];
+#pragma unroll
+    for (int dt = 0; dt < DV / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        mine[dt][i] = f32x4{st.o[dt][4 * i + 0] * inv, st.o[dt][4 * i + 1] * inv,
+                            st.o[dt][4 * i + 2] * inv, st.o[dt][4 * i + 3] * inv};
+    if (row < R) {
+#pragma unroll
+      for (int dt = 0; dt < DV / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, mine[dt][i]), own_o,
+                                                 lane_off + (32 * dt + 8 * i) * 4, 0, kCoherent);
+      if (hh == 0)
+        __hip_atomic_store(a.ws_lse + own * C::BM + r, lse_own, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_vmcnt<0>();  // this wave's partial rows are in memory before it counts
+    int *cnt = a.hs_cnt + (long long)tix * C::NW + wave;
+    int prev = 0;
+    if (lane == 0) prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev == 0) return;  // the other part's wave merges these rows
+    // both parts are in: zero for the next launch
+    if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (row < R) {
+      const float lse_x = __hip_atomic_load(a.ws_lse + other * C::BM + r, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+      // (part 1, part 2) order whichever arrived last: the merged rows do not
+      // depend on the arrival order
+      const float l1 = part == 1 ? lse_own : lse_x;
+      const float l2 = part == 1 ? lse_x : lse_own;
+      const float mx = fmaxf(l1, l2);
+      const float w1 = mx == -INFINITY ? 0.0f : exp2_hw((l1 - mx) * kLog2e);
+      const float w2 = mx == -INFINITY ? 0.0f : exp2_hw((l2 - mx) * kLog2e);
+      const float sw = w1 + w2;
+      const float winv = sw > 0.0f ? 1.0f / sw : 0.0f;
+      __bf16 *op = a.o + ((tok0 + qi) * H + hq) * (long long)DV + 4 * hh;
+#pragma unroll
+      for (int dt = 0; dt < DV / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 x = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(other_o, lane_off + (32 * dt + 8 * i) * 4,
+                                                           0, kCoherent));
+          const f32x4 p1 = part == 1 ? mine[dt][i] : x;
+          const f32x4 p2 = part == 1 ? x : mine[dt][i];
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 out;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[e] = (__bf16)((w1 * p1[e] + w2 * p2[e]) * winv);
+          *(bf16x4 *)(op + 32 * dt + 8 * i) = out;
+        }
+      if (a.lse != nullptr && hh == 0) {
+        const float lse = sw > 0.0f ? mx + log2f(sw) * kLn2 : -INFINITY;
+        a.lse[((long long)b * H + hq) * a.S + qi] = lse;
+      }
+    }
+    return;
+  }
   if (row < R) {
     const float inv = l32 > 0.0f ? 1.0f / l32 : 0.0f;  // a row without keys: O = 0, LSE = -inf
     const int hh = lane >> 5;
@@ -877,8 +988,9 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fw
   char LDS_AS *lds = (char LDS_AS *)lds_raw;
   using C = Cfg<D>;
   fa::Sched s = fa::make_sched(a.B, a.H, a.Hkv, a.S, C::BM, CAUSAL, VARLEN, a.workers,
-                               a.cu_k == a.cu);
-  fa::SchedTables t{nullptr, nullptr, nullptr, nullptr};
+                               a.cu_k == a.cu, a.nsplit);
+  fa::SchedTables t{nullptr, nullptr, nullptr, nullptr, nullptr};
+  int *gtab = nullptr;  // greedy rounds: loads [W], positions by cost rank [W], two slots
   if constexpr (VARLEN) {
     int *tab = (int *)(lds_raw + lds_bytes<D, VARLEN, CAUSAL>());
     t.len = tab;
@@ -895,17 +1007,27 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fw
     if (threadIdx.x == 0) *n_items_sh = fa::tables_phase4(s, t);
     __syncthreads();
     s.n_items = *n_items_sh;
+    gtab = t.key + fa::kMaxVarlenSeqs;
+  } else if constexpr (CAUSAL) {
+    if (s.nsplit > 0) {
+      // the virtual levels of the split schedule, by cost rank
+      int *tab = (int *)(lds_raw + lds_bytes<D, VARLEN, CAUSAL>());
+      t.vl = tab;
+      gtab = tab + fa::kMaxSplitLevels;
+      fa::split_levels(s, t.vl, threadIdx.x, blockDim.x);
+      __syncthreads();
+    }
   }
   int x, w, W;
   fa::worker_slot(s, blockIdx.x, a.workers, &x, &w, &W);
   const int npos = fa::group_positions(s);
-  if constexpr (VARLEN && CAUSAL) {
+  if constexpr (CAUSAL) {
     if (fa::greedy_rounds(s, W)) {
       // Greedy rounds: wave 0 works out each round's assignment for the
       // whole group (every worker of the group computes the same one) and
       // publishes this worker's position; two slots, so a round's slot is
       // rewritten only after every wave has passed the next round's barrier.
-      int *gload = t.key + fa::kMaxVarlenSeqs;  // [W] accumulated costs
+      int *gload = gtab;                          // [W] accumulated costs
       int *gpos = gload + fa::kGreedyMaxW;        // [W] position index by cost rank
       int *gmine = gpos + fa::kGreedyMaxW;        // [2] this worker's position
       if (threadIdx.x < W) gload[threadIdx.x] = 0;
@@ -916,7 +1038,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WAVES_PER_SIMD) void fa_fw
         const int p = gmine[r & 1];
         if (p < 0) continue;  // no tile for this worker in this round
         const fa::Tile tl = fa::decode_position(s, t, x, p);
-        run_tile<D, CAUSAL, VARLEN, EMU, COUNT>(a, tl.b, tl.h, tl.mb, lds);
+        run_tile<D, CAUSAL, VARLEN, EMU, COUNT>(a, tl.b, tl.h, tl.mb, lds, 0, tl.part);
       }
       return;
     }
@@ -1179,6 +1301,7 @@ int validate(const void *q, const void *k, const void *v, void *o, float *lse, i
     if (!(t->tau >= 0.0f && t->tau <= kMaxTau)) return FA_ERR_INVALID_ARG;
     if (t->exp2_emu != 0 && t->exp2_emu != 4 && t->exp2_emu != 8) return FA_ERR_INVALID_ARG;
     if (t->schedule != 0 && t->schedule != 1) return FA_ERR_INVALID_ARG;
+    if (t->split_levels < -1) return FA_ERR_INVALID_ARG;
   }
   if (!supported_dims(D, Dv)) return FA_ERR_UNSUPPORTED;
   // sizes must fit the 32-bit index arithmetic used for rows and tiles
@@ -1201,13 +1324,17 @@ int launch_variant(const Args &a0, int schedule, int cus, hipStream_t stream) {
     if (VARLEN)
       lds += sizeof(int) * (3 * fa::kMaxVarlenSeqs + fa::kMaxVarlenLevels + 2 +
                             2 * fa::kGreedyMaxW + 2);
+    // split levels: their table, then the greedy rounds' arrays
+    if (!VARLEN && CAUSAL && a.nsplit > 0)
+      lds += sizeof(int) * (fa::kMaxSplitLevels + 2 * fa::kGreedyMaxW + 2);
     auto kern = fa_fwd_persistent<D, CAUSAL, VARLEN, EMU, COUNT>;
     if (!allow_lds(kern, lds)) return FA_ERR_HIP;
     FA_LOG_LAUNCH("fa_fwd_persistent<D=%d causal=%d varlen=%d exp2_emu=%d counters=%d>: %d "
                   "workgroups x %d threads, %zu B LDS; B=%d H=%d H_kv=%d S_q=%d S_k=%d, "
-                  "%d-row tiles, up to %lld tiles, tau=%g",
+                  "%d-row tiles, up to %lld tiles, %d split levels, tau=%g",
                   D, (int)CAUSAL, (int)VARLEN, EMU, (int)COUNT, a.workers, C::THREADS, lds, a.B,
-                  a.H, a.Hkv, a.S, a.Sk, C::BM, (long long)a.B * a.H * nmb, (double)a.tau);
+                  a.H, a.Hkv, a.S, a.Sk, C::BM, (long long)a.B * a.H * nmb, a.nsplit,
+                  (double)a.tau);
     hipLaunchKernelGGL(kern, dim3(a.workers), dim3(C::THREADS), lds, stream, a);
   } else {
     const long long grid = (long long)a.B * a.H * nmb;
@@ -1321,6 +1448,155 @@ int bm_for(int D) {
   }
 }
 
+// Waves per workgroup of the forward instance for D.
+int nw_for(int D) {
+  switch (D) {
+    case 64: return Cfg<64>::NW;
+    case 128: return Cfg<128>::NW;
+    case 192: return Cfg<192>::NW;
+    default: return Cfg<256>::NW;
+  }
+}
+
+// ---- dense causal split levels: the plan and the workspace ----
+
+// Makespan, in doubled cost units (fa::tile_cost2), of the busiest worker of
+// group 0 under schedule s (every group of a dense batch holds the same
+// costs): greedy rounds with split levels, the snake order without.
+long long split_makespan(const fa::Sched &s, int workers) {
+  int vl[fa::kMaxSplitLevels];
+  fa::SchedTables t{nullptr, nullptr, nullptr, nullptr, vl};
+  if (s.nsplit > 0) fa::split_levels(s, vl, 0, 1);
+  int x0, w0, W;
+  fa::worker_slot(s, 0, workers, &x0, &w0, &W);
+  const int npos = fa::group_positions(s);
+  if (fa::greedy_rounds(s, W)) {
+    int load[fa::kGreedyMaxW] = {}, take[fa::kGreedyMaxW];
+    for (int r = 0; r * W < npos; ++r) fa::greedy_round(s, t, 0, r, W, npos, load, take);
+    return *std::max_element(load, load + W);
+  }
+  long long worst = 0;
+  for (int w = 0; w < W; ++w) {
+    long long load = 0;
+    for (int r = 0;; ++r) {
+      const int p = fa::snake_position(r, w, W);
+      if (p >= npos) break;
+      load += fa::tile_cost2(s, t, fa::decode_position(s, t, 0, p));
+    }
+    worst = load > worst ? load : worst;
+  }
+  return worst;
+}
+
+// Split levels for a dense causal self-attention launch of `workers`
+// workgroups: `requested` clamped to what the schedule can hold, or, with
+// requested < 0, the count the makespan model above finds best, when the
+// unsplit batch leaves at least half of the workers without a tile and the
+// model shortens the busiest worker's load by at least 5%.  Measured (D =
+// 128, the best count against none): B=1, H=8, S=3000 -19%; B=1, H=16,
+// S=2048 -10%.  Batches that fill the workers gain too little for the
+// exchange of partial rows (B=2, H=16, S=2048: -5% with one level, slower
+// with more), and are left whole.
+int plan_nsplit(int B, int H, int S, int BM, int workers, int requested) {
+  const fa::Sched s0 = fa::make_sched(B, H, H, S, BM, 1, 0, workers);
+  int maxs = fa::kMaxSplitLevels - s0.nmb_max;
+  if (maxs > s0.nmb_max) maxs = s0.nmb_max;
+  if (maxs <= 0 || requested == 0) return 0;
+  if (requested > 0) return requested < maxs ? requested : maxs;
+  static std::mutex mu;
+  static std::map<std::array<int, 4>, int> memo;
+  const std::array<int, 4> key{B, H, S, BM * 4096 + workers};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = memo.find(key);
+    if (it != memo.end()) return it->second;
+  }
+  if ((long long)B * H * s0.nmb_max * 2 > workers) return 0;
+  int x0, w0, W;
+  fa::worker_slot(s0, 0, workers, &x0, &w0, &W);
+  long long total = 0;
+  for (int mb = 0; mb < s0.nmb_max; ++mb) total += fa::split_cost2(s0, mb, 0);
+  total *= (long long)B * s0.hpg;
+  const long long base = split_makespan(s0, workers);
+  int best_n = 0;
+  if (base * 20 > total / W * 21) {  // the busiest worker is >5% above the mean
+    long long best = base;
+    for (int n = 1; n <= maxs; ++n) {
+      const long long m = split_makespan(fa::make_sched(B, H, H, S, BM, 1, 0, workers, 1, n),
+                                         workers);
+      if (m < best) {
+        best = m;
+        best_n = n;
+      }
+    }
+    if (best * 20 > base * 19) best_n = 0;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  memo[key] = best_n;
+  return best_n;
+}
+
+// Bytes of a split launch's arrival counters and of its partial rows (O and
+// LSE of both parts of every split tile).
+size_t split_counter_bytes(int B, int H, int nsplit, int NW) {
+  return (size_t)B * H * nsplit * NW * sizeof(int);
+}
+size_t split_partial_bytes(int B, int H, int nsplit, int BM, int DV) {
+  return (size_t)B * H * nsplit * 2 * BM * (DV + 1) * sizeof(float);
+}
+constexpr size_t kSplitPartialMax = (size_t)512 << 20;  // larger partials: no split
+
+// Workspace of split launches, one per device and stream: launches on one
+// stream run in order and so never share it, launches on different streams
+// get their own.  The counters are zeroed when allocated (on the stream)
+// and every launch leaves them zero.  A buffer grows by waiting for its
+// stream and replacing it; it is kept until the process ends.  nullptr when
+// it cannot be had (an allocation failure, or a stream being captured).
+struct SplitBuf {
+  void *ptr = nullptr;
+  size_t bytes = 0;
+};
+bool split_buffer(std::map<std::pair<int, hipStream_t>, SplitBuf> &bufs, int dev, hipStream_t st,
+                  size_t bytes, bool zero, void **out) {
+  SplitBuf &b = bufs[{dev, st}];
+  if (b.bytes >= bytes) {
+    *out = b.ptr;
+    return true;
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
+  if (b.ptr) {
+    if (hipStreamSynchronize(st) != hipSuccess) return false;
+    (void)hipFree(b.ptr);
+    b.ptr = nullptr;
+    b.bytes = 0;
+  }
+  void *p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) return false;
+  if (zero && hipMemsetAsync(p, 0, bytes, st) != hipSuccess) {
+    (void)hipFree(p);
+    return false;
+  }
+  b.ptr = p;
+  b.bytes = bytes;
+  *out = p;
+  return true;
+}
+bool split_workspace(hipStream_t st, size_t cnt_bytes, size_t part_bytes, int **cnt,
+                     float **part) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, SplitBuf> counters, partials;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  void *c = nullptr, *p = nullptr;
+  if (!split_buffer(counters, dev, st, cnt_bytes, true, &c)) return false;
+  if (!split_buffer(partials, dev, st, part_bytes, false, &p)) return false;
+  *cnt = (int *)c;
+  *part = (float *)p;
+  return true;
+}
+
 // The partial results of fa_fwd_splitkv_noalloc: a fixed array in each
 // device's memory, so that the call allocates nothing.  Host code never
 // passes the array's name to a kernel (on the host it is only a stand-in
@@ -1364,6 +1640,7 @@ fa_tuning fa_tuning_default(void) {
   t.exp2_emu = 0;
   t.schedule = 0;
   t.counters = nullptr;
+  t.split_levels = -1;
   return t;
 }
 
@@ -1398,8 +1675,24 @@ int fa_fwd_general(const void *q, const void *k, const void *v, void *o, float *
   a.workers = 0;
   a.ws_o = a.ws_lse = nullptr;
   a.kbps = 0;
+  a.nsplit = 0;
+  a.hs_cnt = nullptr;
   hipStream_t st = (hipStream_t)stream;
   const bool varlen = cu_seqlens_q != nullptr;
+  if (causal && !varlen && S_q == S_k && t.schedule == 0 && t.split_levels != 0) {
+    const int BM = bm_for(D), NW = nw_for(D);
+    const int n = plan_nsplit(B, H, S_q, BM, dev->cus, t.split_levels);
+    int *cnt = nullptr;
+    float *part = nullptr;
+    if (n > 0 && split_partial_bytes(B, H, n, BM, D_v) <= kSplitPartialMax &&
+        split_workspace(st, split_counter_bytes(B, H, n, NW), split_partial_bytes(B, H, n, BM, D_v),
+                        &cnt, &part)) {
+      a.nsplit = n;
+      a.hs_cnt = cnt;
+      a.ws_o = part;
+      a.ws_lse = part + (size_t)B * H * n * 2 * BM * D_v;
+    }
+  }
   switch (D) {
     case 64: return dispatch_d<64>(a, causal, varlen, t, dev->cus, st);
     case 128: return dispatch_d<128>(a, causal, varlen, t, dev->cus, st);
@@ -1502,6 +1795,8 @@ int splitkv(const void *q, const void *k, const void *v, void *o, float *lse, in
   a.ws_o = (float *)workspace;
   a.ws_lse = a.ws_o + (size_t)splits * slots * D_v;
   a.kbps = kbps;
+  a.nsplit = 0;
+  a.hs_cnt = nullptr;
   hipStream_t st = (hipStream_t)stream;
   const bool varlen = cu_seqlens_q != nullptr;
   switch (D) {
@@ -1579,7 +1874,7 @@ int fa_mfma_ceiling(int mode, int blocks, int reps, fa_mfma_rate *out) {
   if (hipMalloc((void **)&sink, (size_t)workers * 512 * sizeof(float)) != hipSuccess) goto done;
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) goto done;
   for (int r = 0; r < reps; ++r) {
-    hipEventRecord(e0, nullptr);
+    (void)hipEventRecord(e0, nullptr);
     if (mode == 0)
       hipLaunchKernelGGL(mfma_ceiling_kernel<true>, dim3(workers), dim3(512), 0, nullptr, blocks,
                          stamps, sink);
@@ -1587,7 +1882,7 @@ int fa_mfma_ceiling(int mode, int blocks, int reps, fa_mfma_rate *out) {
       hipLaunchKernelGGL(mfma_ceiling_kernel<false>, dim3(workers), dim3(512), 0, nullptr, blocks,
                          stamps, sink);
     if (hipGetLastError() != hipSuccess) goto done;
-    hipEventRecord(e1, nullptr);
+    (void)hipEventRecord(e1, nullptr);
     if (hipEventSynchronize(e1) != hipSuccess) goto done;
     float t = 0.0f;
     if (hipEventElapsedTime(&t, e0, e1) != hipSuccess) goto done;
@@ -1624,10 +1919,10 @@ int fa_mfma_ceiling(int mode, int blocks, int reps, fa_mfma_rate *out) {
   }
   rc = FA_OK;
 done:
-  if (e0) hipEventDestroy(e0);
-  if (e1) hipEventDestroy(e1);
-  if (stamps) hipFree(stamps);
-  if (sink) hipFree(sink);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (stamps) (void)hipFree(stamps);
+  if (sink) (void)hipFree(sink);
   return rc;
 }
 
@@ -1658,7 +1953,7 @@ int fa_schedule_general(int B, int H, int H_kv, int S, int D, int causal, const 
   if (varlen && (B > fa::kMaxVarlenSeqs || s.nmb_max > fa::kMaxVarlenLevels)) return FA_ERR_UNSUPPORTED;
   static thread_local int len[fa::kMaxVarlenSeqs], sorted[fa::kMaxVarlenSeqs],
       off[fa::kMaxVarlenLevels + fa::kMaxVarlenSeqs + 1], key[fa::kMaxVarlenSeqs];
-  fa::SchedTables t{len, sorted, off, key};
+  fa::SchedTables t{len, sorted, off, key, nullptr};
   if (varlen) {
     fa::tables_phase1(s, cu_seqlens, cu_seqlens_k, t, 0, 1);
     fa::tables_phase2(s, t, 0, 1);
@@ -1729,6 +2024,66 @@ const char *fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 109; }
+int fa_split_plan(int B, int H, int S, int D, int workers, int requested, int *nsplit_out) {
+  if (!nsplit_out || B <= 0 || H <= 0 || S <= 0 || workers <= 0 || requested < -1)
+    return FA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128 && D != 192 && D != 256) return FA_ERR_UNSUPPORTED;
+  *nsplit_out = plan_nsplit(B, H, S, bm_for(D), workers, requested);
+  return FA_OK;
+}
+
+int fa_schedule_split(int B, int H, int S, int D, int nsplit, int workers, int *tiles,
+                      int max_rounds, int *rounds_out, int *bm_out) {
+  if (B <= 0 || H <= 0 || S <= 0 || workers <= 0 || !tiles || max_rounds <= 0 || nsplit < 0)
+    return FA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128 && D != 192 && D != 256) return FA_ERR_UNSUPPORTED;
+  const int BM = bm_for(D);
+  if (plan_nsplit(B, H, S, BM, workers, nsplit) != nsplit) return FA_ERR_INVALID_ARG;
+  const fa::Sched s = fa::make_sched(B, H, H, S, BM, 1, 0, workers, 1, nsplit);
+  int vl[fa::kMaxSplitLevels];
+  fa::SchedTables t{nullptr, nullptr, nullptr, nullptr, vl};
+  if (s.nsplit > 0) fa::split_levels(s, vl, 0, 1);
+  const int npos = fa::group_positions(s);
+  int x0, w0, W;
+  fa::worker_slot(s, 0, workers, &x0, &w0, &W);
+  std::vector<int> count(workers, 0);
+  auto put = [&](int wk, int p, int x) {
+    const fa::Tile tl = fa::decode_position(s, t, x, p);
+    if (count[wk] == max_rounds) return false;
+    tiles[(long long)wk * max_rounds + count[wk]++] =
+        ((tl.b * H + tl.h) * s.nmb_max + tl.mb) * 3 + tl.part;
+    return true;
+  };
+  if (fa::greedy_rounds(s, W)) {
+    for (int x = 0; x < s.groups; ++x) {
+      int load[fa::kGreedyMaxW] = {}, take[fa::kGreedyMaxW];
+      for (int r = 0; r * W < npos; ++r) {
+        fa::greedy_round(s, t, x, r, W, npos, load, take);
+        for (int w = 0; w < W; ++w)
+          if (take[w] >= 0 && !put(w * s.groups + x, take[w], x)) return FA_ERR_INVALID_ARG;
+      }
+    }
+  } else {
+    for (int wk = 0; wk < workers; ++wk) {
+      int x, w;
+      fa::worker_slot(s, wk, workers, &x, &w, &W);
+      for (int r = 0;; ++r) {
+        const int p = fa::snake_position(r, w, W);
+        if (p >= npos) break;
+        if (!put(wk, p, x)) return FA_ERR_INVALID_ARG;
+      }
+    }
+  }
+  int rounds = 0;
+  for (int wk = 0; wk < workers; ++wk) {
+    if (count[wk] > rounds) rounds = count[wk];
+    for (int r = count[wk]; r < max_rounds; ++r) tiles[(long long)wk * max_rounds + r] = -1;
+  }
+  if (rounds_out) *rounds_out = rounds;
+  if (bm_out) *bm_out = BM;
+  return FA_OK;
+}
+
+int fa_version(void) { return 110; }
 
 }  // extern "C"

@@ -21,7 +21,8 @@
 // Within an XCD, workers take positions W at a time (one round).  Dense
 // batches, whose rounds hold tiles of equal cost, pair them in "snake"
 // order: round r gives worker w position r*W + w on even rounds and
-// r*W + W-1-w on odd rounds.  Varlen causal batches, whose rounds mix costs
+// r*W + W-1-w on odd rounds.  Varlen causal batches (and dense causal
+// batches with split levels), whose rounds mix costs
 // (chunks of levels, idle positions), pair them greedily: the round's
 // costliest position goes to the worker with the least accumulated cost
 // (greedy_round; host model on the 16-sequence batch: the busiest worker
@@ -52,6 +53,17 @@
 //              (host model on a 16-sequence mixed batch: makespan 1.08x the
 //              ideal, against 1.43x for the level order).
 //
+//   dense causal with split levels: when a batch has few tiles, its
+//              costliest m-blocks outlast the mean worker load (B=2, H=16,
+//              S=2048: 32 key blocks against a mean of 18).  The nsplit
+//              costliest m-blocks then run as two parts, each over one half
+//              of the tile's key blocks (part 1 the first floor(n/2), part 2
+//              the rest with the diagonal), on workers of their own; the part
+//              that finishes second merges the two partial results.  A
+//              "virtual level" is an (m-block, part) pair; the levels are
+//              ordered by cost (descending) and paired with the workers in
+//              greedy rounds.
+//
 // The same code builds the tables on the host (tid = 0, nth = 1) for
 // fa_schedule() and in LDS on the device (tid = thread, nth = block size,
 // with a barrier between phases).
@@ -66,12 +78,14 @@ namespace fa {
 constexpr int kXcds = 8;
 constexpr int kMaxVarlenSeqs = 1024;     // persistent varlen table limit (B)
 constexpr int kMaxVarlenLevels = 2048;   // persistent varlen table limit (nmb_max)
+constexpr int kMaxSplitLevels = 64;      // virtual levels (m-blocks + split parts) of a dense split schedule
 
 struct SchedTables {
   int *len;        // [B] clamped (query) sequence lengths
   int *sorted;     // [B] sequence index by rank (sort key descending, index ascending)
   int *off;        // [nlev + 1] (causal: level-chunk offsets) or [B + 1] (rank offsets)
   int *key;        // [B] sort key: key lengths (by_klen), else the same as len
+  int *vl;         // [nvl] dense split schedule: virtual level by rank, mb | part << 16
 };
 
 struct Sched {
@@ -86,6 +100,8 @@ struct Sched {
   int groups;      // kXcds or 1
   int hpg;         // heads per group
   int n_items;     // number of (b, mb) items
+  int nsplit;      // dense causal: the nsplit costliest m-blocks run as two parts (0: none)
+  int nvl;         // dense causal: virtual levels, nmb_max + nsplit
 };
 
 FA_HD inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -94,7 +110,7 @@ FA_HD inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // level chunks of varlen causal batches apply only then: with key lengths of
 // their own a tile's cost follows its key length rather than its m-block).
 FA_HD inline Sched make_sched(int B, int H, int Hkv, int S, int BM, int causal, int varlen,
-                              int workers, int self_attn = 1) {
+                              int workers, int self_attn = 1, int nsplit = 0) {
   Sched s;
   s.B = B; s.H = H; s.S = S; s.BM = BM; s.causal = causal; s.varlen = varlen;
   s.G = H / Hkv;
@@ -112,8 +128,60 @@ FA_HD inline Sched make_sched(int B, int H, int Hkv, int S, int BM, int causal, 
     s.sub = k < 1 ? 1 : (k > 8 ? 8 : k);
   }
   s.nlev = ceil_div(s.nmb_max, s.sub);
-  s.n_items = B * s.nmb_max;  // dense; varlen fills it from the tables
+  s.nsplit = 0;
+  s.nvl = s.nmb_max;
+  if (!varlen && causal && nsplit > 0) {
+    s.nsplit = nsplit < s.nmb_max ? nsplit : s.nmb_max;
+    s.nvl = s.nmb_max + s.nsplit;
+    if (s.nvl > kMaxSplitLevels) {  // not representable: no split
+      s.nsplit = 0;
+      s.nvl = s.nmb_max;
+    }
+  }
+  s.n_items = B * s.nvl;  // dense; varlen fills it from the tables
   return s;
+}
+
+// ---- dense causal split levels ----
+
+// Key blocks (of 64) of part `part` of m-block mb in a dense causal
+// self-attention batch: part 0 is the whole key range of the tile, part 1
+// its first floor(n/2) blocks, part 2 the other ceil(n/2).
+FA_HD inline int split_blocks(const Sched &s, int mb, int part) {
+  const int e = (mb + 1) * s.BM;
+  const int n = ceil_div(e < s.S ? e : s.S, 64);
+  return part == 0 ? n : (part == 1 ? n / 2 : n - n / 2);
+}
+// Doubled cost (as tile_cost2) of a part; a split part adds the exchange
+// of its partial rows (written through to memory, counted, and for one of
+// the two parts read back and merged), measured at about nine key blocks'
+// time on B=1, H=16, S=2048.
+constexpr int kSplitMergeCost2 = 18;
+FA_HD inline int split_cost2(const Sched &s, int mb, int part) {
+  return 2 * split_blocks(s, mb, part) + 5 + (part ? kSplitMergeCost2 : 0);
+}
+// Virtual level i in natural order: the unsplit m-blocks 0 .. nmb-nsplit-1,
+// then both parts of each split m-block.  Code: mb | part << 16.
+FA_HD inline int split_natural(const Sched &s, int i) {
+  const int nfull = s.nmb_max - s.nsplit;
+  if (i < nfull) return i;
+  const int j = i - nfull;
+  return (nfull + j / 2) | ((1 + (j & 1)) << 16);
+}
+// vl[rank] = the virtual level of that cost rank (cost descending, ties:
+// natural order).
+FA_HD inline void split_levels(const Sched &s, int *vl, int tid, int nth) {
+  for (int i = tid; i < s.nvl; i += nth) {
+    const int ci = split_natural(s, i);
+    const int cost_i = split_cost2(s, ci & 0xffff, ci >> 16);
+    int rank = 0;
+    for (int k = 0; k < s.nvl; ++k) {
+      const int ck = split_natural(s, k);
+      const int cost_k = split_cost2(s, ck & 0xffff, ck >> 16);
+      rank += (cost_k > cost_i) || (cost_k == cost_i && k < i);
+    }
+    vl[rank] = ci;
+  }
 }
 
 // ---- varlen table construction, in phases (barrier between phases) ----
@@ -175,17 +243,25 @@ FA_HD inline int tables_phase4(const Sched &s, SchedTables t) {
 
 struct Tile {
   int b, h, mb;
+  int part;  // 0: the whole tile; 1, 2: a part of a split m-block
 };
 
 // Item index and level j within it (0 <= j < sub) -> (b, mb); b = -1 for a
 // level the sequence does not reach (an idle position).
 FA_HD inline void decode_item(const Sched &s, const SchedTables &t, int it, int j, int *b,
-                              int *mb) {
+                              int *mb, int *part) {
+  *part = 0;
   if (!s.varlen) {
     if (s.causal) {
       const int l = it / s.B;
       *b = it - l * s.B;
-      *mb = s.nmb_max - 1 - l;
+      if (s.nsplit > 0) {
+        const int c = t.vl[l];
+        *mb = c & 0xffff;
+        *part = c >> 16;
+      } else {
+        *mb = s.nmb_max - 1 - l;
+      }
     } else {
       *b = it / s.nmb_max;
       *mb = it - *b * s.nmb_max;
@@ -221,7 +297,7 @@ FA_HD inline Tile decode_position(const Sched &s, const SchedTables &t, int x, i
   const int rem = p - it * per;
   const int j = rem / s.hpg;
   const int hi = rem - j * s.hpg;
-  decode_item(s, t, it, j, &tl.b, &tl.mb);
+  decode_item(s, t, it, j, &tl.b, &tl.mb, &tl.part);
   if (s.kv_grouped) {
     // hi -> (K/V head x + groups*kvl, query head g of it); g innermost
     const int kvl = hi / s.G;
@@ -247,16 +323,17 @@ FA_HD inline int snake_position(int r, int w, int W) {
   return r * W + ((r & 1) ? (W - 1 - w) : w);
 }
 
-// ---- greedy rounds (varlen causal batches) ----
+// ---- greedy rounds (varlen causal batches, dense causal split levels) ----
 constexpr int kGreedyMaxW = 64;  // one lane per worker of a group on the device
 FA_HD inline bool greedy_rounds(const Sched &s, int W) {
-  return s.varlen && s.causal && W <= kGreedyMaxW;
+  return s.causal && (s.varlen || s.nsplit > 0) && W <= kGreedyMaxW;
 }
 
 // Doubled cost of a tile: two per 64-key block it reads, plus 5 for its
 // fixed part (about 2.5 blocks: the pipeline's fill and drain and the
 // epilogue).  The key range follows the kernel's causal bound.
 FA_HD inline int tile_cost2(const Sched &s, const SchedTables &t, const Tile &tl) {
+  if (!s.varlen) return split_cost2(s, tl.mb, tl.part);
   const int L = t.len[tl.b];
   const int Lk = s.by_klen ? t.key[tl.b] : L;
   const int e = tl.mb * s.BM + s.BM + (Lk - L);

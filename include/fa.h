@@ -112,16 +112,43 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  *   schedule   0 = persistent workgroups walking the tiles in
  *              longest-processing-time-first order (paper section 3.3);
  *              1 = one workgroup per tile in natural (batch, head, m-block)
- *              order.  Both give bitwise identical results.
+ *              order.  Both give bitwise identical results when no level is
+ *              split (split_levels below).
  *   counters   NULL, or a device array of 2 uint64 that the call adds to:
  *              [0] wavefront-level rescale events, [1] wavefront-block steps
  *              (their ratio is the rescale rate).  Slower; for measurement.
+ *   split_levels  Dense causal self-attention (no cu_seqlens, S_q = S_k)
+ *              under schedule 0: the number of costliest m-block levels run
+ *              as two parts, each over half of the tile's key blocks on a
+ *              workgroup of its own, the second part to finish merging both
+ *              partial results (O normalised per part and its LSE, combined
+ *              by their LSE weights).  When a batch has few tiles, its
+ *              last m-blocks, which read every key, otherwise outlast the
+ *              mean worker load (B=2, H=16, S=2048: 32 key blocks against a
+ *              mean of 18).  Each split tile exchanges its two parts'
+ *              partial rows through memory, which costs about nine key
+ *              blocks' time, so splitting pays only where workers would
+ *              otherwise idle.  -1 = chosen by the library: only batches
+ *              whose tiles leave at least half of the workers idle, and
+ *              only as many levels as its makespan model finds shorten the
+ *              busiest worker by 5% (B=1, H=8, S=3000: 19% faster; B=2,
+ *              H=16, S=2048 stays whole), 0 = never,
+ *              n > 0 = the n costliest (clamped to what the schedule holds:
+ *              at most ceil(S/BM) levels and 64 levels in all); other
+ *              values are FA_ERR_INVALID_ARG.  A split launch keeps a
+ *              workspace per device and stream (counters and partial rows,
+ *              up to 512 MiB), allocated on first need and kept until the
+ *              process ends; when it cannot be allocated (or the stream is
+ *              being captured into a graph and it would have to grow) the
+ *              launch runs unsplit.  Results of split and unsplit launches
+ *              differ by the fp32 rounding of the merge.  Default -1.
  */
 typedef struct fa_tuning {
     float tau;
     int exp2_emu;
     int schedule;
     unsigned long long *counters;
+    int split_levels;
 } fa_tuning;
 
 fa_tuning fa_tuning_default(void);
@@ -398,6 +425,25 @@ int fa_schedule_general(int B, int H, int H_kv, int S_q, int D, int causal,
                         const int *cu_seqlens_q, const int *cu_seqlens_k, int workers, int *tiles,
                         int max_rounds, int *rounds_out, int *bm_out);
 
+/*
+ * fa_split_plan -- host-only: the split_levels count (fa_tuning) a dense
+ * causal self-attention launch of B x H heads of S tokens with head
+ * dimension D uses on `workers` persistent workgroups, for a requested
+ * count (-1: the makespan model's choice).  No GPU use.
+ */
+int fa_split_plan(int B, int H, int S, int D, int workers, int requested, int *nsplit_out);
+
+/*
+ * fa_schedule_split -- fa_schedule for a dense causal batch with the nsplit
+ * costliest m-block levels split in two parts (0 <= nsplit <= what
+ * fa_split_plan allows; FA_ERR_INVALID_ARG otherwise).  A work item is
+ * encoded as ((seq * H + head) * n_mblocks_max + mblock) * 3 + part, part 0
+ * being a whole tile and parts 1 and 2 the first and second half of a split
+ * tile's key blocks.  No GPU use.
+ */
+int fa_schedule_split(int B, int H, int S, int D, int nsplit, int workers, int *tiles,
+                      int max_rounds, int *rounds_out, int *bm_out);
+
 /* Number of persistent workgroups fa_fwd launches on the current device. */
 int fa_num_workers(int D, int *workers_out);
 
@@ -446,7 +492,8 @@ const char *fa_status_string(int status);
 
 /* Library ABI version: 100 * major + minor (101: fa_fwd_gqa; 102: fa_fwd_hd;
  * 103: fa_fwd_general; 104: fa_bwd; 105: fa_fwd_splitkv; 106: fa_bwd_general;
- * 107: fa_fwd_splitkv_noalloc; 108: fa_mfma_ceiling; 109: fa_bwd_hd). */
+ * 107: fa_fwd_splitkv_noalloc; 108: fa_mfma_ceiling; 109: fa_bwd_hd;
+ * 110: fa_tuning.split_levels, fa_split_plan, fa_schedule_split). */
 int fa_version(void);
 
 #ifdef __cplusplus

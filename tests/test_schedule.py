@@ -232,3 +232,79 @@ def test_schedule_general_rejects_one_sided_key_offsets():
         fa._check("fa_schedule_general", fa.load().fa_schedule_general(
             1, 8, 8, 10, 128, 1, cu.ctypes.data, None, 8, tiles.ctypes.data, 16,
             ctypes.byref(r), ctypes.byref(b)))
+
+
+# ---- dense causal split levels
+
+SPLIT_CASES = [
+    # (B, H, S, D, nsplit)
+    (2, 16, 2048, 128, 8),
+    (2, 16, 2048, 128, 3),
+    (1, 16, 4096, 128, 16),
+    (2, 3, 700, 128, 2),
+    (1, 8, 3000, 256, 12),
+    (1, 2, 900, 64, 2),
+    (2, 16, 1500, 192, 3),
+]
+
+
+def split_part_blocks(mb, part, S, BM):
+    """Key blocks (of 64) a part reads: the whole causal range of m-block mb,
+    its first floor(n/2) blocks, or the rest."""
+    n = -(-min((mb + 1) * BM, S) // 64)
+    return n if part == 0 else (n // 2 if part == 1 else n - n // 2)
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "B%dH%dS%dD%d_n%d" % c)
+def test_split_schedule_covers_every_part_once(case):
+    """Every unsplit tile runs once whole; each of the nsplit costliest
+    m-blocks of every (sequence, head) runs once as part 1 and once as
+    part 2, and never whole."""
+    B, H, S, D, nsplit = case
+    items, BM = fa.schedule_split(B, H, S, D, nsplit, 256)
+    nmb = -(-S // BM)
+    got = sorted(items[items >= 0].tolist())
+    want = []
+    for b in range(B):
+        for h in range(H):
+            for mb in range(nmb):
+                base = ((b * H + h) * nmb + mb) * 3
+                want += [base + 1, base + 2] if mb >= nmb - nsplit else [base]
+    assert got == sorted(want)
+
+
+def test_split_schedule_shortens_the_busiest_worker():
+    """On a one-sequence 2k causal batch (B=1, H=16: half the workers idle
+    unsplit) the library splits levels, and its order's busiest worker
+    carries less than the unsplit order's (cost units: two per key block,
+    five per tile, 18 more per part for the exchange of partial rows)."""
+    B, H, S, D = 1, 16, 2048, 128
+    n = fa.split_plan(B, H, S, D, 256)
+    assert n > 0
+
+    def busiest(nsplit):
+        items, BM = fa.schedule_split(B, H, S, D, nsplit, 256)
+        nmb = -(-S // BM)
+        worst = 0
+        for row in items:
+            load = 0
+            for code in row[row >= 0].tolist():
+                part, mb = code % 3, (code // 3) % nmb
+                load += 2 * split_part_blocks(mb, part, S, BM) + 5 + (18 if part else 0)
+            worst = max(worst, load)
+        return worst
+
+    assert busiest(n) <= 0.85 * busiest(0)
+
+
+def test_split_plan_leaves_large_batches_whole():
+    """Batches that fill the workers (the 2k, 8k and 32k causal workloads)
+    are not split by default; a request is clamped to what the schedule
+    holds (every m-block, at most 64 levels in all)."""
+    for B, H, S in ((1, 16, 32768), (2, 16, 8192), (64, 64, 2048), (2, 16, 2048)):
+        assert fa.split_plan(B, H, S, 128, 256) == 0
+    assert fa.split_plan(2, 16, 2048, 128, 256, requested=100) == 8
+    assert fa.split_plan(2, 16, 2048, 128, 256, requested=0) == 0
+    assert fa.split_plan(1, 16, 16384, 128, 256, requested=5) == 0  # 64 m-blocks: no room
+    with pytest.raises(RuntimeError):
+        fa.schedule_split(2, 16, 2048, 128, 9, 256)  # more than the schedule holds

@@ -444,6 +444,11 @@ def main():
                      "kernel_ms_median": round(r["kernel_ms_median"], 4),
                      "kernel_ms_min": round(r["kernel_ms_min"], 4)},
     }
+    # the peak's inputs as the device reports them (CU count, peak shader clock)
+    dev = fa.device_info()
+    out["roofline"]["device"] = {
+        "cus": dev["cus"], "peak_clock_mhz": dev["peak_clock_mhz"],
+        "peak_from_device": round(4096 * dev["cus"] * dev["peak_clock_mhz"] * 1e-6, 1)}
     if not args.no_ceiling:
         # right after the timed steps, at the clock the GPU has settled to
         c0 = fa.mfma_ceiling(0, CEILING_BLOCKS, 7)

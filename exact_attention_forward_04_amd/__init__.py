@@ -124,6 +124,8 @@ def _declare(lib, backward: bool = True):
     lib.fa_schedule_general.restype = I
     lib.fa_num_workers.argtypes = [I, ctypes.POINTER(I)]
     lib.fa_num_workers.restype = I
+    lib.fa_device_info.argtypes = [ctypes.POINTER(I), ctypes.POINTER(I)]
+    lib.fa_device_info.restype = I
     lib.fa_split_plan.argtypes = [I, I, I, I, I, I, ctypes.POINTER(I)]
     lib.fa_split_plan.restype = I
     lib.fa_schedule_split.argtypes = [I, I, I, I, I, I, P, I, ctypes.POINTER(I), ctypes.POINTER(I)]
@@ -492,6 +494,14 @@ def schedule(B: int, H: int, S: int, D: int, causal: bool, workers: int,
                                  ctypes.byref(bm))
         _check("fa_schedule_gqa", rc)
     return tiles[:, :rounds.value].copy(), bm.value
+
+
+def device_info() -> dict:
+    """The current device as the library sees it (fa_device_info): compute
+    units and peak shader clock."""
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    _check("fa_device_info", load().fa_device_info(ctypes.byref(cus), ctypes.byref(khz)))
+    return {"cus": cus.value, "peak_clock_mhz": khz.value / 1000.0}
 
 
 def split_plan(B: int, H: int, S: int, D: int, workers: int, requested: int = -1) -> int:

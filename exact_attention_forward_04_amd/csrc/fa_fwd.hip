@@ -2002,6 +2002,16 @@ int fa_schedule_general(int B, int H, int H_kv, int S, int D, int causal, const 
   return FA_OK;
 }
 
+int fa_device_info(int *cus_out, int *clock_khz_out) {
+  if (!cus_out || !clock_khz_out) return FA_ERR_INVALID_ARG;
+  DeviceInfo *dev = nullptr;
+  const int rc = current_device(&dev);
+  if (rc != FA_OK) return rc;
+  *cus_out = dev->cus;
+  *clock_khz_out = dev->clock_khz;
+  return FA_OK;
+}
+
 int fa_num_workers(int D, int *workers_out) {
   if (!workers_out) return FA_ERR_INVALID_ARG;
   if (D != 64 && D != 128 && D != 192 && D != 256) return FA_ERR_UNSUPPORTED;

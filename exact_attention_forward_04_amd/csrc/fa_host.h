@@ -19,6 +19,7 @@ namespace {
 struct DeviceInfo {
   int ok = 0;
   int cus = 0;
+  int clock_khz = 0;  // peak shader clock
 };
 
 DeviceInfo g_dev[64];
@@ -32,6 +33,7 @@ int current_device(DeviceInfo **out) {
     if (hipGetDeviceProperties(&p, dev) != hipSuccess) return;
     if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0) return;
     g_dev[dev].cus = p.multiProcessorCount;
+    g_dev[dev].clock_khz = p.clockRate;
     g_dev[dev].ok = 1;
   });
   if (!g_dev[dev].ok) return FA_ERR_NO_DEVICE;

@@ -444,6 +444,14 @@ int fa_split_plan(int B, int H, int S, int D, int workers, int requested, int *n
 int fa_schedule_split(int B, int H, int S, int D, int nsplit, int workers, int *tiles,
                       int max_rounds, int *rounds_out, int *bm_out);
 
+/*
+ * fa_device_info -- the current device as the library sees it: its compute
+ * unit count and peak shader clock in kHz (the figures a dense MFMA peak is
+ * computed from: CUs x 4096 bf16 flop per clock x clock).  FA_ERR_NO_DEVICE
+ * when the current device is not a gfx950.
+ */
+int fa_device_info(int *cus_out, int *clock_khz_out);
+
 /* Number of persistent workgroups fa_fwd launches on the current device. */
 int fa_num_workers(int D, int *workers_out);
 
@@ -493,7 +501,7 @@ const char *fa_status_string(int status);
 /* Library ABI version: 100 * major + minor (101: fa_fwd_gqa; 102: fa_fwd_hd;
  * 103: fa_fwd_general; 104: fa_bwd; 105: fa_fwd_splitkv; 106: fa_bwd_general;
  * 107: fa_fwd_splitkv_noalloc; 108: fa_mfma_ceiling; 109: fa_bwd_hd;
- * 110: fa_tuning.split_levels, fa_split_plan, fa_schedule_split). */
+ * 110: fa_tuning.split_levels, fa_split_plan, fa_schedule_split, fa_device_info). */
 int fa_version(void);
 
 #ifdef __cplusplus

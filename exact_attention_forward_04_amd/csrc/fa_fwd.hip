@@ -717,11 +717,8 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       barrier_after_reads();
       issue_block(j + 1);
     };
-    // S_j, its mask and row max, and the rescale decision.  This body keeps
-    // the max-first form of the rescale test: its exponentials run between
-    // the PV products, and holding the scores until a decision taken after
-    // them (softmax_step's form) would take 32 registers it does not have.
-    auto scores = [&](int j, float &m_use) {
+    // S_j and its mask.
+    auto scores = [&](int j) {
       qk_step<D>(st, la, kslot(j), kslot(j));
       if (wr.need_mask(j, Lk, false)) {
         const int lim = mask_limit<false>(lane, j * kBN, qi + koff, Lk);
@@ -730,6 +727,11 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
 #pragma unroll
           for (int e0 = 0; e0 < 16; e0 += 8) mask_slice(st.s, kb, e0, lim);
       }
+    };
+    // The max-first form of the rescale test: the block's row maximum, then
+    // the decision (rescale_decide).  The first block takes it (no row has a
+    // reference yet); later blocks take the exponential-based form.
+    auto decide = [&](float &m_use) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -743,8 +745,9 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     if (nblocks > 0) {
       issue_block(0);
       open(0);
+      scores(0);
       float m_use;
-      const Rescale r = scores(0, m_use);  // O is still zero: nothing to scale
+      const Rescale r = decide(m_use);  // O is still zero: nothing to scale
       (void)r;
       float lsum[2] = {0.0f, 0.0f};
       const bool last = nblocks == 1;
@@ -758,13 +761,27 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
 #pragma unroll
       for (int t = 0; t < 4; ++t) p_prev[t] = st.p[t];
       open(j);
-      float m_use;
-      const Rescale r = scores(j, m_use);
+      scores(j);
+      const bool last = j == nblocks - 1;
       float lsum[2] = {0.0f, 0.0f};
-      pv_with_exp<D, EMU>(st, la, vslot(j - 1), p_prev, st.s, st.p, m_use, j == nblocks - 1, a,
+      // The exponentials against the reference as it stands, between the PV
+      // products of block j-1 (softmax_step's test): when every lane's share
+      // of the block's row sum stays within 2^tau, so does every p, and the
+      // block needs no row maximum.  Otherwise the wave takes the rescale
+      // path, after those products: the block's row maximum, O and the row
+      // sum scaled to the new reference, the exponentials again.  (Every row
+      // has a reference after block 0, which every row of a non-causal dense
+      // tile sees in full; a row that still had none would fail the test and
+      // take the rescale path, whose exponentials replace these.)
+      pv_with_exp<D, EMU>(st, la, vslot(j - 1), p_prev, st.s, st.p, m_use_of<D>(st), last, a,
                           lsum);
-      st.l32 += lsum[0] + lsum[1];
-      if (r.any) scale_o<D>(st, r.alpha);
+      float ls = lsum[0] + lsum[1];
+      if (__builtin_amdgcn_ballot_w64(!(ls <= a.bound)) != 0)
+        ls = rescale_block<D, EMU, COUNT>(st, lane, last, a);
+      if constexpr (COUNT) {
+        if (lane == 0) atomicAdd(&a.counters[1], 1ull);
+      }
+      st.l32 += ls;
     }
     if (nblocks > 0) {
       open(nblocks);

@@ -682,15 +682,16 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
         __builtin_amdgcn_s_setprio(0);
       }
     }
-  } else if constexpr (!VARLEN && !CAUSAL) {
+  } else if constexpr (!VARLEN) {
     // One wave per SIMD (D = 256: O alone is 128 registers per lane), so
     // the matrix/softmax overlap comes from within the wave.  The iteration
-    // of block j runs S_j = K_j Q^T, the mask, row max and rescale decision
-    // of block j and its exp loop between the PV products of block j-1 (two
-    // P register sets).  O is scaled after those products, which still use
-    // the old scale.  Without a causal mask every wave runs
-    // every block, so the loop has one path: a wave whose rows lie past the
-    // sequence end works on clamped rows and stores nothing.  V_{j-1} is
+    // of block j runs S_j = K_j Q^T and its mask, then the exp loop of block
+    // j between the PV products of block j-1 (two P register sets), then
+    // the rescale decision.  Every wave runs every block of the tile, so the
+    // loop has one path: a wave whose rows lie past the sequence end works
+    // on clamped rows and stores nothing, and under a causal mask the blocks
+    // past a wave's diagonal are fully masked (their exponentials are zero;
+    // at most the tile's last two blocks for some of its waves).  V_{j-1} is
     // read in the iteration of block j, so K sits in a ring of two 32 KiB
     // slots and V in a ring of three (160 KiB in all).  After the barrier
     // that opens iteration j, slot ((j+1)&1) of K (K_{j-1}) and slot
@@ -720,8 +721,8 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
     // S_j and its mask.
     auto scores = [&](int j) {
       qk_step<D>(st, la, kslot(j), kslot(j));
-      if (wr.need_mask(j, Lk, false)) {
-        const int lim = mask_limit<false>(lane, j * kBN, qi + koff, Lk);
+      if (wr.need_mask(j, Lk, CAUSAL)) {
+        const int lim = mask_limit<CAUSAL>(lane, j * kBN, qi + koff, Lk);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -750,7 +751,7 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       const Rescale r = decide(m_use);  // O is still zero: nothing to scale
       (void)r;
       float lsum[2] = {0.0f, 0.0f};
-      const bool last = nblocks == 1;
+      const bool last = wr.last_block == 0;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -762,17 +763,17 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       for (int t = 0; t < 4; ++t) p_prev[t] = st.p[t];
       open(j);
       scores(j);
-      const bool last = j == nblocks - 1;
+      const bool last = j == wr.last_block;  // the wave's last block with keys
       float lsum[2] = {0.0f, 0.0f};
       // The exponentials against the reference as it stands, between the PV
       // products of block j-1 (softmax_step's test): when every lane's share
       // of the block's row sum stays within 2^tau, so does every p, and the
       // block needs no row maximum.  Otherwise the wave takes the rescale
       // path, after those products: the block's row maximum, O and the row
-      // sum scaled to the new reference, the exponentials again.  (Every row
-      // has a reference after block 0, which every row of a non-causal dense
-      // tile sees in full; a row that still had none would fail the test and
-      // take the rescale path, whose exponentials replace these.)
+      // sum scaled to the new reference, the exponentials again.  (A row has
+      // a reference after block 0 unless the causal alignment leaves it no
+      // key there; such a row's scores stay -inf until its first key, whose
+      // exponentials then fail the test and take the rescale path.)
       pv_with_exp<D, EMU>(st, la, vslot(j - 1), p_prev, st.s, st.p, m_use_of<D>(st), last, a,
                           lsum);
       float ls = lsum[0] + lsum[1];
@@ -965,10 +966,10 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
 
 // Dynamic LDS of a kernel instance: the ping-pong K/V ring; for the
 // single-wave body, rings of two K and three V blocks (the pipelined dense
-// non-causal body) or the double buffer.
+// body) or the double buffer (varlen, whose tables need the rest).
 template <int D, bool VARLEN, bool CAUSAL>
 constexpr int lds_bytes() {
-  return Cfg<D>::PINGPONG ? KvLayout<D>::BYTES : (VARLEN || CAUSAL ? 4 : 5) * Cfg<D>::K_BYTES;
+  return Cfg<D>::PINGPONG ? KvLayout<D>::BYTES : (VARLEN ? 4 : 5) * Cfg<D>::K_BYTES;
 }
 
 // Persistent kernel: each workgroup walks its static LPT list.
@@ -1696,7 +1697,9 @@ int fa_fwd_general(const void *q, const void *k, const void *v, void *o, float *
   a.hs_cnt = nullptr;
   hipStream_t st = (hipStream_t)stream;
   const bool varlen = cu_seqlens_q != nullptr;
-  if (causal && !varlen && S_q == S_k && t.schedule == 0 && t.split_levels != 0) {
+  // (not for D = 256, whose pipelined body takes all 160 KiB of LDS: the split
+  // schedule's tables would not fit beside it)
+  if (causal && !varlen && S_q == S_k && t.schedule == 0 && t.split_levels != 0 && D != 256) {
     const int BM = bm_for(D), NW = nw_for(D);
     const int n = plan_nsplit(B, H, S_q, BM, dev->cus, t.split_levels);
     int *cnt = nullptr;
@@ -2055,7 +2058,7 @@ int fa_split_plan(int B, int H, int S, int D, int workers, int requested, int *n
   if (!nsplit_out || B <= 0 || H <= 0 || S <= 0 || workers <= 0 || requested < -1)
     return FA_ERR_INVALID_ARG;
   if (D != 64 && D != 128 && D != 192 && D != 256) return FA_ERR_UNSUPPORTED;
-  *nsplit_out = plan_nsplit(B, H, S, bm_for(D), workers, requested);
+  *nsplit_out = D == 256 ? 0 : plan_nsplit(B, H, S, bm_for(D), workers, requested);
   return FA_OK;
 }
 
@@ -2065,7 +2068,8 @@ int fa_schedule_split(int B, int H, int S, int D, int nsplit, int workers, int *
     return FA_ERR_INVALID_ARG;
   if (D != 64 && D != 128 && D != 192 && D != 256) return FA_ERR_UNSUPPORTED;
   const int BM = bm_for(D);
-  if (plan_nsplit(B, H, S, BM, workers, nsplit) != nsplit) return FA_ERR_INVALID_ARG;
+  if ((D == 256 && nsplit > 0) || plan_nsplit(B, H, S, BM, workers, nsplit) != nsplit)
+    return FA_ERR_INVALID_ARG;
   const fa::Sched s = fa::make_sched(B, H, H, S, BM, 1, 0, workers, 1, nsplit);
   int vl[fa::kMaxSplitLevels];
   fa::SchedTables t{nullptr, nullptr, nullptr, nullptr, vl};

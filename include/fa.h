@@ -118,7 +118,8 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  *              [0] wavefront-level rescale events, [1] wavefront-block steps
  *              (their ratio is the rescale rate).  Slower; for measurement.
  *   split_levels  Dense causal self-attention (no cu_seqlens, S_q = S_k)
- *              under schedule 0: the number of costliest m-block levels run
+ *              with D < 256 under schedule 0: the number of costliest
+ *              m-block levels run
  *              as two parts, each over half of the tile's key blocks on a
  *              workgroup of its own, the second part to finish merging both
  *              partial results (O normalised per part and its LSE, combined
@@ -429,14 +430,15 @@ int fa_schedule_general(int B, int H, int H_kv, int S_q, int D, int causal,
  * fa_split_plan -- host-only: the split_levels count (fa_tuning) a dense
  * causal self-attention launch of B x H heads of S tokens with head
  * dimension D uses on `workers` persistent workgroups, for a requested
- * count (-1: the makespan model's choice).  No GPU use.
+ * count (-1: the makespan model's choice; always 0 for D = 256).  No GPU
+ * use.
  */
 int fa_split_plan(int B, int H, int S, int D, int workers, int requested, int *nsplit_out);
 
 /*
  * fa_schedule_split -- fa_schedule for a dense causal batch with the nsplit
  * costliest m-block levels split in two parts (0 <= nsplit <= what
- * fa_split_plan allows; FA_ERR_INVALID_ARG otherwise).  A work item is
+ * fa_split_plan allows, 0 for D = 256; FA_ERR_INVALID_ARG otherwise).  A work item is
  * encoded as ((seq * H + head) * n_mblocks_max + mblock) * 3 + part, part 0
  * being a whole tile and parts 1 and 2 the first and second half of a split
  * tile's key blocks.  No GPU use.

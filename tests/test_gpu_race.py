@@ -92,7 +92,7 @@ def test_race_check_dense_workloads(libs, name):
     (192, 128, True, 2000),     # two-part K layout, 3-slot K ring
     (192, 128, False, 1100),
     (256, 256, False, 2000),    # the pipelined single-wave body
-    (256, 256, True, 1500),     # the serial body
+    (256, 256, True, 1500),     # the same body under a causal mask
     (64, 64, True, 1500),
 ])
 def test_race_check_head_dims(libs, D, Dv, causal, S):
@@ -102,11 +102,12 @@ def test_race_check_head_dims(libs, D, Dv, causal, S):
                 Dv, causal)
 
 
-def test_race_check_small_varlen(libs):
+@pytest.mark.parametrize("D", [128, 256])   # D = 256 varlen: the serial single-wave body
+def test_race_check_small_varlen(libs, D):
     lens = [1, 63, 64, 65, 300, 1000, 2049, 0, 130]
     cu = cu_seqlens_of(lens)
-    H, D = 4, 128
-    note("race-check varlen", lens)
+    H = 4
+    note("race-check varlen", lens, "D", D)
     q, k, v = draw_qkv((int(cu[-1]), H, D), seed=410)
     dcu = torch.from_numpy(np.asarray(cu, np.int32)).cuda()
     q, k, v = (t.cuda() for t in (q, k, v))

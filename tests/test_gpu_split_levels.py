@@ -50,13 +50,12 @@ def run(q, k, v, scale, levels, stream=None, return_lse=True):
 
 
 CASES = [
-    # (B, S, H, D, D_v, split levels): ragged tails, every head dimension,
-    # some and all m-blocks split
+    # (B, S, H, D, D_v, split levels): ragged tails, every head dimension
+    # that splits (D = 256 never does), some and all m-blocks split
     (1, 1500, 4, 128, 128, -1),   # the library's own choice (one level)
     (1, 1000, 2, 64, 64, 3),
     (1, 1500, 4, 128, 128, 6),
     (2, 1100, 2, 192, 128, 5),
-    (1, 700, 2, 256, 256, 6),
     (1, 300, 2, 128, 128, 2),
     (1, 65, 1, 128, 128, 1),
 ]

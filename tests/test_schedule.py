@@ -242,7 +242,7 @@ SPLIT_CASES = [
     (2, 16, 2048, 128, 3),
     (1, 16, 4096, 128, 16),
     (2, 3, 700, 128, 2),
-    (1, 8, 3000, 256, 12),
+    (1, 8, 3000, 192, 12),
     (1, 2, 900, 64, 2),
     (2, 16, 1500, 192, 3),
 ]
@@ -308,3 +308,8 @@ def test_split_plan_leaves_large_batches_whole():
     assert fa.split_plan(1, 16, 16384, 128, 256, requested=5) == 0  # 64 m-blocks: no room
     with pytest.raises(RuntimeError):
         fa.schedule_split(2, 16, 2048, 128, 9, 256)  # more than the schedule holds
+    # D = 256: its pipelined body takes the whole LDS, so it never splits
+    assert fa.split_plan(1, 8, 3000, 256, 256) == 0
+    assert fa.split_plan(1, 8, 3000, 256, 256, requested=4) == 0
+    with pytest.raises(RuntimeError):
+        fa.schedule_split(1, 8, 3000, 256, 2, 256)

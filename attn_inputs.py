@@ -209,4 +209,7 @@ WORKLOADS = {
     "decode_1x_q1_k32768_h32kv8d128": Workload(
         "decode_1x_q1_k32768_h32kv8d128", 1, 32768, 32, 128, True, seed=11,
         varlen=(1, 32768, 32768), q_range=(1, 1), Hkv=8),
+    # The wide head under a causal mask (the shape of a long-context model
+    # with 256-wide heads), N(0, 1).
+    "causal_b2h16s8192d256": Workload("causal_b2h16s8192d256", 2, 8192, 16, 256, True, seed=12),
 }

@@ -139,6 +139,7 @@ def gather_rows(o, lse, rows, w, cu):
     ("wide_b2h16s8192d256_spread3", 512),
     ("gqa_b2h32kv8s8192d128_causal", 512),
     ("hd192v128_b2h16s8192_causal", 512),
+    ("causal_b2h16s8192d256", 512),
 ])
 def test_named_sampled(name, n):
     w = WORKLOADS[name]
@@ -175,7 +176,7 @@ ALL_OUTPUTS = ["wide_b2h16s8192d256_spread3", "causal_b2h16s8192d128", "dense_b2
                "dense_b2h16s2048d128_causal", "gqa_b2h32kv8s8192d128_causal",
                "hd192v128_b2h16s8192_causal", "long_b1h16s32768d128_causal",
                "varlen_16x512to8192_h32d128_causal",
-               "mixed_16x_q1to2048_k512to8192_h16d128_causal"]
+               "mixed_16x_q1to2048_k512to8192_h16d128_causal", "causal_b2h16s8192d256"]
 
 
 @pytest.mark.parametrize("name", ALL_OUTPUTS)

@@ -79,7 +79,8 @@ def dense_case(B, S, H, D, Dv, causal, seed, Hkv=None, q_std=1.0):
 
 
 @pytest.mark.parametrize("name", ["dense_b2h16s2048d128_causal", "causal_b2h16s8192d128",
-                                  "dense_b2h16s2048d128", "gqa_b2h32kv8s8192d128_causal"])
+                                  "dense_b2h16s2048d128", "gqa_b2h32kv8s8192d128_causal",
+                                  "causal_b2h16s8192d256"])
 def test_race_check_dense_workloads(libs, name):
     w = WORKLOADS[name]
     note("race-check", name)

@@ -15,9 +15,9 @@
 //     w % 8 because the dispatcher deals workgroups to XCDs round-robin.
 //     With grouped-query attention (G = H / Hkv query heads per K/V head)
 //     and Hkv a multiple of 8, XCD x owns the K/V heads x, x+8, ... and all
-//     G query heads of each, visited one K/V head at a time (the survey of
-//     the paper's section 3.3: walk every query head of one K/V head before
-//     moving on), so a K/V head is read into one L2 only.
+//     G query heads of each, visited one K/V head at a time (every query
+//     head of one K/V head before the next, as the paper's section 3.3
+//     orders grouped-query tiles), so a K/V head is read into one L2 only.
 // Within an XCD, workers take positions W at a time (one round).  Dense
 // batches, whose rounds hold tiles of equal cost, pair them in "snake"
 // order: round r gives worker w position r*W + w on even rounds and

@@ -648,6 +648,11 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
         side(1);
       }
     };
+    // A persistent workgroup's waves leave a tile at different times (half
+    // 1's last PV runs after half 0's): every wave is done reading the
+    // previous tile's ring before this tile's first copies overwrite it.
+    // (Placed after the Q load, whose latency covers the wait.)
+    barrier_after_reads();
     if (nblocks > 0) {
       ldk.issue_at(kseq, 0, Lk, kbuf(0), kbuf2(0));
       ldv.issue_at(vseq, 0, Lk, vbuf(0));
@@ -743,6 +748,9 @@ __device__ __forceinline__ void run_tile(const Args &a, int b, int h, int mb, ch
       return r;
     };
     bf16x8 p_prev[4];
+    // every wave is done reading the previous tile's rings (the last PV of a
+    // persistent workgroup's previous tile) before this tile's first copies
+    barrier_after_reads();
     if (nblocks > 0) {
       issue_block(0);
       open(0);

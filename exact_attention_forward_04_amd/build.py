@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = [os.path.join(CSRC, "fa_fwd.hip"), os.path.join(CSRC, "fa_bwd.hip")]
-HEADERS = [os.path.join(CSRC, n) for n in ("fa_sched.h", "exp2_poly.h", "fa_tile.h", "fa_host.h")] + \
+HEADERS = [os.path.join(CSRC, n) for n in ("fa_sched.h", "exp2_poly.h", "fa_tile.h", "fa_host.h",
+                                           "fa_mask_runs.h")] + \
           [os.path.join(ROOT, "include", "fa.h")]
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)

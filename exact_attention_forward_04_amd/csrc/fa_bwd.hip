@@ -48,6 +48,7 @@
 
 #include "fa.h"
 #include "fa_host.h"
+#include "fa_mask_runs.h"
 #include "fa_sched.h"
 #include "fa_tile.h"
 
@@ -531,7 +532,9 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
   // Ring of four slots, copies two blocks ahead (as in fa_bwd_dq).
   if (nblocks > 0) issue(0);
   if (nblocks > 1) issue(1);
-  for (int t = 0; t < nblocks; ++t) {
+  // Block t (masked: with the entry mask).
+  auto step = [&](int t, auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
     if (t + 2 < nblocks) issue(t + 2);
     wait_block(t + 2 < nblocks ? 2 : (t + 1 < nblocks ? 1 : 0));
     barrier_nofence();
@@ -543,10 +546,8 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
       const unsigned qt0 = la.vw0 + lds_u32(qbuf(t)), qt1 = la.vw1 + lds_u32(qbuf(t));
       const float LDS_AS *lse_l = (const float LDS_AS *)sbuf(t);
       const float LDS_AS *del_l = lse_l + kBN;
-      // Blocks off the diagonal and inside the sequence (the common case)
-      // get bounds that keep every entry: one select per entry, no branch
-      // (a branch would duplicate the body, and the two copies would hold
-      // the dK/dV accumulators in different registers).
+      // The bounds of the masked body (blocks that need no mask run without
+      // it; a masked block off the diagonal gets bounds that keep every entry).
       const bool need_mask = (m0 + kBN > L) || (CAUSAL && m0 < key0 - koff + 31);
       const int hi = need_mask ? L - m0 - 4 * hh : INT_MAX;
       const int lo = (need_mask && CAUSAL) ? key - koff - m0 - 4 * hh : INT_MIN;
@@ -598,7 +599,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
           const int g4 = e >> 2, jj = e & 3;
           const int off = 32 * i + 8 * g4 + jj;
           float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -(l4[i][g4][jj] * kLog2e)));
-          p = ((unsigned)(off - lo_c) < span) ? p : 0.0f;
+          if constexpr (MASKED) p = ((unsigned)(off - lo_c) < span) ? p : 0.0f;
           const int tt = 2 * i + (e >> 3);
           p8[tt][e & 7] = (__bf16)p;
           ds8[tt][e & 7] = (__bf16)(p * (dp[i][e] - d4[i][g4][jj]));
@@ -662,6 +663,29 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+  };
+  // The mask costs a subtract, a compare and a select per entry.  At D = 64,
+  // runs of blocks that need none (every block off the diagonal and inside
+  // the sequence) take a body without it; every wave still passes one
+  // barrier per block, whichever body it runs.  D = 128 keeps one body: with
+  // two, the compiler no longer holds its fixed register plan (the
+  // accumulators and K/V operands move between register files inside the
+  // products' stream).
+  if (nblocks > 0) {
+    if constexpr (!ASM) {
+      const fa::MaskRuns runs = fa::mask_runs(CAUSAL, L, qb0, per, key0, koff, kBN);
+      for (int t = 0; t < nblocks;) {
+        const int e = runs.run_end(t);
+        if (e > t) {
+          for (; t < e; ++t) step(t, std::false_type{});
+        } else {
+          step(t, std::true_type{});
+          ++t;
+        }
+      }
+    } else {
+      for (int t = 0; t < nblocks; ++t) step(t, std::true_type{});
     }
   }
 
@@ -999,7 +1023,9 @@ __global__ __launch_bounds__(WideCfg<D>::NW * kWave, 1) void fa_bwd_dkdv_wide(Bw
     for (int e = 0; e < 16; ++e) dv[dt][e] = 0.0f;
 
   if (nblocks > 0) issue(0);
-  for (int t = 0; t < nblocks; ++t) {
+  // Block t (masked: with the entry mask; runs of blocks as in fa_bwd_dkdv).
+  auto step = [&](int t, auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
     wait_vmcnt<0>();
     barrier_after_reads();
     if (t + 1 < nblocks) issue(t + 1);
@@ -1053,7 +1079,7 @@ __global__ __launch_bounds__(WideCfg<D>::NW * kWave, 1) void fa_bwd_dkdv_wide(Bw
             const int e = 4 * g4 + jj;
             const int off = 32 * i + 8 * g4 + jj;
             float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -(l4[jj] * kLog2e)));
-            p = ((unsigned)(off - lo_c) < span) ? p : 0.0f;
+            if constexpr (MASKED) p = ((unsigned)(off - lo_c) < span) ? p : 0.0f;
             const int tt = 2 * i + (e >> 3);
             p8[tt][e & 7] = (__bf16)p;
             ds8[tt][e & 7] = (__bf16)(p * (dp[i][e] - d4[jj]));
@@ -1069,6 +1095,24 @@ __global__ __launch_bounds__(WideCfg<D>::NW * kWave, 1) void fa_bwd_dkdv_wide(Bw
         for (int dt = 0; dt < NTK; ++dt)
           dk[dt] = mfma(ops.tr_d(b1, b2, tt, part * NTK + dt), ds8[tt], dk[dt]);
       }
+    }
+  };
+  // D = 256: mask-free runs as in fa_bwd_dkdv; the (192, 128) pair keeps one
+  // body (a second copy spills).
+  if (nblocks > 0) {
+    if constexpr (D == 256) {
+      const fa::MaskRuns runs = fa::mask_runs(CAUSAL, L, qb0, per, key0, koff, kBN);
+      for (int t = 0; t < nblocks;) {
+        const int e = runs.run_end(t);
+        if (e > t) {
+          for (; t < e; ++t) step(t, std::false_type{});
+        } else {
+          step(t, std::true_type{});
+          ++t;
+        }
+      }
+    } else {
+      for (int t = 0; t < nblocks; ++t) step(t, std::true_type{});
     }
   }
 

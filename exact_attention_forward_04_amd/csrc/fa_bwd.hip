@@ -413,9 +413,13 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_DQ * kWave, BwdCfg<D>::NW_DQ / 4) voi
 // ---------------------------------------------------------------------------
 // dK and dV: one tile of BN keys of K/V head hk.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool VARLEN>
+// FULL: the launch guarantees that no block needs the entry mask (dense,
+// non-causal, the query length a multiple of 64), so every block runs the
+// body without it.
+template <int D, bool CAUSAL, bool VARLEN, bool FULL = false>
 __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) void fa_bwd_dkdv(
     BwdArgs a) {
+  static_assert(!FULL || (!CAUSAL && !VARLEN), "mask-free launches are dense and non-causal");
   using C = BwdCfg<D>;
   constexpr int NW = C::NW_KV;
   constexpr int NS = D / 16;
@@ -673,7 +677,9 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
   // accumulators and K/V operands move between register files inside the
   // products' stream).
   if (nblocks > 0) {
-    if constexpr (!ASM) {
+    if constexpr (FULL) {
+      for (int t = 0; t < nblocks; ++t) step(t, std::false_type{});
+    } else if constexpr (!ASM) {
       const fa::MaskRuns runs = fa::mask_runs(CAUSAL, L, qb0, per, key0, koff, kBN);
       for (int t = 0; t < nblocks;) {
         const int e = runs.run_end(t);
@@ -1163,11 +1169,19 @@ int launch_bwd(const BwdArgs &a, hipStream_t st) {
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   auto k1 = fa_bwd_dq<D, CAUSAL, VARLEN>;
   auto k2 = fa_bwd_dkdv<D, CAUSAL, VARLEN>;
+  // D = 128 keeps one block body; a launch in which no block needs the mask
+  // takes the instance without it (D = 64 runs its mask-free blocks through a
+  // second body, which measured faster than this instance).
+  const bool full = D == 128 && !CAUSAL && !VARLEN && a.S % kBN == 0;
+  if constexpr (D == 128 && !CAUSAL && !VARLEN) {
+    if (full) k2 = fa_bwd_dkdv<D, false, false, true>;
+  }
   if (!allow_lds(k1, C::LDS_DQ) || !allow_lds(k2, C::LDS_KV)) return FA_ERR_HIP;
   FA_LOG_LAUNCH("fa_bwd_dq<D=%d causal=%d varlen=%d>: %lld workgroups x %d threads, %d B LDS; "
-                "fa_bwd_dkdv: %lld workgroups x %d threads, %d B LDS; B=%d H=%d H_kv=%d S_q=%d "
-                "S_k=%d",
-                D, (int)CAUSAL, (int)VARLEN, g1, C::NW_DQ * kWave, C::LDS_DQ, g2,
+                "fa_bwd_dkdv%s: %lld workgroups x %d threads, %d B LDS; B=%d H=%d H_kv=%d "
+                "S_q=%d S_k=%d",
+                D, (int)CAUSAL, (int)VARLEN, g1, C::NW_DQ * kWave, C::LDS_DQ,
+                full ? " (no block masked)" : "", g2,
                 C::NW_KV * kWave, C::LDS_KV, a.B, a.H, a.Hkv, a.S, a.Sk);
   // dQ first: it also writes Delta, which the dK/dV kernel reads.
   hipLaunchKernelGGL(k1, dim3((unsigned)g1), dim3(C::NW_DQ * kWave), C::LDS_DQ, st, a);
@@ -1190,6 +1204,7 @@ int launch_bwd_wide(const BwdArgs &a, hipStream_t st) {
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   auto k1 = fa_bwd_dq_wide<D, CAUSAL, VARLEN>;
   auto k2 = fa_bwd_dkdv_wide<D, CAUSAL, VARLEN>;
+
   if (!allow_lds(k1, C::LDS_DQ) || !allow_lds(k2, C::LDS_KV)) return FA_ERR_HIP;
   FA_LOG_LAUNCH("fa_bwd_dq_wide<D=%d D_v=%d causal=%d varlen=%d>: %lld workgroups x %d threads, "
                 "%d B LDS; fa_bwd_dkdv_wide: %lld workgroups x %d threads, %d B LDS, %d column "

@@ -541,8 +541,19 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
     constexpr bool MASKED = decltype(masked)::value;
     if (t + 2 < nblocks) issue(t + 2);
     wait_block(t + 2 < nblocks ? 2 : (t + 1 < nblocks ? 1 : 0));
-    barrier_nofence();
     const int m0 = (qb0 + t % per) * kBN;
+    if constexpr (ASM && CAUSAL) {
+      // A row without keys (r + koff < 0: more query rows than keys) has
+      // LSE = -inf, and every entry of it is masked.  The D = 128 body masks
+      // scores to -inf before the exponential, where -inf - (-inf) would give
+      // NaN, so wave 0, whose copy of the block's LSE has landed, sets such
+      // rows' LSE to +inf (P = exp2(-inf) = 0 either way) before the barrier.
+      if (wave == 0 && m0 < -koff) {
+        if (m0 + lane < -koff) ((float LDS_AS *)sbuf(t))[lane] = INFINITY;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+    }
+    barrier_nofence();
     if (active && (!CAUSAL || m0 + kBN - 1 >= key0 - koff)) {
       const unsigned qa = la.ky + lds_u32(qbuf(t));
       const unsigned ga = la.ky + lds_u32(gbuf(t));
@@ -550,8 +561,9 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
       const unsigned qt0 = la.vw0 + lds_u32(qbuf(t)), qt1 = la.vw1 + lds_u32(qbuf(t));
       const float LDS_AS *lse_l = (const float LDS_AS *)sbuf(t);
       const float LDS_AS *del_l = lse_l + kBN;
-      // The bounds of the masked body (blocks that need no mask run without
-      // it; a masked block off the diagonal gets bounds that keep every entry).
+      // Mask bounds for this wave's keys (a block that needs no mask gets
+      // bounds that keep every entry; D = 64 runs such blocks through a body
+      // without the mask, and D = 128 skips its score mask on them).
       const bool need_mask = (m0 + kBN > L) || (CAUSAL && m0 < key0 - koff + 31);
       const int hi = need_mask ? L - m0 - 4 * hh : INT_MAX;
       const int lo = (need_mask && CAUSAL) ? key - koff - m0 - 4 * hh : INT_MIN;
@@ -603,7 +615,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
           const int g4 = e >> 2, jj = e & 3;
           const int off = 32 * i + 8 * g4 + jj;
           float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -(l4[i][g4][jj] * kLog2e)));
-          if constexpr (MASKED) p = ((unsigned)(off - lo_c) < span) ? p : 0.0f;
+          if constexpr (MASKED && !ASM) p = ((unsigned)(off - lo_c) < span) ? p : 0.0f;
           const int tt = 2 * i + (e >> 3);
           p8[tt][e & 7] = (__bf16)p;
           ds8[tt][e & 7] = (__bf16)(p * (dp[i][e] - d4[i][g4][jj]));
@@ -611,6 +623,16 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
           // arithmetic can be moved down to the product that reads it
           // (which comes at least one step later).
           if ((e & 7) == 7) asm volatile("" : "+v"(p8[tt]), "+v"(ds8[tt]));
+        }
+      };
+      // Scores of sub-block i that the mask drops set to -inf (D = 128), so
+      // that P = exp2(c*s - log2(e)*LSE) = 0 (the LSE of a row without keys
+      // reads +inf here: see the block's start).
+      auto mask_scores = [&](int i) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int off = 32 * i + 8 * (e >> 2) + (e & 3);
+          s[i][e] = ((unsigned)(off - lo_c) < span) ? s[i][e] : -INFINITY;
         }
       };
       // Operands of step k: rows of Q and dO (phases A, B) or transposed
@@ -649,7 +671,16 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
         }
         if (valu) {
           // S/dP of sub-block ph-1 were produced by the products just before
-          if (st == 0) result_wait_v<ASM>(s[ph - 1], dp[ph - 1]);
+          if (st == 0) {
+            result_wait_v<ASM>(s[ph - 1], dp[ph - 1]);
+            // D = 128 masks the scores instead (-inf before the exponential
+            // gives the same P = 0), and only on blocks that need it: a
+            // wave-uniform branch around the sub-block's selects keeps one
+            // copy of the body, and with it the fixed register plan.
+            if constexpr (ASM && MASKED) {
+              if (need_mask) mask_scores(ph - 1);
+            }
+          }
           __builtin_amdgcn_sched_barrier(0);
           softmax_grad_part(ph - 1, EPS * st, EPS / 2);
           __builtin_amdgcn_sched_barrier(0);
@@ -669,13 +700,14 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_KV * kWave, BwdCfg<D>::NW_KV / 4) voi
       }
     }
   };
-  // The mask costs a subtract, a compare and a select per entry.  At D = 64,
-  // runs of blocks that need none (every block off the diagonal and inside
-  // the sequence) take a body without it; every wave still passes one
-  // barrier per block, whichever body it runs.  D = 128 keeps one body: with
-  // two, the compiler no longer holds its fixed register plan (the
-  // accumulators and K/V operands move between register files inside the
-  // products' stream).
+  // The mask costs a subtract, a compare and a select per entry, and only
+  // the diagonal and tail blocks need it.  D = 64 runs the blocks that need
+  // none (one run per query head, fa_mask_runs.h) through a second copy of
+  // the body without it; every wave still passes one barrier per block,
+  // whichever body it runs.  D = 128 keeps one body (with two, the compiler
+  // no longer holds its fixed register plan: the accumulators and K/V move
+  // between register files inside the products' stream); it masks scores
+  // behind a wave-uniform branch instead (mask_scores).
   if (nblocks > 0) {
     if constexpr (FULL) {
       for (int t = 0; t < nblocks; ++t) step(t, std::false_type{});
@@ -1029,9 +1061,7 @@ __global__ __launch_bounds__(WideCfg<D>::NW * kWave, 1) void fa_bwd_dkdv_wide(Bw
     for (int e = 0; e < 16; ++e) dv[dt][e] = 0.0f;
 
   if (nblocks > 0) issue(0);
-  // Block t (masked: with the entry mask; runs of blocks as in fa_bwd_dkdv).
-  auto step = [&](int t, auto masked) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked)::value;
+  for (int t = 0; t < nblocks; ++t) {
     wait_vmcnt<0>();
     barrier_after_reads();
     if (t + 1 < nblocks) issue(t + 1);
@@ -1085,7 +1115,7 @@ __global__ __launch_bounds__(WideCfg<D>::NW * kWave, 1) void fa_bwd_dkdv_wide(Bw
             const int e = 4 * g4 + jj;
             const int off = 32 * i + 8 * g4 + jj;
             float p = exp2_hw(__builtin_fmaf(s[i][e], a.c, -(l4[jj] * kLog2e)));
-            if constexpr (MASKED) p = ((unsigned)(off - lo_c) < span) ? p : 0.0f;
+            p = ((unsigned)(off - lo_c) < span) ? p : 0.0f;
             const int tt = 2 * i + (e >> 3);
             p8[tt][e & 7] = (__bf16)p;
             ds8[tt][e & 7] = (__bf16)(p * (dp[i][e] - d4[jj]));
@@ -1101,24 +1131,6 @@ __global__ __launch_bounds__(WideCfg<D>::NW * kWave, 1) void fa_bwd_dkdv_wide(Bw
         for (int dt = 0; dt < NTK; ++dt)
           dk[dt] = mfma(ops.tr_d(b1, b2, tt, part * NTK + dt), ds8[tt], dk[dt]);
       }
-    }
-  };
-  // D = 256: mask-free runs as in fa_bwd_dkdv; the (192, 128) pair keeps one
-  // body (a second copy spills).
-  if (nblocks > 0) {
-    if constexpr (D == 256) {
-      const fa::MaskRuns runs = fa::mask_runs(CAUSAL, L, qb0, per, key0, koff, kBN);
-      for (int t = 0; t < nblocks;) {
-        const int e = runs.run_end(t);
-        if (e > t) {
-          for (; t < e; ++t) step(t, std::false_type{});
-        } else {
-          step(t, std::true_type{});
-          ++t;
-        }
-      }
-    } else {
-      for (int t = 0; t < nblocks; ++t) step(t, std::true_type{});
     }
   }
 

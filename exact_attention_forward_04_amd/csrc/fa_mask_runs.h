@@ -1,14 +1,14 @@
 // fa_mask_runs.h -- which query blocks of a dK/dV key tile need the entry
 // mask (host and device).
 //
-// The dK/dV kernels visit, for each query head of a K/V group, the 64-row
+// The dK/dV kernel visits, for each query head of a K/V group, the 64-row
 // query blocks i = 0 .. per-1 (rows m0 = (qb0 + i) * bn ..), against one
 // wave's 32 keys key0 .. key0+31.  A block needs the entry mask when one of
 // its rows lies past the sequence end (m0 + bn > L) or, under the causal
 // mask (bottom-right aligned: row r may use key j when j <= r + koff), when
 // it starts before the diagonal of the wave's last key (m0 < key0 + 31 -
 // koff).  Rows only grow with i, so the blocks i1 <= i < i2 of each head
-// need no mask: the kernels run those through a body without it.
+// need no mask: at D = 64 the kernel runs those through a body without it.
 #pragma once
 
 #ifndef FA_HD

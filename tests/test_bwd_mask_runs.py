@@ -1,7 +1,7 @@
 """The dK/dV kernels' split of query blocks into masked and mask-free runs (CPU).
 
-The D = 64 and D = 256 dK/dV kernels run the query blocks that need no entry
-mask through a body without it (fa_mask_runs.h).  A block taken as mask-free
+The D = 64 dK/dV kernel runs the query blocks that need no entry mask through
+a body without it (fa_mask_runs.h).  A block taken as mask-free
 that does need the mask would give wrong gradients; a block taken as masked
 that needs none only costs time.  This test compiles the header with the
 host compiler and walks the kernels' loop over many tile shapes, checking

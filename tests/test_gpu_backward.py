@@ -72,6 +72,19 @@ def test_backward_small(D, causal):
     full_bwd_check(q, k, v, g, causal, D ** -0.5, what="bwd-small D%d" % D)
 
 
+# S = 512: whole 64-row blocks, so a dense non-causal D = 128 launch takes the
+# dK/dV instance without the entry mask, and D = 64 runs every block of a key
+# tile through the mask-free body; causal, each wave's diagonal blocks sit
+# between mask-free runs, over two query heads per K/V head.
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_whole_blocks(D, causal):
+    B, S, H, H_kv = 1, 512, 4, 2
+    q, k, v = draw_qkv((B, S, H, D), seed=131 + D, kv_heads=H_kv)
+    g = draw_dout((B, S, H, D), seed=132 + D)
+    full_bwd_check(q, k, v, g, causal, D ** -0.5, what="bwd-whole-blocks D%d" % D)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_backward_short_sequences(D):
     """S below one block (and a single row): tails only."""

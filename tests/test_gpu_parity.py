@@ -158,6 +158,34 @@ def test_named_sampled(name, n):
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
 
 
+# ---- the longest sequences: 64-bit row offsets, hundreds to thousands of key
+# blocks per tile, and (varlen) a long sequence packed with short ones, the
+# long one's tiles scheduled first.  Sampled rows include both ends of each
+# head and every sequence boundary.
+LONGEST = [
+    Workload("long_b1h2s131072d128_causal", 1, 131072, 2, 128, True, seed=31),
+    Workload("long_varlen_131072_300_4097_h2d128_causal", 3, 131072, 2, 128, True, seed=32,
+             lengths=(131072, 300, 4097)),
+    Workload("long_b1h1s65536d256_causal", 1, 65536, 1, 256, True, seed=33),
+]
+
+
+@pytest.mark.parametrize("w", LONGEST, ids=lambda w: w.name)
+def test_longest_sequences_sampled(w):
+    note(w.name, "generating inputs")
+    q, k, v, cu, S = make(w)
+    note(w.name, "gpu run")
+    o, lse = run_gpu(q, k, v, w.causal, w.scale, cu, S if cu is not None else None)
+    rows = sample_rows(w, cu, 128, seed=w.seed)
+    note(w.name, "oracle on", len(rows), "rows")
+    o_ref, lse_ref = oracle.attention_rows_bf16(q, k, v, rows, w.scale, w.causal, cu)
+    o_g, lse_g = gather_rows(o, lse, rows, w, cu)
+    st = compare(o_g, lse_g, o_ref, lse_ref)
+    note(w.name, st)
+    assert_close(st, w.name)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
 # ---- every output of the full-size workloads against an fp32 reference
 # computed on the GPU with torch (its error, ~1e-6, is far below the gate).  This
 # complements the sampled oracle rows above: the bf16 rounding of P makes the

@@ -158,9 +158,8 @@ def test_named_sampled(name, n):
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
 
 
-# ---- the longest sequences: 64-bit row offsets, hundreds to thousands of key
-# blocks per tile, and (varlen) a long sequence packed with short ones, the
-# long one's tiles scheduled first.  Sampled rows include both ends of each
+# ---- the longest sequences: up to 2048 key blocks per tile, and (varlen) a
+# long sequence packed with short ones, the long one's tiles scheduled first.  Sampled rows include both ends of each
 # head and every sequence boundary.
 LONGEST = [
     Workload("long_b1h2s131072d128_causal", 1, 131072, 2, 128, True, seed=31),

@@ -118,16 +118,18 @@ def sample_rows(w, cu, n, seed):
 
 
 def gather_rows(o, lse, rows, w, cu):
-    o = tensor_to_f64(o)
-    lse = tensor_to_f64(lse)
+    """The sampled rows of O and LSE as float64 arrays (indexed on the
+    device, so only those rows are copied)."""
+    def take(x, *idx):
+        return tensor_to_f64(x[tuple(torch.as_tensor(i, device=x.device) for i in idx)])
     if cu is None:
         b = rows // (w.H * w.S)
         h = (rows // w.S) % w.H
         i = rows % w.S
-        return o[b, i, h], lse[b, h, i]
+        return take(o, b, i, h), take(lse, b, h, i)
     T = int(cu[-1])
     h, t = rows // T, rows % T
-    return o[t, h], lse[h, t]
+    return take(o, t, h), take(lse, h, t)
 
 
 @pytest.mark.parametrize("name,n", [
@@ -171,6 +173,19 @@ LONGEST = [
 
 @pytest.mark.parametrize("w", LONGEST, ids=lambda w: w.name)
 def test_longest_sequences_sampled(w):
+    _sampled_check(w)
+
+
+# ---- the largest tensors: 1040 sequences of 1024 tokens, 8 query heads on one
+# K/V head, so that Q and O hold 2.18e9 bytes and the rows of the last
+# sequences (among the sampled rows: the end of the last head) sit past 2^31
+# bytes from the tensor start.
+def test_largest_tensors_sampled():
+    w = Workload("big_b1040h8kv1s1024d128_causal", 1040, 1024, 8, 128, True, seed=34, Hkv=1)
+    _sampled_check(w)
+
+
+def _sampled_check(w):
     note(w.name, "generating inputs")
     q, k, v, cu, S = make(w)
     note(w.name, "gpu run")

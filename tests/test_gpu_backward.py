@@ -181,6 +181,43 @@ def test_backward_8k_causal_sampled():
         assert_grad_close(st, ("bwd-8k", name))
 
 
+def test_backward_largest_tensors_sampled():
+    """1040 sequences of 1024 tokens, 8 query heads on one K/V head, causal:
+    Q, O, dO and dQ hold 2.18e9 bytes, and the rows at the end of the last
+    sequence sit past 2^31 bytes from the tensor start.  Gradient rows are
+    gathered on the device and compared with the oracle row by row."""
+    B, S, H, Hkv, D = 1040, 1024, 8, 1, 128
+    scale = D ** -0.5
+    q, k, v = draw_qkv((B, S, H, D), seed=141, kv_heads=Hkv)
+    g = draw_dout((B, S, H, D), seed=141)
+    note("bwd-largest gpu run")
+    dq_, dk_, dv_, dg = (t.cuda() for t in (q, k, v, g))
+    o, lse = fa.attention(dq_, dk_, dv_, causal=True, scale=scale)
+    dq, dk, dv = fa.attention_backward(dq_, dk_, dv_, o, lse, dg, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    last = B - 1
+    q_idx = [(last, H - 1, i) for i in (0, 1, 511, S - 2, S - 1)] + \
+            [(last, 3, 700), (0, 0, 0), (517, 2, 33)]
+    k_idx = [(last, j) for j in (0, 63, 64, 700, S - 1)] + [(3, 10)]
+    q_rows = [(b * H + h) * S + i for b, h, i in q_idx]
+    k_rows = [(b * Hkv) * S + j for b, j in k_idx]
+    note("bwd-largest oracle rows", len(q_rows), len(k_rows))
+    rdq, rdqm, rdk, rdv, rdkm, rdvm = oracle.attention_backward_rows_bf16(
+        q, k, v, g, q_rows, k_rows, scale, True)
+
+    def take(x, idx):
+        cols = [torch.as_tensor(c, device=x.device) for c in zip(*idx)]
+        return tensor_to_f64(x[tuple(cols)])
+    sel_q = take(dq, [(b, i, h) for b, h, i in q_idx])
+    sel_k = take(dk, [(b, j, 0) for b, j in k_idx])
+    sel_v = take(dv, [(b, j, 0) for b, j in k_idx])
+    for name, gg, rr, mm in (("dq", sel_q, rdq, rdqm), ("dk", sel_k, rdk, rdkm),
+                             ("dv", sel_v, rdv, rdvm)):
+        st = compare_grad(gg, rr, mm)
+        note("bwd-largest", name, st)
+        assert_grad_close(st, ("bwd-largest", name))
+
+
 # ---- query and key lengths that differ (fa_bwd_general; bottom-right causal)
 def gpu_grads_general(q, k, v, g, causal, scale, cu=None, cu_k=None, S=None, S_k=None):
     dq_, dk_, dv_, dg = (t.cuda() for t in (q, k, v, g))

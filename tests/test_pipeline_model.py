@@ -10,7 +10,12 @@ timings:
 - the ping-pong body (eight waves in two halves, a four-slot ring of K|V
   blocks, copies two intervals ahead, issued from the softmax phase);
 - the pipelined single-wave body (four waves, K in two slots and V in three,
-  block j+1 copied when iteration j opens).
+  block j+1 copied when iteration j opens);
+- the serial double-buffered body (variable-length batches at D = 256);
+- the backward's rings: the dQ and dK/dV kernels (four slots, copies two
+  blocks ahead, the dK/dV kernel's LSE and Delta copies by waves 0 and 1,
+  and wave 0's write of the LSE of rows without keys before the barrier),
+  and the wide-head kernels' two-slot ring.
 
 Each wave is a sequence of actions in the kernel's order (copy issue, vmcnt
 waits, barriers, LDS reads with a duration).  A copy's share lands after a
@@ -32,8 +37,9 @@ class Violation(Exception):
 
 
 class Model:
-    def __init__(self, waves, rng, latency, slow_wave=None, slow_factor=1.0):
+    def __init__(self, waves, rng, latency, slow_wave=None, slow_factor=1.0, owners=None):
         self.waves = waves
+        self.owners = owners or {}  # kind -> the waves that write it (default: every wave)
         self.rng = rng
         self.latency = latency
         self.slow_wave = slow_wave
@@ -83,6 +89,10 @@ class Model:
                 issued[w].append(land)
                 self.lands.setdefault((kind, slot), []).append((land, w, tag))
                 t[w] += 1.0
+            elif op == "write":  # an LDS store of the wave itself, waited for at once
+                _, kind, slot, tag = act
+                self.lands.setdefault((kind, slot), []).append((t[w] + 1.0, w, tag))
+                t[w] += 2.0
             elif op == "wait":  # s_waitcnt vmcnt(max_outstanding)
                 keep = act[1]
                 done = issued[w][: max(0, len(issued[w]) - keep)]
@@ -97,7 +107,7 @@ class Model:
 
     def check_read(self, reader, kind, slot, tag, t0, t1):
         events = self.lands.get((kind, slot), [])
-        for owner in range(self.waves):
+        for owner in self.owners.get(kind, range(self.waves)):
             mine = [e for e in events if e[1] == owner]
             before = [e for e in mine if e[0] <= t0]
             if not before or max(before)[2] != tag:
@@ -228,6 +238,102 @@ def serial_programs(tiles, end_barrier=True):
             p.append(("compute", 50, 200))
         progs.append(p)
     return progs
+
+
+# ---- the backward's rings
+
+def bwd_programs(n, stats=False, lse_fix=(), fix_after_barrier=False, slots=4):
+    """dQ (stats=False) or dK/dV (stats=True) kernel at D <= 128: four waves,
+    a ring of `slots` slots, block j+2 copied at the top of iteration j, one
+    barrier per block and none at its end.  In dK/dV, wave 0 copies the
+    block's LSE and wave 1 its Delta; for the blocks in lse_fix, wave 0 then
+    overwrites the LSE of rows without keys, before the barrier."""
+    progs = []
+    for w in range(4):
+        p = []
+
+        def issue(j):
+            p.append(("issue", "Q", j % slots, j))
+            p.append(("issue", "G", j % slots, j))
+            if stats and w < 2:
+                p.append(("issue", "L" if w == 0 else "E", j % slots, j))
+        per_block = 2 + (1 if stats and w < 2 else 0)
+        for j in range(min(n, 2)):
+            issue(j)
+        for j in range(n):
+            if j + 2 < n:
+                issue(j + 2)
+                p.append(("wait", 2 * per_block))
+            elif j + 1 < n:
+                p.append(("wait", per_block))
+            else:
+                p.append(("wait", 0))
+            fix = stats and w == 0 and j in lse_fix
+            if fix and not fix_after_barrier:
+                p.append(("write", "L", j % slots, (j, "fixed")))
+            p.append(("barrier",))
+            if fix and fix_after_barrier:
+                p.append(("write", "L", j % slots, (j, "fixed")))
+            if stats:
+                lt = (j, "fixed") if j in lse_fix else j
+                p.append(("read", "L", j % slots, lt, 20, 60))
+                p.append(("read", "E", j % slots, j, 20, 60))
+            p.append(("read", "Q", j % slots, j, 800, 1400))
+            p.append(("compute", 300, 900))
+            p.append(("read", "G", j % slots, j, 800, 1400))
+        progs.append(p)
+    return progs
+
+
+def wide_bwd_programs(n, slots=2):
+    """The wide-head backward kernels: a two-slot ring; block j+1 copied
+    right after the barrier (which drains the wave's LDS reads) that opens
+    block j, into the slot of block j-1."""
+    progs = []
+    for w in range(4):
+        p = []
+        if n > 0:
+            p.append(("issue", "Q", 0, 0))
+        for j in range(n):
+            p.append(("wait", 0))
+            p.append(("barrier",))
+            if j + 1 < n:
+                p.append(("issue", "Q", (j + 1) % slots, j + 1))
+            p.append(("read", "Q", j % slots, j, 1500, 3000))
+        progs.append(p)
+    return progs
+
+
+BWD_OWNERS = {"L": [0], "E": [1]}
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 9])
+@pytest.mark.parametrize("stats", [False, True], ids=["dq", "dkdv"])
+def test_backward_ring_protocols_have_no_race(n, stats):
+    fixes = (0, 1) if stats else ()
+    for seed in range(60):
+        rng = random.Random(seed * 31 + n)
+        lat = (rng.choice([200, 1500]), rng.choice([2500, 6000]))
+        slow = rng.randrange(4) if seed % 3 == 0 else None
+        Model(4, rng, lat, slow, rng.uniform(1.0, 4.0), BWD_OWNERS).run(
+            bwd_programs(n, stats, lse_fix=fixes))
+        Model(4, rng, lat, slow, rng.uniform(1.0, 4.0)).run(wide_bwd_programs(n))
+
+
+def test_model_finds_backward_protocol_mutations():
+    """Planted mutations: the keyless rows' LSE written after the barrier
+    (another wave may read the block's LSE first), a three-slot ring with
+    copies two blocks ahead, and a one-slot wide ring."""
+    def finds(progs, owners=None, slow=2):
+        for seed in range(200):
+            try:
+                Model(4, random.Random(seed), (10, 50), slow, 6.0, owners).run(progs)
+            except Violation:
+                return True
+        return False
+    assert finds(bwd_programs(4, True, lse_fix=(0,), fix_after_barrier=True), BWD_OWNERS, slow=0)
+    assert finds(bwd_programs(6, False, slots=3))
+    assert finds(wide_bwd_programs(4, slots=1))
 
 
 TILE_SETS = [[1], [2], [3], [5], [9], [4, 3], [2, 7, 1], [5, 5, 6], [8, 1, 2, 3]]

@@ -69,16 +69,15 @@ def load(path: str = LIB_PATH):
 
 
 def load_sync_debug(path: str = _build.SYNC_DEBUG_LIB_PATH):
-    """The race-check build of the forward (FA_SYNC_DEBUG: every wait drains
-    every counter, barriers between the pipeline phases), for tests that
-    compare it bit for bit with load()'s library.  Holds the forward entry
-    points only."""
+    """The race-check build of the forward and backward (FA_SYNC_DEBUG: every
+    wait drains every counter, barriers between the pipeline phases), for
+    tests that compare it bit for bit with load()'s library."""
     if not os.path.exists(path):
         _build.build(path, defines=("FA_SYNC_DEBUG",), sources=_build.SYNC_DEBUG_SOURCES)
-    return _declare(ctypes.CDLL(path), backward=False)
+    return _declare(ctypes.CDLL(path))
 
 
-def _declare(lib, backward: bool = True):
+def _declare(lib):
     """Argument and result types of the library's entry points."""
     P, I, F, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_longlong
     lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P]
@@ -103,13 +102,12 @@ def _declare(lib, backward: bool = True):
     lib.fa_splitkv_auto_splits.restype = I
     lib.fa_splitkv_auto_splits_gqa.argtypes = [I, I, I, I, I, I, ctypes.POINTER(I)]
     lib.fa_splitkv_auto_splits_gqa.restype = I
-    if backward:
-        lib.fa_bwd.argtypes = [P] * 10 + [I, I, I, I, I, F, I, P, P]
-        lib.fa_bwd.restype = I
-        lib.fa_bwd_general.argtypes = [P] * 10 + [I, I, I, I, I, I, F, I, P, P, P]
-        lib.fa_bwd_general.restype = I
-        lib.fa_bwd_hd.argtypes = [P] * 10 + [I, I, I, I, I, I, I, F, I, P, P, P]
-        lib.fa_bwd_hd.restype = I
+    lib.fa_bwd.argtypes = [P] * 10 + [I, I, I, I, I, F, I, P, P]
+    lib.fa_bwd.restype = I
+    lib.fa_bwd_general.argtypes = [P] * 10 + [I, I, I, I, I, I, F, I, P, P, P]
+    lib.fa_bwd_general.restype = I
+    lib.fa_bwd_hd.argtypes = [P] * 10 + [I, I, I, I, I, I, I, F, I, P, P, P]
+    lib.fa_bwd_hd.restype = I
     lib.fa_tuning_default.argtypes = []
     lib.fa_tuning_default.restype = Tuning
     lib.fa_exp2_emu.argtypes = [P, P, LL, P]

@@ -3,7 +3,7 @@
 hipcc compiles csrc/fa_fwd.hip (forward) and csrc/fa_bwd.hip (backward) for
 gfx950 into a shared library that sits next to this file; the Python binding
 loads it with ctypes.  A second library, libfa_mi355x_syncdebug.so, holds the
-forward built with FA_SYNC_DEBUG for the race check.  Packed-FP32
+same kernels built with FA_SYNC_DEBUG for the race check.  Packed-FP32
 instruction selection is disabled (-packed-fp32-ops) on purpose.
 """
 from __future__ import annotations
@@ -20,11 +20,11 @@ HEADERS = [os.path.join(CSRC, n) for n in ("fa_sched.h", "exp2_poly.h", "fa_tile
           [os.path.join(ROOT, "include", "fa.h")]
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-# The race-check build of the forward: the same kernels compiled with
+# The race-check build: the forward and backward kernels compiled with
 # FA_SYNC_DEBUG (every wait drains every counter, barriers between the
 # pipeline's phases); its results must equal libfa_mi355x.so's bit for bit.
 SYNC_DEBUG_LIB_PATH = os.path.join(HERE, "libfa_mi355x_syncdebug.so")
-SYNC_DEBUG_SOURCES = [SOURCES[0]]
+SYNC_DEBUG_SOURCES = list(SOURCES)
 TARGETS = [(LIB_PATH, SOURCES, ()),
            (SYNC_DEBUG_LIB_PATH, SYNC_DEBUG_SOURCES, ("FA_SYNC_DEBUG",))]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -11,6 +11,11 @@ phases.  Both builds compute the same values in the same order, so a block
 read before its copy landed, or overwritten while another wave still read
 it, would make their outputs differ.  Every case below must be bitwise
 equal, through the C ABI of each library.
+
+The backward's rings (the dQ kernel's K/V ring, the dK/dV kernels' Q/dO
+ring with their LSE and Delta copies) use the same waits and barriers, and
+the race-check library holds them too: its dQ, dK, dV and Delta must equal
+the pipelined build's bit for bit as well.
 """
 import ctypes
 import sys
@@ -20,7 +25,7 @@ import pytest
 import torch
 
 import exact_attention_forward_04_amd as fa
-from attn_inputs import WORKLOADS, cu_seqlens_of, draw_qkv, make, make_qk
+from attn_inputs import WORKLOADS, cu_seqlens_of, draw_dout, draw_qkv, make, make_qk
 
 pytestmark = pytest.mark.gpu
 
@@ -128,3 +133,75 @@ def test_race_check_mixed_and_splitkv(libs):
                 cu_q=dcq, cu_k=dck)
     assert_same(libs, "mixed split-KV x4", dq, dk, dv, B, w.H, w.kv_heads, Sq, Sk, w.D, w.D,
                 True, cu_q=dcq, cu_k=dck, splits=4)
+
+
+def run_backward(lib, q, k, v, o, lse, g, B, H, Hkv, Sq, Sk, D, Dv, causal, cu_q=None,
+                 cu_k=None):
+    nan = float("nan")
+    dq, dk, dv = (torch.full_like(t, nan) for t in (q, k, v))
+    delta = torch.full_like(lse, nan)
+    cq = cu_q.data_ptr() if cu_q is not None else None
+    ck = cu_k.data_ptr() if cu_k is not None else None
+    rc = lib.fa_bwd_hd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), g.data_ptr(),
+                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       delta.data_ptr(), B, H, Hkv, Sq, Sk, D, Dv, D ** -0.5, int(causal), cq, ck,
+                       torch.cuda.current_stream().cuda_stream)
+    assert rc == fa.FA_OK, fa.status_string(rc)
+    torch.cuda.synchronize()
+    return dq, dk, dv, delta
+
+
+def bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+# (D, D_v, causal, H, H_kv, query lengths, key lengths); one length each is a
+# dense batch of one sequence, several a packed (varlen) batch.
+BWD_CASES = [
+    (128, 128, True, 4, 2, [2000], [2000]),        # dQ ring; dK/dV D=128 with the score mask
+    (128, 128, False, 4, 4, [2048], [2048]),       # dK/dV instance with no masked block
+    (128, 128, True, 4, 1, [333, 1, 700, 64, 0], [130, 50, 900, 64, 10]),  # rows without keys
+    (64, 64, True, 4, 2, [1500], [1500]),          # masked and mask-free runs
+    (64, 64, True, 2, 2, [700, 257, 1024], [300, 257, 1500]),
+    (256, 256, True, 2, 2, [1100], [1100]),        # the wide kernels' two-slot rings
+    (192, 128, True, 2, 1, [1000], [1000]),
+]
+
+
+def _bwd_id(c):
+    D, Dv, causal, H, Hkv, lq, lk = c
+    lay = "s%d" % lq[0] if len(lq) == 1 else "varlen%d" % len(lq)
+    own = "" if lq == lk else "-ownk"
+    return "d%dv%d-%s-h%dkv%d-%s%s" % (D, Dv, "c" if causal else "n", H, Hkv, lay, own)
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=_bwd_id)
+def test_race_check_backward(libs, case):
+    fast, debug = libs
+    D, Dv, causal, H, Hkv, lq, lk = case
+    what = "backward " + _bwd_id(case)
+    note("race-check", what)
+    seed = 420 + D + sum(lq)
+    if len(lq) == 1:
+        B, Sq, Sk = 1, lq[0], lk[0]
+        q, _, _ = draw_qkv((B, Sq, H, D), seed)
+        _, k, v = draw_qkv((B, Sk, H, D), seed + 1, kv_heads=Hkv, v_dim=Dv)
+        dcq = dck = None
+    else:
+        B, Sq, Sk = len(lq), max(lq), max(lk)
+        cq, ck = cu_seqlens_of(lq), cu_seqlens_of(lk)
+        q, _, _ = draw_qkv((int(cq[-1]), H, D), seed)
+        _, k, v = draw_qkv((int(ck[-1]), H, D), seed + 1, kv_heads=Hkv, v_dim=Dv)
+        dcq = torch.from_numpy(np.asarray(cq, np.int32)).cuda()
+        dck = torch.from_numpy(np.asarray(ck, np.int32)).cuda()
+    q, k, v = (t.cuda() for t in (q, k, v))
+    o, lse = run_general(fast, q, k, v, B, H, Hkv, Sq, Sk, D, Dv, causal, cu_q=dcq, cu_k=dck)
+    g = draw_dout(tuple(o.shape), seed + 2).cuda()
+    r1 = run_backward(fast, q, k, v, o, lse, g, B, H, Hkv, Sq, Sk, D, Dv, causal, dcq, dck)
+    r2 = run_backward(debug, q, k, v, o, lse, g, B, H, Hkv, Sq, Sk, D, Dv, causal, dcq, dck)
+    for name, a, b in zip(("dq", "dk", "dv", "delta"), r1, r2):
+        diff = int((bits(a) != bits(b)).sum().item())
+        note(what, name, "elements differing", diff, "of", a.numel())
+        assert diff == 0, (what, name)
+        # the buffers start as NaN: every element must have been written
+        assert not torch.isnan(a.float()).any(), (what, name, "unwritten elements")

@@ -205,3 +205,24 @@ def test_race_check_backward(libs, case):
         assert diff == 0, (what, name)
         # the buffers start as NaN: every element must have been written
         assert not torch.isnan(a.float()).any(), (what, name, "unwritten elements")
+
+
+@pytest.mark.parametrize("name", ["causal_b2h16s8192d128", "gqa_b2h32kv8s8192d128_causal"])
+def test_race_check_backward_workloads(libs, name):
+    """The 8k backward workloads: every CU runs many key and query tiles."""
+    fast, debug = libs
+    w = WORKLOADS[name]
+    what = "backward " + name
+    note("race-check", what)
+    q, k, v, _, S = make(w)
+    q, k, v = (t.cuda() for t in (q, k, v))
+    o, lse = run_general(fast, q, k, v, w.B, w.H, w.kv_heads, S, S, w.D, w.D, w.causal)
+    g = draw_dout(tuple(o.shape), 430).cuda()
+    args = (w.B, w.H, w.kv_heads, S, S, w.D, w.D, w.causal)
+    r1 = run_backward(fast, q, k, v, o, lse, g, *args)
+    r2 = run_backward(debug, q, k, v, o, lse, g, *args)
+    for name_, a, b in zip(("dq", "dk", "dv", "delta"), r1, r2):
+        diff = int((bits(a) != bits(b)).sum().item())
+        note(what, name_, "elements differing", diff, "of", a.numel())
+        assert diff == 0, (what, name_)
+        assert not torch.isnan(a.float()).any(), (what, name_, "unwritten elements")
